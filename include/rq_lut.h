@@ -1,0 +1,204 @@
+/*
+ * rq_lut.h -- C ABI of librq_lut.so: serving residual product-quantized (RQ)
+ * matrices on an MI355X (gfx950) without ever rebuilding the dense matrix.
+ *
+ * The operations are the ones the Gemma-2-2B runtime-compression page
+ * describes in its "LUT serving" paragraph, for the tied embedding / LM head
+ * coded with M=384 subspaces, K=1024 codewords and L=2 residual levels:
+ *   - output logits by lookup+sum in place of a full matmul, handed to
+ *     Gemma-2's own softcap            -> rq_build_lut + rq_lut_logits
+ *   - input rows reconstructed on demand, a handful per prompt
+ *                                      -> rq_decode_rows
+ * and the non-materialising path for RQ-coded MLP weights that the Gemma-2-2B
+ * MLP RQ page names as its natural follow-up   -> rq_lut_matvec.
+ *
+ * The coded matrix. W[rows][D] with D = M*d is split into M contiguous
+ * subspaces of width d; row r's subvector in subspace m is the sum over L
+ * residual levels of one codeword per level from that level's own codebook:
+ *     W[r][m*d + j] = sum_{l<L} C[l][m][ codes[r][l][m] ][j].
+ * (Residual PQ: runtime-compression page, opening and LUT-serving
+ * paragraphs; one codebook per level and subspace is what makes the page's
+ * 412 MB artifact add up.)
+ *
+ * Conventions for every entry point:
+ *   - Memory. All array pointers are DEVICE pointers owned by the caller. The
+ *     library allocates nothing, keeps no state between calls (apart from the
+ *     thread-local text behind rq_last_error) and never synchronises: work is
+ *     enqueued on `stream` and completes asynchronously.
+ *   - Errors. Arguments are checked on the host before anything is launched;
+ *     a failed check returns a negative rq_status and enqueues nothing. A
+ *     failed launch returns RQ_ERR_HIP. rq_last_error() describes the last
+ *     failure on the calling thread.
+ *   - Empty work. B == 0, n == 0 or rows == 0 return RQ_OK and enqueue
+ *     nothing.
+ *   - Codes must be < K; larger codes are a precondition violation (the
+ *     kernels do not check them, except rq_decode_rows which clamps nothing
+ *     and is equally undefined).
+ *   - Alignment. codes, lut, x, x2 and all outputs must be 16-byte aligned,
+ *     workspaces 256-byte aligned (torch allocations satisfy this).
+ *   - Concurrency. Calls on different streams may run concurrently as long as
+ *     they do not share output or workspace buffers.
+ */
+#ifndef RQ_LUT_H
+#define RQ_LUT_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rq_status {
+  RQ_OK = 0,
+  RQ_ERR_NULL = -1,       /* a required pointer is NULL                        */
+  RQ_ERR_SHAPE = -2,      /* inconsistent or unsupported sizes                 */
+  RQ_ERR_DTYPE = -3,      /* unknown dtype / prologue value                    */
+  RQ_ERR_ALIGN = -4,      /* a pointer misses its required alignment           */
+  RQ_ERR_WORKSPACE = -5,  /* workspace NULL or smaller than the query returned */
+  RQ_ERR_HIP = -6         /* a HIP launch failed                               */
+} rq_status;
+
+typedef enum rq_dtype { RQ_F32 = 0, RQ_BF16 = 1 } rq_dtype;
+
+typedef enum rq_prologue {
+  RQ_PRO_NONE = 0,          /* the activation is x                                    */
+  RQ_PRO_GELU_TANH_MUL = 1  /* the activation is gelu_tanh(x) * x2 (Gemma-2 MLP down) */
+} rq_prologue;
+
+/*
+ * Non-owning description of one RQ-coded matrix W[rows][D].
+ *   rows       vocabulary size V for a head, out_features for an MLP matrix
+ *   D, M, d    D == M*d, all >= 1
+ *   K          codewords per codebook, 1 <= K <= 65536 (but see RQ_MAX_K_F32)
+ *   L          residual levels, 1 <= L <= 16
+ *   cb_dtype   RQ_F32 or RQ_BF16, the storage type of the codebooks
+ *   codebooks  device [L][M][K][d] of cb_dtype
+ *   codes      device uint16 [rows][L][M], row-major, 16-byte aligned
+ */
+typedef struct rq_matrix {
+  int64_t rows;
+  int32_t D, M, d, K, L;
+  int32_t cb_dtype;
+  const void* codebooks;
+  const uint16_t* codes;
+} rq_matrix;
+
+/* Largest K whose per-subspace table (K entries) fits the kernels' on-chip
+ * staging: 32768 for fp32 tables, 65536 for bf16 tables. */
+#define RQ_MAX_K_F32 32768
+#define RQ_MAX_K_BF16 65536
+#define RQ_MAX_L 16
+
+/*
+ * Bytes of the lookup table rq_build_lut writes for B activation vectors:
+ * L*M*K*B elements of lut_dtype. Returns 0 for invalid arguments.
+ */
+size_t rq_lut_bytes(const rq_matrix* W, int32_t B, int32_t lut_dtype);
+
+/*
+ * Build the lookup table of each activation vector (runtime-compression page,
+ * LUT-serving paragraph: logits by lookup+sum):
+ *     LUT[l][m][k][b] = sum_{j<d} a[b][m*d + j] * C[l][m][k][j]
+ * with a = x (prologue RQ_PRO_NONE) or a = gelu_tanh(x) * x2 elementwise
+ * (RQ_PRO_GELU_TANH_MUL; gelu_tanh(t) = 0.5 t (1 + tanh(sqrt(2/pi) (t +
+ * 0.044715 t^3)))), computed in fp32 and stored as lut_dtype (bf16: round to
+ * nearest even).
+ *   x, x2   device fp32 [B][D] (x2 only read with the GELU prologue)
+ *   lut     device, rq_lut_bytes(W, B, lut_dtype) bytes, layout [L][M][K][B]
+ *           (the batch index innermost)
+ * W->codes is not read and may be NULL.
+ */
+rq_status rq_build_lut(const rq_matrix* W, const float* x, const float* x2, int32_t prologue,
+                       int32_t B, int32_t lut_dtype, void* lut, hipStream_t stream);
+
+/*
+ * Workspace bytes rq_lut_logits needs for this matrix, batch and top-k size.
+ */
+size_t rq_lut_logits_workspace(const rq_matrix* W, int32_t B, int32_t topk);
+
+/*
+ * Head logits by lookup+sum, then Gemma-2's final-logit softcap and the
+ * selection of the next token (runtime-compression page, LUT-serving
+ * paragraph):
+ *     z[b][r]      = sum_{l<L} sum_{m<M} LUT[l][m][codes[r][l][m]][b]   (fp32)
+ *     logits[b][r] = softcap * tanh(z[b][r] / softcap)   (softcap <= 0: z)
+ *     argmax[b]    = lowest r with the largest logits[b][r]
+ *     top-k        = the topk largest logits of each b, ordered by value
+ *                    descending then index ascending
+ *   lut        the table rq_build_lut wrote for the same W and B
+ *   logits     device fp32 [B][rows], or NULL to skip storing logits
+ *   argmax     device int32 [B], or NULL
+ *   topk       0 (no top-k) or 1..min(rows, 1024); topk_ids int32 [B][topk]
+ *              and topk_vals fp32 [B][topk] (topk_vals may be NULL)
+ *   ws         device workspace of at least rq_lut_logits_workspace() bytes
+ * Each logit is summed in a fixed order, so repeated calls give
+ * bit-identical results; argmax and top-k are taken on the fp32 logits the
+ * call produces. Rows with equal logits are selected by lowest index.
+ */
+rq_status rq_lut_logits(const rq_matrix* W, const void* lut, int32_t lut_dtype, int32_t B,
+                        float softcap, float* logits, int32_t* argmax, int32_t topk,
+                        int32_t* topk_ids, float* topk_vals, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/*
+ * On-demand reconstruction of selected rows (runtime-compression page,
+ * LUT-serving paragraph: input token rows rebuilt on demand):
+ *     out[i][m*d + j] = sum_{l<L} C[l][m][codes[ids[i]][l][m]][j]
+ * summed in fp64 in level order, rounded once to fp32, then (out_dtype
+ * RQ_BF16) rounded to bf16 to nearest even.
+ *   ids      device int32 [n]; an id outside [0, rows) yields a zero row and,
+ *            when bad_ids is not NULL, one atomic increment of *bad_ids
+ *   out      device [n][D] of out_dtype
+ *   bad_ids  device int32 counter or NULL (not reset by the call)
+ */
+rq_status rq_decode_rows(const rq_matrix* W, const int32_t* ids, int32_t n, int32_t out_dtype,
+                         void* out, int32_t* bad_ids, hipStream_t stream);
+
+/*
+ * Workspace bytes rq_lut_matvec needs (the fp32 table plus partial sums).
+ */
+size_t rq_lut_matvec_workspace(const rq_matrix* W, int32_t B);
+
+/*
+ * Matrix-vector product with an RQ-coded weight, by lookup+sum, never
+ * materialising W (the non-materialising MLP path of the Gemma-2-2B MLP RQ
+ * page, final paragraphs):
+ *     y[b][r] = sum_{l,m} LUT_a[l][m][codes[r][l][m]][b] = <W[r], a[b]>
+ * with a = x or a = gelu_tanh(x) * x2 as in rq_build_lut, fp32 table and fp32
+ * sums. A Gemma-2 MLP block is three calls: g = gate(x), u = up(x),
+ * y = down(gelu_tanh(g) * u) via RQ_PRO_GELU_TANH_MUL.
+ *   x, x2  device fp32 [B][D];  y  device fp32 [B][rows]
+ *   ws     device workspace of at least rq_lut_matvec_workspace() bytes
+ */
+rq_status rq_lut_matvec(const rq_matrix* W, const float* x, const float* x2, int32_t prologue,
+                        int32_t B, float* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Comparison baseline: the standard dense path with the head stored as a
+ * dense bf16 matrix E[rows][D] (row-major), as deployed before LUT serving
+ * (runtime-compression page, variant table "Uncompressed" row):
+ *     logits[b][r] = softcap(sum_i E[r][i] * h[b][i]) in fp32, plus argmax.
+ *   E       device bf16 bit patterns [rows][D], 16-byte aligned, D % 8 == 0
+ *   h       device fp32 [B][D], 1 <= B <= 16
+ *   logits  device fp32 [B][rows] (required); argmax device int32 [B] or NULL
+ *   ws      device workspace of at least rq_dense_logits_workspace() bytes
+ */
+size_t rq_dense_logits_workspace(int64_t rows, int32_t B);
+rq_status rq_dense_logits(const uint16_t* E, int64_t rows, int32_t D, const float* h, int32_t B,
+                          float softcap, float* logits, int32_t* argmax, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* Static text for a status code. */
+const char* rq_status_string(rq_status s);
+/* Description of the last failure on the calling thread ("" if none). */
+const char* rq_last_error(void);
+/* Library version, "major.minor.patch". */
+const char* rq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RQ_LUT_H */
