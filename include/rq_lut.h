@@ -31,9 +31,9 @@
  *     failure on the calling thread.
  *   - Empty work. B == 0, n == 0 or rows == 0 return RQ_OK and enqueue
  *     nothing.
- *   - Codes must be < K; larger codes are a precondition violation (the
- *     kernels do not check them, except rq_decode_rows which clamps nothing
- *     and is equally undefined).
+ *   - Codes must be < K; a larger code is a precondition violation that the
+ *     kernels do not check (it reads a neighbouring table entry; results are
+ *     undefined, memory outside the library's own buffers is never touched).
  *   - Alignment. codes, lut, x, x2 and all outputs must be 16-byte aligned,
  *     workspaces 256-byte aligned (torch allocations satisfy this).
  *   - Concurrency. Calls on different streams may run concurrently as long as
@@ -68,22 +68,50 @@ typedef enum rq_prologue {
 } rq_prologue;
 
 /*
+ * Code layouts. The pages fix only that codes are 16-bit integers; the order
+ * in memory is this library's choice. With NP = L*M (level, subspace) pairs
+ * numbered p = l*M + m:
+ *   RQ_CODES_ROWS    codes[r][l][m]: uint16 [rows][NP], the interchange layout
+ *   RQ_CODES_PAIRED  codes[p/2][r][p%2]: uint16 [ceil(NP/2)][rows][2]; for NP
+ *                    odd the unused last slot of every row is 0
+ * Every entry point reads both. PAIRED is the serving layout: the code stream
+ * for any run of consecutive pairs is contiguous over rows, so wave-wide loads
+ * are fully coalesced. rq_pack_codes converts ROWS to PAIRED once, at load.
+ * With RQ_CODES_ROWS, rq_lut_logits and rq_lut_matvec need NP even.
+ */
+typedef enum rq_codes_layout { RQ_CODES_ROWS = 0, RQ_CODES_PAIRED = 1 } rq_codes_layout;
+
+/*
  * Non-owning description of one RQ-coded matrix W[rows][D].
- *   rows       vocabulary size V for a head, out_features for an MLP matrix
- *   D, M, d    D == M*d, all >= 1
- *   K          codewords per codebook, 1 <= K <= 65536 (but see RQ_MAX_K_F32)
- *   L          residual levels, 1 <= L <= 16
- *   cb_dtype   RQ_F32 or RQ_BF16, the storage type of the codebooks
- *   codebooks  device [L][M][K][d] of cb_dtype
- *   codes      device uint16 [rows][L][M], row-major, 16-byte aligned
+ *   rows          vocabulary size V for a head, out_features for an MLP matrix,
+ *                 1 <= rows < 2^31
+ *   D, M, d       D == M*d, all >= 1
+ *   K             codewords per codebook, 1 <= K <= 65536 (but see RQ_MAX_K_F32)
+ *   L             residual levels, 1 <= L <= RQ_MAX_L
+ *   cb_dtype      RQ_F32 or RQ_BF16, the storage type of the codebooks
+ *   codes_layout  RQ_CODES_ROWS or RQ_CODES_PAIRED
+ *   codebooks     device [L][M][K][d] of cb_dtype
+ *   codes         device uint16 in codes_layout, 16-byte aligned
  */
 typedef struct rq_matrix {
   int64_t rows;
   int32_t D, M, d, K, L;
   int32_t cb_dtype;
+  int32_t codes_layout;
   const void* codebooks;
   const uint16_t* codes;
 } rq_matrix;
+
+/* Bytes of the RQ_CODES_PAIRED layout: ceil(L*M/2) * rows * 4. */
+size_t rq_paired_codes_bytes(int64_t rows, int32_t L, int32_t M);
+
+/*
+ * Convert codes from RQ_CODES_ROWS (src, uint16 [rows][L*M]) to
+ * RQ_CODES_PAIRED (dst, rq_paired_codes_bytes bytes). src and dst must not
+ * overlap. A pure permutation: the codes are copied bit for bit.
+ */
+rq_status rq_pack_codes(const uint16_t* src, int64_t rows, int32_t L, int32_t M, uint16_t* dst,
+                        hipStream_t stream);
 
 /* Largest K whose per-subspace table (K entries) fits the kernels' on-chip
  * staging: 32768 for fp32 tables, 65536 for bf16 tables. */
@@ -114,9 +142,10 @@ rq_status rq_build_lut(const rq_matrix* W, const float* x, const float* x2, int3
                        int32_t B, int32_t lut_dtype, void* lut, hipStream_t stream);
 
 /*
- * Workspace bytes rq_lut_logits needs for this matrix, batch and top-k size.
+ * Workspace bytes rq_lut_logits needs for this matrix, batch, top-k size and
+ * table dtype (0 for invalid arguments).
  */
-size_t rq_lut_logits_workspace(const rq_matrix* W, int32_t B, int32_t topk);
+size_t rq_lut_logits_workspace(const rq_matrix* W, int32_t B, int32_t topk, int32_t lut_dtype);
 
 /*
  * Head logits by lookup+sum, then Gemma-2's final-logit softcap and the

@@ -1,0 +1,14 @@
+"""lut_logits_amd -- residual product-quantized (RQ) LUT serving on MI355X (gfx950).
+
+The compute lives in librq_lut.so (hand-written HIP kernels behind the C ABI
+of include/rq_lut.h); `binding` marshals torch tensors into those calls.
+`synth` draws seeded synthetic inputs; `formats` holds the storage
+accounting.
+"""
+from . import formats, synth  # noqa: F401
+from .binding import (RQ_BF16, RQ_CODES_PAIRED, RQ_CODES_ROWS, RQ_F32, RQ_PRO_GELU_TANH_MUL,  # noqa: F401
+                      RQ_PRO_NONE, DeviceMatrix, RQError, build_lut, decode_rows, dense_logits, lib, lut_bytes,
+                      lut_logits, lut_logits_workspace, lut_matvec, lut_matvec_workspace, pack_codes, to_device,
+                      workspace)
+
+__version__ = "0.1.0"

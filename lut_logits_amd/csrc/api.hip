@@ -1,0 +1,259 @@
+// api.hip -- the C ABI of librq_lut.so (declared in include/rq_lut.h).
+//
+// Host-side argument checks (run before anything is launched), workspace
+// sizing and the launch sequence of each entry point. No allocation, no
+// synchronisation: everything is enqueued on the caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+
+#include "rq_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+rq_status fail(rq_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+rq_status launched(hipError_t e, const char* what) {
+  if (e == hipSuccess) return RQ_OK;
+  return fail(RQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t round_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
+
+bool valid_dtype(int32_t t) { return t == RQ_F32 || t == RQ_BF16; }
+
+// Shape, dtype, layout and pointer checks of a matrix descriptor.
+rq_status check_matrix(const rq_matrix* W, bool need_codes) {
+  if (!W) return fail(RQ_ERR_NULL, "matrix descriptor is NULL");
+  if (W->rows < 0 || W->rows >= ((int64_t)1 << 31)) return fail(RQ_ERR_SHAPE, "rows=%lld out of range", (long long)W->rows);
+  if (W->M < 1 || W->d < 1 || (int64_t)W->M * W->d != W->D)
+    return fail(RQ_ERR_SHAPE, "need D == M*d with M, d >= 1 (D=%d M=%d d=%d)", W->D, W->M, W->d);
+  if (W->K < 1 || W->K > 65536) return fail(RQ_ERR_SHAPE, "K=%d outside [1, 65536]", W->K);
+  if (W->L < 1 || W->L > RQ_MAX_L) return fail(RQ_ERR_SHAPE, "L=%d outside [1, %d]", W->L, RQ_MAX_L);
+  if ((int64_t)W->L * W->M > (1 << 24)) return fail(RQ_ERR_SHAPE, "L*M=%lld too large", (long long)W->L * W->M);
+  if (!valid_dtype(W->cb_dtype)) return fail(RQ_ERR_DTYPE, "unknown codebook dtype %d", W->cb_dtype);
+  if (W->codes_layout != RQ_CODES_ROWS && W->codes_layout != RQ_CODES_PAIRED)
+    return fail(RQ_ERR_DTYPE, "unknown codes layout %d", W->codes_layout);
+  if (!W->codebooks) return fail(RQ_ERR_NULL, "codebooks is NULL");
+  if (!aligned(W->codebooks, W->cb_dtype == RQ_F32 ? 4 : 2)) return fail(RQ_ERR_ALIGN, "codebooks misaligned");
+  if (need_codes) {
+    if (!W->codes) return fail(RQ_ERR_NULL, "codes is NULL");
+    if (!aligned(W->codes, 16)) return fail(RQ_ERR_ALIGN, "codes must be 16-byte aligned");
+  }
+  return RQ_OK;
+}
+
+size_t lut_elems(const rq_matrix* W, int32_t B) { return (size_t)W->L * W->M * W->K * (size_t)B; }
+
+// Largest K the lookup kernels can stage for one (level, subspace) pair.
+rq_status check_table_fits(const rq_matrix* W, int lut_bf16) {
+  const int kmax = lut_bf16 ? RQ_MAX_K_BF16 : RQ_MAX_K_F32;
+  if (W->K > kmax) return fail(RQ_ERR_SHAPE, "K=%d exceeds %d for %s tables", W->K, kmax, lut_bf16 ? "bf16" : "fp32");
+  return RQ_OK;
+}
+
+struct LogitsWs {
+  size_t partial, keys, cand, total;
+};
+
+LogitsWs logits_ws(const rq_matrix* W, const rq::GatherPlan& plan, int32_t B, int32_t topk) {
+  const int nblk = rq::epi_blocks(W->rows);
+  LogitsWs w;
+  w.partial = 0;
+  w.keys = round_up((size_t)plan.G * B * W->rows * sizeof(float), 256);
+  w.cand = w.keys + round_up((size_t)B * nblk * sizeof(uint64_t), 256);
+  w.total = w.cand + round_up((size_t)B * nblk * (size_t)std::max(topk, 0) * sizeof(uint64_t), 256);
+  return w;
+}
+
+rq_status check_lut_call(const rq_matrix* W, int32_t B, int32_t lut_dtype) {
+  rq_status s = check_matrix(W, true);
+  if (s != RQ_OK) return s;
+  if (B < 0 || B > 65535) return fail(RQ_ERR_SHAPE, "B=%d outside [0, 65535]", B);
+  if (!valid_dtype(lut_dtype)) return fail(RQ_ERR_DTYPE, "unknown table dtype %d", lut_dtype);
+  s = check_table_fits(W, lut_dtype == RQ_BF16);
+  if (s != RQ_OK) return s;
+  if (W->codes_layout == RQ_CODES_ROWS && ((W->L * W->M) & 1))
+    return fail(RQ_ERR_ALIGN, "row-major codes need L*M even (L*M=%d); pack them with rq_pack_codes", W->L * W->M);
+  return RQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rq_version(void) { return "0.1.0"; }
+
+const char* rq_last_error(void) { return g_last_error; }
+
+const char* rq_status_string(rq_status s) {
+  switch (s) {
+    case RQ_OK: return "ok";
+    case RQ_ERR_NULL: return "null pointer";
+    case RQ_ERR_SHAPE: return "bad shape";
+    case RQ_ERR_DTYPE: return "bad dtype";
+    case RQ_ERR_ALIGN: return "misaligned pointer";
+    case RQ_ERR_WORKSPACE: return "workspace too small";
+    case RQ_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+size_t rq_paired_codes_bytes(int64_t rows, int32_t L, int32_t M) {
+  if (rows < 0 || L < 1 || M < 1) return 0;
+  return (size_t)(((int64_t)L * M + 1) / 2) * (size_t)rows * 4;
+}
+
+rq_status rq_pack_codes(const uint16_t* src, int64_t rows, int32_t L, int32_t M, uint16_t* dst, hipStream_t stream) {
+  if (rows < 0 || rows >= ((int64_t)1 << 31) || L < 1 || L > RQ_MAX_L || M < 1 || (int64_t)L * M > (1 << 24))
+    return fail(RQ_ERR_SHAPE, "bad pack shape rows=%lld L=%d M=%d", (long long)rows, L, M);
+  if (rows == 0) return RQ_OK;
+  if (!src || !dst) return fail(RQ_ERR_NULL, "pack: NULL buffer");
+  if (!aligned(src, 2) || !aligned(dst, 16)) return fail(RQ_ERR_ALIGN, "pack: misaligned buffer");
+  return launched(rq::launch_pack_codes(src, rows, L * M, dst, stream), "rq_pack_codes");
+}
+
+size_t rq_lut_bytes(const rq_matrix* W, int32_t B, int32_t lut_dtype) {
+  if (!W || B < 0 || !valid_dtype(lut_dtype) || W->L < 1 || W->M < 1 || W->K < 1) return 0;
+  return lut_elems(W, B) * (lut_dtype == RQ_BF16 ? 2 : 4);
+}
+
+rq_status rq_build_lut(const rq_matrix* W, const float* x, const float* x2, int32_t prologue, int32_t B,
+                       int32_t lut_dtype, void* lut, hipStream_t stream) {
+  rq_status s = check_matrix(W, false);
+  if (s != RQ_OK) return s;
+  if (B < 0 || B > 65535) return fail(RQ_ERR_SHAPE, "B=%d outside [0, 65535]", B);
+  if (!valid_dtype(lut_dtype)) return fail(RQ_ERR_DTYPE, "unknown table dtype %d", lut_dtype);
+  if (prologue != RQ_PRO_NONE && prologue != RQ_PRO_GELU_TANH_MUL) return fail(RQ_ERR_DTYPE, "unknown prologue %d", prologue);
+  if (B == 0) return RQ_OK;
+  if (!x || !lut || (prologue == RQ_PRO_GELU_TANH_MUL && !x2)) return fail(RQ_ERR_NULL, "build_lut: NULL buffer");
+  if (!aligned(x, 4) || (x2 && !aligned(x2, 4)) || !aligned(lut, 16)) return fail(RQ_ERR_ALIGN, "build_lut: misaligned buffer");
+  return launched(rq::launch_build_lut(W, x, x2, prologue, B, lut_dtype == RQ_BF16, lut, stream), "rq_build_lut");
+}
+
+size_t rq_lut_logits_workspace(const rq_matrix* W, int32_t B, int32_t topk, int32_t lut_dtype) {
+  if (check_lut_call(W, B, lut_dtype) != RQ_OK || topk < 0) return 0;
+  if (B == 0 || W->rows == 0) return 0;
+  const rq::GatherPlan plan = rq::plan_gather(W, B, lut_dtype == RQ_BF16);
+  if (plan.BT == 0) return 0;
+  return logits_ws(W, plan, B, topk).total;
+}
+
+rq_status rq_lut_logits(const rq_matrix* W, const void* lut, int32_t lut_dtype, int32_t B, float softcap,
+                        float* logits, int32_t* argmax, int32_t topk, int32_t* topk_ids, float* topk_vals, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+  rq_status s = check_lut_call(W, B, lut_dtype);
+  if (s != RQ_OK) return s;
+  if (topk < 0 || topk > 1024 || (W->rows > 0 && topk > W->rows))
+    return fail(RQ_ERR_SHAPE, "topk=%d outside [0, min(rows, 1024)]", topk);
+  if (B == 0 || W->rows == 0) return RQ_OK;
+  if (!lut) return fail(RQ_ERR_NULL, "lut is NULL");
+  if (topk > 0 && !topk_ids) return fail(RQ_ERR_NULL, "topk_ids is NULL");
+  if (!aligned(lut, 16)) return fail(RQ_ERR_ALIGN, "lut must be 16-byte aligned");
+  if ((logits && !aligned(logits, 4)) || (argmax && !aligned(argmax, 4)) || (topk_ids && !aligned(topk_ids, 4)) ||
+      (topk_vals && !aligned(topk_vals, 4)))
+    return fail(RQ_ERR_ALIGN, "output misaligned");
+  const rq::GatherPlan plan = rq::plan_gather(W, B, lut_dtype == RQ_BF16);
+  if (plan.BT == 0) return fail(RQ_ERR_SHAPE, "no table tiling fits on chip for K=%d", W->K);
+  const LogitsWs w = logits_ws(W, plan, B, topk);
+  if (!ws || ws_bytes < w.total) return fail(RQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, w.total);
+  if (!aligned(ws, 256)) return fail(RQ_ERR_ALIGN, "workspace must be 256-byte aligned");
+  char* base = static_cast<char*>(ws);
+  float* partial = reinterpret_cast<float*>(base + w.partial);
+  uint64_t* keys = reinterpret_cast<uint64_t*>(base + w.keys);
+  uint64_t* cand = reinterpret_cast<uint64_t*>(base + w.cand);
+  const bool select = argmax || topk > 0;
+  hipError_t e = rq::launch_gather(W, plan, lut, lut_dtype == RQ_BF16, B, partial, nullptr, 0, stream);
+  if (e != hipSuccess) return launched(e, "rq_lut_logits: lookup+sum");
+  e = rq::launch_epilogue(partial, plan.G, B, W->rows, softcap, logits, select ? keys : nullptr, topk, cand, stream);
+  if (e != hipSuccess) return launched(e, "rq_lut_logits: epilogue");
+  if (!select) return RQ_OK;
+  e = rq::launch_select(keys, rq::epi_blocks(W->rows), B, argmax, cand, topk, topk_ids, topk_vals, stream);
+  return launched(e, "rq_lut_logits: selection");
+}
+
+rq_status rq_decode_rows(const rq_matrix* W, const int32_t* ids, int32_t n, int32_t out_dtype, void* out,
+                         int32_t* bad_ids, hipStream_t stream) {
+  rq_status s = check_matrix(W, true);
+  if (s != RQ_OK) return s;
+  if (n < 0) return fail(RQ_ERR_SHAPE, "n=%d < 0", n);
+  if (!valid_dtype(out_dtype)) return fail(RQ_ERR_DTYPE, "unknown output dtype %d", out_dtype);
+  if (n == 0) return RQ_OK;
+  if (!ids || !out) return fail(RQ_ERR_NULL, "decode_rows: NULL buffer");
+  if (!aligned(ids, 4) || !aligned(out, 4) || (bad_ids && !aligned(bad_ids, 4)))
+    return fail(RQ_ERR_ALIGN, "decode_rows: misaligned buffer");
+  return launched(rq::launch_decode_rows(W, ids, n, out_dtype == RQ_BF16, out, bad_ids, stream), "rq_decode_rows");
+}
+
+size_t rq_lut_matvec_workspace(const rq_matrix* W, int32_t B) {
+  if (check_lut_call(W, B, RQ_F32) != RQ_OK || B == 0 || W->rows == 0) return 0;
+  const rq::GatherPlan plan = rq::plan_gather(W, B, 0);
+  if (plan.BT == 0) return 0;
+  return round_up(lut_elems(W, B) * sizeof(float), 256) + round_up((size_t)plan.G * B * W->rows * sizeof(float), 256);
+}
+
+rq_status rq_lut_matvec(const rq_matrix* W, const float* x, const float* x2, int32_t prologue, int32_t B, float* y,
+                        void* ws, size_t ws_bytes, hipStream_t stream) {
+  rq_status s = check_lut_call(W, B, RQ_F32);
+  if (s != RQ_OK) return s;
+  if (prologue != RQ_PRO_NONE && prologue != RQ_PRO_GELU_TANH_MUL) return fail(RQ_ERR_DTYPE, "unknown prologue %d", prologue);
+  if (B == 0 || W->rows == 0) return RQ_OK;
+  if (!x || !y || (prologue == RQ_PRO_GELU_TANH_MUL && !x2)) return fail(RQ_ERR_NULL, "lut_matvec: NULL buffer");
+  if (!aligned(x, 4) || (x2 && !aligned(x2, 4)) || !aligned(y, 4)) return fail(RQ_ERR_ALIGN, "lut_matvec: misaligned buffer");
+  const rq::GatherPlan plan = rq::plan_gather(W, B, 0);
+  if (plan.BT == 0) return fail(RQ_ERR_SHAPE, "no table tiling fits on chip for K=%d", W->K);
+  const size_t lut_bytes = round_up(lut_elems(W, B) * sizeof(float), 256);
+  const size_t need = lut_bytes + round_up((size_t)plan.G * B * W->rows * sizeof(float), 256);
+  if (!ws || ws_bytes < need) return fail(RQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (!aligned(ws, 256)) return fail(RQ_ERR_ALIGN, "workspace must be 256-byte aligned");
+  char* base = static_cast<char*>(ws);
+  float* lut = reinterpret_cast<float*>(base);
+  float* partial = reinterpret_cast<float*>(base + lut_bytes);
+  hipError_t e = rq::launch_build_lut(W, x, x2, prologue, B, 0, lut, stream);
+  if (e != hipSuccess) return launched(e, "rq_lut_matvec: table build");
+  e = rq::launch_gather(W, plan, lut, 0, B, partial, nullptr, 0, stream);
+  if (e != hipSuccess) return launched(e, "rq_lut_matvec: lookup+sum");
+  return launched(rq::launch_epilogue(partial, plan.G, B, W->rows, 0.0f, y, nullptr, 0, nullptr, stream),
+                  "rq_lut_matvec: reduction");
+}
+
+size_t rq_dense_logits_workspace(int64_t rows, int32_t B) {
+  if (rows <= 0 || B < 1 || B > 16) return 0;
+  return round_up((size_t)B * rq::dense_blocks(rows) * sizeof(uint64_t), 256);
+}
+
+rq_status rq_dense_logits(const uint16_t* E, int64_t rows, int32_t D, const float* h, int32_t B, float softcap,
+                          float* logits, int32_t* argmax, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (rows < 0 || rows >= ((int64_t)1 << 31)) return fail(RQ_ERR_SHAPE, "rows out of range");
+  if (D < 8 || D % 8 != 0 || D > 4096) return fail(RQ_ERR_SHAPE, "dense head needs D %% 8 == 0 and 8 <= D <= 4096");
+  if (B < 0 || B > 16) return fail(RQ_ERR_SHAPE, "dense head supports 0 <= B <= 16");
+  if (rows == 0 || B == 0) return RQ_OK;
+  if (!E || !h || !logits) return fail(RQ_ERR_NULL, "dense_logits: NULL buffer");
+  if (!aligned(E, 16) || !aligned(h, 4) || !aligned(logits, 4) || (argmax && !aligned(argmax, 4)))
+    return fail(RQ_ERR_ALIGN, "dense_logits: misaligned buffer");
+  uint64_t* keys = nullptr;
+  if (argmax) {
+    const size_t need = rq_dense_logits_workspace(rows, B);
+    if (!ws || ws_bytes < need) return fail(RQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    if (!aligned(ws, 256)) return fail(RQ_ERR_ALIGN, "workspace must be 256-byte aligned");
+    keys = static_cast<uint64_t*>(ws);
+  }
+  hipError_t e = rq::launch_dense_logits(E, rows, D, h, B, softcap, logits, keys, argmax, stream);
+  if (e != hipSuccess) return launched(e, "rq_dense_logits");
+  if (!argmax) return RQ_OK;
+  return launched(rq::launch_select(keys, rq::dense_blocks(rows), B, argmax, nullptr, 0, nullptr, nullptr, stream),
+                  "rq_dense_logits: argmax");
+}
+
+}  // extern "C"

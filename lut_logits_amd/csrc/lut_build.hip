@@ -1,0 +1,115 @@
+// lut_build.hip -- the per-activation lookup table of an RQ-coded matrix.
+//
+//   LUT[l][m][k][b] = sum_{j<d} a[b][m*d + j] * C[l][m][k][j]
+//
+// (Gemma-2-2B runtime-compression page, LUT-serving paragraph: logits by
+// lookup+sum; the table is the inner product of each subvector of the hidden
+// state with every codeword of that subspace.)  a = x, or gelu_tanh(x) * x2
+// for the down projection of a Gemma-2 MLP block (MLP RQ page, closing
+// paragraphs).
+//
+// One workgroup covers 256 codewords of one (level, subspace) pair p = l*M+m.
+// It first stages a[b][m*d .. m*d+d) for all b in LDS (prologue applied once
+// per workgroup), then each thread keeps its codeword in registers and writes
+// B consecutive table entries. Work: L*M*K*B*d FMAs; bytes: the codebooks
+// once plus the table once -- a few microseconds at Gemma shapes, far from
+// the matrix cores' territory, so plain VALU FMAs are used.
+#include "rq_internal.h"
+
+namespace rq {
+namespace {
+
+constexpr int kBuildThreads = 256;
+constexpr int kActStage = 4096;   // floats of the activation slice staged per workgroup
+constexpr int kMaxRegD = 8;       // subspace widths up to this keep the codeword in registers
+
+template <typename CbT>
+__device__ __forceinline__ float cb_load(const CbT* p);
+template <>
+__device__ __forceinline__ float cb_load<float>(const float* p) { return *p; }
+template <>
+__device__ __forceinline__ float cb_load<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+
+template <typename OutT>
+__device__ __forceinline__ void lut_store(OutT* p, float v);
+template <>
+__device__ __forceinline__ void lut_store<float>(float* p, float v) { *p = v; }
+template <>
+__device__ __forceinline__ void lut_store<uint16_t>(uint16_t* p, float v) { *p = f32_to_bf16(v); }
+
+__device__ __forceinline__ float activation(const float* x, const float* x2, int gelu, size_t i) {
+  const float v = x[i];
+  return gelu ? gelu_tanh(v) * x2[i] : v;
+}
+
+template <typename CbT, typename OutT>
+__global__ __launch_bounds__(kBuildThreads) void build_lut_kernel(const CbT* __restrict__ cb,
+                                                                  const float* __restrict__ x,
+                                                                  const float* __restrict__ x2, int gelu, int B,
+                                                                  int D, int M, int d, int K, int ktiles,
+                                                                  OutT* __restrict__ lut) {
+  __shared__ float act[kActStage];
+  const int p = blockIdx.x / ktiles;                 // (level, subspace) pair
+  const int m = p % M;
+  const int k = (blockIdx.x - p * ktiles) * kBuildThreads + threadIdx.x;
+  const bool staged = (int64_t)B * d <= kActStage;   // uniform over the workgroup
+  const size_t col0 = (size_t)m * d;
+  if (staged) {
+    for (int i = threadIdx.x; i < B * d; i += kBuildThreads) {
+      const int b = i / d;
+      act[i] = activation(x, x2, gelu, (size_t)b * D + col0 + (i - b * d));
+    }
+    __syncthreads();
+  }
+  if (k >= K) return;
+  const CbT* c = cb + ((size_t)p * K + k) * d;
+  OutT* out = lut + ((size_t)p * K + k) * B;
+  if (d <= kMaxRegD && staged) {
+    float cw[kMaxRegD];
+#pragma unroll
+    for (int j = 0; j < kMaxRegD; ++j) cw[j] = (j < d) ? cb_load(c + j) : 0.0f;
+    for (int b = 0; b < B; ++b) {
+      const float* a = act + b * d;
+      float acc = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kMaxRegD; ++j)
+        if (j < d) acc = fmaf(a[j], cw[j], acc);
+      lut_store(out + b, acc);
+    }
+  } else {
+    for (int b = 0; b < B; ++b) {
+      float acc = 0.0f;
+      for (int j = 0; j < d; ++j) {
+        const float a = staged ? act[b * d + j] : activation(x, x2, gelu, (size_t)b * D + col0 + j);
+        acc = fmaf(a, cb_load(c + j), acc);
+      }
+      lut_store(out + b, acc);
+    }
+  }
+}
+
+template <typename CbT, typename OutT>
+hipError_t launch_typed(const rq_matrix* W, const float* x, const float* x2, int gelu, int B, OutT* lut,
+                        hipStream_t stream) {
+  const int NP = W->L * W->M;
+  const int ktiles = (W->K + kBuildThreads - 1) / kBuildThreads;
+  const int64_t blocks = (int64_t)NP * ktiles;
+  hipLaunchKernelGGL((build_lut_kernel<CbT, OutT>), dim3((unsigned)blocks), dim3(kBuildThreads), 0, stream,
+                     static_cast<const CbT*>(W->codebooks), x, x2, gelu, B, W->D, W->M, W->d, W->K, ktiles, lut);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_build_lut(const rq_matrix* W, const float* x, const float* x2, int prologue, int B,
+                            int lut_bf16, void* lut, hipStream_t stream) {
+  const int gelu = prologue == RQ_PRO_GELU_TANH_MUL;
+  if (W->cb_dtype == RQ_BF16) {
+    if (lut_bf16) return launch_typed<uint16_t, uint16_t>(W, x, x2, gelu, B, (uint16_t*)lut, stream);
+    return launch_typed<uint16_t, float>(W, x, x2, gelu, B, (float*)lut, stream);
+  }
+  if (lut_bf16) return launch_typed<float, uint16_t>(W, x, x2, gelu, B, (uint16_t*)lut, stream);
+  return launch_typed<float, float>(W, x, x2, gelu, B, (float*)lut, stream);
+}
+
+}  // namespace rq

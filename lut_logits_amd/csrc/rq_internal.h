@@ -1,0 +1,97 @@
+// rq_internal.h -- declarations shared by the HIP sources of librq_lut.so.
+//
+// Device helpers (bf16 conversion, selection keys) and the host-side launch
+// functions each kernel file provides to the C-ABI layer in api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "rq_lut.h"
+
+namespace rq {
+
+// ---------------------------------------------------------------- device helpers
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// fp32 -> bf16 bit pattern, round to nearest, ties to even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Selection key with a total order: a larger value gives a larger key, and
+// among equal values the lower index gives the larger key. -0 counts as +0.
+__device__ __forceinline__ uint64_t select_key(float v, uint32_t idx) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)ord << 32) | (uint64_t)(0xffffffffu - idx);
+}
+__device__ __forceinline__ uint32_t key_index(uint64_t key) { return 0xffffffffu - (uint32_t)key; }
+__device__ __forceinline__ float key_value(uint64_t key) {
+  const uint32_t ord = (uint32_t)(key >> 32);
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord);
+}
+
+__device__ __forceinline__ float gelu_tanh(float t) {
+  const float k = 0.7978845608028654f;  // sqrt(2/pi)
+  return 0.5f * t * (1.0f + tanhf(k * (t + 0.044715f * t * t * t)));
+}
+
+// Code of pair p for row r: codes[(p >> 1) * s_blk + r * s_row + (p & 1)].
+// RQ_CODES_ROWS: s_blk = 2, s_row = NP.  RQ_CODES_PAIRED: s_blk = 2 * rows, s_row = 2.
+struct CodeView {
+  const uint16_t* codes;
+  int64_t s_blk;
+  int64_t s_row;
+};
+
+// ---------------------------------------------------------------- host side
+
+constexpr int kCUs = 256;                 // MI355X compute units
+constexpr int kLdsBytes = 160 * 1024;     // LDS per workgroup on gfx950
+constexpr int kGatherThreads = 1024;
+
+CodeView code_view(const rq_matrix* W);
+
+// Tiling of one lookup+sum pass (chosen from the shapes alone).
+struct GatherPlan {
+  int BT;        // batch values per table entry staged on chip (1, 4 or 16)
+  int P;         // (level, subspace) pairs per staged chunk
+  int chunks;    // ceil(NP / P)
+  int cpg;       // chunks per group
+  int G;         // groups: partial sums per output, reduced in a fixed order
+  int steps;     // row steps per slab
+  int rps;       // rows per step
+  int S;         // row slabs
+  int NBT;       // batch tiles
+  size_t lds;    // dynamic LDS bytes per workgroup
+  int64_t wgs() const { return (int64_t)G * S * NBT; }
+};
+GatherPlan plan_gather(const rq_matrix* W, int B, int lut_bf16);
+
+// Launchers: return hipSuccess or the launch error. All enqueue on `stream`.
+hipError_t launch_build_lut(const rq_matrix* W, const float* x, const float* x2, int prologue, int B,
+                            int lut_bf16, void* lut, hipStream_t stream);
+hipError_t launch_gather(const rq_matrix* W, const GatherPlan& plan, const void* lut, int lut_bf16, int B,
+                         float* partial, uint64_t* zero_words, int n_zero_words, hipStream_t stream);
+hipError_t launch_epilogue(const float* partial, int G, int B, int64_t rows, float softcap, float* out,
+                           uint64_t* block_keys, int topk, uint64_t* cand, hipStream_t stream);
+hipError_t launch_select(const uint64_t* block_keys, int nblk, int B, int32_t* argmax, const uint64_t* cand,
+                         int topk, int32_t* topk_ids, float* topk_vals, hipStream_t stream);
+hipError_t launch_decode_rows(const rq_matrix* W, const int32_t* ids, int n, int out_bf16, void* out,
+                              int32_t* bad_ids, hipStream_t stream);
+hipError_t launch_pack_codes(const uint16_t* src, int64_t rows, int NP, uint16_t* dst, hipStream_t stream);
+hipError_t launch_dense_logits(const uint16_t* E, int64_t rows, int D, const float* h, int B, float softcap,
+                               float* logits, uint64_t* block_keys, int32_t* argmax, hipStream_t stream);
+
+constexpr int kEpiRowsPerBlock = 1024;   // rows per epilogue workgroup
+inline int epi_blocks(int64_t rows) { return (int)((rows + kEpiRowsPerBlock - 1) / kEpiRowsPerBlock); }
+constexpr int kDenseRowsPerBlock = 256;
+inline int dense_blocks(int64_t rows) { return (int)((rows + kDenseRowsPerBlock - 1) / kDenseRowsPerBlock); }
+
+}  // namespace rq

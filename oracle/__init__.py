@@ -17,7 +17,7 @@ import os
 
 import numpy as np
 
-from .build import LIB, build
+from .build import LIB, build as _build_lib
 
 _ERR = {-1: "null pointer", -2: "bad shape", -7: "code >= K"}
 
@@ -42,7 +42,7 @@ class Oracle:
 
     def __init__(self, libpath=LIB):
         if libpath == LIB and not os.path.exists(LIB):
-            build()
+            _build_lib()
         self.lib = lib = ctypes.CDLL(libpath)
         i64, i32, vp, dbl = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_double
         lib.oracle_matvec.argtypes = [i64, i32, i32, i32, i32, i32, vp, i32, _u16p, _dp, i32, _dp, i32]

@@ -1,0 +1,123 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol, and rejects bad
+arguments before launching anything (no GPU needed: every call here fails its host checks)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from lut_logits_amd import binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "rq_lut.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert len(names) >= 14
+    lib = B.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(B.EXPORTS)
+
+
+def test_version_and_status_strings():
+    lib = B.lib()
+    assert lib.rq_version().decode().count(".") == 2
+    for s in range(-6, 1):
+        assert lib.rq_status_string(s)
+    assert lib.rq_status_string(-99) == b"unknown status"
+
+
+def gemma_desc(**kw):
+    f = dict(rows=256000, D=2304, M=384, d=6, K=1024, L=2, cb_dtype=B.RQ_BF16, codes_layout=B.RQ_CODES_PAIRED,
+             codebooks=0x10000, codes=0x20000)
+    f.update(kw)
+    return B.rq_matrix(**f)
+
+
+def call_logits(W, Bn=1, topk=0, lut=0x30000, ws=0x40000, ws_bytes=1 << 40, lut_dtype=B.RQ_F32, topk_ids=0x50000):
+    lib = B.lib()
+    return lib.rq_lut_logits(ctypes.byref(W) if W is not None else None, lut, lut_dtype, Bn, 30.0, 0x60000, 0x70000,
+                             topk, topk_ids, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=2305), B.RQ_ERR_SHAPE),
+    (dict(K=0), B.RQ_ERR_SHAPE),
+    (dict(K=65537), B.RQ_ERR_SHAPE),
+    (dict(K=40000), B.RQ_ERR_SHAPE),          # fp32 table of one pair does not fit on chip
+    (dict(L=0), B.RQ_ERR_SHAPE),
+    (dict(L=17), B.RQ_ERR_SHAPE),
+    (dict(rows=-1), B.RQ_ERR_SHAPE),
+    (dict(cb_dtype=7), B.RQ_ERR_DTYPE),
+    (dict(codes_layout=5), B.RQ_ERR_DTYPE),
+    (dict(codebooks=0), B.RQ_ERR_NULL),
+    (dict(codes=0), B.RQ_ERR_NULL),
+    (dict(codes=0x20002), B.RQ_ERR_ALIGN),
+    (dict(codes_layout=B.RQ_CODES_ROWS, L=1, M=383, D=2298), B.RQ_ERR_ALIGN),   # odd L*M needs the paired layout
+])
+def test_lut_logits_rejects(kw, status):
+    assert call_logits(gemma_desc(**kw)) == status
+    assert B.lib().rq_last_error()
+
+
+def test_lut_logits_argument_checks():
+    W = gemma_desc()
+    assert call_logits(None) == B.RQ_ERR_NULL
+    assert call_logits(W, Bn=-1) == B.RQ_ERR_SHAPE
+    assert call_logits(W, topk=1025) == B.RQ_ERR_SHAPE
+    assert call_logits(W, topk=5, topk_ids=0) == B.RQ_ERR_NULL
+    assert call_logits(W, lut=0) == B.RQ_ERR_NULL
+    assert call_logits(W, lut=0x30004) == B.RQ_ERR_ALIGN
+    assert call_logits(W, ws=0) == B.RQ_ERR_WORKSPACE
+    assert call_logits(W, ws_bytes=100) == B.RQ_ERR_WORKSPACE
+    assert call_logits(W, ws=0x40010) == B.RQ_ERR_ALIGN
+    assert call_logits(W, lut_dtype=9) == B.RQ_ERR_DTYPE
+    # empty work is a no-op even with no buffers
+    assert call_logits(W, Bn=0, lut=0, ws=0, ws_bytes=0) == B.RQ_OK
+    assert call_logits(gemma_desc(rows=0), lut=0, ws=0, ws_bytes=0) == B.RQ_OK
+
+
+def test_workspace_queries():
+    lib = B.lib()
+    W = gemma_desc()
+    ws1 = lib.rq_lut_logits_workspace(ctypes.byref(W), 1, 0, B.RQ_F32)
+    assert ws1 >= 256000 * 4 and ws1 % 256 == 0
+    assert lib.rq_lut_logits_workspace(ctypes.byref(W), 16, 50, B.RQ_F32) > ws1
+    assert lib.rq_lut_logits_workspace(ctypes.byref(gemma_desc(D=1)), 1, 0, B.RQ_F32) == 0
+    assert lib.rq_lut_bytes(ctypes.byref(W), 1, B.RQ_F32) == 2 * 384 * 1024 * 4
+    assert lib.rq_lut_bytes(ctypes.byref(W), 3, B.RQ_BF16) == 2 * 384 * 1024 * 3 * 2
+    assert lib.rq_paired_codes_bytes(256000, 2, 384) == 393_216_000
+    assert lib.rq_paired_codes_bytes(10, 1, 5) == 3 * 10 * 4
+    Wm = gemma_desc(rows=9216, D=2304, M=1152, d=2, cb_dtype=B.RQ_F32)
+    assert lib.rq_lut_matvec_workspace(ctypes.byref(Wm), 1) >= 2 * 1152 * 1024 * 4
+    assert lib.rq_dense_logits_workspace(256000, 1) > 0
+    assert lib.rq_dense_logits_workspace(256000, 17) == 0
+
+
+def test_other_entry_points_reject():
+    lib = B.lib()
+    W = gemma_desc()
+    assert lib.rq_build_lut(ctypes.byref(W), None, None, 0, 1, 0, 0x30000, None) == B.RQ_ERR_NULL
+    assert lib.rq_build_lut(ctypes.byref(W), 0x1000, None, 1, 1, 0, 0x30000, None) == B.RQ_ERR_NULL   # GELU needs x2
+    assert lib.rq_build_lut(ctypes.byref(W), 0x1000, None, 3, 1, 0, 0x30000, None) == B.RQ_ERR_DTYPE
+    assert lib.rq_build_lut(ctypes.byref(W), 0x1000, None, 0, 1, 0, 0x30008, None) == B.RQ_ERR_ALIGN
+    assert lib.rq_build_lut(ctypes.byref(W), None, None, 0, 0, 0, None, None) == B.RQ_OK
+    assert lib.rq_decode_rows(ctypes.byref(W), None, 4, 0, 0x1000, None, None) == B.RQ_ERR_NULL
+    assert lib.rq_decode_rows(ctypes.byref(W), 0x1000, -1, 0, 0x1000, None, None) == B.RQ_ERR_SHAPE
+    assert lib.rq_decode_rows(ctypes.byref(W), 0x1000, 4, 2, 0x1000, None, None) == B.RQ_ERR_DTYPE
+    assert lib.rq_decode_rows(ctypes.byref(W), None, 0, 0, None, None, None) == B.RQ_OK
+    assert lib.rq_lut_matvec(ctypes.byref(W), 0x1000, None, 0, 1, 0x2000, None, 0, None) == B.RQ_ERR_WORKSPACE
+    assert lib.rq_lut_matvec(ctypes.byref(W), 0x1000, None, 1, 1, 0x2000, None, 0, None) == B.RQ_ERR_NULL
+    assert lib.rq_pack_codes(None, 10, 2, 3, 0x1000, None) == B.RQ_ERR_NULL
+    assert lib.rq_pack_codes(0x1000, 10, 0, 3, 0x1000, None) == B.RQ_ERR_SHAPE
+    assert lib.rq_pack_codes(0x1000, 10, 2, 3, 0x1008, None) == B.RQ_ERR_ALIGN
+    assert lib.rq_dense_logits(0x1000, 100, 2300, 0x2000, 1, 30.0, 0x3000, None, None, 0, None) == B.RQ_ERR_SHAPE
+    assert lib.rq_dense_logits(0x1000, 100, 2304, 0x2000, 17, 30.0, 0x3000, None, None, 0, None) == B.RQ_ERR_SHAPE
+    assert lib.rq_dense_logits(0x1000, 100, 2304, 0x2000, 1, 30.0, 0x3000, 0x4000, None, 0, None) == B.RQ_ERR_WORKSPACE

@@ -1,0 +1,310 @@
+"""HIP path vs the CPU oracle, element by element, through the C ABI (needs an MI355X)."""
+import numpy as np
+import pytest
+import torch
+
+import lut_logits_amd as la
+import oracle
+from lut_logits_amd import synth
+from gpu_util import check_argmax, check_logits, dev, host, oracle_head, to_dev
+
+pytestmark = pytest.mark.gpu
+
+O = oracle.default
+
+
+def _rand(seed, rows, D, M, K, L, cb_dtype="f32", sigmas=None):
+    rng = np.random.default_rng(seed)
+    sig = sigmas or tuple(0.02 * 0.25 ** l for l in range(L))
+    return synth.gen_matrix(rng, rows, D, M, K, L, sig, cb_dtype), rng
+
+
+# ------------------------------------------------------------------ layout
+
+@pytest.mark.parametrize("rows,NP", [(1, 1), (63, 7), (4097, 34), (130, 768)])
+def test_pack_codes_bit_exact(rows, NP):
+    rng = np.random.default_rng(rows + NP)
+    codes = rng.integers(0, 65536, size=(rows, NP), dtype=np.uint16)
+    out = host(la.pack_codes(dev(codes.view(np.int16)), rows, 1, NP)).view(np.uint16)
+    NQ = (NP + 1) // 2
+    padded = np.zeros((rows, 2 * NQ), np.uint16)
+    padded[:, :NP] = codes
+    want = padded.reshape(rows, NQ, 2).transpose(1, 0, 2).reshape(-1)
+    assert np.array_equal(out, want)
+
+
+# ------------------------------------------------------------------ row decode
+
+@pytest.mark.parametrize("layout", ["rows", "paired"])
+@pytest.mark.parametrize("L,cb_dtype,out_dtype", [(2, "f32", "f32"), (2, "f32", "bf16"), (2, "bf16", "bf16"),
+                                                  (3, "f32", "f32"), (4, "bf16", "f32"), (1, "f32", "f32")])
+def test_decode_rows_bit_exact(layout, L, cb_dtype, out_dtype):
+    mat, rng = _rand(30 + L, 4096, 96, 16, 256, L, cb_dtype)
+    ids = np.concatenate([rng.integers(0, 4096, 8), [0, 4095, -1, 4096, 2 ** 31 - 1]]).astype(np.int32)
+    W = to_dev(mat, layout)
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = host(la.decode_rows(W, dev(ids), out_dtype, bad_ids=bad))
+    want, nbad = O().decode_rows(mat.codes, mat.codebooks, mat.cb_is_bf16, ids, out_dtype == "bf16")
+    if out_dtype == "bf16":
+        out = out.view(np.uint16)
+    assert np.array_equal(out, want)
+    assert int(bad.item()) == nbad == 3
+
+
+def test_decode_rows_gemma_shape():
+    """64 token ids on the 256000 x 2304 head (bf16 codebooks, bf16 rows), bit-exact."""
+    cfg = synth.CONFIGS["gemma_b1"]
+    mat, _, ids = synth.make_head(cfg)
+    W = to_dev(mat)
+    out = host(la.decode_rows(W, dev(ids), "bf16")).view(np.uint16)
+    want, nbad = O().decode_rows(mat.codes, mat.codebooks, True, ids, True)
+    assert nbad == 0 and np.array_equal(out, want)
+
+
+# ------------------------------------------------------------------ table build
+
+@pytest.mark.parametrize("cb_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("B", [1, 3, 16])
+def test_build_lut(cb_dtype, B):
+    mat, rng = _rand(40 + B, 8, 96, 16, 256, 2, cb_dtype)
+    h = synth.gen_hidden(rng, B, 96)
+    W = to_dev(mat)
+    lut = host(la.build_lut(W, dev(h))).reshape(2, 16, 256, B)
+    ref = O().build_lut(mat.codebooks, mat.cb_is_bf16, h).transpose(1, 2, 3, 0)   # [L][M][K][B]
+    # d=6 fp32 FMAs: error <= 6 * 2^-24 * sum_j |a_j c_j|
+    cbf = mat.codebooks_f32().astype(np.float64)
+    bound = np.einsum("bmj,lmkj->lmkb", np.abs(h.astype(np.float64)).reshape(B, 16, 6), np.abs(cbf)) * 6 * 2.0 ** -24
+    assert np.all(np.abs(lut - ref) <= bound + 1e-30)
+
+
+def test_build_lut_exact_and_bf16_table():
+    mat, h = synth.gen_exact(7, rows=4, D=96, M=16, K=256, L=2, B=2)
+    W = to_dev(mat)
+    lut = host(la.build_lut(W, dev(h))).reshape(2, 16, 256, 2)
+    ref = O().build_lut(mat.codebooks, False, h).transpose(1, 2, 3, 0)
+    assert np.array_equal(lut, ref)
+    lutb = host(la.build_lut(W, dev(h), lut_dtype="bf16")).view(np.uint16).reshape(2, 16, 256, 2)
+    # exact fp32 values, then one rounding to bf16 (nearest even)
+    assert np.array_equal(lutb, synth.f32_to_bf16_bits(ref.astype(np.float32)))
+
+
+def test_build_lut_gelu_prologue():
+    mat, rng = _rand(50, 8, 96, 48, 64, 2)
+    g = synth.gen_hidden(rng, 2, 96) * np.float32(2.0)
+    u = synth.gen_hidden(rng, 2, 96)
+    W = to_dev(mat)
+    lut = host(la.build_lut(W, dev(g), x2=dev(u), prologue=la.RQ_PRO_GELU_TANH_MUL)).reshape(2, 48, 64, 2)
+    a = O().gelu_mul(g.astype(np.float64), u.astype(np.float64))
+    ref = O().build_lut(mat.codebooks, False, a).transpose(1, 2, 3, 0)
+    scale = np.abs(ref).max()
+    assert np.abs(lut - ref).max() <= 1e-5 * scale
+
+
+# ------------------------------------------------------------------ logits: exact arithmetic
+
+EXACT_SHAPES = [
+    # rows, D, M, K, L, B
+    (4097, 96, 16, 256, 2, 1),
+    (4097, 102, 17, 1000, 2, 1),    # odd M, K not a power of two, ragged rows
+    (1, 6, 1, 1, 1, 1),             # one row, one codeword, one pair
+    (300, 34, 17, 5, 1, 2),         # odd L*M (paired layout only), ragged batch tile
+    (2049, 96, 16, 256, 2, 16),
+    (1500, 96, 16, 128, 3, 17),     # batch 16 + ragged 1
+    (700, 96, 96, 64, 2, 5),        # d = 1
+    (333, 64, 1, 512, 2, 3),        # M = 1, d = D
+]
+
+
+@pytest.mark.parametrize("shape", EXACT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("layout", ["rows", "paired"])
+def test_lut_logits_exact(shape, layout):
+    """Small-integer inputs: every fp32 step is exact, so logits (softcap off) equal the oracle bit for bit."""
+    rows, D, M, K, L, B = shape
+    if layout == "rows" and (L * M) % 2:
+        pytest.skip("row-major codes need L*M even")
+    mat, h = synth.gen_exact(rows + K, rows, D, M, K, L, B)
+    W = to_dev(mat, layout)
+    lut = la.build_lut(W, dev(h))
+    lg, am, _, _ = la.lut_logits(W, lut, B, softcap=0.0)
+    z, _ = O().logits(mat.codes, mat.codebooks, False, h, 0.0)
+    got = host(lg)
+    assert np.array_equal(got.astype(np.float64), z)
+    assert np.array_equal(host(am), np.argmax(got, axis=1).astype(np.int32))
+
+
+def test_lut_logits_bf16_codebooks_exact():
+    mat, h = synth.gen_exact(3, 2500, 96, 16, 300, 2, 4, cb_dtype="bf16")
+    W = to_dev(mat)
+    lg, _, _, _ = la.lut_logits(W, la.build_lut(W, dev(h)), 4, softcap=0.0)
+    z, _ = O().logits(mat.codes, mat.codebooks, True, h, 0.0)
+    assert np.array_equal(host(lg).astype(np.float64), z)
+
+
+# ------------------------------------------------------------------ logits: float parity
+
+def test_tiny_config():
+    """The tiny RQ head: V=4096, D=96, M=16, K=256, L=2, fp32 codebooks, softcap 30, argmax, 8 decoded rows."""
+    cfg = synth.CONFIGS["tiny"]
+    mat, h, ids = synth.make_head(cfg)
+    for layout in ("rows", "paired"):
+        W = to_dev(mat, layout)
+        lg, am, _, _ = la.lut_logits(W, la.build_lut(W, dev(h)), 1, softcap=cfg.softcap)
+        _, ref = oracle_head(mat, h, cfg.softcap)
+        check_logits(host(lg), ref)
+        check_argmax(host(am), host(lg), ref)
+        rows = host(la.decode_rows(W, dev(ids)))
+        want, _ = O().decode_rows(mat.codes, mat.codebooks, False, ids, False)
+        assert np.array_equal(rows, want)
+
+
+@pytest.mark.parametrize("B", [1, 2, 16, 20])
+def test_float_parity_batched(B):
+    mat, rng = _rand(60 + B, 3000, 96, 16, 512, 2, "bf16")
+    h = synth.gen_hidden(rng, B, 96)
+    W = to_dev(mat)
+    lg, am, _, _ = la.lut_logits(W, la.build_lut(W, dev(h)), B, softcap=30.0)
+    _, ref = oracle_head(mat, h, 30.0)
+    check_logits(host(lg), ref)
+    check_argmax(host(am), host(lg), ref)
+
+
+def test_argmax_ties_lowest_index():
+    """K = 1: every row decodes to the same vector, every logit ties, the argmax is row 0."""
+    mat, rng = _rand(70, 5000, 96, 16, 1, 2)
+    h = synth.gen_hidden(rng, 3, 96)
+    W = to_dev(mat)
+    lg, am, ti, _ = la.lut_logits(W, la.build_lut(W, dev(h)), 3, softcap=30.0, topk=5)
+    g = host(lg)
+    assert np.all(g == g[:, :1])
+    assert list(host(am)) == [0, 0, 0]
+    assert np.array_equal(host(ti), np.tile(np.arange(5, dtype=np.int32), (3, 1)))
+
+
+def test_no_logits_output_and_determinism():
+    mat, rng = _rand(80, 9000, 96, 16, 256, 2)
+    h = synth.gen_hidden(rng, 1, 96)
+    W = to_dev(mat)
+    lut = la.build_lut(W, dev(h))
+    lg1, am1, _, _ = la.lut_logits(W, lut, 1)
+    lg2, am2, _, _ = la.lut_logits(W, lut, 1)
+    _, am3, _, _ = la.lut_logits(W, lut, 1, logits=False)
+    assert torch.equal(lg1, lg2) and torch.equal(am1, am2) and torch.equal(am1, am3)
+
+
+def test_output_canaries():
+    """Nothing outside [B][rows] of the logits buffer is written."""
+    mat, rng = _rand(81, 1000, 96, 16, 256, 2)
+    h = synth.gen_hidden(rng, 2, 96)
+    W = to_dev(mat)
+    buf = torch.full((2 * 1000 + 64,), float("nan"), device="cuda")
+    la.lut_logits(W, la.build_lut(W, dev(h)), 2, out=buf[:2000].view(2, 1000))
+    tail = host(buf[2000:])
+    assert np.all(np.isnan(tail))
+    assert not np.any(np.isnan(host(buf[:2000])))
+
+
+def test_empty_work_is_noop():
+    mat, rng = _rand(82, 10, 96, 16, 16, 2)
+    W = to_dev(mat)
+    h = torch.zeros((0, 96), device="cuda")
+    lut = la.build_lut(W, h)
+    assert lut.numel() == 0
+    out = la.decode_rows(W, torch.zeros(0, dtype=torch.int32, device="cuda"))
+    assert out.shape == (0, 96)
+
+
+# ------------------------------------------------------------------ top-k with bf16 tables
+
+def _bf16_tol(mat, h, ref):
+    lut64 = O().build_lut(mat.codebooks, mat.cb_is_bf16, h)
+    absum = O().lut_sum(mat.codes, np.abs(lut64))
+    return 2.0 ** -8 * absum + 1e-5 * np.abs(ref).max(axis=1, keepdims=True)
+
+
+@pytest.mark.parametrize("lut_dtype", ["f32", "bf16"])
+def test_topk(lut_dtype):
+    K, L, B, k = 4096, 4, 5, 50
+    mat, rng = _rand(90, 6000, 96, 16, K, L, "bf16", sigmas=(0.02, 0.008, 0.003, 0.001))
+    h = synth.gen_hidden(rng, B, 96)
+    W = to_dev(mat)
+    lut = la.build_lut(W, dev(h), lut_dtype=lut_dtype)
+    lg, am, ti, tv = la.lut_logits(W, lut, B, softcap=30.0, lut_dtype=lut_dtype, topk=k)
+    g, ids, vals, amh = host(lg), host(ti), host(tv), host(am)
+    _, ref = oracle_head(mat, h, 30.0)
+    tolv = _bf16_tol(mat, h, ref) if lut_dtype == "bf16" else 1e-5 * np.abs(ref).max(axis=1, keepdims=True) * np.ones_like(ref)
+    check_logits(g, ref, tol=tolv.max(axis=1) if lut_dtype == "bf16" else None)
+    for b in range(B):
+        # self-consistent: exactly the top-k of the GPU's own logits, by (value desc, id asc)
+        order = np.lexsort((np.arange(g.shape[1]), -g[b]))[:k]
+        assert np.array_equal(ids[b], order)
+        assert np.array_equal(vals[b], g[b, order])
+        assert amh[b] == ids[b, 0]
+        # against the oracle
+        t = tolv[b].max()
+        kth = np.sort(ref[b])[::-1][k - 1]
+        must = np.nonzero(ref[b] > kth + 2 * t)[0]
+        assert set(must.tolist()) <= set(ids[b].tolist())
+        assert np.all(ref[b, ids[b]] >= kth - 2 * t)
+        oref = np.lexsort((np.arange(ref.shape[1]), -ref[b]))[:k]
+        srt = ref[b, oref]
+        for i in range(k):   # ranks whose gaps to both neighbours exceed 2t are fixed exactly
+            lo = srt[i + 1] if i + 1 < k else kth - 1e9
+            hi = srt[i - 1] if i > 0 else srt[i] + 1e9
+            if hi - srt[i] > 2 * t and srt[i] - lo > 2 * t:
+                assert ids[b, i] == oref[i]
+
+
+# ------------------------------------------------------------------ MLP LUT-matvec
+
+def test_lut_matvec_small_chain():
+    rng = np.random.default_rng(100)
+    hid, inter = 96, 160
+    gate = synth.gen_matrix(rng, inter, hid, 48, 64, 2, (0.02, 0.005), "f32")
+    up = synth.gen_matrix(rng, inter, hid, 48, 64, 2, (0.02, 0.005), "f32")
+    down = synth.gen_matrix(rng, hid, inter, 80, 64, 2, (0.02, 0.005), "f32")
+    x = synth.gen_hidden(rng, 2, hid)
+    Wg, Wu, Wd = to_dev(gate), to_dev(up), to_dev(down)
+    g = la.lut_matvec(Wg, dev(x))
+    u = la.lut_matvec(Wu, dev(x))
+    y = la.lut_matvec(Wd, g, x2=u, prologue=la.RQ_PRO_GELU_TANH_MUL)
+    og, ou, oa, oy = O().mlp((gate.codes, gate.codebooks, False), (up.codes, up.codebooks, False),
+                             (down.codes, down.codebooks, False), x)
+    check_logits(host(g), og)
+    check_logits(host(u), ou)
+    check_logits(host(y), oy)
+
+
+def test_mlp_layer_gemma_shapes():
+    """One Gemma-2-2B MLP layer: gate/up 9216x2304 (d=2), down 2304x9216 (d=2), K=1024, L=2, fp32 codebooks."""
+    gate, up, down = synth.make_mlp_layer(0)
+    x = synth.make_mlp_x()
+    Wg, Wu, Wd = to_dev(gate), to_dev(up), to_dev(down)
+    g = la.lut_matvec(Wg, dev(x))
+    u = la.lut_matvec(Wu, dev(x))
+    y = la.lut_matvec(Wd, g, x2=u, prologue=la.RQ_PRO_GELU_TANH_MUL)
+    og, ou, oa, oy = O().mlp((gate.codes, gate.codebooks, False), (up.codes, up.codebooks, False),
+                             (down.codes, down.codebooks, False), x)
+    check_logits(host(g), og)
+    check_logits(host(u), ou)
+    check_logits(host(y), oy)
+    # down alone, fed the oracle's gate/up outputs rounded to fp32
+    g32, u32 = og.astype(np.float32), ou.astype(np.float32)
+    y1 = la.lut_matvec(Wd, dev(g32), x2=dev(u32), prologue=la.RQ_PRO_GELU_TANH_MUL)
+    a = O().gelu_mul(g32.astype(np.float64), u32.astype(np.float64))
+    check_logits(host(y1), O().matvec(down.codes, down.codebooks, False, a))
+
+
+# ------------------------------------------------------------------ dense comparison head
+
+def test_dense_comparator():
+    """The dense bf16 head against an fp64 numpy product of the same bf16 values."""
+    mat, rng = _rand(110, 5000, 96, 16, 256, 2, "bf16")
+    h = synth.gen_hidden(rng, 3, 96)
+    W = to_dev(mat)
+    E = la.decode_rows(W, torch.arange(5000, dtype=torch.int32, device="cuda"), "bf16")
+    lg, am = la.dense_logits(E, dev(h), softcap=0.0)
+    Ef = synth.bf16_bits_to_f32(host(E).view(np.uint16)).astype(np.float64)
+    hb = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(h)).astype(np.float64)
+    ref = hb @ Ef.T
+    check_logits(host(lg), ref)
+    assert np.array_equal(host(am), np.argmax(host(lg), axis=1).astype(np.int32))
