@@ -1,0 +1,239 @@
+"""Benchmark of the RQ LUT logits head on one MI355X.
+
+One step = one pass of the serving hot path for one decode token on the
+Gemma-2-2B-shaped tied head (256000 x 2304, M=384 subspaces of d=6, K=1024,
+L=2, bf16 codebooks, fp32 table):
+  rq_decode_rows (64 input token rows, bf16)  ->  rq_build_lut (B=1)  ->
+  rq_lut_logits (lookup+sum, softcap 30, fp32 logits, argmax).
+Inputs are synthetic (seeded), resident in HBM before timing; two copies of
+the code stream are rotated so the 256 MB Infinity Cache cannot serve
+repeated reads.
+
+Prints ONE JSON line. value = vocab rows per second of the whole step.
+Besides it: per-call times (HIP events on the stream the library launches
+on), the roofline of the dominant kernel, the batched (B=16) head, one MLP
+layer by LUT-matvec, the dense bf16 head on the same GPU, and the CPU oracle
+timed on the host's cores.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "LUT-logits vocab-rows/s at B=1/16 + achieved HBM GB/s vs peak (256000x2304 head)"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--no-extras", action="store_true", help="only the headline step (used under profilers)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 256 MiB device copy (counter calibration under rocprofv3 --pmc)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the head shards over the vocabulary with one tiny all-gather; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import lut_logits_amd as la
+    from lut_logits_amd import formats, synth
+
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    cfg = synth.CONFIGS["gemma_b1"]
+    V, D, M, K, L = cfg.V, cfg.D, cfg.M, cfg.K, cfg.L
+    mat, h, ids = synth.make_head(cfg)
+    # two resident copies of the matrix (rotation defeats the 256 MB Infinity Cache)
+    Ws = [la.to_device(mat), la.to_device(mat)]
+    ht = torch.from_numpy(h).to(dev)
+    idt = torch.from_numpy(ids).to(dev)
+    lut = la.build_lut(Ws[0], ht)
+    logits = torch.empty((1, V), dtype=torch.float32, device=dev)
+    ws = la.workspace(la.lut_logits_workspace(Ws[0], 1), dev)
+    torch.cuda.synchronize()
+
+    def step(i):
+        W = Ws[i & 1]
+        la.decode_rows(W, idt, "bf16")
+        la.build_lut(W, ht, out=lut)
+        return la.lut_logits(W, lut, 1, softcap=cfg.softcap, out=logits, ws=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # per-call durations: events between the calls, on the stream the library launches on
+    n_calls = min(args.steps, 100)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_calls)]
+    for i in range(n_calls):
+        W = Ws[i & 1]
+        ev[i][0].record()
+        la.decode_rows(W, idt, "bf16")
+        ev[i][1].record()
+        la.build_lut(W, ht, out=lut)
+        ev[i][2].record()
+        la.lut_logits(W, lut, 1, softcap=cfg.softcap, out=logits, ws=ws)
+        ev[i][3].record()
+    torch.cuda.synchronize()
+    t_dec = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    t_build = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    t_logits = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    t_logits_med = float(np.median([e[2].elapsed_time(e[3]) for e in ev]))
+
+    code_bytes = formats.code_bytes(V, L, M)
+    lut_b = formats.lut_bytes(1, L, M, K)
+    algo_bytes = code_bytes + lut_b + V * 4   # codes + table once + fp32 logits out
+    achieved = algo_bytes / (t_logits * 1e-3) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": V / (ms_step * 1e-3),
+        "unit": "vocab-rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; Gaussian codewords, uniform codes, N(0,1) hidden state)",
+        "config": {"workload": "Gemma-2-2B tied head 256000x2304 RQ M=384 d=6 K=1024 L=2, bf16 codebooks, "
+                               "fp32 table, B=1: decode 64 rows + build table + lookup+sum + softcap 30 + argmax",
+                   "global_batch": 1, "rows": V, "D": D, "M": M, "K": K, "L": L, "codes_layout": "blocked"},
+        "roofline": {"bound": "hbm", "kernel": "rq_lut_logits call (lookup+sum, epilogue, selection)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "algorithmic_bytes": algo_bytes, "traffic": None},
+        "calls_ms": {"decode_rows_64": t_dec, "build_lut": t_build, "lut_logits": t_logits,
+                     "lut_logits_median": t_logits_med},
+        "resident_bytes": {"lut_head": Ws[0].resident_bytes() + lut_b + ws.numel(),
+                           "dense_bf16_head": formats.dense_bytes(V, D)},
+    }
+
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = src.numel()
+
+    if not args.no_extras:
+        out.update(extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, dev))
+    del Ws, lut, ws
+    torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(mat, h, cfg)
+    print(json.dumps(out))
+
+
+def timed(fn, n, torch):
+    """Mean milliseconds of fn() over n calls (HIP events on the current stream) after 3 warm-up calls."""
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(n):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, dev):
+    res = {}
+    V = cfg.V
+    # batched head, B=16 (same matrix; one table per vector)
+    c16 = synth.CONFIGS["gemma_b16"]
+    h16 = torch.from_numpy(synth.gen_hidden(np.random.default_rng(c16.seed), 16, cfg.D)).to(dev)
+    lut16 = la.build_lut(Ws[0], h16)
+    lg16 = torch.empty((16, V), dtype=torch.float32, device=dev)
+    ws16 = la.workspace(la.lut_logits_workspace(Ws[0], 16), dev)
+
+    def head16(i=0):
+        W = Ws[i & 1]
+        la.build_lut(W, h16, out=lut16)
+        la.lut_logits(W, lut16, 16, softcap=30.0, out=lg16, ws=ws16)
+
+    t16 = timed(head16, 20, torch)
+    res["b16"] = {"ms_per_call": t16, "vocab_rows_per_s": V / (t16 * 1e-3), "token_rows_per_s": 16 * V / (t16 * 1e-3)}
+    del lut16, lg16, ws16
+
+    # dense bf16 head on the same GPU: E = bf16(decode(all rows)), built by rq_decode_rows
+    E = la.decode_rows(Ws[0], torch.arange(V, dtype=torch.int32, device=dev), "bf16")
+    E2 = E.clone()
+    Es = [E, E2]
+    lgd = torch.empty((16, V), dtype=torch.float32, device=dev)
+    wsd = la.workspace(la.dense_logits_workspace(V, 16), dev)
+    td1 = timed(lambda i=0: la.dense_logits(Es[i & 1], ht, 30.0, ws=wsd, out=lgd[:1]), 50, torch)
+    td16 = timed(lambda i=0: la.dense_logits(Es[i & 1], h16, 30.0, ws=wsd, out=lgd), 20, torch)
+    res["dense_bf16"] = {"ms_b1": td1, "ms_b16": td16, "gbs_b1": formats.dense_bytes(V, cfg.D) / (td1 * 1e-3) / 1e9,
+                         "resident_bytes": formats.dense_bytes(V, cfg.D)}
+    del E, E2, Es, lgd, wsd, h16
+
+    # one Gemma-2-2B MLP layer by LUT-matvec (gate, up, down with the gelu_tanh*up prologue)
+    layers = [synth.make_mlp_layer(i) for i in range(2)]
+    dl = [[la.to_device(m) for m in lay] for lay in layers]
+    x = torch.from_numpy(synth.make_mlp_x()).to(dev)
+    wsm = la.workspace(max(la.lut_matvec_workspace(w, 1) for lay in dl for w in lay), dev)
+    g = torch.empty((1, synth.MLP_INTER), device=dev)
+    u = torch.empty_like(g)
+    y = torch.empty((1, synth.MLP_HIDDEN), device=dev)
+
+    def mlp(i=0):
+        Wg, Wu, Wd = dl[i & 1]
+        la.lut_matvec(Wg, x, ws=wsm, out=g)
+        la.lut_matvec(Wu, x, ws=wsm, out=u)
+        la.lut_matvec(Wd, g, x2=u, prologue=la.RQ_PRO_GELU_TANH_MUL, ws=wsm, out=y)
+
+    tm = timed(mlp, 20, torch)
+    code_b = sum(formats.code_bytes(m.rows, m.L, m.M) for m in layers[0])
+    cb_b = sum(m.codebooks.nbytes for m in layers[0])
+    res["mlp_layer"] = {"ms": tm, "code_bytes": code_b, "codebook_bytes": cb_b,
+                        "gbs_codes_plus_codebooks": (code_b + cb_b) / (tm * 1e-3) / 1e9,
+                        "ms_26_layers_est": 26 * tm}
+    return res
+
+
+def cpu_baseline(mat, h, cfg):
+    """The CPU oracle (decode + matmul in fp64) on the full head, repeated for >= 5 s of host time."""
+    import oracle
+
+    o = oracle.default()
+    nt = o.max_threads()
+    passes, t0 = 0, time.time()
+    while passes < 10 and (passes == 0 or time.time() - t0 < 5.0):
+        o.logits(mat.codes, mat.codebooks, mat.cb_is_bf16, h, cfg.softcap, nthreads=nt)
+        passes += 1
+    dt = time.time() - t0
+    return {"value": passes * cfg.V / dt, "unit": "vocab-rows/s", "cores": nt, "kind": "oracle",
+            "sample": f"full 256000-row head at B=1 (decode+matmul+softcap in fp64), {passes} passes, {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -34,8 +34,11 @@
  *   - Codes must be < K; a larger code is a precondition violation that the
  *     kernels do not check (it reads a neighbouring table entry; results are
  *     undefined, memory outside the library's own buffers is never touched).
- *   - Alignment. codes, lut, x, x2 and all outputs must be 16-byte aligned,
- *     workspaces 256-byte aligned (torch allocations satisfy this).
+ *   - Alignment. codes and lut must be 16-byte aligned, other arrays 4-byte
+ *     aligned, workspaces 256-byte aligned (torch allocations satisfy this).
+ *   - Workspaces hold per-call scratch only (no state carries over between
+ *     calls, no initial contents are required). Calls that overlap in time
+ *     must not share a workspace.
  *   - Concurrency. Calls on different streams may run concurrently as long as
  *     they do not share output or workspace buffers.
  */
@@ -71,25 +74,27 @@ typedef enum rq_prologue {
  * Code layouts. The pages fix only that codes are 16-bit integers; the order
  * in memory is this library's choice. With NP = L*M (level, subspace) pairs
  * numbered p = l*M + m:
- *   RQ_CODES_ROWS    codes[r][l][m]: uint16 [rows][NP], the interchange layout
- *   RQ_CODES_PAIRED  codes[p/2][r][p%2]: uint16 [ceil(NP/2)][rows][2]; for NP
- *                    odd the unused last slot of every row is 0
- * Every entry point reads both. PAIRED is the serving layout: the code stream
- * for any run of consecutive pairs is contiguous over rows, so wave-wide loads
- * are fully coalesced. rq_pack_codes converts ROWS to PAIRED once, at load.
- * With RQ_CODES_ROWS, rq_lut_logits and rq_lut_matvec need NP even.
+ *   RQ_CODES_ROWS     codes[r][l][m]: uint16 [rows][NP], the interchange layout
+ *   RQ_CODES_BLOCKED  codes[p/8][r][p%8]: uint16 [ceil(NP/8)][rows][8]; each
+ *                     row's codes for 8 consecutive pairs are 16 contiguous
+ *                     bytes, and consecutive rows are adjacent. Unused slots
+ *                     of the last block (NP not a multiple of 8) are 0.
+ * Every entry point reads both. BLOCKED is the serving layout: a wave loads
+ * 64 rows x 16 bytes as one contiguous 1 KB run, whatever chunk of pairs it
+ * works on. rq_pack_codes converts ROWS to BLOCKED once, at load. With
+ * RQ_CODES_ROWS, rq_lut_logits and rq_lut_matvec need NP % 8 == 0.
  */
-typedef enum rq_codes_layout { RQ_CODES_ROWS = 0, RQ_CODES_PAIRED = 1 } rq_codes_layout;
+typedef enum rq_codes_layout { RQ_CODES_ROWS = 0, RQ_CODES_BLOCKED = 1 } rq_codes_layout;
 
 /*
  * Non-owning description of one RQ-coded matrix W[rows][D].
  *   rows          vocabulary size V for a head, out_features for an MLP matrix,
- *                 1 <= rows < 2^31
+ *                 0 <= rows < 2^29
  *   D, M, d       D == M*d, all >= 1
  *   K             codewords per codebook, 1 <= K <= 65536 (but see RQ_MAX_K_F32)
  *   L             residual levels, 1 <= L <= RQ_MAX_L
  *   cb_dtype      RQ_F32 or RQ_BF16, the storage type of the codebooks
- *   codes_layout  RQ_CODES_ROWS or RQ_CODES_PAIRED
+ *   codes_layout  RQ_CODES_ROWS or RQ_CODES_BLOCKED
  *   codebooks     device [L][M][K][d] of cb_dtype
  *   codes         device uint16 in codes_layout, 16-byte aligned
  */
@@ -102,12 +107,12 @@ typedef struct rq_matrix {
   const uint16_t* codes;
 } rq_matrix;
 
-/* Bytes of the RQ_CODES_PAIRED layout: ceil(L*M/2) * rows * 4. */
-size_t rq_paired_codes_bytes(int64_t rows, int32_t L, int32_t M);
+/* Bytes of the RQ_CODES_BLOCKED layout: ceil(L*M/8) * rows * 16. */
+size_t rq_blocked_codes_bytes(int64_t rows, int32_t L, int32_t M);
 
 /*
  * Convert codes from RQ_CODES_ROWS (src, uint16 [rows][L*M]) to
- * RQ_CODES_PAIRED (dst, rq_paired_codes_bytes bytes). src and dst must not
+ * RQ_CODES_BLOCKED (dst, rq_blocked_codes_bytes bytes). src and dst must not
  * overlap. A pure permutation: the codes are copied bit for bit.
  */
 rq_status rq_pack_codes(const uint16_t* src, int64_t rows, int32_t L, int32_t M, uint16_t* dst,
@@ -186,7 +191,8 @@ rq_status rq_decode_rows(const rq_matrix* W, const int32_t* ids, int32_t n, int3
                          void* out, int32_t* bad_ids, hipStream_t stream);
 
 /*
- * Workspace bytes rq_lut_matvec needs (the fp32 table plus partial sums).
+ * Workspace bytes rq_lut_matvec needs (the fp32 table and partial
+ * sums).
  */
 size_t rq_lut_matvec_workspace(const rq_matrix* W, int32_t B);
 
@@ -213,6 +219,7 @@ rq_status rq_lut_matvec(const rq_matrix* W, const float* x, const float* x2, int
  *   h       device fp32 [B][D], 1 <= B <= 16
  *   logits  device fp32 [B][rows] (required); argmax device int32 [B] or NULL
  *   ws      device workspace of at least rq_dense_logits_workspace() bytes
+ *           (only used when argmax != NULL)
  */
 size_t rq_dense_logits_workspace(int64_t rows, int32_t B);
 rq_status rq_dense_logits(const uint16_t* E, int64_t rows, int32_t D, const float* h, int32_t B,

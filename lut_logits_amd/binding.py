@@ -16,10 +16,10 @@ LIB_PATH = os.path.join(HERE, "librq_lut.so")
 RQ_OK, RQ_ERR_NULL, RQ_ERR_SHAPE, RQ_ERR_DTYPE, RQ_ERR_ALIGN, RQ_ERR_WORKSPACE, RQ_ERR_HIP = 0, -1, -2, -3, -4, -5, -6
 RQ_F32, RQ_BF16 = 0, 1
 RQ_PRO_NONE, RQ_PRO_GELU_TANH_MUL = 0, 1
-RQ_CODES_ROWS, RQ_CODES_PAIRED = 0, 1
+RQ_CODES_ROWS, RQ_CODES_BLOCKED = 0, 1
 
 # Every symbol include/rq_lut.h declares.
-EXPORTS = ("rq_paired_codes_bytes", "rq_pack_codes", "rq_lut_bytes", "rq_build_lut", "rq_lut_logits_workspace",
+EXPORTS = ("rq_blocked_codes_bytes", "rq_pack_codes", "rq_lut_bytes", "rq_build_lut", "rq_lut_logits_workspace",
            "rq_lut_logits", "rq_decode_rows", "rq_lut_matvec_workspace", "rq_lut_matvec",
            "rq_dense_logits_workspace", "rq_dense_logits", "rq_status_string", "rq_last_error", "rq_version")
 
@@ -49,7 +49,7 @@ def lib():
             raise RuntimeError(f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
         L = ctypes.CDLL(LIB_PATH)
         sig = {
-            "rq_paired_codes_bytes": (_sz, [_i64, _i32, _i32]),
+            "rq_blocked_codes_bytes": (_sz, [_i64, _i32, _i32]),
             "rq_pack_codes": (_i32, [_vp, _i64, _i32, _i32, _vp, _vp]),
             "rq_lut_bytes": (_sz, [_MP, _i32, _i32]),
             "rq_build_lut": (_i32, [_MP, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
@@ -99,7 +99,7 @@ class DeviceMatrix:
         self.cb_dtype, self.layout = cb_dtype, layout
         self.codebooks, self.codes = codebooks, codes
         self.desc = rq_matrix(rows, D, M, D // M, K, L, _dtype_code(cb_dtype),
-                              RQ_CODES_PAIRED if layout == "paired" else RQ_CODES_ROWS,
+                              RQ_CODES_BLOCKED if layout == "blocked" else RQ_CODES_ROWS,
                               codebooks.data_ptr(), codes.data_ptr() if codes is not None else 0)
 
     @property
@@ -110,7 +110,7 @@ class DeviceMatrix:
         return self.codebooks.numel() * self.codebooks.element_size() + self.codes.numel() * self.codes.element_size()
 
 
-def to_device(mat, layout="paired", device="cuda"):
+def to_device(mat, layout="blocked", device="cuda"):
     """Upload a host RQMatrix (lut_logits_amd.synth) and, for the paired layout, repack its codes on the GPU."""
     cb_np = mat.codebooks.view(np.int16) if mat.cb_is_bf16 else mat.codebooks
     cb = torch.from_numpy(np.ascontiguousarray(cb_np)).to(device)
@@ -119,16 +119,16 @@ def to_device(mat, layout="paired", device="cuda"):
         return DeviceMatrix(mat.rows, mat.D, mat.M, mat.K, mat.L, mat.cb_dtype, cb, rows_codes, "rows")
     packed = pack_codes(rows_codes, mat.rows, mat.L, mat.M)
     del rows_codes
-    return DeviceMatrix(mat.rows, mat.D, mat.M, mat.K, mat.L, mat.cb_dtype, cb, packed, "paired")
+    return DeviceMatrix(mat.rows, mat.D, mat.M, mat.K, mat.L, mat.cb_dtype, cb, packed, "blocked")
 
 
-def paired_codes_bytes(rows, L, M):
-    return lib().rq_paired_codes_bytes(rows, L, M)
+def blocked_codes_bytes(rows, L, M):
+    return lib().rq_blocked_codes_bytes(rows, L, M)
 
 
 def pack_codes(rows_codes, rows, L, M):
     """rq_pack_codes: [rows][L*M] uint16 -> the paired layout (returned as an int16 tensor)."""
-    nbytes = paired_codes_bytes(rows, L, M)
+    nbytes = blocked_codes_bytes(rows, L, M)
     dst = torch.empty(nbytes // 2, dtype=torch.int16, device=rows_codes.device)
     check(lib().rq_pack_codes(_ptr(rows_codes), rows, L, M, _ptr(dst), _stream()))
     return dst
@@ -153,28 +153,30 @@ def lut_logits_workspace(W, B, topk=0, lut_dtype="f32"):
 
 
 def workspace(nbytes, device="cuda"):
-    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    """A workspace buffer: zero-filled once, as the library requires before first use."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
-def lut_logits(W, lut, B, softcap=30.0, lut_dtype="f32", logits=True, argmax=True, topk=0, ws=None, out=None):
+def lut_logits(W, lut, B, softcap=30.0, lut_dtype="f32", logits=True, argmax=True, topk=0, ws=None, out=None,
+               argmax_out=None):
     """rq_lut_logits: returns (logits [B][rows] | None, argmax [B] | None, topk_ids | None, topk_vals | None)."""
     dev = lut.device
     lg = (out if out is not None else torch.empty((B, W.rows), dtype=torch.float32, device=dev)) if logits else None
-    am = torch.empty(B, dtype=torch.int32, device=dev) if argmax else None
+    am = (argmax_out if argmax_out is not None else torch.empty(B, dtype=torch.int32, device=dev)) if argmax else None
     ti = torch.empty((B, topk), dtype=torch.int32, device=dev) if topk else None
     tv = torch.empty((B, topk), dtype=torch.float32, device=dev) if topk else None
-    need = lut_logits_workspace(W, B, topk, lut_dtype)
     if ws is None:
-        ws = workspace(need, dev)
+        ws = workspace(lut_logits_workspace(W, B, topk, lut_dtype), dev)
     check(lib().rq_lut_logits(W.ref, _ptr(lut), _dtype_code(lut_dtype), B, softcap, _ptr(lg), _ptr(am), topk,
                               _ptr(ti), _ptr(tv), _ptr(ws), ws.numel(), _stream()))
     return lg, am, ti, tv
 
 
-def decode_rows(W, ids, out_dtype="f32", bad_ids=None):
+def decode_rows(W, ids, out_dtype="f32", bad_ids=None, out=None):
     """rq_decode_rows: rows [n][D] (fp32, or bf16 bit patterns as int16)."""
     n = ids.shape[0]
-    out = torch.empty((n, W.D), dtype=torch.int16 if out_dtype == "bf16" else torch.float32, device=ids.device)
+    if out is None:
+        out = torch.empty((n, W.D), dtype=torch.int16 if out_dtype == "bf16" else torch.float32, device=ids.device)
     check(lib().rq_decode_rows(W.ref, _ptr(ids), n, _dtype_code(out_dtype), _ptr(out), _ptr(bad_ids), _stream()))
     return out
 

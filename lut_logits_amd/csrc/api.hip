@@ -36,14 +36,14 @@ bool valid_dtype(int32_t t) { return t == RQ_F32 || t == RQ_BF16; }
 // Shape, dtype, layout and pointer checks of a matrix descriptor.
 rq_status check_matrix(const rq_matrix* W, bool need_codes) {
   if (!W) return fail(RQ_ERR_NULL, "matrix descriptor is NULL");
-  if (W->rows < 0 || W->rows >= ((int64_t)1 << 31)) return fail(RQ_ERR_SHAPE, "rows=%lld out of range", (long long)W->rows);
+  if (W->rows < 0 || W->rows >= ((int64_t)1 << 29)) return fail(RQ_ERR_SHAPE, "rows=%lld out of range", (long long)W->rows);
   if (W->M < 1 || W->d < 1 || (int64_t)W->M * W->d != W->D)
     return fail(RQ_ERR_SHAPE, "need D == M*d with M, d >= 1 (D=%d M=%d d=%d)", W->D, W->M, W->d);
   if (W->K < 1 || W->K > 65536) return fail(RQ_ERR_SHAPE, "K=%d outside [1, 65536]", W->K);
   if (W->L < 1 || W->L > RQ_MAX_L) return fail(RQ_ERR_SHAPE, "L=%d outside [1, %d]", W->L, RQ_MAX_L);
   if ((int64_t)W->L * W->M > (1 << 24)) return fail(RQ_ERR_SHAPE, "L*M=%lld too large", (long long)W->L * W->M);
   if (!valid_dtype(W->cb_dtype)) return fail(RQ_ERR_DTYPE, "unknown codebook dtype %d", W->cb_dtype);
-  if (W->codes_layout != RQ_CODES_ROWS && W->codes_layout != RQ_CODES_PAIRED)
+  if (W->codes_layout != RQ_CODES_ROWS && W->codes_layout != RQ_CODES_BLOCKED)
     return fail(RQ_ERR_DTYPE, "unknown codes layout %d", W->codes_layout);
   if (!W->codebooks) return fail(RQ_ERR_NULL, "codebooks is NULL");
   if (!aligned(W->codebooks, W->cb_dtype == RQ_F32 ? 4 : 2)) return fail(RQ_ERR_ALIGN, "codebooks misaligned");
@@ -63,17 +63,21 @@ rq_status check_table_fits(const rq_matrix* W, int lut_bf16) {
   return RQ_OK;
 }
 
+// Workspace of rq_lut_logits, in this order (each part 256-byte aligned):
+//   partial sums [G][B][rows] fp32 (G > 1 only), a logits scratch [B][rows]
+//   fp32 (top-k without a logits output), the per-block selection keys
+//   [B][key_blocks] uint64 and the top-k candidates [B][nblk][topk] uint64.
 struct LogitsWs {
-  size_t partial, keys, cand, total;
+  size_t partial, scratch, keys, cand, total;
 };
 
-LogitsWs logits_ws(const rq_matrix* W, const rq::GatherPlan& plan, int32_t B, int32_t topk) {
-  const int nblk = rq::epi_blocks(W->rows);
+LogitsWs logits_ws(const rq_matrix* W, const rq::GatherPlan& plan, int32_t B, int32_t topk, bool logits_out) {
   LogitsWs w;
   w.partial = 0;
-  w.keys = round_up((size_t)plan.G * B * W->rows * sizeof(float), 256);
-  w.cand = w.keys + round_up((size_t)B * nblk * sizeof(uint64_t), 256);
-  w.total = w.cand + round_up((size_t)B * nblk * (size_t)std::max(topk, 0) * sizeof(uint64_t), 256);
+  w.scratch = w.partial + (plan.G > 1 ? round_up((size_t)plan.G * B * W->rows * sizeof(float), 256) : 0);
+  w.keys = w.scratch + (topk > 0 && !logits_out ? round_up((size_t)B * W->rows * sizeof(float), 256) : 0);
+  w.cand = w.keys + round_up((size_t)B * rq::key_blocks(plan, W->rows) * sizeof(uint64_t), 256);
+  w.total = w.cand + (topk > 0 ? round_up((size_t)B * rq::epi_blocks(W->rows) * topk * sizeof(uint64_t), 256) : 0);
   return w;
 }
 
@@ -84,8 +88,12 @@ rq_status check_lut_call(const rq_matrix* W, int32_t B, int32_t lut_dtype) {
   if (!valid_dtype(lut_dtype)) return fail(RQ_ERR_DTYPE, "unknown table dtype %d", lut_dtype);
   s = check_table_fits(W, lut_dtype == RQ_BF16);
   if (s != RQ_OK) return s;
-  if (W->codes_layout == RQ_CODES_ROWS && ((W->L * W->M) & 1))
-    return fail(RQ_ERR_ALIGN, "row-major codes need L*M even (L*M=%d); pack them with rq_pack_codes", W->L * W->M);
+  if (W->codes_layout == RQ_CODES_ROWS && ((W->L * W->M) & 7))
+    return fail(RQ_ERR_ALIGN, "row-major codes need L*M %% 8 == 0 (L*M=%d); pack them with rq_pack_codes", W->L * W->M);
+  const int64_t code_bytes = W->codes_layout == RQ_CODES_ROWS ? W->rows * (int64_t)W->L * W->M * 2
+                                                              : W->rows * (((int64_t)W->L * W->M + 7) / 8) * 16;
+  if (code_bytes >= ((int64_t)1 << 32))
+    return fail(RQ_ERR_SHAPE, "code array of %lld bytes exceeds the 4 GiB a lookup pass addresses", (long long)code_bytes);
   return RQ_OK;
 }
 
@@ -110,13 +118,13 @@ const char* rq_status_string(rq_status s) {
   return "unknown status";
 }
 
-size_t rq_paired_codes_bytes(int64_t rows, int32_t L, int32_t M) {
+size_t rq_blocked_codes_bytes(int64_t rows, int32_t L, int32_t M) {
   if (rows < 0 || L < 1 || M < 1) return 0;
-  return (size_t)(((int64_t)L * M + 1) / 2) * (size_t)rows * 4;
+  return (size_t)(((int64_t)L * M + 7) / 8) * (size_t)rows * 16;
 }
 
 rq_status rq_pack_codes(const uint16_t* src, int64_t rows, int32_t L, int32_t M, uint16_t* dst, hipStream_t stream) {
-  if (rows < 0 || rows >= ((int64_t)1 << 31) || L < 1 || L > RQ_MAX_L || M < 1 || (int64_t)L * M > (1 << 24))
+  if (rows < 0 || rows >= ((int64_t)1 << 29) || L < 1 || L > RQ_MAX_L || M < 1 || (int64_t)L * M > (1 << 24))
     return fail(RQ_ERR_SHAPE, "bad pack shape rows=%lld L=%d M=%d", (long long)rows, L, M);
   if (rows == 0) return RQ_OK;
   if (!src || !dst) return fail(RQ_ERR_NULL, "pack: NULL buffer");
@@ -147,7 +155,7 @@ size_t rq_lut_logits_workspace(const rq_matrix* W, int32_t B, int32_t topk, int3
   if (B == 0 || W->rows == 0) return 0;
   const rq::GatherPlan plan = rq::plan_gather(W, B, lut_dtype == RQ_BF16);
   if (plan.BT == 0) return 0;
-  return logits_ws(W, plan, B, topk).total;
+  return logits_ws(W, plan, B, topk, false).total;   // enough with or without a logits output
 }
 
 rq_status rq_lut_logits(const rq_matrix* W, const void* lut, int32_t lut_dtype, int32_t B, float softcap,
@@ -166,20 +174,21 @@ rq_status rq_lut_logits(const rq_matrix* W, const void* lut, int32_t lut_dtype, 
     return fail(RQ_ERR_ALIGN, "output misaligned");
   const rq::GatherPlan plan = rq::plan_gather(W, B, lut_dtype == RQ_BF16);
   if (plan.BT == 0) return fail(RQ_ERR_SHAPE, "no table tiling fits on chip for K=%d", W->K);
-  const LogitsWs w = logits_ws(W, plan, B, topk);
+  const LogitsWs w = logits_ws(W, plan, B, topk, logits != nullptr);
   if (!ws || ws_bytes < w.total) return fail(RQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, w.total);
   if (!aligned(ws, 256)) return fail(RQ_ERR_ALIGN, "workspace must be 256-byte aligned");
   char* base = static_cast<char*>(ws);
-  float* partial = reinterpret_cast<float*>(base + w.partial);
-  uint64_t* keys = reinterpret_cast<uint64_t*>(base + w.keys);
-  uint64_t* cand = reinterpret_cast<uint64_t*>(base + w.cand);
   const bool select = argmax || topk > 0;
-  hipError_t e = rq::launch_gather(W, plan, lut, lut_dtype == RQ_BF16, B, partial, nullptr, 0, stream);
+  rq::GatherOut o;
+  o.partial = reinterpret_cast<float*>(base + w.partial);
+  o.out = logits ? logits : (topk > 0 ? reinterpret_cast<float*>(base + w.scratch) : nullptr);
+  o.softcap = softcap;
+  o.block_keys = select ? reinterpret_cast<uint64_t*>(base + w.keys) : nullptr;
+  hipError_t e = rq::launch_gather(W, plan, lut, lut_dtype == RQ_BF16, B, o, stream);
   if (e != hipSuccess) return launched(e, "rq_lut_logits: lookup+sum");
-  e = rq::launch_epilogue(partial, plan.G, B, W->rows, softcap, logits, select ? keys : nullptr, topk, cand, stream);
-  if (e != hipSuccess) return launched(e, "rq_lut_logits: epilogue");
   if (!select) return RQ_OK;
-  e = rq::launch_select(keys, rq::epi_blocks(W->rows), B, argmax, cand, topk, topk_ids, topk_vals, stream);
+  e = rq::launch_select(o.block_keys, rq::key_blocks(plan, W->rows), B, argmax, o.out, W->rows, topk,
+                        reinterpret_cast<uint64_t*>(base + w.cand), topk_ids, topk_vals, stream);
   return launched(e, "rq_lut_logits: selection");
 }
 
@@ -196,11 +205,25 @@ rq_status rq_decode_rows(const rq_matrix* W, const int32_t* ids, int32_t n, int3
   return launched(rq::launch_decode_rows(W, ids, n, out_dtype == RQ_BF16, out, bad_ids, stream), "rq_decode_rows");
 }
 
+// Workspace of rq_lut_matvec: the fp32 table [L][M][K][B], then the partial
+// sums [G][B][rows] (G > 1).
+struct MatvecWs {
+  size_t lut, partial, total;
+};
+
+MatvecWs matvec_ws(const rq_matrix* W, const rq::GatherPlan& plan, int32_t B) {
+  MatvecWs m;
+  m.lut = 0;
+  m.partial = round_up(lut_elems(W, B) * sizeof(float), 256);
+  m.total = m.partial + (plan.G > 1 ? round_up((size_t)plan.G * B * W->rows * sizeof(float), 256) : 0);
+  return m;
+}
+
 size_t rq_lut_matvec_workspace(const rq_matrix* W, int32_t B) {
   if (check_lut_call(W, B, RQ_F32) != RQ_OK || B == 0 || W->rows == 0) return 0;
   const rq::GatherPlan plan = rq::plan_gather(W, B, 0);
   if (plan.BT == 0) return 0;
-  return round_up(lut_elems(W, B) * sizeof(float), 256) + round_up((size_t)plan.G * B * W->rows * sizeof(float), 256);
+  return matvec_ws(W, plan, B).total;
 }
 
 rq_status rq_lut_matvec(const rq_matrix* W, const float* x, const float* x2, int32_t prologue, int32_t B, float* y,
@@ -213,19 +236,19 @@ rq_status rq_lut_matvec(const rq_matrix* W, const float* x, const float* x2, int
   if (!aligned(x, 4) || (x2 && !aligned(x2, 4)) || !aligned(y, 4)) return fail(RQ_ERR_ALIGN, "lut_matvec: misaligned buffer");
   const rq::GatherPlan plan = rq::plan_gather(W, B, 0);
   if (plan.BT == 0) return fail(RQ_ERR_SHAPE, "no table tiling fits on chip for K=%d", W->K);
-  const size_t lut_bytes = round_up(lut_elems(W, B) * sizeof(float), 256);
-  const size_t need = lut_bytes + round_up((size_t)plan.G * B * W->rows * sizeof(float), 256);
-  if (!ws || ws_bytes < need) return fail(RQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  const MatvecWs m = matvec_ws(W, plan, B);
+  if (!ws || ws_bytes < m.total) return fail(RQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, m.total);
   if (!aligned(ws, 256)) return fail(RQ_ERR_ALIGN, "workspace must be 256-byte aligned");
   char* base = static_cast<char*>(ws);
-  float* lut = reinterpret_cast<float*>(base);
-  float* partial = reinterpret_cast<float*>(base + lut_bytes);
+  float* lut = reinterpret_cast<float*>(base + m.lut);
   hipError_t e = rq::launch_build_lut(W, x, x2, prologue, B, 0, lut, stream);
   if (e != hipSuccess) return launched(e, "rq_lut_matvec: table build");
-  e = rq::launch_gather(W, plan, lut, 0, B, partial, nullptr, 0, stream);
-  if (e != hipSuccess) return launched(e, "rq_lut_matvec: lookup+sum");
-  return launched(rq::launch_epilogue(partial, plan.G, B, W->rows, 0.0f, y, nullptr, 0, nullptr, stream),
-                  "rq_lut_matvec: reduction");
+  rq::GatherOut o;
+  o.partial = reinterpret_cast<float*>(base + m.partial);
+  o.out = y;
+  o.softcap = 0.0f;
+  o.block_keys = nullptr;
+  return launched(rq::launch_gather(W, plan, lut, 0, B, o, stream), "rq_lut_matvec: lookup+sum");
 }
 
 size_t rq_dense_logits_workspace(int64_t rows, int32_t B) {
@@ -249,10 +272,10 @@ rq_status rq_dense_logits(const uint16_t* E, int64_t rows, int32_t D, const floa
     if (!aligned(ws, 256)) return fail(RQ_ERR_ALIGN, "workspace must be 256-byte aligned");
     keys = static_cast<uint64_t*>(ws);
   }
-  hipError_t e = rq::launch_dense_logits(E, rows, D, h, B, softcap, logits, keys, argmax, stream);
-  if (e != hipSuccess) return launched(e, "rq_dense_logits");
-  if (!argmax) return RQ_OK;
-  return launched(rq::launch_select(keys, rq::dense_blocks(rows), B, argmax, nullptr, 0, nullptr, nullptr, stream),
+  hipError_t e = rq::launch_dense_logits(E, rows, D, h, B, softcap, logits, keys, stream);
+  if (e != hipSuccess || !argmax) return launched(e, "rq_dense_logits");
+  return launched(rq::launch_select(keys, rq::dense_blocks(rows), B, argmax, logits, rows, 0, nullptr, nullptr,
+                                    nullptr, stream),
                   "rq_dense_logits: argmax");
 }
 

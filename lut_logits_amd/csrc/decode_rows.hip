@@ -1,5 +1,5 @@
 // decode_rows.hip -- on-demand reconstruction of selected rows, and the
-// one-time repacking of codes into the paired serving layout.
+// one-time repacking of codes into the blocked serving layout.
 //
 // Gemma-2-2B runtime-compression page, LUT-serving paragraph: the full
 // embedding is never rebuilt; the rows of the input tokens are reconstructed
@@ -49,7 +49,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_rows_kernel(CodeView cv
       const int j = e - m * d;
       for (int l = 0; l < L; ++l) {
         const int p = l * M + m;
-        const uint32_t code = cv.codes[(int64_t)(p >> 1) * cv.s_blk + id * cv.s_row + (p & 1)];
+        const uint32_t code = cv.codes[(int64_t)(p >> 3) * cv.s_blk + id * cv.s_row + (p & 7)];
         s += cb_value(cb + ((size_t)p * K + code) * d + j);
       }
     }
@@ -57,35 +57,35 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_rows_kernel(CodeView cv
   }
 }
 
-// codes[r][p] (uint16, [rows][NP]) -> words[q][r] = codes[r][2q] | codes[r][2q+1] << 16.
-// A 64-row x 64-word tile goes through LDS so both sides stay coalesced.
-constexpr int kPackTile = 64;
+// codes[r][p] (uint16, [rows][NP]) -> blocks[q][r] = codes[r][8q .. 8q+8) (16 bytes,
+// zero past NP). A 64-row x 16-block tile goes through LDS so that the reads
+// (256 contiguous bytes per row) and the writes (1 KB per block) stay coalesced.
+constexpr int kPackRows = 64;
+constexpr int kPackBlocks = 16;
 
 __global__ __launch_bounds__(256) void pack_codes_kernel(const uint16_t* __restrict__ src, int64_t rows, int NP,
-                                                         uint32_t* __restrict__ dst) {
-  __shared__ uint32_t tile[kPackTile][kPackTile + 1];
-  const int NQ = (NP + 1) >> 1;
-  const int64_t r0 = (int64_t)blockIdx.x * kPackTile;
-  const int q0 = blockIdx.y * kPackTile;
-  // read: each row's 128 consecutive codes (64 words), 4 rows per pass of 256 threads
-  for (int t = threadIdx.x; t < kPackTile * kPackTile; t += 256) {
-    const int rr = t / kPackTile;
-    const int qq = t - rr * kPackTile;
+                                                         uint4* __restrict__ dst) {
+  __shared__ uint4 tile[kPackRows][kPackBlocks + 1];
+  const int NQ = (NP + 7) >> 3;
+  const int64_t r0 = (int64_t)blockIdx.x * kPackRows;
+  const int q0 = blockIdx.y * kPackBlocks;
+  for (int t = threadIdx.x; t < kPackRows * kPackBlocks; t += 256) {
+    const int rr = t / kPackBlocks;
+    const int qq = t - rr * kPackBlocks;
     const int64_t r = r0 + rr;
     const int q = q0 + qq;
-    uint32_t w = 0;
+    uint32_t c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (r < rows && q < NQ) {
-      const uint16_t* row = src + r * NP;
-      const int p = 2 * q;
-      w = row[p];
-      if (p + 1 < NP) w |= (uint32_t)row[p + 1] << 16;
+      const uint16_t* row = src + r * NP + 8 * q;
+      for (int i = 0; i < 8; ++i)
+        if (8 * q + i < NP) c[i] = row[i];
     }
-    tile[rr][qq] = w;
+    tile[rr][qq] = make_uint4(c[0] | (c[1] << 16), c[2] | (c[3] << 16), c[4] | (c[5] << 16), c[6] | (c[7] << 16));
   }
   __syncthreads();
-  for (int t = threadIdx.x; t < kPackTile * kPackTile; t += 256) {
-    const int qq = t / kPackTile;
-    const int rr = t - qq * kPackTile;
+  for (int t = threadIdx.x; t < kPackRows * kPackBlocks; t += 256) {
+    const int qq = t / kPackRows;
+    const int rr = t - qq * kPackRows;
     const int64_t r = r0 + rr;
     const int q = q0 + qq;
     if (r < rows && q < NQ) dst[(int64_t)q * rows + r] = tile[rr][qq];
@@ -112,20 +112,20 @@ hipError_t launch_decode_rows(const rq_matrix* W, const int32_t* ids, int n, int
 }
 
 hipError_t launch_pack_codes(const uint16_t* src, int64_t rows, int NP, uint16_t* dst, hipStream_t stream) {
-  const int NQ = (NP + 1) >> 1;
-  dim3 grid((unsigned)((rows + kPackTile - 1) / kPackTile), (unsigned)((NQ + kPackTile - 1) / kPackTile));
-  hipLaunchKernelGGL(pack_codes_kernel, grid, dim3(256), 0, stream, src, rows, NP, reinterpret_cast<uint32_t*>(dst));
+  const int NQ = (NP + 7) >> 3;
+  dim3 grid((unsigned)((rows + kPackRows - 1) / kPackRows), (unsigned)((NQ + kPackBlocks - 1) / kPackBlocks));
+  hipLaunchKernelGGL(pack_codes_kernel, grid, dim3(256), 0, stream, src, rows, NP, reinterpret_cast<uint4*>(dst));
   return hipGetLastError();
 }
 
 CodeView code_view(const rq_matrix* W) {
   CodeView v;
   v.codes = W->codes;
-  if (W->codes_layout == RQ_CODES_PAIRED) {
-    v.s_blk = 2 * W->rows;
-    v.s_row = 2;
+  if (W->codes_layout == RQ_CODES_BLOCKED) {
+    v.s_blk = 8 * W->rows;
+    v.s_row = 8;
   } else {
-    v.s_blk = 2;
+    v.s_blk = 8;
     v.s_row = (int64_t)W->L * W->M;
   }
   return v;

@@ -5,8 +5,8 @@
 // table, "Uncompressed" row). This kernel is that path on the same GPU, so the
 // LUT head can be timed against it: E[rows][D] bf16 times up to 16 hidden
 // vectors rounded to bf16, accumulated in fp32 on the matrix cores
-// (v_mfma_f32_16x16x32_bf16), then the same softcap and argmax keys as the
-// LUT epilogue.
+// (v_mfma_f32_16x16x32_bf16), then the same softcap and argmax selection as
+// the LUT head (best key per block, reduced by the selection kernel).
 //
 // A wave owns 16 rows at a time: each lane loads 16 bytes (8 bf16) of one row
 // per k-step, so a wave-wide load is 16 rows x 64 contiguous bytes, and the
@@ -81,16 +81,15 @@ __global__ __launch_bounds__(kDenseThreads) void dense_logits_kernel(const uint1
       }
     }
   }
-  if (block_keys) {
-    __syncthreads();
-    if (threadIdx.x < B) block_keys[(size_t)threadIdx.x * gridDim.x + blockIdx.x] = bmax[threadIdx.x];
-  }
+  if (!block_keys) return;
+  __syncthreads();
+  if (threadIdx.x < B) block_keys[(size_t)threadIdx.x * gridDim.x + blockIdx.x] = bmax[threadIdx.x];
 }
 
 }  // namespace
 
 hipError_t launch_dense_logits(const uint16_t* E, int64_t rows, int D, const float* h, int B, float softcap,
-                               float* logits, uint64_t* block_keys, int32_t* /*argmax*/, hipStream_t stream) {
+                               float* logits, uint64_t* block_keys, hipStream_t stream) {
   const size_t lds = (size_t)16 * (D + 8) * sizeof(uint16_t);
   hipError_t e = hipFuncSetAttribute((const void*)dense_logits_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);

@@ -1,32 +1,44 @@
-// lut_gather.hip -- lookup+sum over the code stream, the logits epilogue and
-// the selection of argmax / top-k.
+// lut_gather.hip -- lookup+sum over the code stream with the logits epilogue
+// fused in, and the top-k selection.
 //
 //   z[b][r] = sum_{l<L} sum_{m<M} LUT[l][m][codes[r][l][m]][b]
+//   out[b][r] = softcap * tanh(z / softcap)  (or z),   argmax[b] = first max
 //
 // (Gemma-2-2B runtime-compression page, LUT-serving paragraph: output logits
-// by lookup+sum in place of a full matmul, then Gemma-2's own softcap.)
+// by lookup+sum in place of a full matmul, handed to Gemma-2's softcap.)
 //
 // Design for gfx950:
-//  * The table of one activation is L*M*K entries (3 MiB in fp32 at Gemma
-//    shapes), far larger than a CU's 160 KB of LDS. It is cut into chunks of
+//  * The table of one activation (L*M*K entries, 3 MiB in fp32 at Gemma
+//    shapes) is far larger than a CU's 160 KB of LDS. It is cut into chunks of
 //    P (level, subspace) pairs; a workgroup stages one chunk in LDS with
-//    coalesced 16-byte copies and then streams the codes of its row slab
-//    against it. Pairs are split into G groups of chunks; every group writes
-//    one partial sum per (row, batch), and the epilogue adds the G partials
-//    in a fixed order, so results are bit-reproducible and no atomics touch
-//    the sums.
-//  * One lane owns one row (for 16-wide batch tiles, a quad of lanes owns one
-//    row and each lane 4 batch entries, so a lookup is one contiguous 64-byte
-//    LDS read per quad). Codes are read as 32-bit words holding two
-//    consecutive pairs; in the paired layout the words of consecutive rows
-//    are adjacent, so every wave-wide load is one contiguous run.
-//  * Each lane issues the loads of all its row steps before touching LDS, so
-//    up to NSTEP loads per lane are in flight to hide HBM latency.
-//  * The workgroup -> (group, slab) mapping keeps all workgroups of one XCD on
-//    the same group of chunks, so its L2 serves their table staging.
+//    coalesced 16-byte copies and streams the codes of its row slab against
+//    it. The pairs are split into G groups of consecutive chunks; a workgroup
+//    owns one (group, slab, batch tile).
+//  * One lane owns one row (for 16-wide batch tiles a quad of lanes owns one
+//    row and each lane 4 batch entries, so one lookup is one contiguous 64-byte
+//    LDS read per quad). Codes are read 16 bytes (8 consecutive pairs) per
+//    row and load; in the blocked layout consecutive rows are adjacent, so a
+//    wave-wide load is one contiguous 1 KB run. The next block is loaded while
+//    the lookups of the current one run, across chunk switches too, so
+//    2*NSTEP 16-byte loads per lane are in flight -- enough bytes in flight
+//    (tens of MB chip-wide) to cover HBM latency at full bandwidth.
+//  * Finishing: with G == 1 the gather kernel applies the softcap, stores the
+//    logits and the best selection key of its slab. With G > 1 it stores
+//    partial sums, and a finish kernel adds the G partials of each output in
+//    group order (bit-reproducible, no atomics on the sums), applies the
+//    softcap and stores the logits and per-block keys. A selection kernel
+//    turns the keys into argmax ids. Cross-workgroup hand-offs go through
+//    kernel boundaries only: on this multi-XCD part a device-scope fence
+//    inside the kernel writes back and invalidates the XCD's L2, which cost
+//    several times the whole pass when every workgroup issued one.
+//  * The workgroup -> (group, slab) numbering keeps the workgroups of one XCD
+//    on the same group of chunks, so that XCD's L2 serves their staging.
 #include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "rq_internal.h"
 
@@ -35,16 +47,14 @@ namespace {
 
 struct GatherArgs {
   CodeView cv;
-  const void* lut;      // [NP][K][B]
+  const void* lut;            // [NP][K][B]
   int64_t rows;
   int NP, K, B;
   int P, chunks, cpg, G, steps, S, NBT;
-  float* partial;       // [G][B][rows]
-};
-
-template <typename T, int N>
-struct alignas(sizeof(T) * N) Vec {
-  T v[N];
+  float* partial;             // [G][B][rows] (G > 1)
+  float* out;                 // [B][rows] or null (G == 1)
+  float softcap;              // <= 0: none
+  uint64_t* block_keys;       // [B][S] best selection key per slab, or null (G == 1)
 };
 
 // Lookup of BQ consecutive batch entries of one table row, accumulated in fp32.
@@ -76,16 +86,19 @@ __device__ __forceinline__ void stage_chunk(LutT* tab, const LutT* __restrict__ 
   const size_t n = (size_t)pc * K * BT;
   if (B == BT) {
     const LutT* src = lut + (size_t)p0 * K * B;
-    const size_t nbytes = n * sizeof(LutT);
     if ((((size_t)K * B * sizeof(LutT)) & 15) == 0) {   // chunk starts 16-byte aligned
       const uint4* s4 = reinterpret_cast<const uint4*>(src);
       uint4* d4 = reinterpret_cast<uint4*>(tab);
-      const size_t n4 = nbytes / 16;
+      const size_t n4 = n * sizeof(LutT) / 16;
+      // up to 8 loads per thread in flight before the first LDS write (one
+      // round trip per chunk of up to 128 KB)
       size_t i = tid;
-      for (; i + 3 * kGatherThreads < n4; i += 4 * kGatherThreads) {
-        const uint4 a = s4[i], b = s4[i + kGatherThreads], c = s4[i + 2 * kGatherThreads],
-                    d = s4[i + 3 * kGatherThreads];
-        d4[i] = a; d4[i + kGatherThreads] = b; d4[i + 2 * kGatherThreads] = c; d4[i + 3 * kGatherThreads] = d;
+      for (; i + 7 * kGatherThreads < n4; i += 8 * kGatherThreads) {
+        uint4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = s4[i + u * kGatherThreads];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) d4[i + u * kGatherThreads] = v[u];
       }
       for (; i < n4; i += kGatherThreads) d4[i] = s4[i];
       for (size_t e = n4 * 16 / sizeof(LutT) + tid; e < n; e += kGatherThreads) tab[e] = src[e];
@@ -102,13 +115,31 @@ __device__ __forceinline__ void stage_chunk(LutT* tab, const LutT* __restrict__ 
   }
 }
 
-template <typename LutT, int BT, int NSTEP>
+__device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsigned long long b) { return a > b ? a : b; }
+
+// Value of one table entry as fp32 (BQ == 1).
+template <typename LutT>
+__device__ __forceinline__ float lut_value(const LutT* e);
+template <>
+__device__ __forceinline__ float lut_value<float>(const float* e) { return *e; }
+template <>
+__device__ __forceinline__ float lut_value<uint16_t>(const uint16_t* e) { return bf16_to_f32(*e); }
+
+__device__ __forceinline__ uint32_t code_of(const uint4& w, int t) {
+  const uint32_t word = (t >> 1) == 0 ? w.x : (t >> 1) == 1 ? w.y : (t >> 1) == 2 ? w.z : w.w;
+  return (t & 1) ? (word >> 16) : (word & 0xffffu);
+}
+
+// ALIGNED: every chunk starts on a block of 8 pairs (P % 8 == 0 or a single
+// chunk), so chunk switches are only checked at the first pair of a block.
+template <typename LutT, int BT, int NSTEP, bool ALIGNED>
 __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs a) {
   constexpr int QL = (BT >= 16) ? 4 : 1;   // lanes per row
   constexpr int BQ = BT / QL;              // batch entries per lane
   constexpr int RPS = kGatherThreads / QL; // rows per step
   extern __shared__ __align__(16) unsigned char smem[];
   LutT* tab = reinterpret_cast<LutT*>(smem);
+  __shared__ unsigned long long s_keys[BT];
 
   // XCD-aware numbering: consecutive workgroup ids land on different XCDs, so
   // give each XCD a contiguous range of logical ids (same chunk group).
@@ -132,74 +163,138 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs a) {
 #pragma unroll
     for (int i = 0; i < BQ; ++i) acc[st][i] = 0.0f;
 
-  // Word offsets of this lane's rows (row r's word for block q is at q*s_blk + r*s_row).
-  int64_t roff[NSTEP];
-  bool live[NSTEP];
+  // Byte offsets of this lane's rows inside one block of codes. Rows past the
+  // end read the last row (in bounds); their sums are never stored.
+  // Steps beyond the slab repeat step 0's row, so every load is issued
+  // unconditionally (a fixed number of loads per block keeps the wait counts
+  // exact) without touching other slabs' codes.
+  uint32_t roff[NSTEP];
 #pragma unroll
   for (int st = 0; st < NSTEP; ++st) {
-    const int64_t r = row0 + (int64_t)st * RPS;
-    live[st] = (st < a.steps) && (r < a.rows);
-    roff[st] = live[st] ? r * a.cv.s_row : 0;
+    const int64_t r = min(row0 + (int64_t)(st < a.steps ? st : 0) * RPS, a.rows - 1);
+    roff[st] = (uint32_t)(r * a.cv.s_row * 2);
   }
+  // The code stream is read with buffer loads: a scalar resource, the row
+  // offset in a VGPR and the block offset in an SGPR, so the hot loop holds no
+  // 64-bit per-lane addresses. (The host keeps the code array below 4 GiB.)
+  const __amdgpu_buffer_rsrc_t code_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.cv.codes, (short)0, (int)0xffffffffu, 0x00020000);
+  const uint32_t blk_bytes = (uint32_t)(a.cv.s_blk * 2);
+  const int steps = a.steps;
 
   const LutT* lut = static_cast<const LutT*>(a.lut);
+  const int pa = g * a.cpg * a.P;                       // this group's pairs [pa, pb)
+  const int pb = min(a.NP, (g * a.cpg + a.cpg) * a.P);
+
+  // 16 bytes = the codes of 8 consecutive pairs of one row. Two register
+  // buffers alternate: while one block is looked up, the next one loads into
+  // the other buffer (no register copy, so no wait on the load in flight).
+  auto load_block = [&](uint4 (&dst)[NSTEP], int q) {
+    const uint32_t boff = (uint32_t)q * blk_bytes;
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(code_rsrc, (int)roff[st], (int)boff, 0);
+      dst[st] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+  };
+  // Lookups of the pairs of block q that lie in [lo, hi), against the chunk staged at p0.
+  auto lookup_block = [&](const uint4 (&w)[NSTEP], int q, int lo, int hi, int p0) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int p = 8 * q + t;                 // uniform
+      if (p < lo || p >= hi) continue;
+      const LutT* base = tab + (size_t)(p - p0) * a.K * BT + rq * BQ;
+      if (BQ == 1) {
+        // issue every lookup of this pair before adding, so the LDS reads overlap
+        float v[NSTEP];
+#pragma unroll
+        for (int st = 0; st < NSTEP; ++st) v[st] = lut_value(base + code_of(w[st], t) * BT);
+#pragma unroll
+        for (int st = 0; st < NSTEP; ++st) acc[st][0] += v[st];
+      } else {
+#pragma unroll
+        for (int st = 0; st < NSTEP; ++st) lookup_add<LutT, BQ>(acc[st], base + code_of(w[st], t) * BT);
+      }
+    }
+  };
   const int c_begin = g * a.cpg;
   const int c_end = min(a.chunks, c_begin + a.cpg);
+  uint4 wa[NSTEP], wb[NSTEP];
   for (int c = c_begin; c < c_end; ++c) {
     const int p0 = c * a.P;
     const int pc = min(a.P, a.NP - p0);
+    const int lo = max(p0, pa), hi = min(p0 + pc, pb);
+    const int q0 = lo >> 3, q1 = (hi + 7) >> 3;
+    load_block(wa, q0);
     __syncthreads();
     stage_chunk<LutT, BT>(tab, lut, p0, pc, a.K, a.B, b0);
     __syncthreads();
-    const int q0 = p0 >> 1;
-    const int q1 = (p0 + pc + 1) >> 1;
-    for (int q = q0; q < q1; ++q) {
-      const uint16_t* blk = a.cv.codes + (int64_t)q * a.cv.s_blk;
-      uint32_t w[NSTEP];
-#pragma unroll
-      for (int st = 0; st < NSTEP; ++st)
-        w[st] = live[st] ? *reinterpret_cast<const uint32_t*>(blk + roff[st]) : 0u;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int pp = 2 * q + t - p0;        // pair index within the chunk (uniform)
-        if (pp < 0 || pp >= pc) continue;
-        const LutT* base = tab + (size_t)pp * a.K * BT + rq * BQ;
-#pragma unroll
-        for (int st = 0; st < NSTEP; ++st) {
-          const uint32_t code = t ? (w[st] >> 16) : (w[st] & 0xffffu);
-          lookup_add<LutT, BQ>(acc[st], base + (size_t)code * BT);
-        }
-      }
+    // The loads are unconditional (past the end they repeat the last block,
+    // a cache hit), so the same count is always in flight.
+    for (int q = q0; q < q1; q += 2) {
+      load_block(wb, min(q + 1, q1 - 1));
+      lookup_block(wa, q, lo, hi, p0);
+      load_block(wa, min(q + 2, q1 - 1));
+      lookup_block(wb, q + 1, lo, hi, p0);
     }
   }
 
+  // ---- G > 1: store the partial sums; the finish kernel adds them in group order
+  if (a.G > 1) {
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st) {
+      const int64_t r = row0 + (int64_t)st * RPS;
+      if (st >= steps || r >= a.rows) continue;
+#pragma unroll
+      for (int i = 0; i < BQ; ++i) {
+        const int b = b0 + rq * BQ + i;
+        if (b < a.B) a.partial[((size_t)g * a.B + b) * a.rows + r] = acc[st][i];
+      }
+    }
+    return;
+  }
+
+  // ---- G == 1: the sums are final: softcap, store, best selection key per slab
+  unsigned long long kbest[BQ];
+#pragma unroll
+  for (int i = 0; i < BQ; ++i) kbest[i] = 0ull;
 #pragma unroll
   for (int st = 0; st < NSTEP; ++st) {
-    if (!live[st]) continue;
     const int64_t r = row0 + (int64_t)st * RPS;
+    if (st >= steps || r >= a.rows) continue;
 #pragma unroll
     for (int i = 0; i < BQ; ++i) {
       const int b = b0 + rq * BQ + i;
-      if (b < a.B) a.partial[((size_t)g * a.B + b) * a.rows + r] = acc[st][i];
+      if (b >= a.B) continue;
+      const float z = acc[st][i];
+      const float v = a.softcap > 0.0f ? a.softcap * tanhf(z / a.softcap) : z;
+      if (a.out) a.out[(size_t)b * a.rows + r] = v;
+      kbest[i] = umax64(kbest[i], select_key(v, (uint32_t)r));
     }
   }
+  if (!a.block_keys) return;
+  if (tid < BT) s_keys[tid] = 0ull;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < BQ; ++i)
+    if (kbest[i]) atomicMax(&s_keys[rq * BQ + i], kbest[i]);   // LDS atomics, this workgroup only
+  __syncthreads();
+  if (tid < BT && b0 + tid < a.B) a.block_keys[(size_t)(b0 + tid) * a.S + s] = s_keys[tid];
 }
 
-template <int BT>
-constexpr int nstep_for() { return BT == 1 ? 8 : (BT == 4 ? 4 : 8); }
-
-template <typename LutT, int BT>
+template <typename LutT, int BT, int NSTEP>
 hipError_t launch_gather_typed(const GatherArgs& a, const GatherPlan& plan, hipStream_t stream) {
-  auto kern = gather_kernel<LutT, BT, nstep_for<BT>()>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  const bool aligned = (plan.P % 8 == 0) || plan.chunks == 1;
+  auto kern = aligned ? gather_kernel<LutT, BT, NSTEP, true> : gather_kernel<LutT, BT, NSTEP, false>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)plan.wgs()), dim3(kGatherThreads), plan.lds, stream, a);
   return hipGetLastError();
 }
 
-// ------------------------------------------------------------------ epilogue
+// ------------------------------------------------------------------ top-k
 
-constexpr int kEpiThreads = 256;
+constexpr int kTopkThreads = 256;
 
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
   const uint32_t lo = __shfl_xor((unsigned)(uint32_t)v, mask, 64);
@@ -233,82 +328,88 @@ __device__ void bitonic_sort_desc(uint64_t* s, int n) {
   }
 }
 
-// z = sum of the G partials (fixed order), logits = softcap(z); per block of
-// 1024 rows: the largest selection key and, with top-k, the block's k best keys.
-__global__ __launch_bounds__(kEpiThreads) void epilogue_kernel(const float* __restrict__ partial, int G, int B,
-                                                               int64_t rows, float softcap, float* __restrict__ out,
-                                                               uint64_t* __restrict__ block_keys, int topk,
-                                                               uint64_t* __restrict__ cand) {
+// The k best selection keys of each 1024-row block of the logits.
+__global__ __launch_bounds__(kTopkThreads) void topk_block_kernel(const float* __restrict__ logits, int64_t rows,
+                                                                  int topk, uint64_t* __restrict__ cand) {
   __shared__ uint64_t keys[kEpiRowsPerBlock];
-  __shared__ uint64_t wmax[kEpiThreads / 64];
   const int blk = blockIdx.x;
   const int b = blockIdx.y;
   const int nblk = gridDim.x;
-  uint64_t best = 0;
-#pragma unroll
-  for (int i = 0; i < kEpiRowsPerBlock / kEpiThreads; ++i) {
-    const int local = i * kEpiThreads + threadIdx.x;
+  for (int local = threadIdx.x; local < kEpiRowsPerBlock; local += kTopkThreads) {
     const int64_t r = (int64_t)blk * kEpiRowsPerBlock + local;
-    uint64_t key = 0;
-    if (r < rows) {
-      float z = 0.0f;
-      for (int g = 0; g < G; ++g) z += partial[((size_t)g * B + b) * rows + r];
-      const float v = softcap > 0.0f ? softcap * tanhf(z / softcap) : z;
-      if (out) out[(size_t)b * rows + r] = v;
-      key = select_key(v, (uint32_t)r);
+    keys[local] = r < rows ? select_key(logits[(size_t)b * rows + r], (uint32_t)r) : 0ull;
+  }
+  __syncthreads();
+  bitonic_sort_desc(keys, kEpiRowsPerBlock);
+  uint64_t* dst = cand + ((size_t)b * nblk + blk) * topk;
+  for (int i = threadIdx.x; i < topk; i += kTopkThreads) dst[i] = keys[i];
+}
+
+constexpr int kFinishThreads = 1024;
+
+// z = sum of the G partial sums of each output in group order, then the
+// softcap; the best selection key of each block of 1024 rows.
+__global__ __launch_bounds__(kFinishThreads) void finish_kernel(const float* __restrict__ partial, int G, int B,
+                                                                int64_t rows, float softcap, float* __restrict__ out,
+                                                                uint64_t* __restrict__ block_keys) {
+  __shared__ unsigned long long s_best;
+  const int blk = blockIdx.x;
+  const int b = blockIdx.y;
+  const int64_t r = (int64_t)blk * kFinishThreads + threadIdx.x;
+  if (threadIdx.x == 0) s_best = 0ull;
+  unsigned long long key = 0ull;
+  if (r < rows) {
+    const float* src = partial + (size_t)b * rows + r;
+    const size_t gstride = (size_t)B * rows;
+    float z = 0.0f;
+    int g = 0;
+    for (; g + 4 <= G; g += 4) {   // four loads in flight, added in group order
+      const float v0 = src[(size_t)g * gstride], v1 = src[(size_t)(g + 1) * gstride];
+      const float v2 = src[(size_t)(g + 2) * gstride], v3 = src[(size_t)(g + 3) * gstride];
+      z += v0; z += v1; z += v2; z += v3;
     }
-    if (topk > 0) keys[local] = key;
-    best = key > best ? key : best;
+    for (; g < G; ++g) z += src[(size_t)g * gstride];
+    const float v = softcap > 0.0f ? softcap * tanhf(z / softcap) : z;
+    if (out) out[(size_t)b * rows + r] = v;
+    key = select_key(v, (uint32_t)r);
   }
-  if (block_keys) {
-    best = wave_max_u64(best);
-    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = best;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      uint64_t m = wmax[0];
-      for (int w = 1; w < kEpiThreads / 64; ++w) m = wmax[w] > m ? wmax[w] : m;
-      block_keys[(size_t)b * nblk + blk] = m;
-    }
-  }
-  if (topk > 0) {
-    __syncthreads();
-    bitonic_sort_desc(keys, kEpiRowsPerBlock);
-    uint64_t* dst = cand + ((size_t)b * nblk + blk) * topk;
-    for (int i = threadIdx.x; i < topk; i += kEpiThreads) dst[i] = keys[i];
-  }
+  if (!block_keys) return;
+  __syncthreads();
+  const uint64_t w = wave_max_u64(key);
+  if ((threadIdx.x & 63) == 0) atomicMax(&s_best, (unsigned long long)w);
+  __syncthreads();
+  if (threadIdx.x == 0) block_keys[(size_t)b * gridDim.x + blk] = s_best;
 }
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelCap = 4096;
 
-// Per batch entry: argmax from the block maxima; top-k by merging the blocks'
-// candidates through a 4096-key LDS buffer that always keeps the best k.
-__global__ __launch_bounds__(kSelThreads) void select_kernel(const uint64_t* __restrict__ block_keys, int nblk,
-                                                             int32_t* __restrict__ argmax,
+// Per batch entry: argmax from the blocks' best keys; top-k by merging the
+// blocks' candidates through a 4096-key LDS buffer that always keeps the best k.
+__global__ __launch_bounds__(kSelThreads) void select_kernel(const uint64_t* __restrict__ block_keys, int nkb,
+                                                             int32_t* __restrict__ argmax, int ncb,
                                                              const uint64_t* __restrict__ cand, int topk,
                                                              int32_t* __restrict__ topk_ids,
                                                              float* __restrict__ topk_vals) {
   __shared__ uint64_t buf[kSelCap];
-  __shared__ uint64_t wmax[kSelThreads / 64];
+  __shared__ unsigned long long s_best;
   const int b = blockIdx.x;
   if (argmax) {
+    if (threadIdx.x == 0) s_best = 0ull;
+    __syncthreads();
     uint64_t best = 0;
-    for (int i = threadIdx.x; i < nblk; i += kSelThreads) {
-      const uint64_t k = block_keys[(size_t)b * nblk + i];
+    for (int i = threadIdx.x; i < nkb; i += kSelThreads) {
+      const uint64_t k = block_keys[(size_t)b * nkb + i];
       best = k > best ? k : best;
     }
     best = wave_max_u64(best);
-    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = best;
+    if ((threadIdx.x & 63) == 0) atomicMax(&s_best, (unsigned long long)best);
     __syncthreads();
-    if (threadIdx.x == 0) {
-      uint64_t m = wmax[0];
-      for (int w = 1; w < kSelThreads / 64; ++w) m = wmax[w] > m ? wmax[w] : m;
-      argmax[b] = (int32_t)key_index(m);
-    }
+    if (threadIdx.x == 0) argmax[b] = (int32_t)key_index(s_best);
   }
   if (topk <= 0) return;
-  const uint64_t* src = cand + (size_t)b * nblk * topk;
-  const size_t total = (size_t)nblk * topk;
+  const uint64_t* src = cand + (size_t)b * ncb * topk;
+  const size_t total = (size_t)ncb * topk;
   const int room = kSelCap - topk;
   for (int i = threadIdx.x; i < topk; i += kSelThreads) buf[i] = 0;
   for (size_t start = 0; start < total; start += room) {
@@ -327,77 +428,143 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const uint64_t* __r
 
 // ------------------------------------------------------------------ planning
 
-// Rough per-CU clock costs on gfx950 at 2.4 GHz, from measurements of this
-// library's probes: HBM streams ~6.4 TB/s chip-wide, L2->LDS staging ~64 B/clk
-// per CU, random 4-byte LDS lookups ~9 per clk per CU, quad-contiguous
-// 64-byte lookups ~120 B/clk per CU.
-double lookup_clk(int BT, int es) {
-  if (BT == 1) return 1.0 / 9.0;
-  if (BT == 4) return 4.0 * es / 60.0;
-  return 16.0 * es / 120.0;
+int nstep_for(int BT) { return 4; }
+
+#ifdef RQ_TUNING
+// Tuning builds only: RQ_GATHER_PLAN="P,steps,G" replaces the heuristic's choice.
+bool tuning_override(GatherPlan& p, int NP, int64_t rows) {
+  const char* s = getenv("RQ_GATHER_PLAN");
+  if (!s) return false;
+  int P, steps, G;
+  if (sscanf(s, "%d,%d,%d", &P, &steps, &G) != 3) return false;
+  p.P = std::min(P, NP);
+  p.chunks = (NP + p.P - 1) / p.P;
+  p.steps = std::min(steps, nstep_for(p.BT));
+  p.cpg = (p.chunks + G - 1) / G;
+  p.G = (p.chunks + p.cpg - 1) / p.cpg;
+  p.S = (int)((rows + (int64_t)p.steps * p.rps - 1) / ((int64_t)p.steps * p.rps));
+  return true;
 }
+#endif
 
 }  // namespace
 
-GatherPlan plan_gather(const rq_matrix* W, int B, int lut_bf16) {
-  const int NP = W->L * W->M;
-  const int K = W->K;
-  const int64_t rows = W->rows;
+namespace {
+
+// Cost model of one lookup+sum pass, in microseconds, fitted to measurements
+// of this kernel on MI355X: the code stream shares ~6.4 TB/s over the active
+// CUs; each staged chunk costs a round trip (~2 us) plus its bytes at
+// ~150 GB/s per CU (staging is not overlapped with the stream); random 4-byte
+// LDS lookups run at ~9 per clock per CU (quad-contiguous 64-byte lookups at
+// ~120 B/clock); G > 1 adds the partial-sum traffic and a finish launch.
+double plan_cost_us(int64_t rows, int NP, int K, int B, int es, int BT, int P, int steps, int G, int cpg) {
+  const int QL = BT >= 16 ? 4 : 1;
+  const int rps = kGatherThreads / QL;
+  const int64_t S = (rows + (int64_t)steps * rps - 1) / ((int64_t)steps * rps);
+  const int NBT = (B + BT - 1) / BT;
+  const int64_t wgs = (int64_t)G * S * NBT;
+  const int64_t rounds = (wgs + kCUs - 1) / kCUs;
+  const int64_t active = std::min<int64_t>(wgs, kCUs);
+  const double slab_rows = (double)std::min<int64_t>(rows, (int64_t)steps * rps);
+  const double pairs = (double)cpg * P;
+  const double chunk_bytes = (double)P * K * BT * es;
+  const double t_stage = cpg * (2.0 + chunk_bytes / 150e3);
+  const double per_cu_bw = std::min(150e3, 6.4e6 / (double)active);          // bytes per us
+  const double t_codes = slab_rows * pairs * 2.0 / per_cu_bw;
+  const double lookups_per_us = BT == 1 ? 9.0 * 2400.0 : (120.0 * 2400.0) / (BT * es);
+  const double t_look = slab_rows * pairs / lookups_per_us;
+  const double t_wg = t_stage + std::max(t_codes, t_look);
+  const double t_stream = (double)rows * NP * 2.0 * NBT / 6.4e6;
+  const double t_partial = G > 1 ? 5.0 + (double)G * B * rows * 8.0 / 6.4e6 : 0.0;
+  return std::max(t_stream, (double)rounds * t_wg) + t_partial;
+}
+
+GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16) {
   const int es = lut_bf16 ? 2 : 4;
-  const double hbm_bpc = 6.4e12 / 2.4e9;   // bytes per clock, whole chip
   GatherPlan best{};
+  int BT = 1;
+  if (B > 1) BT = ((size_t)K * 16 * es * 2 <= (size_t)kLdsBudget && B >= 16) ? 16 : 4;
+  if ((size_t)K * BT * es > (size_t)kLdsBudget) BT = 1;
+  if ((size_t)K * BT * es > (size_t)kLdsBudget) return best;
+  const int QL = BT >= 16 ? 4 : 1;
+  const int rps = kGatherThreads / QL;
+  const int nstep = nstep_for(BT);
+  const int NBT = (B + BT - 1) / BT;
+  int pmax = (int)std::min<int64_t>(NP, kLdsBudget / ((size_t)K * BT * es));
+  if (pmax < NP && pmax > 1) pmax &= ~1;
   double best_cost = 1e300;
-  const int bts[3] = {1, 4, 16};
-  for (int bi = 0; bi < 3; ++bi) {
-    const int BT = bts[bi];
-    if ((B == 1) != (BT == 1)) continue;
-    const size_t entry = (size_t)K * BT * es;
-    if (entry > (size_t)kLdsBytes) continue;
-    const int pmax = (int)std::min<int64_t>(NP, kLdsBytes / entry);
-    const int QL = BT >= 16 ? 4 : 1;
-    const int rps = kGatherThreads / QL;
-    const int nstep = BT == 1 ? 8 : (BT == 4 ? 4 : 8);
-    const int NBT = (B + BT - 1) / BT;
-    for (int P = pmax; P >= 1 && P >= pmax / 2; --P) {
-      if (P > 1 && P < NP && (P & 1)) continue;   // chunks start on a 2-pair word
-      const int chunks = (NP + P - 1) / P;
-      const size_t lds = (size_t)P * entry;
-      const int per_cu = std::max(1, std::min(2, (int)(kLdsBytes / lds)));
-      for (int steps = 1; steps <= nstep; ++steps) {
-        const int64_t slab = (int64_t)steps * rps;
-        const int64_t S = (rows + slab - 1) / slab;
-        const int64_t slab_rows = std::min<int64_t>(rows, slab);
-        int last_G = -1;
-        for (int cpg = 1; cpg <= chunks; ++cpg) {
-          const int G = (chunks + cpg - 1) / cpg;
-          if (G == last_G) continue;
-          last_G = G;
-          const int64_t wgs = (int64_t)G * S * NBT;
-          if (wgs > (int64_t)1 << 30) continue;
-          const int64_t cap = (int64_t)kCUs * per_cu;
-          const int64_t rounds = (wgs + cap - 1) / cap;
-          const double t_stage = (double)cpg * lds / 64.0;
-          const double t_look = (double)cpg * P * slab_rows * lookup_clk(BT, es);
-          const double t_codes = (double)cpg * P * slab_rows * 2.0 / 32.0;
-          // per_cu workgroups share one CU; a co-resident workgroup hides most of the staging
-          const double t_round = std::max(t_look, t_codes) * per_cu;
-          const double stage_exposed = per_cu == 1 ? t_stage : 0.3 * t_stage;
-          const double hbm = ((double)rows * NP * 2.0 * NBT + (double)G * B * rows * 4.0 * 2.0) / hbm_bpc;
-          const double cost = std::max(hbm, (double)rounds * t_round) + (double)rounds * stage_exposed;
-          if (cost < best_cost * 0.999) {
-            best_cost = cost;
-            best.BT = BT; best.P = P; best.chunks = chunks; best.cpg = cpg; best.G = G;
-            best.steps = steps; best.rps = rps; best.S = (int)S; best.NBT = NBT; best.lds = lds;
-          }
+  int tried = 0;
+  for (int P = pmax; P >= 1 && P >= pmax / 2 && tried < 8; --P) {
+    if (P < NP && P > 1 && (P & 1)) continue;
+    ++tried;
+    const int chunks = (NP + P - 1) / P;
+    for (int steps = nstep; steps >= 1; --steps) {
+      const int64_t S = (rows + (int64_t)steps * rps - 1) / ((int64_t)steps * rps);
+      if (S * NBT > (1 << 24)) continue;
+      const int64_t gmax = std::max<int64_t>(1, std::min<int64_t>(chunks, 4 * kCUs / (S * NBT) + 1));
+      for (int64_t G0 = 1; G0 <= gmax; ++G0) {
+        const int cpg = (int)((chunks + G0 - 1) / G0);
+        const int G = (chunks + cpg - 1) / cpg;
+        if (G != G0) continue;
+        // prefer aligned chunks (staging outside the block loop) on near-ties
+        const double cost = plan_cost_us(rows, NP, K, B, es, BT, P, steps, G, cpg) * ((P % 8 == 0 || chunks == 1) ? 1.0 : 1.03);
+        if (cost < best_cost * 0.999) {
+          best_cost = cost;
+          best.BT = BT; best.P = P; best.chunks = chunks; best.cpg = cpg; best.G = G;
+          best.steps = steps; best.rps = rps; best.S = (int)S; best.NBT = NBT;
         }
       }
     }
   }
+  best.lds = (size_t)best.P * K * BT * es;
   return best;
 }
 
+// Plans are a pure function of the shapes; a small memo keeps the search
+// off the per-call path.
+struct PlanKey {
+  int64_t rows;
+  int NP, K, B, bf16;
+  bool operator==(const PlanKey& o) const {
+    return rows == o.rows && NP == o.NP && K == o.K && B == o.B && bf16 == o.bf16;
+  }
+};
+std::mutex g_plan_mu;
+PlanKey g_plan_keys[32];
+GatherPlan g_plans[32];
+int g_plan_n = 0, g_plan_next = 0;
+
+}  // namespace
+
+// Tiling heuristic. The table staging traffic is S*NBT full tables whatever P
+// and G are, so P is taken as large as LDS allows; then (steps, G) are chosen
+// to fill every CU with one workgroup per round, preferring few groups
+// (partial-sum traffic) and long slabs (loads in flight per lane).
+GatherPlan plan_gather(const rq_matrix* W, int B, int lut_bf16) {
+  const PlanKey key{W->rows, W->L * W->M, W->K, B, lut_bf16};
+  GatherPlan plan{};
+  bool hit = false;
+  {
+    std::lock_guard<std::mutex> lock(g_plan_mu);
+    for (int i = 0; i < g_plan_n; ++i)
+      if (g_plan_keys[i] == key) { plan = g_plans[i]; hit = true; break; }
+  }
+  if (!hit) {
+    plan = search_plan(key.rows, key.NP, key.K, B, lut_bf16);
+    std::lock_guard<std::mutex> lock(g_plan_mu);
+    g_plan_keys[g_plan_next] = key;
+    g_plans[g_plan_next] = plan;
+    g_plan_next = (g_plan_next + 1) % 32;
+    if (g_plan_n < 32) ++g_plan_n;
+  }
+#ifdef RQ_TUNING
+  if (tuning_override(plan, key.NP, key.rows)) plan.lds = (size_t)plan.P * W->K * plan.BT * (lut_bf16 ? 2 : 4);
+#endif
+  return plan;
+}
+
 hipError_t launch_gather(const rq_matrix* W, const GatherPlan& plan, const void* lut, int lut_bf16, int B,
-                         float* partial, uint64_t* /*zero_words*/, int /*n_zero_words*/, hipStream_t stream) {
+                         const GatherOut& o, hipStream_t stream) {
   GatherArgs a;
   a.cv = code_view(W);
   a.lut = lut;
@@ -407,28 +574,42 @@ hipError_t launch_gather(const rq_matrix* W, const GatherPlan& plan, const void*
   a.B = B;
   a.P = plan.P; a.chunks = plan.chunks; a.cpg = plan.cpg; a.G = plan.G;
   a.steps = plan.steps; a.S = plan.S; a.NBT = plan.NBT;
-  a.partial = partial;
+  a.partial = o.partial;
+  a.out = o.out;
+  a.softcap = o.softcap;
+  a.block_keys = plan.G == 1 ? o.block_keys : nullptr;
+  hipError_t e;
   if (lut_bf16) {
-    if (plan.BT == 1) return launch_gather_typed<uint16_t, 1>(a, plan, stream);
-    if (plan.BT == 4) return launch_gather_typed<uint16_t, 4>(a, plan, stream);
-    return launch_gather_typed<uint16_t, 16>(a, plan, stream);
+    if (plan.BT == 1) e = launch_gather_typed<uint16_t, 1, 4>(a, plan, stream);
+    else if (plan.BT == 4) e = launch_gather_typed<uint16_t, 4, 4>(a, plan, stream);
+    else e = launch_gather_typed<uint16_t, 16, 4>(a, plan, stream);
+  } else {
+    if (plan.BT == 1) e = launch_gather_typed<float, 1, 4>(a, plan, stream);
+    else if (plan.BT == 4) e = launch_gather_typed<float, 4, 4>(a, plan, stream);
+    else e = launch_gather_typed<float, 16, 4>(a, plan, stream);
   }
-  if (plan.BT == 1) return launch_gather_typed<float, 1>(a, plan, stream);
-  if (plan.BT == 4) return launch_gather_typed<float, 4>(a, plan, stream);
-  return launch_gather_typed<float, 16>(a, plan, stream);
-}
-
-hipError_t launch_epilogue(const float* partial, int G, int B, int64_t rows, float softcap, float* out,
-                           uint64_t* block_keys, int topk, uint64_t* cand, hipStream_t stream) {
-  dim3 grid((unsigned)epi_blocks(rows), (unsigned)B);
-  hipLaunchKernelGGL(epilogue_kernel, grid, dim3(kEpiThreads), 0, stream, partial, G, B, rows, softcap, out,
-                     block_keys, topk, cand);
+  if (e != hipSuccess || plan.G == 1) return e;
+  dim3 grid((unsigned)((W->rows + kFinishThreads - 1) / kFinishThreads), (unsigned)B);
+  hipLaunchKernelGGL(finish_kernel, grid, dim3(kFinishThreads), 0, stream, o.partial, plan.G, B, W->rows, o.softcap,
+                     o.out, o.block_keys);
   return hipGetLastError();
 }
 
-hipError_t launch_select(const uint64_t* block_keys, int nblk, int B, int32_t* argmax, const uint64_t* cand,
-                         int topk, int32_t* topk_ids, float* topk_vals, hipStream_t stream) {
-  hipLaunchKernelGGL(select_kernel, dim3((unsigned)B), dim3(kSelThreads), 0, stream, block_keys, nblk, argmax,
+int key_blocks(const GatherPlan& plan, int64_t rows) {
+  return plan.G == 1 ? plan.S : (int)((rows + kFinishThreads - 1) / kFinishThreads);
+}
+
+hipError_t launch_select(const uint64_t* block_keys, int nkb, int B, int32_t* argmax, const float* logits,
+                         int64_t rows, int topk, uint64_t* cand, int32_t* topk_ids, float* topk_vals,
+                         hipStream_t stream) {
+  const int ncb = epi_blocks(rows);
+  if (topk > 0) {
+    hipLaunchKernelGGL(topk_block_kernel, dim3((unsigned)ncb, (unsigned)B), dim3(kTopkThreads), 0, stream, logits,
+                       rows, topk, cand);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(select_kernel, dim3((unsigned)B), dim3(kSelThreads), 0, stream, block_keys, nkb, argmax, ncb,
                      cand, topk, topk_ids, topk_vals);
   return hipGetLastError();
 }

@@ -42,8 +42,8 @@ __device__ __forceinline__ float gelu_tanh(float t) {
   return 0.5f * t * (1.0f + tanhf(k * (t + 0.044715f * t * t * t)));
 }
 
-// Code of pair p for row r: codes[(p >> 1) * s_blk + r * s_row + (p & 1)].
-// RQ_CODES_ROWS: s_blk = 2, s_row = NP.  RQ_CODES_PAIRED: s_blk = 2 * rows, s_row = 2.
+// Code of pair p for row r: codes[(p >> 3) * s_blk + r * s_row + (p & 7)].
+// RQ_CODES_ROWS: s_blk = 8, s_row = NP.  RQ_CODES_BLOCKED: s_blk = 8 * rows, s_row = 8.
 struct CodeView {
   const uint16_t* codes;
   int64_t s_blk;
@@ -54,6 +54,7 @@ struct CodeView {
 
 constexpr int kCUs = 256;                 // MI355X compute units
 constexpr int kLdsBytes = 160 * 1024;     // LDS per workgroup on gfx950
+constexpr int kLdsBudget = kLdsBytes - 1024;   // for the staged table (the rest: small static arrays)
 constexpr int kGatherThreads = 1024;
 
 CodeView code_view(const rq_matrix* W);
@@ -77,17 +78,28 @@ GatherPlan plan_gather(const rq_matrix* W, int B, int lut_bf16);
 // Launchers: return hipSuccess or the launch error. All enqueue on `stream`.
 hipError_t launch_build_lut(const rq_matrix* W, const float* x, const float* x2, int prologue, int B,
                             int lut_bf16, void* lut, hipStream_t stream);
+// Outputs and workspace of one lookup+sum pass.
+struct GatherOut {
+  float* partial;        // [G][B][rows] partial sums (G > 1)
+  float* out;            // [B][rows] results after the softcap, or null
+  float softcap;         // <= 0: none
+  uint64_t* block_keys;  // [B][key_blocks()] best selection key per block of rows, or null
+};
+// The lookup+sum pass: the gather kernel, and for G > 1 the finish kernel that
+// adds the partial sums in group order.
 hipError_t launch_gather(const rq_matrix* W, const GatherPlan& plan, const void* lut, int lut_bf16, int B,
-                         float* partial, uint64_t* zero_words, int n_zero_words, hipStream_t stream);
-hipError_t launch_epilogue(const float* partial, int G, int B, int64_t rows, float softcap, float* out,
-                           uint64_t* block_keys, int topk, uint64_t* cand, hipStream_t stream);
-hipError_t launch_select(const uint64_t* block_keys, int nblk, int B, int32_t* argmax, const uint64_t* cand,
-                         int topk, int32_t* topk_ids, float* topk_vals, hipStream_t stream);
+                         const GatherOut& o, hipStream_t stream);
+int key_blocks(const GatherPlan& plan, int64_t rows);
+// argmax from the per-block keys (argmax may be null) and, with topk > 0, the
+// top-k of the logits (cand: [B][epi_blocks(rows)][topk] scratch).
+hipError_t launch_select(const uint64_t* block_keys, int nkb, int B, int32_t* argmax, const float* logits,
+                         int64_t rows, int topk, uint64_t* cand, int32_t* topk_ids, float* topk_vals,
+                         hipStream_t stream);
 hipError_t launch_decode_rows(const rq_matrix* W, const int32_t* ids, int n, int out_bf16, void* out,
                               int32_t* bad_ids, hipStream_t stream);
 hipError_t launch_pack_codes(const uint16_t* src, int64_t rows, int NP, uint16_t* dst, hipStream_t stream);
 hipError_t launch_dense_logits(const uint16_t* E, int64_t rows, int D, const float* h, int B, float softcap,
-                               float* logits, uint64_t* block_keys, int32_t* argmax, hipStream_t stream);
+                               float* logits, uint64_t* block_keys, hipStream_t stream);
 
 constexpr int kEpiRowsPerBlock = 1024;   // rows per epilogue workgroup
 inline int epi_blocks(int64_t rows) { return (int)((rows + kEpiRowsPerBlock - 1) / kEpiRowsPerBlock); }

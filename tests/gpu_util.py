@@ -54,5 +54,5 @@ def check_argmax(am_gpu, logits_gpu, ref, tol=None):
         assert ref[b, am_gpu[b]] >= ref[b].max() - 2 * t, f"b={b}: argmax {am_gpu[b]} is not a maximum of the oracle"
 
 
-def to_dev(mat, layout="paired"):
+def to_dev(mat, layout="blocked"):
     return la.to_device(mat, layout=layout)

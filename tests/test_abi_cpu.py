@@ -35,7 +35,7 @@ def test_version_and_status_strings():
 
 
 def gemma_desc(**kw):
-    f = dict(rows=256000, D=2304, M=384, d=6, K=1024, L=2, cb_dtype=B.RQ_BF16, codes_layout=B.RQ_CODES_PAIRED,
+    f = dict(rows=256000, D=2304, M=384, d=6, K=1024, L=2, cb_dtype=B.RQ_BF16, codes_layout=B.RQ_CODES_BLOCKED,
              codebooks=0x10000, codes=0x20000)
     f.update(kw)
     return B.rq_matrix(**f)
@@ -55,12 +55,13 @@ def call_logits(W, Bn=1, topk=0, lut=0x30000, ws=0x40000, ws_bytes=1 << 40, lut_
     (dict(L=0), B.RQ_ERR_SHAPE),
     (dict(L=17), B.RQ_ERR_SHAPE),
     (dict(rows=-1), B.RQ_ERR_SHAPE),
+    (dict(rows=1 << 29), B.RQ_ERR_SHAPE),
     (dict(cb_dtype=7), B.RQ_ERR_DTYPE),
     (dict(codes_layout=5), B.RQ_ERR_DTYPE),
     (dict(codebooks=0), B.RQ_ERR_NULL),
     (dict(codes=0), B.RQ_ERR_NULL),
     (dict(codes=0x20002), B.RQ_ERR_ALIGN),
-    (dict(codes_layout=B.RQ_CODES_ROWS, L=1, M=383, D=2298), B.RQ_ERR_ALIGN),   # odd L*M needs the paired layout
+    (dict(codes_layout=B.RQ_CODES_ROWS, L=1, M=383, D=2298), B.RQ_ERR_ALIGN),   # L*M % 8 != 0 needs the blocked layout
 ])
 def test_lut_logits_rejects(kw, status):
     assert call_logits(gemma_desc(**kw)) == status
@@ -88,13 +89,14 @@ def test_workspace_queries():
     lib = B.lib()
     W = gemma_desc()
     ws1 = lib.rq_lut_logits_workspace(ctypes.byref(W), 1, 0, B.RQ_F32)
-    assert ws1 >= 256000 * 4 and ws1 % 256 == 0
+    assert ws1 > 0 and ws1 % 256 == 0
     assert lib.rq_lut_logits_workspace(ctypes.byref(W), 16, 50, B.RQ_F32) > ws1
     assert lib.rq_lut_logits_workspace(ctypes.byref(gemma_desc(D=1)), 1, 0, B.RQ_F32) == 0
     assert lib.rq_lut_bytes(ctypes.byref(W), 1, B.RQ_F32) == 2 * 384 * 1024 * 4
     assert lib.rq_lut_bytes(ctypes.byref(W), 3, B.RQ_BF16) == 2 * 384 * 1024 * 3 * 2
-    assert lib.rq_paired_codes_bytes(256000, 2, 384) == 393_216_000
-    assert lib.rq_paired_codes_bytes(10, 1, 5) == 3 * 10 * 4
+    assert lib.rq_blocked_codes_bytes(256000, 2, 384) == 393_216_000
+    assert lib.rq_blocked_codes_bytes(10, 1, 5) == 1 * 10 * 16
+    assert lib.rq_blocked_codes_bytes(10, 3, 3) == 2 * 10 * 16
     Wm = gemma_desc(rows=9216, D=2304, M=1152, d=2, cb_dtype=B.RQ_F32)
     assert lib.rq_lut_matvec_workspace(ctypes.byref(Wm), 1) >= 2 * 1152 * 1024 * 4
     assert lib.rq_dense_logits_workspace(256000, 1) > 0

@@ -21,21 +21,21 @@ def _rand(seed, rows, D, M, K, L, cb_dtype="f32", sigmas=None):
 
 # ------------------------------------------------------------------ layout
 
-@pytest.mark.parametrize("rows,NP", [(1, 1), (63, 7), (4097, 34), (130, 768)])
+@pytest.mark.parametrize("rows,NP", [(1, 1), (63, 7), (4097, 34), (130, 768), (65, 1000)])
 def test_pack_codes_bit_exact(rows, NP):
     rng = np.random.default_rng(rows + NP)
     codes = rng.integers(0, 65536, size=(rows, NP), dtype=np.uint16)
     out = host(la.pack_codes(dev(codes.view(np.int16)), rows, 1, NP)).view(np.uint16)
-    NQ = (NP + 1) // 2
-    padded = np.zeros((rows, 2 * NQ), np.uint16)
+    NQ = (NP + 7) // 8
+    padded = np.zeros((rows, 8 * NQ), np.uint16)
     padded[:, :NP] = codes
-    want = padded.reshape(rows, NQ, 2).transpose(1, 0, 2).reshape(-1)
+    want = padded.reshape(rows, NQ, 8).transpose(1, 0, 2).reshape(-1)
     assert np.array_equal(out, want)
 
 
 # ------------------------------------------------------------------ row decode
 
-@pytest.mark.parametrize("layout", ["rows", "paired"])
+@pytest.mark.parametrize("layout", ["rows", "blocked"])
 @pytest.mark.parametrize("L,cb_dtype,out_dtype", [(2, "f32", "f32"), (2, "f32", "bf16"), (2, "bf16", "bf16"),
                                                   (3, "f32", "f32"), (4, "bf16", "f32"), (1, "f32", "f32")])
 def test_decode_rows_bit_exact(layout, L, cb_dtype, out_dtype):
@@ -107,7 +107,7 @@ EXACT_SHAPES = [
     (4097, 96, 16, 256, 2, 1),
     (4097, 102, 17, 1000, 2, 1),    # odd M, K not a power of two, ragged rows
     (1, 6, 1, 1, 1, 1),             # one row, one codeword, one pair
-    (300, 34, 17, 5, 1, 2),         # odd L*M (paired layout only), ragged batch tile
+    (300, 34, 17, 5, 1, 2),         # L*M not a multiple of 8 (blocked layout only), ragged batch tile
     (2049, 96, 16, 256, 2, 16),
     (1500, 96, 16, 128, 3, 17),     # batch 16 + ragged 1
     (700, 96, 96, 64, 2, 5),        # d = 1
@@ -116,12 +116,12 @@ EXACT_SHAPES = [
 
 
 @pytest.mark.parametrize("shape", EXACT_SHAPES, ids=lambda s: "x".join(map(str, s)))
-@pytest.mark.parametrize("layout", ["rows", "paired"])
+@pytest.mark.parametrize("layout", ["rows", "blocked"])
 def test_lut_logits_exact(shape, layout):
     """Small-integer inputs: every fp32 step is exact, so logits (softcap off) equal the oracle bit for bit."""
     rows, D, M, K, L, B = shape
-    if layout == "rows" and (L * M) % 2:
-        pytest.skip("row-major codes need L*M even")
+    if layout == "rows" and (L * M) % 8:
+        pytest.skip("row-major codes need L*M % 8 == 0")
     mat, h = synth.gen_exact(rows + K, rows, D, M, K, L, B)
     W = to_dev(mat, layout)
     lut = la.build_lut(W, dev(h))
@@ -146,7 +146,7 @@ def test_tiny_config():
     """The tiny RQ head: V=4096, D=96, M=16, K=256, L=2, fp32 codebooks, softcap 30, argmax, 8 decoded rows."""
     cfg = synth.CONFIGS["tiny"]
     mat, h, ids = synth.make_head(cfg)
-    for layout in ("rows", "paired"):
+    for layout in ("rows", "blocked"):
         W = to_dev(mat, layout)
         lg, am, _, _ = la.lut_logits(W, la.build_lut(W, dev(h)), 1, softcap=cfg.softcap)
         _, ref = oracle_head(mat, h, cfg.softcap)
