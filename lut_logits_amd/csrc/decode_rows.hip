@@ -6,10 +6,10 @@
 // on demand, a handful per prompt. Row r, element m*d + j, is the sum over
 // the L levels of C[l][m][codes[r][l][m]][j].
 //
-// One workgroup per requested id. The level sum is taken in fp64 in level
-// order and rounded once to fp32 (then to bf16, nearest-even, if asked), so
-// the result does not depend on how many levels are summed. The work is a few
-// hundred kilobytes per prompt: latency-bound by design.
+// The level sum is taken in fp64 in level order and rounded once to fp32
+// (then to bf16, nearest-even, if asked), so the result does not depend on how
+// many levels are summed. The work is a few hundred kilobytes per prompt:
+// latency-bound by design.
 #include "rq_internal.h"
 
 namespace rq {
@@ -31,29 +31,43 @@ __device__ __forceinline__ void out_store<float>(float* p, float v) { *p = v; }
 template <>
 __device__ __forceinline__ void out_store<uint16_t>(uint16_t* p, float v) { *p = f32_to_bf16(v); }
 
+// One thread per (requested row, subspace): it loads the L codes of its
+// subspace, then the L codewords, so every load of the row is in flight at
+// once (two dependent round trips per call, whatever D is).
 template <typename CbT, typename OutT>
 __global__ __launch_bounds__(kDecodeThreads) void decode_rows_kernel(CodeView cv, const CbT* __restrict__ cb,
                                                                      int64_t rows, int D, int M, int d, int K,
-                                                                     int L, const int32_t* __restrict__ ids,
+                                                                     int L, const int32_t* __restrict__ ids, int n,
                                                                      OutT* __restrict__ out,
                                                                      int32_t* __restrict__ bad) {
-  const int i = blockIdx.x;
+  const int64_t t = (int64_t)blockIdx.x * kDecodeThreads + threadIdx.x;
+  if (t >= (int64_t)n * M) return;
+  const int i = (int)(t / M);
+  const int m = (int)(t - (int64_t)i * M);
   const int64_t id = ids[i];
   const bool ok = id >= 0 && id < rows;
-  if (!ok && threadIdx.x == 0 && bad) atomicAdd(bad, 1);
-  OutT* dst = out + (size_t)i * D;
-  for (int e = threadIdx.x; e < D; e += kDecodeThreads) {
+  if (!ok && m == 0 && bad) atomicAdd(bad, 1);
+  OutT* dst = out + (size_t)i * D + (size_t)m * d;
+  if (!ok) {
+    for (int j = 0; j < d; ++j) out_store(dst + j, 0.0f);
+    return;
+  }
+  constexpr int kMaxL = RQ_MAX_L;
+  uint32_t code[kMaxL];
+#pragma unroll
+  for (int l = 0; l < kMaxL; ++l) {
+    if (l >= L) break;
+    const int p = l * M + m;
+    code[l] = cv.codes[(int64_t)(p >> 3) * cv.s_blk + id * cv.s_row + (p & 7)];
+  }
+  for (int j = 0; j < d; ++j) {
     double s = 0.0;
-    if (ok) {
-      const int m = e / d;
-      const int j = e - m * d;
-      for (int l = 0; l < L; ++l) {
-        const int p = l * M + m;
-        const uint32_t code = cv.codes[(int64_t)(p >> 3) * cv.s_blk + id * cv.s_row + (p & 7)];
-        s += cb_value(cb + ((size_t)p * K + code) * d + j);
-      }
+#pragma unroll
+    for (int l = 0; l < kMaxL; ++l) {
+      if (l >= L) break;
+      s += cb_value(cb + ((size_t)(l * M + m) * K + code[l]) * d + j);
     }
-    out_store(dst + e, (float)s);
+    out_store(dst + j, (float)s);
   }
 }
 
@@ -94,9 +108,11 @@ __global__ __launch_bounds__(256) void pack_codes_kernel(const uint16_t* __restr
 
 template <typename CbT, typename OutT>
 hipError_t decode_typed(const rq_matrix* W, const int32_t* ids, int n, void* out, int32_t* bad, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_rows_kernel<CbT, OutT>), dim3((unsigned)n), dim3(kDecodeThreads), 0, stream,
-                     code_view(W), static_cast<const CbT*>(W->codebooks), W->rows, W->D, W->M, W->d, W->K, W->L,
-                     ids, static_cast<OutT*>(out), bad);
+  const int64_t threads = (int64_t)n * W->M;
+  const unsigned blocks = (unsigned)((threads + kDecodeThreads - 1) / kDecodeThreads);
+  hipLaunchKernelGGL((decode_rows_kernel<CbT, OutT>), dim3(blocks), dim3(kDecodeThreads), 0, stream, code_view(W),
+                     static_cast<const CbT*>(W->codebooks), W->rows, W->D, W->M, W->d, W->K, W->L, ids, n,
+                     static_cast<OutT*>(out), bad);
   return hipGetLastError();
 }
 

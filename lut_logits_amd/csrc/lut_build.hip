@@ -8,12 +8,14 @@
 // for the down projection of a Gemma-2 MLP block (MLP RQ page, closing
 // paragraphs).
 //
-// One workgroup covers 256 codewords of one (level, subspace) pair p = l*M+m.
-// It first stages a[b][m*d .. m*d+d) for all b in LDS (prologue applied once
-// per workgroup), then each thread keeps its codeword in registers and writes
-// B consecutive table entries. Work: L*M*K*B*d FMAs; bytes: the codebooks
-// once plus the table once -- a few microseconds at Gemma shapes, far from
-// the matrix cores' territory, so plain VALU FMAs are used.
+// General kernel: one workgroup covers 256 codewords of one (level, subspace)
+// pair p = l*M+m. It first stages a[b][m*d .. m*d+d) for all b in LDS
+// (prologue applied once per workgroup), then each thread keeps its codeword
+// in registers and writes B consecutive table entries. A single activation
+// with d in {2, 6, 8} takes a vectorised path (build_lut_b1_kernel).
+// Work: L*M*K*B*d FMAs; bytes: the codebooks once plus the table once -- a
+// few microseconds at Gemma shapes, far from the matrix cores' territory, so
+// plain VALU FMAs are used.
 #include "rq_internal.h"
 
 namespace rq {
@@ -88,9 +90,68 @@ __global__ __launch_bounds__(kBuildThreads) void build_lut_kernel(const CbT* __r
   }
 }
 
+constexpr int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
+
+// Fast path for one activation vector and a small compile-time subspace width:
+// each thread reads CW consecutive codewords of one (level, subspace) pair with
+// 16-byte loads (CW chosen so CW codewords fill whole 16-byte words) and writes
+// their CW table entries. The activation slice is the same for every thread of
+// the pair and comes from cache.
+template <typename CbT, typename OutT, int DS>
+__global__ __launch_bounds__(kBuildThreads) void build_lut_b1_kernel(const CbT* __restrict__ cb,
+                                                                     const float* __restrict__ x,
+                                                                     const float* __restrict__ x2, int gelu, int M,
+                                                                     int K, int64_t total, OutT* __restrict__ lut) {
+  constexpr int ES = (int)sizeof(CbT);
+  constexpr int CW = 16 / gcd_int(16, DS * ES);
+  constexpr int NV = CW * DS * ES / 16;
+  const int64_t t = (int64_t)blockIdx.x * kBuildThreads + threadIdx.x;
+  if (t >= total) return;
+  const int per_pair = K / CW;
+  const int p = (int)(t / per_pair);
+  const int k0 = (int)(t - (int64_t)p * per_pair) * CW;
+  const int m = p % M;
+  const uint4* src = reinterpret_cast<const uint4*>(cb + ((size_t)p * K + k0) * DS);
+  uint4 raw[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) raw[v] = src[v];
+  float a[DS];
+#pragma unroll
+  for (int j = 0; j < DS; ++j) a[j] = activation(x, x2, gelu, (size_t)m * DS + j);
+  const CbT* e = reinterpret_cast<const CbT*>(raw);
+  OutT* out = lut + (size_t)p * K + k0;
+#pragma unroll
+  for (int w = 0; w < CW; ++w) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < DS; ++j) acc = fmaf(a[j], cb_load(e + w * DS + j), acc);
+    lut_store(out + w, acc);
+  }
+}
+
+template <typename CbT, typename OutT, int DS>
+bool try_b1(const rq_matrix* W, const float* x, const float* x2, int gelu, OutT* lut, hipStream_t stream,
+            hipError_t* err) {
+  constexpr int ES = (int)sizeof(CbT);
+  constexpr int CW = 16 / gcd_int(16, DS * ES);
+  if (W->d != DS || W->K % CW != 0 || ((uintptr_t)W->codebooks & 15)) return false;
+  const int64_t total = (int64_t)W->L * W->M * (W->K / CW);
+  hipLaunchKernelGGL((build_lut_b1_kernel<CbT, OutT, DS>), dim3((unsigned)((total + kBuildThreads - 1) / kBuildThreads)),
+                     dim3(kBuildThreads), 0, stream, static_cast<const CbT*>(W->codebooks), x, x2, gelu, W->M, W->K,
+                     total, lut);
+  *err = hipGetLastError();
+  return true;
+}
+
 template <typename CbT, typename OutT>
 hipError_t launch_typed(const rq_matrix* W, const float* x, const float* x2, int gelu, int B, OutT* lut,
                         hipStream_t stream) {
+  if (B == 1) {
+    hipError_t e;
+    if (try_b1<CbT, OutT, 6>(W, x, x2, gelu, lut, stream, &e)) return e;
+    if (try_b1<CbT, OutT, 2>(W, x, x2, gelu, lut, stream, &e)) return e;
+    if (try_b1<CbT, OutT, 8>(W, x, x2, gelu, lut, stream, &e)) return e;
+  }
   const int NP = W->L * W->M;
   const int ktiles = (W->K + kBuildThreads - 1) / kBuildThreads;
   const int64_t blocks = (int64_t)NP * ktiles;

@@ -130,10 +130,39 @@ __device__ __forceinline__ uint32_t code_of(const uint4& w, int t) {
   return (t & 1) ? (word >> 16) : (word & 0xffffu);
 }
 
-// ALIGNED: every chunk starts on a block of 8 pairs (P % 8 == 0 or a single
-// chunk), so chunk switches are only checked at the first pair of a block.
-template <typename LutT, int BT, int NSTEP, bool ALIGNED>
-__global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs a) {
+// REG: the table slice of one chunk is contiguous and at most kRegStage
+// 16-byte words per thread (B == BT, chunk <= 128 KB), so the next chunk is
+// loaded into registers while the current one is in use and only written to
+// LDS at the switch -- its HBM/L2 latency is hidden behind a whole chunk.
+constexpr int kRegStage = 8;
+
+// Eight 16-byte words of a chunk held in registers. A native vector type keeps
+// the copies first-class values (HIP's uint4 struct is copied through memory).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+struct ChunkRegs {
+  u32x4 w0, w1, w2, w3, w4, w5, w6, w7;
+};
+__device__ __forceinline__ void chunk_to_regs(ChunkRegs& r, const u32x4* __restrict__ src, int tid, int last) {
+  const int T = kGatherThreads;
+  r.w0 = src[min(tid, last)];         r.w1 = src[min(tid + T, last)];
+  r.w2 = src[min(tid + 2 * T, last)]; r.w3 = src[min(tid + 3 * T, last)];
+  r.w4 = src[min(tid + 4 * T, last)]; r.w5 = src[min(tid + 5 * T, last)];
+  r.w6 = src[min(tid + 6 * T, last)]; r.w7 = src[min(tid + 7 * T, last)];
+}
+__device__ __forceinline__ void regs_to_lds(const ChunkRegs& r, u32x4* dst, int tid, int last) {
+  const int T = kGatherThreads;
+  dst[min(tid, last)] = r.w0;         dst[min(tid + T, last)] = r.w1;
+  dst[min(tid + 2 * T, last)] = r.w2; dst[min(tid + 3 * T, last)] = r.w3;
+  dst[min(tid + 4 * T, last)] = r.w4; dst[min(tid + 5 * T, last)] = r.w5;
+  dst[min(tid + 6 * T, last)] = r.w6; dst[min(tid + 7 * T, last)] = r.w7;
+}
+
+// One 1024-thread workgroup per CU (its LDS chunk fills the CU), i.e. four
+// waves per SIMD: the register budget is 128 VGPRs, stated explicitly so the
+// compiler does not trade registers for an occupancy the LDS cannot reach.
+template <typename LutT, int BT, int NSTEP, bool REG>
+__global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(1, 4)))
+void gather_kernel(GatherArgs a) {
   constexpr int QL = (BT >= 16) ? 4 : 1;   // lanes per row
   constexpr int BQ = BT / QL;              // batch entries per lane
   constexpr int RPS = kGatherThreads / QL; // rows per step
@@ -220,6 +249,15 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs a) {
   const int c_begin = g * a.cpg;
   const int c_end = min(a.chunks, c_begin + a.cpg);
   uint4 wa[NSTEP], wb[NSTEP];
+  ChunkRegs nxt;
+  const u32x4* lut4 = reinterpret_cast<const u32x4*>(lut);
+  const int words_per_pair = a.K * BT * (int)sizeof(LutT) / 16;   // REG: 16-byte words per pair
+  // REG: chunk c's words go to registers with a fixed count of unconditional
+  // loads (clamped to the last word of the chunk).
+  if (REG) {
+    const int n4 = min(a.P, a.NP - c_begin * a.P) * words_per_pair;
+    chunk_to_regs(nxt, lut4 + (size_t)c_begin * a.P * words_per_pair, tid, n4 - 1);
+  }
   for (int c = c_begin; c < c_end; ++c) {
     const int p0 = c * a.P;
     const int pc = min(a.P, a.NP - p0);
@@ -227,7 +265,16 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs a) {
     const int q0 = lo >> 3, q1 = (hi + 7) >> 3;
     load_block(wa, q0);
     __syncthreads();
-    stage_chunk<LutT, BT>(tab, lut, p0, pc, a.K, a.B, b0);
+    if (REG) {
+      // words past the chunk were loaded clamped to its last word, so writing
+      // them clamped stores that same value again
+      regs_to_lds(nxt, reinterpret_cast<u32x4*>(tab), tid, pc * words_per_pair - 1);
+      const int cn = min(c + 1, c_end - 1);
+      const int n4n = min(a.P, a.NP - cn * a.P) * words_per_pair;
+      chunk_to_regs(nxt, lut4 + (size_t)cn * a.P * words_per_pair, tid, n4n - 1);
+    } else {
+      stage_chunk<LutT, BT>(tab, lut, p0, pc, a.K, a.B, b0);
+    }
     __syncthreads();
     // The loads are unconditional (past the end they repeat the last block,
     // a cache hit), so the same count is always in flight.
@@ -238,7 +285,6 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs a) {
       lookup_block(wb, q + 1, lo, hi, p0);
     }
   }
-
   // ---- G > 1: store the partial sums; the finish kernel adds them in group order
   if (a.G > 1) {
 #pragma unroll
@@ -284,8 +330,10 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs a) {
 
 template <typename LutT, int BT, int NSTEP>
 hipError_t launch_gather_typed(const GatherArgs& a, const GatherPlan& plan, hipStream_t stream) {
-  const bool aligned = (plan.P % 8 == 0) || plan.chunks == 1;
-  auto kern = aligned ? gather_kernel<LutT, BT, NSTEP, true> : gather_kernel<LutT, BT, NSTEP, false>;
+  const size_t chunk_bytes = (size_t)plan.P * a.K * BT * sizeof(LutT);
+  const bool reg = a.B == BT && chunk_bytes % 16 == 0 && chunk_bytes <= (size_t)kRegStage * 16 * kGatherThreads &&
+                   ((size_t)a.K * BT * sizeof(LutT)) % 16 == 0;
+  auto kern = reg ? gather_kernel<LutT, BT, NSTEP, true> : gather_kernel<LutT, BT, NSTEP, false>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)plan.wgs()), dim3(kGatherThreads), plan.lds, stream, a);
