@@ -23,7 +23,8 @@
  * Conventions for every entry point:
  *   - Memory. All array pointers are DEVICE pointers owned by the caller. The
  *     library allocates nothing, keeps no state between calls (apart from the
- *     thread-local text behind rq_last_error) and never synchronises: work is
+ *     thread-local text behind rq_last_error and the one-shot events of
+ *     rq_set_stage_events) and never synchronises: work is
  *     enqueued on `stream` and completes asynchronously.
  *   - Errors. Arguments are checked on the host before anything is launched;
  *     a failed check returns a negative rq_status and enqueues nothing. A
@@ -225,6 +226,18 @@ size_t rq_dense_logits_workspace(int64_t rows, int32_t B);
 rq_status rq_dense_logits(const uint16_t* E, int64_t rows, int32_t D, const float* h, int32_t B,
                           float softcap, float* logits, int32_t* argmax, void* ws, size_t ws_bytes,
                           hipStream_t stream);
+
+/*
+ * Measurement hook. The next lookup+sum kernel that rq_lut_logits or
+ * rq_lut_matvec launches from the calling thread is bracketed by
+ * hipEventRecord(before, stream) and hipEventRecord(after, stream), so that
+ * hipEventElapsedTime(before, after) is that one kernel's duration on its own
+ * stream (the selection/epilogue kernels of the same call fall outside). The
+ * hook is one-shot and thread-local: it is cleared when used, and by a call
+ * with both events NULL. The events stay owned by the caller and must have
+ * been created (hipEventCreate) without hipEventDisableTiming.
+ */
+rq_status rq_set_stage_events(hipEvent_t before, hipEvent_t after);
 
 /* Static text for a status code. */
 const char* rq_status_string(rq_status s);

@@ -21,7 +21,7 @@ RQ_CODES_ROWS, RQ_CODES_BLOCKED = 0, 1
 # Every symbol include/rq_lut.h declares.
 EXPORTS = ("rq_blocked_codes_bytes", "rq_pack_codes", "rq_lut_bytes", "rq_build_lut", "rq_lut_logits_workspace",
            "rq_lut_logits", "rq_decode_rows", "rq_lut_matvec_workspace", "rq_lut_matvec",
-           "rq_dense_logits_workspace", "rq_dense_logits", "rq_status_string", "rq_last_error", "rq_version")
+           "rq_dense_logits_workspace", "rq_dense_logits", "rq_set_stage_events", "rq_status_string", "rq_last_error", "rq_version")
 
 
 class RQError(RuntimeError):
@@ -60,6 +60,7 @@ def lib():
             "rq_lut_matvec": (_i32, [_MP, _vp, _vp, _i32, _i32, _vp, _vp, _sz, _vp]),
             "rq_dense_logits_workspace": (_sz, [_i64, _i32]),
             "rq_dense_logits": (_i32, [_vp, _i64, _i32, _vp, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
+            "rq_set_stage_events": (_i32, [_vp, _vp]),
             "rq_status_string": (ctypes.c_char_p, [_i32]),
             "rq_last_error": (ctypes.c_char_p, []),
             "rq_version": (ctypes.c_char_p, []),
@@ -210,3 +211,15 @@ def dense_logits(E, h, softcap=30.0, argmax=True, ws=None, out=None):
     check(lib().rq_dense_logits(_ptr(E), rows, D, _ptr(h), B, softcap, _ptr(lg), _ptr(am), _ptr(ws),
                                 ws.numel() if ws is not None else 0, _stream()))
     return lg, am
+
+
+def set_stage_events(before, after):
+    """rq_set_stage_events: bracket the next lookup+sum kernel launched from this thread with two
+    torch.cuda.Event objects (timing enabled), or clear the hook with (None, None)."""
+    def handle(ev):
+        if ev is None:
+            return None
+        if not ev.cuda_event:   # torch creates the HIP event lazily, on first record
+            ev.record()
+        return ctypes.c_void_p(ev.cuda_event)
+    check(lib().rq_set_stage_events(handle(before), handle(after)))

@@ -13,6 +13,7 @@
 namespace {
 
 thread_local char g_last_error[512] = "";
+thread_local hipEvent_t g_stage_before = nullptr, g_stage_after = nullptr;
 
 rq_status fail(rq_status s, const char* fmt, ...) {
   va_list ap;
@@ -99,9 +100,24 @@ rq_status check_lut_call(const rq_matrix* W, int32_t B, int32_t lut_dtype) {
 
 }  // namespace
 
+namespace rq {
+void take_stage_events(hipEvent_t* before, hipEvent_t* after) {
+  *before = g_stage_before;
+  *after = g_stage_after;
+  g_stage_before = g_stage_after = nullptr;
+}
+}  // namespace rq
+
 extern "C" {
 
 const char* rq_version(void) { return "0.1.0"; }
+
+rq_status rq_set_stage_events(hipEvent_t before, hipEvent_t after) {
+  if ((before == nullptr) != (after == nullptr)) return fail(RQ_ERR_NULL, "rq_set_stage_events: both events or neither");
+  g_stage_before = before;
+  g_stage_after = after;
+  return RQ_OK;
+}
 
 const char* rq_last_error(void) { return g_last_error; }
 

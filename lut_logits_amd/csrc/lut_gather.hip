@@ -336,8 +336,13 @@ hipError_t launch_gather_typed(const GatherArgs& a, const GatherPlan& plan, hipS
   auto kern = reg ? gather_kernel<LutT, BT, NSTEP, true> : gather_kernel<LutT, BT, NSTEP, false>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget);
   if (e != hipSuccess) return e;
+  hipEvent_t before, after;
+  take_stage_events(&before, &after);
+  if (before && (e = hipEventRecord(before, stream)) != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)plan.wgs()), dim3(kGatherThreads), plan.lds, stream, a);
-  return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (after) e = hipEventRecord(after, stream);
+  return e;
 }
 
 // ------------------------------------------------------------------ top-k
@@ -479,12 +484,17 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const uint64_t* __r
 int nstep_for(int BT) { return 4; }
 
 #ifdef RQ_TUNING
-// Tuning builds only: RQ_GATHER_PLAN="P,steps,G" replaces the heuristic's choice.
-bool tuning_override(GatherPlan& p, int NP, int64_t rows) {
+// Tuning builds only: RQ_GATHER_PLAN="P,steps,G[,BT]" replaces the heuristic's choice.
+bool tuning_override(GatherPlan& p, int NP, int64_t rows, int B) {
   const char* s = getenv("RQ_GATHER_PLAN");
   if (!s) return false;
-  int P, steps, G;
-  if (sscanf(s, "%d,%d,%d", &P, &steps, &G) != 3) return false;
+  int P, steps, G, BT = 0;
+  if (sscanf(s, "%d,%d,%d,%d", &P, &steps, &G, &BT) < 3) return false;
+  if (BT == 1 || BT == 4 || BT == 16) {
+    p.BT = BT;
+    p.rps = kGatherThreads / (BT >= 16 ? 4 : 1);
+    p.NBT = (B + BT - 1) / BT;
+  }
   p.P = std::min(P, NP);
   p.chunks = (NP + p.P - 1) / p.P;
   p.steps = std::min(steps, nstep_for(p.BT));
@@ -606,7 +616,7 @@ GatherPlan plan_gather(const rq_matrix* W, int B, int lut_bf16) {
     if (g_plan_n < 32) ++g_plan_n;
   }
 #ifdef RQ_TUNING
-  if (tuning_override(plan, key.NP, key.rows)) plan.lds = (size_t)plan.P * W->K * plan.BT * (lut_bf16 ? 2 : 4);
+  if (tuning_override(plan, key.NP, key.rows, B)) plan.lds = (size_t)plan.P * W->K * plan.BT * (lut_bf16 ? 2 : 4);
 #endif
   return plan;
 }

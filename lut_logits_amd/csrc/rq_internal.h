@@ -87,6 +87,9 @@ struct GatherOut {
 };
 // The lookup+sum pass: the gather kernel, and for G > 1 the finish kernel that
 // adds the partial sums in group order.
+// One-shot events around the next lookup+sum launch of this thread (rq_set_stage_events).
+void take_stage_events(hipEvent_t* before, hipEvent_t* after);
+
 hipError_t launch_gather(const rq_matrix* W, const GatherPlan& plan, const void* lut, int lut_bf16, int B,
                          const GatherOut& o, hipStream_t stream);
 int key_blocks(const GatherPlan& plan, int64_t rows);

@@ -56,3 +56,38 @@ def check_argmax(am_gpu, logits_gpu, ref, tol=None):
 
 def to_dev(mat, layout="blocked"):
     return la.to_device(mat, layout=layout)
+
+
+def bf16_table_tol(mat, h, ref, chunk=8):
+    """Per-element tolerance of logits from a bf16 table: 2^-8 * sum_{l,m} |LUT64 entry used| + 1e-5 * max|ref|
+    (twice the RNE unit roundoff of every looked-up entry), built a few vectors at a time."""
+    o = oracle.default()
+    tol = np.empty_like(ref)
+    for b0 in range(0, h.shape[0], chunk):
+        lut64 = o.build_lut(mat.codebooks, mat.cb_is_bf16, h[b0:b0 + chunk])
+        tol[b0:b0 + chunk] = 2.0 ** -8 * o.lut_sum(mat.codes, np.abs(lut64))
+    return tol + REL_TOL * np.abs(ref).max(axis=1, keepdims=True)
+
+
+def check_topk(g, ids, vals, am, ref, tolv, k):
+    """Top-k rules: self-consistency with the GPU's own logits (value desc, id asc), the oracle's
+    must-include set, every id within 2t of the oracle's k-th value, and exact ids at every rank whose
+    gaps to both neighbours exceed 2t (t = the worst per-element tolerance of that vector)."""
+    for b in range(ref.shape[0]):
+        order = np.lexsort((np.arange(g.shape[1]), -g[b]))[:k]
+        assert np.array_equal(ids[b], order), f"b={b}: top-k is not that of the GPU logits"
+        assert np.array_equal(vals[b], g[b, order])
+        if am is not None:
+            assert am[b] == ids[b, 0]
+        t = tolv[b].max()
+        kth = np.sort(ref[b])[::-1][k - 1]
+        must = np.nonzero(ref[b] > kth + 2 * t)[0]
+        assert set(must.tolist()) <= set(ids[b].tolist()), f"b={b}: an oracle top-k id is missing"
+        assert np.all(ref[b, ids[b]] >= kth - 2 * t), f"b={b}: a returned id is below the oracle's k-th"
+        oref = np.lexsort((np.arange(ref.shape[1]), -ref[b]))[:k]
+        srt = ref[b, oref]
+        for i in range(k):
+            lo = srt[i + 1] if i + 1 < k else kth - 1e9
+            hi = srt[i - 1] if i > 0 else srt[i] + 1e9
+            if hi - srt[i] > 2 * t and srt[i] - lo > 2 * t:
+                assert ids[b, i] == oref[i], f"b={b}: rank {i} differs where the gaps exceed 2t"
