@@ -178,6 +178,35 @@ rq_status rq_lut_logits(const rq_matrix* W, const void* lut, int32_t lut_dtype, 
                         hipStream_t stream);
 
 /*
+ * One-call head: the same logits, argmax and top-k as rq_build_lut followed by
+ * rq_lut_logits with an fp32 table, computed from the hidden vectors directly
+ * (runtime-compression page, LUT-serving paragraph; the sum is regrouped by
+ * distributivity, which is exact in exact arithmetic):
+ *     z[b][r] = sum_{l<L} sum_{m<M} < C[l][m][codes[r][l][m]], h[b][m*d .. m*d+d) >
+ * The library picks the method from the shapes:
+ *   - the table path (rq_build_lut into the workspace, then the lookup+sum);
+ *   - for B >= RQ_MM_MIN_B with bf16 codebooks, even d <= 8, K <= 1024 and
+ *     RQ_CODES_BLOCKED codes: the codebooks are staged on chip and the
+ *     contraction with h runs on the matrix cores, h split exactly into three
+ *     bf16 parts (fp32-level accuracy, like the fp32 table).
+ *   h       device fp32 [B][D]
+ *   other arguments as for rq_lut_logits; ws of at least rq_logits_workspace()
+ *   bytes.
+ * Results are deterministic for a given (W, B) but, being summed in a
+ * different order, are not bit-identical to the two-call form.
+ */
+#define RQ_MM_MIN_B 8
+#define RQ_METHOD_TABLE 0
+#define RQ_METHOD_MATRIX_CORES 1
+/* The method rq_logits uses for this matrix and batch (RQ_METHOD_*), or a
+ * negative rq_status for invalid arguments. */
+int32_t rq_logits_method(const rq_matrix* W, int32_t B);
+size_t rq_logits_workspace(const rq_matrix* W, int32_t B, int32_t topk);
+rq_status rq_logits(const rq_matrix* W, const float* h, int32_t B, float softcap, float* logits,
+                    int32_t* argmax, int32_t topk, int32_t* topk_ids, float* topk_vals, void* ws,
+                    size_t ws_bytes, hipStream_t stream);
+
+/*
  * On-demand reconstruction of selected rows (runtime-compression page,
  * LUT-serving paragraph: input token rows rebuilt on demand):
  *     out[i][m*d + j] = sum_{l<L} C[l][m][codes[ids[i]][l][m]][j]

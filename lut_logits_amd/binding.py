@@ -17,10 +17,11 @@ RQ_OK, RQ_ERR_NULL, RQ_ERR_SHAPE, RQ_ERR_DTYPE, RQ_ERR_ALIGN, RQ_ERR_WORKSPACE, 
 RQ_F32, RQ_BF16 = 0, 1
 RQ_PRO_NONE, RQ_PRO_GELU_TANH_MUL = 0, 1
 RQ_CODES_ROWS, RQ_CODES_BLOCKED = 0, 1
+RQ_METHOD_TABLE, RQ_METHOD_MATRIX_CORES = 0, 1
 
 # Every symbol include/rq_lut.h declares.
 EXPORTS = ("rq_blocked_codes_bytes", "rq_pack_codes", "rq_lut_bytes", "rq_build_lut", "rq_lut_logits_workspace",
-           "rq_lut_logits", "rq_decode_rows", "rq_lut_matvec_workspace", "rq_lut_matvec",
+           "rq_lut_logits", "rq_logits_method", "rq_logits_workspace", "rq_logits", "rq_decode_rows", "rq_lut_matvec_workspace", "rq_lut_matvec",
            "rq_dense_logits_workspace", "rq_dense_logits", "rq_set_stage_events", "rq_status_string", "rq_last_error", "rq_version")
 
 
@@ -55,6 +56,9 @@ def lib():
             "rq_build_lut": (_i32, [_MP, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
             "rq_lut_logits_workspace": (_sz, [_MP, _i32, _i32, _i32]),
             "rq_lut_logits": (_i32, [_MP, _vp, _i32, _i32, _f32, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
+            "rq_logits_method": (_i32, [_MP, _i32]),
+            "rq_logits_workspace": (_sz, [_MP, _i32, _i32]),
+            "rq_logits": (_i32, [_MP, _vp, _i32, _f32, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
             "rq_decode_rows": (_i32, [_MP, _vp, _i32, _i32, _vp, _vp, _vp]),
             "rq_lut_matvec_workspace": (_sz, [_MP, _i32]),
             "rq_lut_matvec": (_i32, [_MP, _vp, _vp, _i32, _i32, _vp, _vp, _sz, _vp]),
@@ -170,6 +174,34 @@ def lut_logits(W, lut, B, softcap=30.0, lut_dtype="f32", logits=True, argmax=Tru
         ws = workspace(lut_logits_workspace(W, B, topk, lut_dtype), dev)
     check(lib().rq_lut_logits(W.ref, _ptr(lut), _dtype_code(lut_dtype), B, softcap, _ptr(lg), _ptr(am), topk,
                               _ptr(ti), _ptr(tv), _ptr(ws), ws.numel(), _stream()))
+    return lg, am, ti, tv
+
+
+def logits_method(W, B):
+    """rq_logits_method: RQ_METHOD_TABLE or RQ_METHOD_MATRIX_CORES."""
+    m = lib().rq_logits_method(W.ref, B)
+    if m < 0:
+        raise RQError(m, lib().rq_last_error().decode())
+    return m
+
+
+def logits_workspace(W, B, topk=0):
+    return lib().rq_logits_workspace(W.ref, B, topk)
+
+
+def logits(W, h, softcap=30.0, logits=True, argmax=True, topk=0, ws=None, out=None, argmax_out=None):
+    """rq_logits (one call from the hidden vectors h [B][D] fp32): returns
+    (logits [B][rows] | None, argmax [B] | None, topk_ids | None, topk_vals | None)."""
+    B = h.shape[0]
+    dev = h.device
+    lg = (out if out is not None else torch.empty((B, W.rows), dtype=torch.float32, device=dev)) if logits else None
+    am = (argmax_out if argmax_out is not None else torch.empty(B, dtype=torch.int32, device=dev)) if argmax else None
+    ti = torch.empty((B, topk), dtype=torch.int32, device=dev) if topk else None
+    tv = torch.empty((B, topk), dtype=torch.float32, device=dev) if topk else None
+    if ws is None:
+        ws = workspace(logits_workspace(W, B, topk), dev)
+    check(lib().rq_logits(W.ref, _ptr(h), B, softcap, _ptr(lg), _ptr(am), topk, _ptr(ti), _ptr(tv), _ptr(ws),
+                          ws.numel(), _stream()))
     return lg, am, ti, tv
 
 

@@ -208,6 +208,101 @@ rq_status rq_lut_logits(const rq_matrix* W, const void* lut, int32_t lut_dtype, 
   return launched(e, "rq_lut_logits: selection");
 }
 
+// Workspace of rq_logits. Matrix-core method: the split hidden vectors, then
+// the partial sums [G][B][rows]; table method: the fp32 table [L][M][K][B], then
+// the partial sums of the lookup+sum. Both end with the logits scratch (top-k
+// without a logits output), the selection keys and the top-k candidates.
+struct HeadWs {
+  bool mm;
+  rq::MmPlan mp;
+  rq::GatherPlan gp;
+  size_t front, partial, scratch, keys, cand, total;
+  int nkb;
+};
+
+HeadWs head_ws(const rq_matrix* W, int32_t B, int32_t topk, bool logits_out) {
+  HeadWs w{};
+  w.mm = B >= RQ_MM_MIN_B && rq::mm_supported(W);
+  size_t partial_bytes;
+  w.front = 0;
+  if (w.mm) {
+    w.mp = rq::plan_mm(W, B);
+    w.partial = round_up(rq::mm_hp_bytes(W, w.mp), 256);
+    partial_bytes = (size_t)w.mp.G * B * W->rows * sizeof(float);
+    w.nkb = rq::finish_key_blocks(w.mp.G, W->rows);
+  } else {
+    w.gp = rq::plan_gather(W, B, 0);
+    w.partial = round_up(lut_elems(W, B) * sizeof(float), 256);
+    partial_bytes = w.gp.G > 1 ? (size_t)w.gp.G * B * W->rows * sizeof(float) : 0;
+    w.nkb = rq::key_blocks(w.gp, W->rows);
+  }
+  w.scratch = w.partial + round_up(partial_bytes, 256);
+  w.keys = w.scratch + (topk > 0 && !logits_out ? round_up((size_t)B * W->rows * sizeof(float), 256) : 0);
+  w.cand = w.keys + round_up((size_t)B * w.nkb * sizeof(uint64_t), 256);
+  w.total = w.cand + (topk > 0 ? round_up((size_t)B * rq::epi_blocks(W->rows) * topk * sizeof(uint64_t), 256) : 0);
+  return w;
+}
+
+int32_t rq_logits_method(const rq_matrix* W, int32_t B) {
+  const rq_status s = check_lut_call(W, B, RQ_F32);
+  if (s != RQ_OK) return s;
+  return B >= RQ_MM_MIN_B && rq::mm_supported(W) ? RQ_METHOD_MATRIX_CORES : RQ_METHOD_TABLE;
+}
+
+size_t rq_logits_workspace(const rq_matrix* W, int32_t B, int32_t topk) {
+  if (check_lut_call(W, B, RQ_F32) != RQ_OK || topk < 0) return 0;
+  if (B == 0 || W->rows == 0) return 0;
+  const HeadWs w = head_ws(W, B, topk, false);
+  if (!w.mm && w.gp.BT == 0) return 0;
+  return w.total;
+}
+
+rq_status rq_logits(const rq_matrix* W, const float* h, int32_t B, float softcap, float* logits, int32_t* argmax,
+                    int32_t topk, int32_t* topk_ids, float* topk_vals, void* ws, size_t ws_bytes,
+                    hipStream_t stream) {
+  rq_status s = check_lut_call(W, B, RQ_F32);
+  if (s != RQ_OK) return s;
+  if (topk < 0 || topk > 1024 || (W->rows > 0 && topk > W->rows))
+    return fail(RQ_ERR_SHAPE, "topk=%d outside [0, min(rows, 1024)]", topk);
+  if (B == 0 || W->rows == 0) return RQ_OK;
+  if (!h) return fail(RQ_ERR_NULL, "h is NULL");
+  if (topk > 0 && !topk_ids) return fail(RQ_ERR_NULL, "topk_ids is NULL");
+  if (!aligned(h, 4) || (logits && !aligned(logits, 4)) || (argmax && !aligned(argmax, 4)) ||
+      (topk_ids && !aligned(topk_ids, 4)) || (topk_vals && !aligned(topk_vals, 4)))
+    return fail(RQ_ERR_ALIGN, "argument misaligned");
+  const HeadWs w = head_ws(W, B, topk, logits != nullptr);
+  if (!w.mm && w.gp.BT == 0) return fail(RQ_ERR_SHAPE, "no table tiling fits on chip for K=%d", W->K);
+  if (!ws || ws_bytes < w.total) return fail(RQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, w.total);
+  if (!aligned(ws, 256)) return fail(RQ_ERR_ALIGN, "workspace must be 256-byte aligned");
+  char* base = static_cast<char*>(ws);
+  const bool select = argmax || topk > 0;
+  float* partial = reinterpret_cast<float*>(base + w.partial);
+  float* out = logits ? logits : (topk > 0 ? reinterpret_cast<float*>(base + w.scratch) : nullptr);
+  uint64_t* keys = select ? reinterpret_cast<uint64_t*>(base + w.keys) : nullptr;
+  hipError_t e;
+  if (w.mm) {
+    e = rq::launch_mm_logits(W, w.mp, h, B, base + w.front, partial, stream);
+    if (e != hipSuccess) return launched(e, "rq_logits: matrix-core pass");
+    e = rq::launch_finish(partial, w.mp.G, B, W->rows, softcap, out, keys, stream);
+    if (e != hipSuccess) return launched(e, "rq_logits: finish");
+  } else {
+    void* lut = base + w.front;
+    e = rq::launch_build_lut(W, h, nullptr, RQ_PRO_NONE, B, 0, lut, stream);
+    if (e != hipSuccess) return launched(e, "rq_logits: table build");
+    rq::GatherOut o;
+    o.partial = partial;
+    o.out = out;
+    o.softcap = softcap;
+    o.block_keys = keys;
+    e = rq::launch_gather(W, w.gp, lut, 0, B, o, stream);
+    if (e != hipSuccess) return launched(e, "rq_logits: lookup+sum");
+  }
+  if (!select) return RQ_OK;
+  e = rq::launch_select(keys, w.nkb, B, argmax, out, W->rows, topk, reinterpret_cast<uint64_t*>(base + w.cand),
+                        topk_ids, topk_vals, stream);
+  return launched(e, "rq_logits: selection");
+}
+
 rq_status rq_decode_rows(const rq_matrix* W, const int32_t* ids, int32_t n, int32_t out_dtype, void* out,
                          int32_t* bad_ids, hipStream_t stream) {
   rq_status s = check_matrix(W, true);
@@ -221,25 +316,34 @@ rq_status rq_decode_rows(const rq_matrix* W, const int32_t* ids, int32_t n, int3
   return launched(rq::launch_decode_rows(W, ids, n, out_dtype == RQ_BF16, out, bad_ids, stream), "rq_decode_rows");
 }
 
-// Workspace of rq_lut_matvec: the fp32 table [L][M][K][B], then the partial
-// sums [G][B][rows] (G > 1).
+// Workspace of rq_lut_matvec. Fused table build (one activation vector, fp32
+// codebooks, d in {1, 2, 4}): the partial sums [G][rows]. Otherwise: the fp32
+// table [L][M][K][B], then the partial sums [G][B][rows] (G > 1).
 struct MatvecWs {
-  size_t lut, partial, total;
+  bool fused;
+  rq::GatherPlan plan;
+  size_t front, partial, total;
 };
 
-MatvecWs matvec_ws(const rq_matrix* W, const rq::GatherPlan& plan, int32_t B) {
-  MatvecWs m;
-  m.lut = 0;
-  m.partial = round_up(lut_elems(W, B) * sizeof(float), 256);
-  m.total = m.partial + (plan.G > 1 ? round_up((size_t)plan.G * B * W->rows * sizeof(float), 256) : 0);
+MatvecWs matvec_ws(const rq_matrix* W, int32_t B) {
+  MatvecWs m{};
+  m.fused = rq::fused_build_supported(W, B);
+  if (m.fused) {
+    m.plan = rq::plan_gather(W, B, 0, 1);
+    if (m.plan.BT == 0) m.fused = false;
+  }
+  if (!m.fused) m.plan = rq::plan_gather(W, B, 0);
+  m.front = 0;
+  m.partial = m.fused ? 0 : round_up(lut_elems(W, B) * sizeof(float), 256);
+  m.total = m.partial + (m.plan.G > 1 ? round_up((size_t)m.plan.G * B * W->rows * sizeof(float), 256) : 0);
   return m;
 }
 
 size_t rq_lut_matvec_workspace(const rq_matrix* W, int32_t B) {
   if (check_lut_call(W, B, RQ_F32) != RQ_OK || B == 0 || W->rows == 0) return 0;
-  const rq::GatherPlan plan = rq::plan_gather(W, B, 0);
-  if (plan.BT == 0) return 0;
-  return matvec_ws(W, plan, B).total;
+  const MatvecWs m = matvec_ws(W, B);
+  if (m.plan.BT == 0) return 0;
+  return m.total;
 }
 
 rq_status rq_lut_matvec(const rq_matrix* W, const float* x, const float* x2, int32_t prologue, int32_t B, float* y,
@@ -250,21 +354,25 @@ rq_status rq_lut_matvec(const rq_matrix* W, const float* x, const float* x2, int
   if (B == 0 || W->rows == 0) return RQ_OK;
   if (!x || !y || (prologue == RQ_PRO_GELU_TANH_MUL && !x2)) return fail(RQ_ERR_NULL, "lut_matvec: NULL buffer");
   if (!aligned(x, 4) || (x2 && !aligned(x2, 4)) || !aligned(y, 4)) return fail(RQ_ERR_ALIGN, "lut_matvec: misaligned buffer");
-  const rq::GatherPlan plan = rq::plan_gather(W, B, 0);
-  if (plan.BT == 0) return fail(RQ_ERR_SHAPE, "no table tiling fits on chip for K=%d", W->K);
-  const MatvecWs m = matvec_ws(W, plan, B);
+  const MatvecWs m = matvec_ws(W, B);
+  if (m.plan.BT == 0) return fail(RQ_ERR_SHAPE, "no table tiling fits on chip for K=%d", W->K);
   if (!ws || ws_bytes < m.total) return fail(RQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, m.total);
   if (!aligned(ws, 256)) return fail(RQ_ERR_ALIGN, "workspace must be 256-byte aligned");
   char* base = static_cast<char*>(ws);
-  float* lut = reinterpret_cast<float*>(base + m.lut);
-  hipError_t e = rq::launch_build_lut(W, x, x2, prologue, B, 0, lut, stream);
-  if (e != hipSuccess) return launched(e, "rq_lut_matvec: table build");
   rq::GatherOut o;
   o.partial = reinterpret_cast<float*>(base + m.partial);
   o.out = y;
   o.softcap = 0.0f;
   o.block_keys = nullptr;
-  return launched(rq::launch_gather(W, plan, lut, 0, B, o, stream), "rq_lut_matvec: lookup+sum");
+  hipError_t e;
+  if (m.fused)
+    return launched(rq::launch_gather(W, m.plan, nullptr, 0, B, o, stream, x,
+                                      prologue == RQ_PRO_GELU_TANH_MUL ? x2 : nullptr),
+                    "rq_lut_matvec: fused lookup+sum");
+  float* lut = reinterpret_cast<float*>(base + m.front);
+  e = rq::launch_build_lut(W, x, x2, prologue, B, 0, lut, stream);
+  if (e != hipSuccess) return launched(e, "rq_lut_matvec: table build");
+  return launched(rq::launch_gather(W, m.plan, lut, 0, B, o, stream), "rq_lut_matvec: lookup+sum");
 }
 
 size_t rq_dense_logits_workspace(int64_t rows, int32_t B) {

@@ -47,7 +47,10 @@ namespace {
 
 struct GatherArgs {
   CodeView cv;
-  const void* lut;            // [NP][K][B]
+  const void* lut;            // [NP][K][B] (fused table build: the fp32 codebooks [NP][K][d])
+  const float* act;           // fused table build: the activation vector [D] (with act2: gelu_tanh(act) * act2)
+  const float* act2;
+  int D, M;                   // fused table build: row width and subspaces
   int64_t rows;
   int NP, K, B;
   int P, chunks, cpg, G, steps, S, NBT;
@@ -149,6 +152,48 @@ __device__ __forceinline__ void chunk_to_regs(ChunkRegs& r, const u32x4* __restr
   r.w4 = src[min(tid + 4 * T, last)]; r.w5 = src[min(tid + 5 * T, last)];
   r.w6 = src[min(tid + 6 * T, last)]; r.w7 = src[min(tid + 7 * T, last)];
 }
+// Fused table build (B == 1, fp32 codebooks, subspace width FD dividing 4):
+// the registers hold codebook words instead of table words; each word is 4/FD
+// codewords of one pair, whose table entries
+//     LUT[p][k] = sum_{j<FD} act[m*FD + j] * C[p][k][j]      (m = p mod M)
+// are computed with the same fmaf chain as the table-build kernel and written
+// to LDS. act sits in LDS after the chunk.
+template <int FD>
+__device__ __forceinline__ void fused_word(const u32x4 w, int i, float* tab, const float* act_s, int p0, int K, int M) {
+  constexpr int EPW = 4 / FD;
+  const int e0 = i * EPW;                 // entry index within the chunk: (pair - p0) * K + k
+  const int m = (p0 + e0 / K) % M;
+  float v[EPW];
+#pragma unroll
+  for (int t = 0; t < EPW; ++t) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < FD; ++j) {
+      // element to a scalar first: hipcc folds __builtin_bit_cast of a vector
+      // element to element 0
+      const uint32_t bits = w[t * FD + j];
+      acc = fmaf(act_s[m * FD + j], __uint_as_float(bits), acc);
+    }
+    v[t] = acc;
+  }
+  if (EPW == 4) *reinterpret_cast<float4*>(tab + e0) = make_float4(v[0], v[1 % EPW], v[2 % EPW], v[3 % EPW]);
+  else if (EPW == 2) *reinterpret_cast<float2*>(tab + e0) = make_float2(v[0], v[1 % EPW]);
+  else tab[e0] = v[0];
+}
+template <int FD>
+__device__ __forceinline__ void regs_to_lds_fused(const ChunkRegs& r, float* tab, const float* act_s, int tid,
+                                                  int last, int p0, int K, int M) {
+  const int T = kGatherThreads;
+  fused_word<FD>(r.w0, min(tid, last), tab, act_s, p0, K, M);
+  fused_word<FD>(r.w1, min(tid + T, last), tab, act_s, p0, K, M);
+  fused_word<FD>(r.w2, min(tid + 2 * T, last), tab, act_s, p0, K, M);
+  fused_word<FD>(r.w3, min(tid + 3 * T, last), tab, act_s, p0, K, M);
+  fused_word<FD>(r.w4, min(tid + 4 * T, last), tab, act_s, p0, K, M);
+  fused_word<FD>(r.w5, min(tid + 5 * T, last), tab, act_s, p0, K, M);
+  fused_word<FD>(r.w6, min(tid + 6 * T, last), tab, act_s, p0, K, M);
+  fused_word<FD>(r.w7, min(tid + 7 * T, last), tab, act_s, p0, K, M);
+}
+
 __device__ __forceinline__ void regs_to_lds(const ChunkRegs& r, u32x4* dst, int tid, int last) {
   const int T = kGatherThreads;
   dst[min(tid, last)] = r.w0;         dst[min(tid + T, last)] = r.w1;
@@ -160,9 +205,11 @@ __device__ __forceinline__ void regs_to_lds(const ChunkRegs& r, u32x4* dst, int 
 // One 1024-thread workgroup per CU (its LDS chunk fills the CU), i.e. four
 // waves per SIMD: the register budget is 128 VGPRs, stated explicitly so the
 // compiler does not trade registers for an occupancy the LDS cannot reach.
-template <typename LutT, int BT, int NSTEP, bool REG>
+// FD > 0: fused table build (see fused_word); requires LutT float, BT 1, REG.
+template <typename LutT, int BT, int NSTEP, bool REG, int FD = 0>
 __global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(1, 4)))
 void gather_kernel(GatherArgs a) {
+  static_assert(FD == 0 || (BT == 1 && REG && sizeof(LutT) == 4 && 4 % FD == 0), "fused build: fp32, B=1, FD | 4");
   constexpr int QL = (BT >= 16) ? 4 : 1;   // lanes per row
   constexpr int BQ = BT / QL;              // batch entries per lane
   constexpr int RPS = kGatherThreads / QL; // rows per step
@@ -251,7 +298,12 @@ void gather_kernel(GatherArgs a) {
   uint4 wa[NSTEP], wb[NSTEP];
   ChunkRegs nxt;
   const u32x4* lut4 = reinterpret_cast<const u32x4*>(lut);
-  const int words_per_pair = a.K * BT * (int)sizeof(LutT) / 16;   // REG: 16-byte words per pair
+  // REG: 16-byte words per pair (of the table, or with FD of the codebook)
+  const int words_per_pair = FD ? a.K * FD / 4 : a.K * BT * (int)sizeof(LutT) / 16;
+  // FD: the activation vector goes to LDS after the chunk, once
+  float* act_s = reinterpret_cast<float*>(smem + (size_t)a.P * a.K * sizeof(float));
+  if (FD)
+    for (int i = tid; i < a.D; i += kGatherThreads) act_s[i] = a.act2 ? gelu_tanh(a.act[i]) * a.act2[i] : a.act[i];
   // REG: chunk c's words go to registers with a fixed count of unconditional
   // loads (clamped to the last word of the chunk).
   if (REG) {
@@ -268,7 +320,11 @@ void gather_kernel(GatherArgs a) {
     if (REG) {
       // words past the chunk were loaded clamped to its last word, so writing
       // them clamped stores that same value again
-      regs_to_lds(nxt, reinterpret_cast<u32x4*>(tab), tid, pc * words_per_pair - 1);
+      if (FD)
+        regs_to_lds_fused<FD ? FD : 1>(nxt, reinterpret_cast<float*>(tab), act_s, tid, pc * words_per_pair - 1, p0, a.K,
+                                       a.M);
+      else
+        regs_to_lds(nxt, reinterpret_cast<u32x4*>(tab), tid, pc * words_per_pair - 1);
       const int cn = min(c + 1, c_end - 1);
       const int n4n = min(a.P, a.NP - cn * a.P) * words_per_pair;
       chunk_to_regs(nxt, lut4 + (size_t)cn * a.P * words_per_pair, tid, n4n - 1);
@@ -328,12 +384,13 @@ void gather_kernel(GatherArgs a) {
   if (tid < BT && b0 + tid < a.B) a.block_keys[(size_t)(b0 + tid) * a.S + s] = s_keys[tid];
 }
 
-template <typename LutT, int BT, int NSTEP>
+template <typename LutT, int BT, int NSTEP, int FD = 0>
 hipError_t launch_gather_typed(const GatherArgs& a, const GatherPlan& plan, hipStream_t stream) {
   const size_t chunk_bytes = (size_t)plan.P * a.K * BT * sizeof(LutT);
   const bool reg = a.B == BT && chunk_bytes % 16 == 0 && chunk_bytes <= (size_t)kRegStage * 16 * kGatherThreads &&
                    ((size_t)a.K * BT * sizeof(LutT)) % 16 == 0;
-  auto kern = reg ? gather_kernel<LutT, BT, NSTEP, true> : gather_kernel<LutT, BT, NSTEP, false>;
+  auto kern = FD ? gather_kernel<LutT, BT, NSTEP, true, FD>
+                 : (reg ? gather_kernel<LutT, BT, NSTEP, true> : gather_kernel<LutT, BT, NSTEP, false>);
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget);
   if (e != hipSuccess) return e;
   hipEvent_t before, after;
@@ -400,33 +457,54 @@ __global__ __launch_bounds__(kTopkThreads) void topk_block_kernel(const float* _
 
 constexpr int kFinishThreads = 1024;
 
-// z = sum of the G partial sums of each output in group order, then the
-// softcap; the best selection key of each block of 1024 rows.
+// z = sum of the G partial sums of each output in a fixed order, then the
+// softcap; the best selection key of each block of rows.
+// TPR "parts" per row: part t adds groups t, t+TPR, t+2*TPR, ... in order and
+// the parts are then added in order 0..TPR-1 (fixed order, so bit-reproducible).
+// A block covers kFinishThreads/TPR rows; each wave reads 64 consecutive rows of
+// one group (coalesced). Many groups over few rows (MLP shapes) need TPR > 1 to
+// keep enough loads in flight; TPR == 1 is a plain sum in group order.
+template <int TPR>
 __global__ __launch_bounds__(kFinishThreads) void finish_kernel(const float* __restrict__ partial, int G, int B,
                                                                 int64_t rows, float softcap, float* __restrict__ out,
                                                                 uint64_t* __restrict__ block_keys) {
+  constexpr int RPB = kFinishThreads / TPR;
   __shared__ unsigned long long s_best;
+  __shared__ float s_part[TPR > 1 ? TPR : 1][TPR > 1 ? RPB : 1];
   const int blk = blockIdx.x;
   const int b = blockIdx.y;
-  const int64_t r = (int64_t)blk * kFinishThreads + threadIdx.x;
+  const int part = threadIdx.x / RPB;
+  const int local = threadIdx.x - part * RPB;
+  const int64_t r = (int64_t)blk * RPB + local;
   if (threadIdx.x == 0) s_best = 0ull;
-  unsigned long long key = 0ull;
+  float z = 0.0f;
   if (r < rows) {
     const float* src = partial + (size_t)b * rows + r;
     const size_t gstride = (size_t)B * rows;
-    float z = 0.0f;
-    int g = 0;
-    for (; g + 4 <= G; g += 4) {   // four loads in flight, added in group order
-      const float v0 = src[(size_t)g * gstride], v1 = src[(size_t)(g + 1) * gstride];
-      const float v2 = src[(size_t)(g + 2) * gstride], v3 = src[(size_t)(g + 3) * gstride];
+    int g = part;
+    for (; g + 3 * TPR < G; g += 4 * TPR) {   // four loads in flight, added in order
+      const float v0 = src[(size_t)g * gstride], v1 = src[(size_t)(g + TPR) * gstride];
+      const float v2 = src[(size_t)(g + 2 * TPR) * gstride], v3 = src[(size_t)(g + 3 * TPR) * gstride];
       z += v0; z += v1; z += v2; z += v3;
     }
-    for (; g < G; ++g) z += src[(size_t)g * gstride];
+    for (; g < G; g += TPR) z += src[(size_t)g * gstride];
+  }
+  if (TPR > 1) {
+    s_part[part][local] = z;
+    __syncthreads();
+    if (part == 0) {
+      z = s_part[0][local];
+#pragma unroll
+      for (int t = 1; t < TPR; ++t) z += s_part[t][local];
+    }
+  }
+  unsigned long long key = 0ull;
+  if (part == 0 && r < rows) {
     const float v = softcap > 0.0f ? softcap * tanhf(z / softcap) : z;
     if (out) out[(size_t)b * rows + r] = v;
     key = select_key(v, (uint32_t)r);
   }
-  if (!block_keys) return;
+  if (!block_keys) return;   // uniform: a kernel argument
   __syncthreads();
   const uint64_t w = wave_max_u64(key);
   if ((threadIdx.x & 63) == 0) atomicMax(&s_best, (unsigned long long)w);
@@ -515,7 +593,8 @@ namespace {
 // ~150 GB/s per CU (staging is not overlapped with the stream); random 4-byte
 // LDS lookups run at ~9 per clock per CU (quad-contiguous 64-byte lookups at
 // ~120 B/clock); G > 1 adds the partial-sum traffic and a finish launch.
-double plan_cost_us(int64_t rows, int NP, int K, int B, int es, int BT, int P, int steps, int G, int cpg) {
+double plan_cost_us(int64_t rows, int NP, int K, int B, int es, int BT, int P, int steps, int G, int cpg,
+                    int stage_es) {
   const int QL = BT >= 16 ? 4 : 1;
   const int rps = kGatherThreads / QL;
   const int64_t S = (rows + (int64_t)steps * rps - 1) / ((int64_t)steps * rps);
@@ -525,7 +604,7 @@ double plan_cost_us(int64_t rows, int NP, int K, int B, int es, int BT, int P, i
   const int64_t active = std::min<int64_t>(wgs, kCUs);
   const double slab_rows = (double)std::min<int64_t>(rows, (int64_t)steps * rps);
   const double pairs = (double)cpg * P;
-  const double chunk_bytes = (double)P * K * BT * es;
+  const double chunk_bytes = (double)P * K * BT * stage_es;
   const double t_stage = cpg * (2.0 + chunk_bytes / 150e3);
   const double per_cu_bw = std::min(150e3, 6.4e6 / (double)active);          // bytes per us
   const double t_codes = slab_rows * pairs * 2.0 / per_cu_bw;
@@ -537,8 +616,13 @@ double plan_cost_us(int64_t rows, int NP, int K, int B, int es, int BT, int P, i
   return std::max(t_stream, (double)rounds * t_wg) + t_partial;
 }
 
-GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16) {
+// fused_d > 0: the table is built while staging from fp32 codebooks of
+// subspace width fused_d (B == 1): a chunk's staged bytes are its codebook
+// rows (4*fused_d per entry, at most 128 KB so they fit the staging
+// registers), and the activation vector (D floats) shares the LDS.
+GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16, int fused_d, int D) {
   const int es = lut_bf16 ? 2 : 4;
+  const int stage_es = fused_d ? 4 * fused_d : es;
   GatherPlan best{};
   int BT = 1;
   if (B > 1) BT = ((size_t)K * 16 * es * 2 <= (size_t)kLdsBudget && B >= 16) ? 16 : 4;
@@ -549,6 +633,12 @@ GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16) {
   const int nstep = nstep_for(BT);
   const int NBT = (B + BT - 1) / BT;
   int pmax = (int)std::min<int64_t>(NP, kLdsBudget / ((size_t)K * BT * es));
+  if (fused_d) {
+    const int64_t lds_left = (int64_t)kLdsBudget - (int64_t)D * 4;
+    pmax = (int)std::min<int64_t>({(int64_t)NP, lds_left / ((int64_t)K * 4),
+                                   (int64_t)kRegStage * 16 * kGatherThreads / ((int64_t)K * stage_es)});
+    if (pmax < 1) return best;
+  }
   if (pmax < NP && pmax > 1) pmax &= ~1;
   double best_cost = 1e300;
   int tried = 0;
@@ -565,7 +655,8 @@ GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16) {
         const int G = (chunks + cpg - 1) / cpg;
         if (G != G0) continue;
         // prefer aligned chunks (staging outside the block loop) on near-ties
-        const double cost = plan_cost_us(rows, NP, K, B, es, BT, P, steps, G, cpg) * ((P % 8 == 0 || chunks == 1) ? 1.0 : 1.03);
+        const double cost = plan_cost_us(rows, NP, K, B, es, BT, P, steps, G, cpg, stage_es) *
+                            ((P % 8 == 0 || chunks == 1) ? 1.0 : 1.03);
         if (cost < best_cost * 0.999) {
           best_cost = cost;
           best.BT = BT; best.P = P; best.chunks = chunks; best.cpg = cpg; best.G = G;
@@ -574,7 +665,7 @@ GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16) {
       }
     }
   }
-  best.lds = (size_t)best.P * K * BT * es;
+  best.lds = (size_t)best.P * K * BT * es + (fused_d ? (size_t)D * 4 : 0);
   return best;
 }
 
@@ -582,9 +673,9 @@ GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16) {
 // off the per-call path.
 struct PlanKey {
   int64_t rows;
-  int NP, K, B, bf16;
+  int NP, K, B, bf16, fused_d, D;
   bool operator==(const PlanKey& o) const {
-    return rows == o.rows && NP == o.NP && K == o.K && B == o.B && bf16 == o.bf16;
+    return rows == o.rows && NP == o.NP && K == o.K && B == o.B && bf16 == o.bf16 && fused_d == o.fused_d && D == o.D;
   }
 };
 std::mutex g_plan_mu;
@@ -598,8 +689,9 @@ int g_plan_n = 0, g_plan_next = 0;
 // and G are, so P is taken as large as LDS allows; then (steps, G) are chosen
 // to fill every CU with one workgroup per round, preferring few groups
 // (partial-sum traffic) and long slabs (loads in flight per lane).
-GatherPlan plan_gather(const rq_matrix* W, int B, int lut_bf16) {
-  const PlanKey key{W->rows, W->L * W->M, W->K, B, lut_bf16};
+GatherPlan plan_gather(const rq_matrix* W, int B, int lut_bf16, int fused) {
+  const int fd = fused ? W->d : 0;
+  const PlanKey key{W->rows, W->L * W->M, W->K, B, lut_bf16, fd, fused ? W->D : 0};
   GatherPlan plan{};
   bool hit = false;
   {
@@ -608,7 +700,7 @@ GatherPlan plan_gather(const rq_matrix* W, int B, int lut_bf16) {
       if (g_plan_keys[i] == key) { plan = g_plans[i]; hit = true; break; }
   }
   if (!hit) {
-    plan = search_plan(key.rows, key.NP, key.K, B, lut_bf16);
+    plan = search_plan(key.rows, key.NP, key.K, B, lut_bf16, fd, key.D);
     std::lock_guard<std::mutex> lock(g_plan_mu);
     g_plan_keys[g_plan_next] = key;
     g_plans[g_plan_next] = plan;
@@ -616,16 +708,26 @@ GatherPlan plan_gather(const rq_matrix* W, int B, int lut_bf16) {
     if (g_plan_n < 32) ++g_plan_n;
   }
 #ifdef RQ_TUNING
-  if (tuning_override(plan, key.NP, key.rows, B)) plan.lds = (size_t)plan.P * W->K * plan.BT * (lut_bf16 ? 2 : 4);
+  if (tuning_override(plan, key.NP, key.rows, B))
+    plan.lds = (size_t)plan.P * W->K * plan.BT * (lut_bf16 ? 2 : 4) + (fd ? (size_t)key.D * 4 : 0);
 #endif
   return plan;
 }
 
+bool fused_build_supported(const rq_matrix* W, int B) {
+  return B == 1 && W->cb_dtype == RQ_F32 && (W->d == 1 || W->d == 2 || W->d == 4) &&
+         ((uintptr_t)W->codebooks % 16) == 0 && ((size_t)W->K * W->d) % 4 == 0;
+}
+
 hipError_t launch_gather(const rq_matrix* W, const GatherPlan& plan, const void* lut, int lut_bf16, int B,
-                         const GatherOut& o, hipStream_t stream) {
+                         const GatherOut& o, hipStream_t stream, const float* fused_act, const float* fused_x2) {
   GatherArgs a;
   a.cv = code_view(W);
-  a.lut = lut;
+  a.lut = fused_act ? W->codebooks : lut;
+  a.act = fused_act;
+  a.act2 = fused_x2;
+  a.D = W->D;
+  a.M = W->M;
   a.rows = W->rows;
   a.NP = W->L * W->M;
   a.K = W->K;
@@ -637,7 +739,11 @@ hipError_t launch_gather(const rq_matrix* W, const GatherPlan& plan, const void*
   a.softcap = o.softcap;
   a.block_keys = plan.G == 1 ? o.block_keys : nullptr;
   hipError_t e;
-  if (lut_bf16) {
+  if (fused_act) {
+    if (W->d == 1) e = launch_gather_typed<float, 1, 4, 1>(a, plan, stream);
+    else if (W->d == 2) e = launch_gather_typed<float, 1, 4, 2>(a, plan, stream);
+    else e = launch_gather_typed<float, 1, 4, 4>(a, plan, stream);
+  } else if (lut_bf16) {
     if (plan.BT == 1) e = launch_gather_typed<uint16_t, 1, 4>(a, plan, stream);
     else if (plan.BT == 4) e = launch_gather_typed<uint16_t, 4, 4>(a, plan, stream);
     else e = launch_gather_typed<uint16_t, 16, 4>(a, plan, stream);
@@ -647,14 +753,36 @@ hipError_t launch_gather(const rq_matrix* W, const GatherPlan& plan, const void*
     else e = launch_gather_typed<float, 16, 4>(a, plan, stream);
   }
   if (e != hipSuccess || plan.G == 1) return e;
-  dim3 grid((unsigned)((W->rows + kFinishThreads - 1) / kFinishThreads), (unsigned)B);
-  hipLaunchKernelGGL(finish_kernel, grid, dim3(kFinishThreads), 0, stream, o.partial, plan.G, B, W->rows, o.softcap,
-                     o.out, o.block_keys);
+  return launch_finish(o.partial, plan.G, B, W->rows, o.softcap, o.out, o.block_keys, stream);
+}
+
+int finish_parts(int G) { return G <= 8 ? 1 : (G <= 64 ? 4 : 16); }
+int finish_rows_per_block(int G) { return kFinishThreads / finish_parts(G); }
+
+hipError_t launch_finish(const float* partial, int G, int B, int64_t rows, float softcap, float* out,
+                         uint64_t* block_keys, hipStream_t stream) {
+  const int tpr = finish_parts(G);
+  const int rpb = kFinishThreads / tpr;
+  dim3 grid((unsigned)((rows + rpb - 1) / rpb), (unsigned)B);
+  if (tpr == 1)
+    hipLaunchKernelGGL(finish_kernel<1>, grid, dim3(kFinishThreads), 0, stream, partial, G, B, rows, softcap, out,
+                       block_keys);
+  else if (tpr == 4)
+    hipLaunchKernelGGL(finish_kernel<4>, grid, dim3(kFinishThreads), 0, stream, partial, G, B, rows, softcap, out,
+                       block_keys);
+  else
+    hipLaunchKernelGGL(finish_kernel<16>, grid, dim3(kFinishThreads), 0, stream, partial, G, B, rows, softcap, out,
+                       block_keys);
   return hipGetLastError();
 }
 
 int key_blocks(const GatherPlan& plan, int64_t rows) {
-  return plan.G == 1 ? plan.S : (int)((rows + kFinishThreads - 1) / kFinishThreads);
+  return plan.G == 1 ? plan.S : finish_key_blocks(plan.G, rows);
+}
+
+int finish_key_blocks(int G, int64_t rows) {
+  const int rpb = finish_rows_per_block(G);
+  return (int)((rows + rpb - 1) / rpb);
 }
 
 hipError_t launch_select(const uint64_t* block_keys, int nkb, int B, int32_t* argmax, const float* logits,

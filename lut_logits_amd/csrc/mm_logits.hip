@@ -1,0 +1,407 @@
+// mm_logits.hip -- head logits for a batch of hidden vectors on the matrix
+// cores, reading the same RQ codes but never building a per-vector table.
+//
+// What is computed is the runtime-compression page's lookup+sum (LUT-serving
+// paragraph) in its other association: instead of LUT[l][m][k][b] =
+// <h_b on subspace m, C[l][m][k]> followed by a sum of looked-up entries,
+//     z[b][r] = sum_{l,m} < C[l][m][code[r][l][m]], h_b on subspace m >,
+// which is the same number in exact arithmetic (distributivity). For B >= 16
+// the table is B times larger than the codebook it comes from, and staging it
+// through LDS dominates; the codebook costs 16 bytes per codeword whatever B
+// is, and the B-fold work becomes a dense contraction for the matrix cores.
+//
+// Exactness. Codebooks are bf16 (exact MFMA operands). Each fp32 hidden value
+// is split into three bf16 parts, x = p0 + p1 + p2 exactly (each part is the
+// RNE of what the previous ones left; 3 x 8 significant bits cover fp32's 24).
+// Every bf16 x bf16 product is exact in fp32 and the matrix cores accumulate in
+// fp32, so the result carries fp32 accumulation error only, as the table path
+// does.
+//
+// Mapping onto v_mfma_f32_16x16x32_bf16 (A: 16 rows x 32 k, B: 32 k x 16
+// columns, C: 16 x 16 fp32):
+//   - A rows are 16 vocab rows; the 32 k split into four slots of 8, one
+//     subspace each (d <= 8 values, zero-padded).
+//   - B columns are 16 hidden vectors; B's slot kg holds the same subspace's
+//     slice of one part of h.
+//   - Lane (i = lane % 16, kg = lane / 16) feeds A row i, slot kg, and receives
+//     C rows 4*kg .. 4*kg+3 of column i.
+// The blocked code layout gives each row 16 bytes per block of 8 (level,
+// subspace) pairs; dword kg of it holds the codes of pairs 2kg and 2kg+1. So a
+// lane loads exactly one dword per row tile and block (a wave reads 16 rows x 16
+// contiguous bytes, no byte twice) and the block is done as two "half-blocks":
+// half s uses pairs {8q + 2kg + s : kg < 4}, the low or high 16 bits.
+//
+// Work split: workgroup (group g, slab s, batch tile bt) accumulates 16*NT
+// hidden vectors over slab s's rows (8 waves x T tiles x 16 rows) for group
+// g's code blocks. Half-blocks stream through a two-slot LDS ring: 4 pairs x K
+// codewords (16 B each, padded) plus the three parts of h for those pairs; the
+// next half's codebook sits in registers while the current one is in use.
+// Partial sums go to [G][B][rows] and the finish kernel adds them in group
+// order, applies the softcap and emits the selection keys.
+#include "rq_internal.h"
+
+namespace rq {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+#ifndef RQ_MM_THREADS
+#define RQ_MM_THREADS 512
+#endif
+constexpr int kMmThreads = RQ_MM_THREADS;   // one workgroup per CU (LDS); 512: 2 waves per SIMD, 256 VGPRs each
+constexpr int kMmWaves = kMmThreads / 64;
+constexpr int kParts = 3;           // bf16 parts of each hidden value
+constexpr int kMaxCwPerThread = 4 * kMmMaxK / kMmThreads;   // codewords of a half-block per thread
+
+struct MmArgs {
+  const uint16_t* cb;     // bf16 codebooks [NP][K][d]
+  const uint16_t* codes;  // RQ_CODES_BLOCKED
+  const u32x4* hp;        // [kParts][M][Bp] 8-bf16 vectors (zero past d and past B)
+  float* partial;         // [G][B][rows]
+  int64_t rows;
+  int K, M, NP, NQ, B, Bp, G, qpg, S;
+};
+
+// hp[part][m][n] = part `part` of h[n][m*d .. m*d+d), padded to 8 with zeros.
+__global__ void split_h_kernel(const float* __restrict__ h, int B, int D, int M, int d, int Bp,
+                               u32x4* __restrict__ hp) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= M * Bp) return;
+  const int m = t / Bp;
+  const int n = t - m * Bp;
+  uint32_t w[kParts][4];
+#pragma unroll
+  for (int pr = 0; pr < kParts; ++pr)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[pr][q] = 0u;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float x = (n < B && j < d) ? h[(size_t)n * D + (size_t)m * d + j] : 0.0f;
+#pragma unroll
+    for (int pr = 0; pr < kParts; ++pr) {
+      const uint16_t b = f32_to_bf16(x);
+      x -= bf16_to_f32(b);   // exact: the rounding error of an fp32 -> bf16 RNE fits fp32
+      w[pr][j >> 1] |= (uint32_t)b << (16 * (j & 1));
+    }
+  }
+#pragma unroll
+  for (int pr = 0; pr < kParts; ++pr) {
+    u32x4 v = {w[pr][0], w[pr][1], w[pr][2], w[pr][3]};
+    hp[((size_t)pr * M + m) * Bp + n] = v;
+  }
+}
+
+template <int DS, int NT>
+struct Staged {
+  static constexpr int kH = (kParts * 4 * 16 * NT + kMmThreads - 1) / kMmThreads;   // h vectors per thread
+  uint32_t cw[kMaxCwPerThread][DS / 2];
+  u32x4 hv[kH];
+};
+
+template <int DS, int NT, int T>
+__global__ __launch_bounds__(kMmThreads) void mm_logits_kernel(MmArgs a) {
+  extern __shared__ __align__(16) u32x4 ring[];   // [2][4*K + kParts*4*16*NT]
+  const int K = a.K;
+  const int cw_entries = 4 * K;
+  const int h_entries = kParts * 4 * 16 * NT;
+  const int slot_entries = cw_entries + h_entries;
+
+  // workgroup -> (batch tile, group, slab). Workgroups are dealt to the 8 XCDs
+  // round robin (dispatch index mod 8); with g = index mod G and G dividing 8,
+  // every workgroup of an XCD works on the same group(s) of code blocks, so
+  // their codebooks stay in that XCD's L2.
+  const int per_bt = a.G * a.S;
+  const int bt = blockIdx.x / per_bt;
+  const int li = blockIdx.x - bt * per_bt;
+  const int g = li % a.G;
+  const int s = li / a.G;
+  const int q0 = g * a.qpg;
+  const int q1 = min(a.NQ, q0 + a.qpg);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int i16 = lane & 15;
+  const int kg = lane >> 4;
+  const int64_t tile0 = (int64_t)s * (kMmWaves * T * 16) + (int64_t)wave * (T * 16);
+
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc((void*)a.codes, (short)0, (int)0xffffffffu,
+                                                                        0x00020000);
+  const uint32_t blk_bytes = (uint32_t)a.rows * 16u;
+  uint32_t voff[T];
+#pragma unroll
+  for (int j = 0; j < T; ++j) {
+    const int64_t r = min(tile0 + 16 * j + i16, a.rows - 1);
+    voff[j] = (uint32_t)r * 16u + (uint32_t)kg * 4u;
+  }
+  auto load_codes = [&](uint32_t (&dst)[T], int q) {
+#pragma unroll
+    for (int j = 0; j < T; ++j) dst[j] = __builtin_amdgcn_raw_buffer_load_b32(crs, voff[j], (uint32_t)q * blk_bytes, 0);
+  };
+
+  // ---- staging of one half-block into registers, then into a ring slot
+  const int n_bt = 16 * NT;
+  // Thread tid stages codeword entries (tid + u*kMmThreads) mod cw_entries and
+  // h entries (tid + u*kMmThreads) mod h_entries: indices wrap instead of being
+  // guarded, so some entries are written twice with the same value and no
+  // branch (whose join would make the compiler wait for every load in flight)
+  // is needed.
+  auto stage_load = [&](Staged<DS, NT>& st, int q, int hs) {
+#pragma unroll
+    for (int u = 0; u < kMaxCwPerThread; ++u) {
+      const int c = (tid + u * kMmThreads) % cw_entries;
+      const int kk = c / K;
+      const int k = c - kk * K;
+      const int p = min(8 * q + 2 * kk + hs, a.NP - 1);
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(a.cb + ((size_t)p * K + k) * DS);
+#pragma unroll
+      for (int w = 0; w < DS / 2; ++w) st.cw[u][w] = src[w];
+    }
+#pragma unroll
+    for (int u = 0; u < Staged<DS, NT>::kH; ++u) {
+      const int e = (tid + u * kMmThreads) % h_entries;
+      const int pr = e / (4 * n_bt);
+      const int rem = e - pr * 4 * n_bt;
+      const int kk = rem / n_bt;
+      const int n = rem - kk * n_bt;
+      const int p = min(8 * q + 2 * kk + hs, a.NP - 1);
+      const int m = p % a.M;
+      st.hv[u] = a.hp[((size_t)pr * a.M + m) * a.Bp + (size_t)bt * n_bt + n];
+    }
+  };
+  auto stage_store = [&](const Staged<DS, NT>& st, int slot, int q, int hs) {
+    u32x4* base = ring + slot * slot_entries;
+#pragma unroll
+    for (int u = 0; u < kMaxCwPerThread; ++u) {
+      const int c = (tid + u * kMmThreads) % cw_entries;
+      const bool live = 8 * q + 2 * (c / K) + hs < a.NP;
+      u32x4 v = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int w = 0; w < DS / 2; ++w) v[w] = live ? st.cw[u][w] : 0u;
+      base[c] = v;
+    }
+#pragma unroll
+    for (int u = 0; u < Staged<DS, NT>::kH; ++u) {
+      const int e = (tid + u * kMmThreads) % h_entries;
+      const int pr = e / (4 * n_bt);
+      const int kk = (e - pr * 4 * n_bt) / n_bt;
+      const bool live = 8 * q + 2 * kk + hs < a.NP;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      base[cw_entries + e] = live ? st.hv[u] : z;
+    }
+  };
+
+  floatx4 acc[T][NT];
+#pragma unroll
+  for (int j = 0; j < T; ++j)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[j][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int slot, const uint32_t (&codes)[T], int hs) {
+    const u32x4* base = ring + slot * slot_entries;
+    bf16x8 hb[kParts][NT];
+#pragma unroll
+    for (int pr = 0; pr < kParts; ++pr)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        hb[pr][t] = __builtin_bit_cast(bf16x8, base[cw_entries + (pr * 4 + kg) * n_bt + 16 * t + i16]);
+    const u32x4* cwb = base + kg * K;
+    // Software pipeline: the codewords of the next kI tiles are read from LDS
+    // while the matrix cores work on the current kI tiles.
+    constexpr int kI = 4;
+    constexpr int kGroups = (T + kI - 1) / kI;
+    bf16x8 av[2][kI];
+#pragma unroll
+    for (int u = 0; u < kI; ++u)
+      av[0][u] = __builtin_bit_cast(bf16x8, cwb[(codes[min(u, T - 1)] >> (16 * hs)) & 0xffffu]);
+#pragma unroll
+    for (int gi = 0; gi < kGroups; ++gi) {
+      const int cur = gi & 1;
+      if (gi + 1 < kGroups) {
+#pragma unroll
+        for (int u = 0; u < kI; ++u) {
+          const int j = min((gi + 1) * kI + u, T - 1);
+          av[cur ^ 1][u] = __builtin_bit_cast(bf16x8, cwb[(codes[j] >> (16 * hs)) & 0xffffu]);
+        }
+      }
+#pragma unroll
+      for (int pr = 0; pr < kParts; ++pr)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int u = 0; u < kI; ++u) {
+            const int j = gi * kI + u;
+            if (j < T) acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[cur][u], hb[pr][t], acc[j][t], 0, 0, 0);
+          }
+    }
+  };
+
+  if (q0 < q1) {
+    uint32_t ca[T], cbk[T];
+    Staged<DS, NT> st;
+    load_codes(ca, q0);
+    stage_load(st, q0, 0);
+    int slot = 0;
+    for (int q = q0; q < q1; q += 2) {
+      // block q (codes in ca), prefetching block q+1's codes into cbk
+      stage_store(st, slot, q, 0);
+      __syncthreads();
+      stage_load(st, q, 1);
+      __builtin_amdgcn_sched_barrier(0);   // keep the staging loads ahead of the code loads (vmcnt is in order)
+      load_codes(cbk, min(q + 1, q1 - 1));
+      compute(slot, ca, 0);
+      slot ^= 1;
+      stage_store(st, slot, q, 1);
+      __syncthreads();
+      stage_load(st, min(q + 1, q1 - 1), 0);
+      compute(slot, ca, 1);
+      slot ^= 1;
+      if (q + 1 < q1) {
+        // block q+1 (codes in cbk), prefetching block q+2's codes into ca
+        stage_store(st, slot, q + 1, 0);
+        __syncthreads();
+        stage_load(st, q + 1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_codes(ca, min(q + 2, q1 - 1));
+        compute(slot, cbk, 0);
+        slot ^= 1;
+        stage_store(st, slot, q + 1, 1);
+        __syncthreads();
+        stage_load(st, min(q + 2, q1 - 1), 0);
+        compute(slot, cbk, 1);
+        slot ^= 1;
+      }
+    }
+  }
+
+  // acc[j][t][e] = z[batch bt*16NT + 16t + i16][row tile0 + 16j + 4kg + e]
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int b = bt * n_bt + 16 * t + i16;
+    if (b >= a.B) continue;
+    float* dst = a.partial + ((size_t)g * a.B + b) * a.rows;
+#pragma unroll
+    for (int j = 0; j < T; ++j) {
+      const int64_t r = tile0 + 16 * j + 4 * kg;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (r + e < a.rows) dst[r + e] = acc[j][t][e];
+    }
+  }
+}
+
+// Row tiles per wave for NT column tiles: the accumulators (4*T*NT VGPRs), the
+// code registers (2*T) and the staged half-block share a wave's 256 VGPRs.
+constexpr int tiles_for(int NT) {
+  return kMmThreads == 512 ? (NT == 1 ? 16 : NT == 2 ? 8 : 3) : (NT == 1 ? 8 : NT == 2 ? 4 : 2);
+}
+
+template <int DS, int NT>
+hipError_t launch_typed(const MmArgs& a, int wgs, size_t lds, hipStream_t stream) {
+  auto kern = mm_logits_kernel<DS, NT, tiles_for(NT)>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(kMmThreads), lds, stream, a);
+  return hipGetLastError();
+}
+
+template <int DS>
+hipError_t launch_ds(const MmArgs& a, const MmPlan& p, hipStream_t stream) {
+  const int wgs = p.G * p.S * p.NBT;
+  if (p.NT == 1) return launch_typed<DS, 1>(a, wgs, p.lds, stream);
+  if (p.NT == 2) return launch_typed<DS, 2>(a, wgs, p.lds, stream);
+  return launch_typed<DS, 4>(a, wgs, p.lds, stream);
+}
+
+#ifdef RQ_TUNING
+// Tuning builds only: RQ_MM_PLAN="G" replaces the planner's group count.
+void mm_tuning_override(MmPlan& p) {
+  const char* s = getenv("RQ_MM_PLAN");
+  int G;
+  if (s && sscanf(s, "%d", &G) == 1 && G >= 1) p.G = G;
+}
+#endif
+
+}  // namespace
+
+bool mm_supported(const rq_matrix* W) {
+  return W->cb_dtype == RQ_BF16 && W->codes_layout == RQ_CODES_BLOCKED && W->d <= 8 && (W->d % 2) == 0 &&
+         W->K <= kMmMaxK && ((uintptr_t)W->codebooks % 4) == 0;
+}
+
+MmPlan plan_mm(const rq_matrix* W, int B) {
+  MmPlan p{};
+  p.NT = B <= 16 ? 1 : (B <= 32 ? 2 : 4);
+  p.T = tiles_for(p.NT);
+  p.NBT = (B + 16 * p.NT - 1) / (16 * p.NT);
+  p.Bp = p.NBT * 16 * p.NT;
+  const int64_t slab = (int64_t)kMmWaves * p.T * 16;
+  p.S = (int)((W->rows + slab - 1) / slab);
+  p.NQ = (W->L * W->M + 7) / 8;
+  // Group count: workgroups run in rounds of one per CU; a round costs the
+  // blocks one workgroup handles (about 5.5 us per block for 16 waves' worth of
+  // 16x16 tiles, measured at the Gemma head), and every group beyond the first
+  // adds B*rows fp32 partial sums written and read back (at ~5 TB/s).
+  int G = 1;
+  double best = 1e30;
+  for (int g = 1; g <= std::min(p.NQ, 64); g *= 2) {   // powers of two: g = index mod G keeps XCDs on their groups
+    const int qpg = (p.NQ + g - 1) / g;
+    const int gg = (p.NQ + qpg - 1) / qpg;
+    const int64_t wgs = (int64_t)gg * p.S * p.NBT;
+    const double rounds = (double)((wgs + kCUs - 1) / kCUs);
+    const double per_block = 5.5 * (double)(p.T * p.NT) / 16.0;
+    const double cost = rounds * qpg * per_block + (gg > 1 ? (double)gg * B * W->rows * 8.0 / 5.0e6 : 0.0);
+    if (cost < best * 0.999) { best = cost; G = gg; }
+  }
+#ifdef RQ_TUNING
+  p.G = G;
+  mm_tuning_override(p);
+  G = std::max(1, std::min(p.G, p.NQ));
+#endif
+  p.qpg = (p.NQ + G - 1) / G;
+  p.G = (p.NQ + p.qpg - 1) / p.qpg;
+  p.lds = (size_t)2 * (4 * (size_t)W->K + (size_t)kParts * 4 * 16 * p.NT) * 16;
+  return p;
+}
+
+size_t mm_hp_bytes(const rq_matrix* W, const MmPlan& p) { return (size_t)kParts * W->M * p.Bp * 16; }
+
+hipError_t launch_mm_logits(const rq_matrix* W, const MmPlan& p, const float* h, int B, void* hp, float* partial,
+                            hipStream_t stream) {
+  const int n = W->M * p.Bp;
+  hipLaunchKernelGGL(split_h_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, h, B, W->D, W->M, W->d,
+                     p.Bp, static_cast<u32x4*>(hp));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  MmArgs a;
+  a.cb = static_cast<const uint16_t*>(W->codebooks);
+  a.codes = W->codes;
+  a.hp = static_cast<const u32x4*>(hp);
+  a.partial = partial;
+  a.rows = W->rows;
+  a.K = W->K;
+  a.M = W->M;
+  a.NP = W->L * W->M;
+  a.NQ = p.NQ;
+  a.B = B;
+  a.Bp = p.Bp;
+  a.G = p.G;
+  a.qpg = p.qpg;
+  a.S = p.S;
+  hipEvent_t before, after;
+  take_stage_events(&before, &after);
+  if (before && (e = hipEventRecord(before, stream)) != hipSuccess) return e;
+  switch (W->d) {
+    case 2: e = launch_ds<2>(a, p, stream); break;
+    case 4: e = launch_ds<4>(a, p, stream); break;
+    case 6: e = launch_ds<6>(a, p, stream); break;
+    default: e = launch_ds<8>(a, p, stream); break;
+  }
+  if (e != hipSuccess) return e;
+  if (after) e = hipEventRecord(after, stream);
+  return e;
+}
+
+}  // namespace rq

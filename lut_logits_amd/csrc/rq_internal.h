@@ -5,6 +5,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -73,7 +75,11 @@ struct GatherPlan {
   size_t lds;    // dynamic LDS bytes per workgroup
   int64_t wgs() const { return (int64_t)G * S * NBT; }
 };
-GatherPlan plan_gather(const rq_matrix* W, int B, int lut_bf16);
+// fused != 0: the table is built while staging (fused_build_supported).
+GatherPlan plan_gather(const rq_matrix* W, int B, int lut_bf16, int fused = 0);
+// Whether the lookup+sum can build the table itself while staging: one
+// activation vector, fp32 codebooks with d in {1, 2, 4}, 16-byte aligned.
+bool fused_build_supported(const rq_matrix* W, int B);
 
 // Launchers: return hipSuccess or the launch error. All enqueue on `stream`.
 hipError_t launch_build_lut(const rq_matrix* W, const float* x, const float* x2, int prologue, int B,
@@ -90,14 +96,45 @@ struct GatherOut {
 // One-shot events around the next lookup+sum launch of this thread (rq_set_stage_events).
 void take_stage_events(hipEvent_t* before, hipEvent_t* after);
 
+// fused_act != null: build the table while staging from W's codebooks and the
+// activation vector fused_act [D], or gelu_tanh(fused_act) * fused_x2 when
+// fused_x2 != null (plan from plan_gather(W, 1, 0, 1)); lut is ignored.
 hipError_t launch_gather(const rq_matrix* W, const GatherPlan& plan, const void* lut, int lut_bf16, int B,
-                         const GatherOut& o, hipStream_t stream);
+                         const GatherOut& o, hipStream_t stream, const float* fused_act = nullptr,
+                         const float* fused_x2 = nullptr);
 int key_blocks(const GatherPlan& plan, int64_t rows);
 // argmax from the per-block keys (argmax may be null) and, with topk > 0, the
 // top-k of the logits (cand: [B][epi_blocks(rows)][topk] scratch).
 hipError_t launch_select(const uint64_t* block_keys, int nkb, int B, int32_t* argmax, const float* logits,
                          int64_t rows, int topk, uint64_t* cand, int32_t* topk_ids, float* topk_vals,
                          hipStream_t stream);
+// The finish pass alone: adds G partial sums [G][B][rows] in a fixed order,
+// applies the softcap, writes out [B][rows] and one selection key per block of
+// rows (block_keys [B][finish_key_blocks(G, rows)], or null).
+int finish_key_blocks(int G, int64_t rows);
+hipError_t launch_finish(const float* partial, int G, int B, int64_t rows, float softcap, float* out,
+                         uint64_t* block_keys, hipStream_t stream);
+
+// Batched head on the matrix cores (bf16 codebooks staged in LDS, hidden
+// vectors split into three bf16 parts): partial sums [G][B][rows].
+constexpr int kMmMaxK = 1024;
+struct MmPlan {
+  int NT;      // 16-column MFMA tiles per batch tile
+  int T;       // 16-row tiles per wave
+  int NBT;     // batch tiles
+  int Bp;      // padded batch (NBT * 16 * NT)
+  int S;       // row slabs
+  int NQ;      // code blocks of 8 (level, subspace) pairs
+  int G;       // groups of code blocks (partial sums per output)
+  int qpg;     // code blocks per group
+  size_t lds;  // dynamic LDS bytes per workgroup
+};
+bool mm_supported(const rq_matrix* W);
+MmPlan plan_mm(const rq_matrix* W, int B);
+size_t mm_hp_bytes(const rq_matrix* W, const MmPlan& p);
+hipError_t launch_mm_logits(const rq_matrix* W, const MmPlan& p, const float* h, int B, void* hp, float* partial,
+                            hipStream_t stream);
+
 hipError_t launch_decode_rows(const rq_matrix* W, const int32_t* ids, int n, int out_bf16, void* out,
                               int32_t* bad_ids, hipStream_t stream);
 hipError_t launch_pack_codes(const uint16_t* src, int64_t rows, int NP, uint16_t* dst, hipStream_t stream);

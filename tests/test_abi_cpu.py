@@ -98,7 +98,9 @@ def test_workspace_queries():
     assert lib.rq_blocked_codes_bytes(10, 1, 5) == 1 * 10 * 16
     assert lib.rq_blocked_codes_bytes(10, 3, 3) == 2 * 10 * 16
     Wm = gemma_desc(rows=9216, D=2304, M=1152, d=2, cb_dtype=B.RQ_F32)
-    assert lib.rq_lut_matvec_workspace(ctypes.byref(Wm), 1) >= 2 * 1152 * 1024 * 4
+    # one vector with fp32 codebooks builds its table while staging: no table in the workspace
+    assert 0 < lib.rq_lut_matvec_workspace(ctypes.byref(Wm), 1) < 2 * 1152 * 1024 * 4
+    assert lib.rq_lut_matvec_workspace(ctypes.byref(Wm), 2) >= 2 * 1152 * 1024 * 4 * 2
     assert lib.rq_dense_logits_workspace(256000, 1) > 0
     assert lib.rq_dense_logits_workspace(256000, 17) == 0
 
@@ -123,3 +125,37 @@ def test_other_entry_points_reject():
     assert lib.rq_dense_logits(0x1000, 100, 2300, 0x2000, 1, 30.0, 0x3000, None, None, 0, None) == B.RQ_ERR_SHAPE
     assert lib.rq_dense_logits(0x1000, 100, 2304, 0x2000, 17, 30.0, 0x3000, None, None, 0, None) == B.RQ_ERR_SHAPE
     assert lib.rq_dense_logits(0x1000, 100, 2304, 0x2000, 1, 30.0, 0x3000, 0x4000, None, 0, None) == B.RQ_ERR_WORKSPACE
+
+
+def test_logits_method_and_checks():
+    """rq_logits routes B >= RQ_MM_MIN_B with bf16 codebooks, even d <= 8, K <= 1024 and blocked codes to the
+    matrix cores, everything else to the table path; its host checks run before any launch."""
+    lib = B.lib()
+    W = gemma_desc()
+    m = lambda w, b: lib.rq_logits_method(ctypes.byref(w), b)
+    assert m(W, 1) == B.RQ_METHOD_TABLE
+    assert m(W, 7) == B.RQ_METHOD_TABLE
+    assert m(W, 8) == B.RQ_METHOD_MATRIX_CORES
+    assert m(W, 128) == B.RQ_METHOD_MATRIX_CORES
+    assert m(gemma_desc(cb_dtype=B.RQ_F32), 16) == B.RQ_METHOD_TABLE           # fp32 codebooks
+    assert m(gemma_desc(K=4096, L=4), 64) == B.RQ_METHOD_TABLE                 # K above the staged maximum
+    assert m(gemma_desc(codes_layout=B.RQ_CODES_ROWS), 16) == B.RQ_METHOD_TABLE
+    assert m(gemma_desc(M=256, d=9), 16) == B.RQ_METHOD_TABLE                  # d > 8
+    assert m(gemma_desc(M=768, d=3), 16) == B.RQ_METHOD_TABLE                  # odd d
+    assert m(gemma_desc(M=1152, d=2), 16) == B.RQ_METHOD_MATRIX_CORES
+    assert m(gemma_desc(D=2305), 16) == B.RQ_ERR_SHAPE
+    ws16 = lib.rq_logits_workspace(ctypes.byref(W), 16, 0)
+    assert ws16 > 0 and ws16 % 256 == 0
+    assert lib.rq_logits_workspace(ctypes.byref(W), 16, 50) > ws16
+    assert lib.rq_logits_workspace(ctypes.byref(W), 1, 0) >= 2 * 384 * 1024 * 4   # holds the fp32 table
+    call = lambda **kw: lib.rq_logits(ctypes.byref(kw.pop("W", W)), kw.pop("h", 0x1000), kw.pop("Bn", 16), 30.0,
+                                      0x60000, 0x70000, kw.pop("topk", 0), kw.pop("ids", 0x50000), None,
+                                      kw.pop("ws", 0x40000), kw.pop("ws_bytes", 1 << 40), None)
+    assert call(h=0) == B.RQ_ERR_NULL
+    assert call(h=0x1002) == B.RQ_ERR_ALIGN
+    assert call(ws=0) == B.RQ_ERR_WORKSPACE
+    assert call(ws_bytes=ws16 - 1) == B.RQ_ERR_WORKSPACE
+    assert call(ws=0x40040) == B.RQ_ERR_ALIGN
+    assert call(topk=3, ids=0) == B.RQ_ERR_NULL
+    assert call(Bn=-2) == B.RQ_ERR_SHAPE
+    assert call(Bn=0, h=0, ws=0, ws_bytes=0) == B.RQ_OK

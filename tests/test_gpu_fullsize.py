@@ -46,6 +46,20 @@ def test_gemma_head_batched_full(name):
     print(f"{name}: worst |gpu-oracle|/max|oracle| = {worst:.2e}")
 
 
+@pytest.mark.parametrize("name", ["gemma_b16", "gemma_b128"])
+def test_gemma_head_one_call_full(name):
+    """rq_logits on the full head at B=16 and B=128 (the matrix-core method): every logit and argmax."""
+    cfg = synth.CONFIGS[name]
+    mat, h, _ = synth.make_head(cfg)
+    W = to_dev(mat)
+    assert la.logits_method(W, cfg.B) == la.RQ_METHOD_MATRIX_CORES
+    lg, am, _, _ = la.logits(W, dev(h), softcap=cfg.softcap)
+    _, ref = oracle_head(mat, h, cfg.softcap)
+    worst = check_logits(host(lg), ref)
+    check_argmax(host(am), host(lg), ref)
+    print(f"{name} one call: worst |gpu-oracle|/max|oracle| = {worst:.2e}")
+
+
 def test_stress_head_full():
     """Stress head: K=4096, L=4, B=64, bf16 table, softcap 30 and per-vector top-50."""
     cfg = synth.CONFIGS["stress"]

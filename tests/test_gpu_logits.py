@@ -1,0 +1,120 @@
+"""rq_logits, the one-call head, on both of its methods (needs an MI355X).
+
+The matrix-core method stages bf16 codebooks on chip and contracts them with the hidden vectors split
+into three bf16 parts; the table method builds the fp32 table and runs the lookup+sum. Both are compared
+with the CPU oracle through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import lut_logits_amd as la
+import oracle
+from lut_logits_amd import synth
+from gpu_util import check_argmax, check_logits, check_topk, dev, host, oracle_head, to_dev
+
+pytestmark = pytest.mark.gpu
+
+O = oracle.default
+
+MM_EXACT = [
+    # rows, D, M, K, L, B
+    (4097, 96, 16, 256, 2, 16),     # d=6, one column tile, ragged rows
+    (2049, 96, 16, 1024, 2, 8),     # the smallest batch routed to the matrix cores, K at its maximum
+    (3000, 102, 17, 1000, 2, 33),   # odd M: the last code block is partly empty; K not a power of two; 33 of 64 columns
+    (1500, 96, 48, 64, 2, 20),      # d=2
+    (1200, 96, 24, 128, 3, 64),     # d=4, L=3, four column tiles
+    (700, 64, 8, 256, 1, 100),      # d=8, one code block, two batch tiles (64 + 36)
+    (1, 6, 1, 1, 1, 16),            # one row, one codeword, one pair
+]
+
+
+@pytest.mark.parametrize("shape", MM_EXACT, ids=lambda s: "x".join(map(str, s)))
+def test_logits_matrix_cores_exact(shape):
+    """Small-integer inputs: every product and sum is exact in fp32, so z matches the oracle bit for bit."""
+    rows, D, M, K, L, B = shape
+    mat, h = synth.gen_exact(rows + 7 * K, rows, D, M, K, L, B, cb_dtype="bf16")
+    W = to_dev(mat)
+    assert la.logits_method(W, B) == la.RQ_METHOD_MATRIX_CORES
+    lg, am, _, _ = la.logits(W, dev(h), softcap=0.0)
+    z, _ = O().logits(mat.codes, mat.codebooks, True, h, 0.0)
+    got = host(lg)
+    assert np.array_equal(got.astype(np.float64), z)
+    assert np.array_equal(host(am), np.argmax(got, axis=1).astype(np.int32))
+
+
+def test_logits_split_reaches_fp32():
+    """One subspace of d=6, L=1: z is a 6-term dot product. Splitting h into three bf16 parts keeps it to
+    fp32 rounding (|err| <= 2^-20 |z|-scale); two parts would leave ~2^-16 and fail this bound."""
+    rng = np.random.default_rng(7)
+    mat = synth.gen_matrix(rng, 64, 6, 1, 16, 1, (1.0,), "bf16")
+    h = synth.gen_hidden(rng, 16, 6)
+    W = to_dev(mat)
+    assert la.logits_method(W, 16) == la.RQ_METHOD_MATRIX_CORES
+    lg, _, _, _ = la.logits(W, dev(h), softcap=0.0)
+    z, _ = O().logits(mat.codes, mat.codebooks, True, h, 0.0)
+    c = synth.bf16_bits_to_f32(mat.codebooks).astype(np.float64)[0, 0]          # [K][6]
+    scale = np.abs(h.astype(np.float64)) @ np.abs(c[mat.codes[:, 0, 0]]).T     # sum_j |h_j c_j|
+    assert np.all(np.abs(host(lg) - z) <= 2.0 ** -20 * scale)
+
+
+@pytest.mark.parametrize("B", [3, 8, 16, 24, 48, 128])
+def test_logits_float_parity(B):
+    """Gaussian inputs at the Gemma subspace shape (d=6, K=1024, L=2, bf16 codebooks), softcap 30, argmax."""
+    rng = np.random.default_rng(300 + B)
+    mat = synth.gen_matrix(rng, 5000, 96, 16, 1024, 2, (0.02, 0.005), "bf16")
+    h = synth.gen_hidden(rng, B, 96)
+    W = to_dev(mat)
+    want = la.RQ_METHOD_MATRIX_CORES if B >= 8 else la.RQ_METHOD_TABLE
+    assert la.logits_method(W, B) == want
+    lg, am, _, _ = la.logits(W, dev(h), softcap=30.0)
+    _, ref = oracle_head(mat, h, 30.0)
+    check_logits(host(lg), ref)
+    check_argmax(host(am), host(lg), ref)
+
+
+def test_logits_topk_and_outputs():
+    """Top-k on the matrix-core method; argmax alone without a logits output; canaries past [B][rows];
+    repeated calls give identical bits."""
+    rng = np.random.default_rng(400)
+    mat = synth.gen_matrix(rng, 3001, 96, 16, 512, 2, (0.02, 0.005), "bf16")
+    h = synth.gen_hidden(rng, 20, 96)
+    W, hd = to_dev(mat), dev(h)
+    buf = torch.full((20 * 3001 + 64,), float("nan"), device="cuda")
+    lg, am, ti, tv = la.logits(W, hd, softcap=30.0, topk=10, out=buf[:20 * 3001].view(20, 3001))
+    assert np.all(np.isnan(host(buf[20 * 3001:])))
+    g = host(lg)
+    _, ref = oracle_head(mat, h, 30.0)
+    check_logits(g, ref)
+    tol = 1e-5 * np.abs(ref).max(axis=1, keepdims=True) * np.ones_like(ref)
+    check_topk(g, host(ti), host(tv), host(am), ref, tol, 10)
+    lg2, am2, _, _ = la.logits(W, hd, softcap=30.0)
+    _, am3, _, _ = la.logits(W, hd, softcap=30.0, logits=False)
+    assert torch.equal(lg, lg2) and torch.equal(am, am2) and torch.equal(am, am3)
+
+
+def test_logits_table_method_matches_two_call_form():
+    """Below the matrix-core batch (and for fp32 codebooks) rq_logits is rq_build_lut + rq_lut_logits."""
+    rng = np.random.default_rng(500)
+    for cb in ("f32", "bf16"):
+        mat = synth.gen_matrix(rng, 4000, 96, 16, 256, 2, (0.02, 0.005), cb)
+        h = synth.gen_hidden(rng, 16 if cb == "f32" else 2, 96)
+        W, hd = to_dev(mat), dev(h)
+        assert la.logits_method(W, h.shape[0]) == la.RQ_METHOD_TABLE
+        lg, am, _, _ = la.logits(W, hd, softcap=30.0)
+        lg2, am2, _, _ = la.lut_logits(W, la.build_lut(W, hd), h.shape[0], softcap=30.0)
+        assert torch.equal(lg, lg2) and torch.equal(am, am2)
+
+
+def test_logits_ties_and_empty():
+    """K = 1: every logit ties and the argmax is row 0 on the matrix cores too; B = 0 is a no-op."""
+    rng = np.random.default_rng(600)
+    mat = synth.gen_matrix(rng, 5000, 96, 16, 1, 2, (0.02, 0.005), "bf16")
+    W = to_dev(mat)
+    h = synth.gen_hidden(rng, 16, 96)
+    lg, am, ti, _ = la.logits(W, dev(h), softcap=30.0, topk=5)
+    g = host(lg)
+    assert np.all(g == g[:, :1])
+    assert np.all(host(am) == 0)
+    assert np.array_equal(host(ti), np.tile(np.arange(5, dtype=np.int32), (16, 1)))
+    lg0, _, _, _ = la.logits(W, torch.zeros((0, 96), device="cuda"), argmax=False)
+    assert lg0.shape == (0, 5000)

@@ -254,6 +254,35 @@ def test_lut_matvec_small_chain():
     check_logits(host(y), oy)
 
 
+@pytest.mark.parametrize("d", [1, 2, 4])
+@pytest.mark.parametrize("layout", ["rows", "blocked"])
+def test_lut_matvec_fused_build_exact(d, layout):
+    """One activation vector with fp32 codebooks: the table is built while staging. Exact inputs, ragged rows
+    and (blocked layout) a partly empty last code block: bit-exact against the oracle."""
+    D = 120
+    M = D // d
+    if layout == "rows" and (2 * M) % 8:
+        pytest.skip("row-major codes need L*M % 8 == 0")
+    mat, x = synth.gen_exact(40 + d, 3001, D, M, 256, 2, 1)
+    W = to_dev(mat, layout)
+    y = la.lut_matvec(W, dev(x))
+    assert np.array_equal(host(y).astype(np.float64), O().matvec(mat.codes, mat.codebooks, False, x))
+
+
+def test_lut_matvec_fused_build_gelu_and_fallback():
+    """The GELU*up prologue feeding the fused build, and a row width whose activation vector does not fit
+    beside a table chunk in LDS (the separate table build is used instead)."""
+    rng = np.random.default_rng(120)
+    for rows, D, M, K in ((2500, 128, 64, 256), (300, 40000, 20000, 16)):
+        mat = synth.gen_matrix(rng, rows, D, M, K, 2, (0.02, 0.005), "f32")
+        g = synth.gen_hidden(rng, 1, D)
+        u = synth.gen_hidden(rng, 1, D)
+        W = to_dev(mat)
+        y = la.lut_matvec(W, dev(g), x2=dev(u), prologue=la.RQ_PRO_GELU_TANH_MUL)
+        a = O().gelu_mul(g.astype(np.float64), u.astype(np.float64))
+        check_logits(host(y), O().matvec(mat.codes, mat.codebooks, False, a))
+
+
 def test_mlp_layer_gemma_shapes():
     """One Gemma-2-2B MLP layer: gate/up 9216x2304 (d=2), down 2304x9216 (d=2), K=1024, L=2, fp32 codebooks."""
     gate, up, down = synth.make_mlp_layer(0)
