@@ -208,10 +208,16 @@ def extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, dev):
             la.logits(Ws[i & 1], hB, softcap=30.0, out=lgB, argmax_out=amB, ws=wsB)
 
         tB = timed(headB, 20, torch)
+        mm = la.logits_method(Ws[0], B) == la.RQ_METHOD_MATRIX_CORES
+        # matrix-core work: per 16 rows x 16 vectors x 4 subspaces (k = 32 with d = 6 padded to 8), one
+        # 16x16x32 bf16 MFMA per level and per bf16 part of h (3): dense-equivalent flops at 2.5 PFLOP/s
+        n_mfma = (V // 16) * ((B + 15) // 16) * (cfg.L * cfg.M // 4) * 3
+        mfma_tflops = n_mfma * 16 * 16 * 32 * 2 / (tB * 1e-3) / 1e12
         res[f"b{B}"] = {"ms_per_call": tB, "vocab_rows_per_s": V / (tB * 1e-3), "token_rows_per_s": B * V / (tB * 1e-3),
-                        "method": "matrix_cores" if la.logits_method(Ws[0], B) == la.RQ_METHOD_MATRIX_CORES
-                        else "table",
-                        "code_stream_gbs": formats.code_bytes(V, cfg.L, cfg.M) / (tB * 1e-3) / 1e9}
+                        "method": "matrix_cores" if mm else "table",
+                        "code_stream_gbs": formats.code_bytes(V, cfg.L, cfg.M) / (tB * 1e-3) / 1e9,
+                        "mfma_tflops": mfma_tflops if mm else None,
+                        "mfma_frac_of_bf16_peak": mfma_tflops / 2500.0 if mm else None}
         del lgB, amB, wsB
     # the two-call table form at B=16, for comparison
     h16 = hb[:16].contiguous()
@@ -258,9 +264,31 @@ def extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, dev):
     tm = timed(mlp, 20, torch)
     code_b = sum(formats.code_bytes(m.rows, m.L, m.M) for m in layers[0])
     cb_b = sum(m.codebooks.nbytes for m in layers[0])
+    gbs = (code_b + cb_b) / (tm * 1e-3) / 1e9
     res["mlp_layer"] = {"ms": tm, "code_bytes": code_b, "codebook_bytes": cb_b,
-                        "gbs_codes_plus_codebooks": (code_b + cb_b) / (tm * 1e-3) / 1e9,
+                        "gbs_codes_plus_codebooks": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
                         "ms_26_layers_est": 26 * tm}
+    del dl, wsm, g, u, y
+    torch.cuda.empty_cache()
+
+    # stress head: K=4096, L=4, B=64, bf16 table, softcap 30, top-50 (one call pair: build + logits)
+    cs = synth.CONFIGS["stress"]
+    smat, sh, _ = synth.make_head(cs)
+    SW = la.to_device(smat)
+    shd = torch.from_numpy(sh).to(dev)
+    slut = la.build_lut(SW, shd, lut_dtype="bf16")
+    slg = torch.empty((cs.B, cs.V), dtype=torch.float32, device=dev)
+    sws = la.workspace(la.lut_logits_workspace(SW, cs.B, cs.topk, "bf16"), dev)
+
+    def stress(i=0):
+        la.build_lut(SW, shd, lut_dtype="bf16", out=slut)
+        la.lut_logits(SW, slut, cs.B, softcap=cs.softcap, lut_dtype="bf16", topk=cs.topk, out=slg, ws=sws)
+
+    ts = timed(stress, 3, torch)
+    res["stress"] = {"ms_per_call": ts, "vocab_rows_per_s": cs.V / (ts * 1e-3),
+                     "code_stream_gbs": formats.code_bytes(cs.V, cs.L, cs.M) / (ts * 1e-3) / 1e9,
+                     "method": "table (bf16), 16-vector batch tiles"}
+    del SW, slut, slg, sws
     return res
 
 

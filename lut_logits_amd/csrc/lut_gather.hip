@@ -139,6 +139,12 @@ __device__ __forceinline__ uint32_t code_of(const uint4& w, int t) {
 // LDS at the switch -- its HBM/L2 latency is hidden behind a whole chunk.
 constexpr int kRegStage = 8;
 
+// Cache policy bits of the code-stream loads (0: default).
+#ifndef RQ_CODE_CPOL
+#define RQ_CODE_CPOL 0
+#endif
+constexpr int kCodeCachePolicy = RQ_CODE_CPOL;
+
 // Eight 16-byte words of a chunk held in registers. A native vector type keeps
 // the copies first-class values (HIP's uint4 struct is copied through memory).
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -269,7 +275,7 @@ void gather_kernel(GatherArgs a) {
     const uint32_t boff = (uint32_t)q * blk_bytes;
 #pragma unroll
     for (int st = 0; st < NSTEP; ++st) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(code_rsrc, (int)roff[st], (int)boff, 0);
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(code_rsrc, (int)roff[st], (int)boff, kCodeCachePolicy);
       dst[st] = make_uint4(v[0], v[1], v[2], v[3]);
     }
   };
