@@ -194,6 +194,30 @@ def timed(fn, n, torch):
 def extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, dev):
     res = {}
     V = cfg.V
+    # the same B=1 step on the 10-bit code stream (1024 bytes per row instead of 1536)
+    P10 = [la.to_device(mat, layout="packed10"), la.to_device(mat, layout="packed10")]
+    lut10 = la.build_lut(P10[0], ht)
+    lg10 = torch.empty((1, V), dtype=torch.float32, device=dev)
+    ws10 = la.workspace(la.lut_logits_workspace(P10[0], 1), dev)
+
+    def step10(i=0):
+        W = P10[i & 1]
+        la.build_lut(W, ht, out=lut10)
+        la.lut_logits(W, lut10, 1, softcap=cfg.softcap, out=lg10, ws=ws10)
+
+    t10 = timed(step10, 100, torch)
+    gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
+    for i in range(50):
+        la.set_stage_events(*gev[i])
+        step10(i)
+    torch.cuda.synchronize()
+    tg10 = float(np.mean([a.elapsed_time(b) for a, b in gev]))
+    cb10 = la.packed10_codes_bytes(V, cfg.L, cfg.M)
+    res["b1_packed10"] = {"ms_build_plus_logits": t10, "vocab_rows_per_s_build_plus_logits": V / (t10 * 1e-3),
+                          "gather_kernel_ms": tg10, "code_bytes": cb10,
+                          "gather_gbs": (cb10 + formats.lut_bytes(1, cfg.L, cfg.M, cfg.K)) / (tg10 * 1e-3) / 1e9}
+    del P10, lut10, lg10, ws10
+
     # batched heads, B=16 and B=128 (same matrix): rq_logits, which puts B >= 8 on the matrix cores
     # (codebooks staged on chip, no per-vector table); logits [B][V] + argmax
     c16 = synth.CONFIGS["gemma_b16"]

@@ -80,12 +80,25 @@ typedef enum rq_prologue {
  *                     row's codes for 8 consecutive pairs are 16 contiguous
  *                     bytes, and consecutive rows are adjacent. Unused slots
  *                     of the last block (NP not a multiple of 8) are 0.
- * Every entry point reads both. BLOCKED is the serving layout: a wave loads
- * 64 rows x 16 bytes as one contiguous 1 KB run, whatever chunk of pairs it
- * works on. rq_pack_codes converts ROWS to BLOCKED once, at load. With
- * RQ_CODES_ROWS, rq_lut_logits and rq_lut_matvec need NP % 8 == 0.
+ *   RQ_CODES_PACKED10 the 10-bit code stream (K <= 1024): [ceil(NP/12)][rows]
+ *                     of 16 bytes; in block q, 32-bit word w of a row holds
+ *                     the codes of pairs 12q + 3w + i at bits [10i, 10i+10),
+ *                     i < 3 (bits 30-31 and unused slots are 0). 1024 bytes
+ *                     per Gemma-head row instead of 1536, the 10-bit packing
+ *                     behind the runtime-compression page's 265 MB artifact,
+ *                     laid out so every load stays 16-byte aligned and every
+ *                     code is one bit-field extract.
+ * Every entry point reads all three. BLOCKED and PACKED10 are serving layouts:
+ * a wave loads 64 rows x 16 bytes as one contiguous 1 KB run, whatever chunk of
+ * pairs it works on. rq_pack_codes and rq_pack_codes10 convert ROWS to them
+ * once, at load. With RQ_CODES_ROWS, rq_lut_logits and rq_lut_matvec need
+ * NP % 8 == 0.
  */
-typedef enum rq_codes_layout { RQ_CODES_ROWS = 0, RQ_CODES_BLOCKED = 1 } rq_codes_layout;
+typedef enum rq_codes_layout {
+  RQ_CODES_ROWS = 0,
+  RQ_CODES_BLOCKED = 1,
+  RQ_CODES_PACKED10 = 2
+} rq_codes_layout;
 
 /*
  * Non-owning description of one RQ-coded matrix W[rows][D].
@@ -95,7 +108,7 @@ typedef enum rq_codes_layout { RQ_CODES_ROWS = 0, RQ_CODES_BLOCKED = 1 } rq_code
  *   K             codewords per codebook, 1 <= K <= 65536 (but see RQ_MAX_K_F32)
  *   L             residual levels, 1 <= L <= RQ_MAX_L
  *   cb_dtype      RQ_F32 or RQ_BF16, the storage type of the codebooks
- *   codes_layout  RQ_CODES_ROWS or RQ_CODES_BLOCKED
+ *   codes_layout  RQ_CODES_ROWS, RQ_CODES_BLOCKED or RQ_CODES_PACKED10 (K <= 1024)
  *   codebooks     device [L][M][K][d] of cb_dtype
  *   codes         device uint16 in codes_layout, 16-byte aligned
  */
@@ -118,6 +131,18 @@ size_t rq_blocked_codes_bytes(int64_t rows, int32_t L, int32_t M);
  */
 rq_status rq_pack_codes(const uint16_t* src, int64_t rows, int32_t L, int32_t M, uint16_t* dst,
                         hipStream_t stream);
+
+/* Bytes of the RQ_CODES_PACKED10 layout: ceil(L*M/12) * rows * 16. */
+size_t rq_packed10_codes_bytes(int64_t rows, int32_t L, int32_t M);
+
+/*
+ * Convert codes from RQ_CODES_ROWS (src, uint16 [rows][L*M]) to
+ * RQ_CODES_PACKED10 (dst, rq_packed10_codes_bytes bytes). Codes must be below
+ * 1024 (a precondition: the bits above the tenth are dropped). src and dst
+ * must not overlap.
+ */
+rq_status rq_pack_codes10(const uint16_t* src, int64_t rows, int32_t L, int32_t M, uint16_t* dst,
+                          hipStream_t stream);
 
 /* Largest K whose per-subspace table (K entries) fits the kernels' on-chip
  * staging: 32768 for fp32 tables, 65536 for bf16 tables. */

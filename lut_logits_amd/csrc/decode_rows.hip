@@ -1,5 +1,5 @@
 // decode_rows.hip -- on-demand reconstruction of selected rows, and the
-// one-time repacking of codes into the blocked serving layout.
+// one-time repacking of codes into the serving layouts.
 //
 // Gemma-2-2B runtime-compression page, LUT-serving paragraph: the full
 // embedding is never rebuilt; the rows of the input tokens are reconstructed
@@ -57,8 +57,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_rows_kernel(CodeView cv
 #pragma unroll
   for (int l = 0; l < kMaxL; ++l) {
     if (l >= L) break;
-    const int p = l * M + m;
-    code[l] = cv.codes[(int64_t)(p >> 3) * cv.s_blk + id * cv.s_row + (p & 7)];
+    code[l] = code_at(cv, id, l * M + m);
   }
   for (int j = 0; j < d; ++j) {
     double s = 0.0;
@@ -106,6 +105,22 @@ __global__ __launch_bounds__(256) void pack_codes_kernel(const uint16_t* __restr
   }
 }
 
+// codes[r][p] (uint16, [rows][NP]) -> RQ_CODES_PACKED10: thread (block q, row r)
+// packs codes 12q .. 12q+11 of row r, three per 32-bit word (zero past NP);
+// consecutive threads write consecutive rows' 16 bytes.
+__global__ __launch_bounds__(256) void pack_codes10_kernel(const uint16_t* __restrict__ src, int64_t rows, int NP,
+                                                           uint4* __restrict__ dst) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int q = blockIdx.y;
+  if (r >= rows) return;
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  for (int t = 0; t < 12; ++t) {
+    const int p = 12 * q + t;
+    if (p < NP) w[t / 3] |= ((uint32_t)src[r * NP + p] & 0x3ffu) << (10 * (t % 3));
+  }
+  dst[(int64_t)q * rows + r] = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 template <typename CbT, typename OutT>
 hipError_t decode_typed(const rq_matrix* W, const int32_t* ids, int n, void* out, int32_t* bad, hipStream_t stream) {
   const int64_t threads = (int64_t)n * W->M;
@@ -134,10 +149,18 @@ hipError_t launch_pack_codes(const uint16_t* src, int64_t rows, int NP, uint16_t
   return hipGetLastError();
 }
 
+hipError_t launch_pack_codes10(const uint16_t* src, int64_t rows, int NP, uint16_t* dst, hipStream_t stream) {
+  const int NQ = (NP + 11) / 12;
+  dim3 grid((unsigned)((rows + 255) / 256), (unsigned)NQ);
+  hipLaunchKernelGGL(pack_codes10_kernel, grid, dim3(256), 0, stream, src, rows, NP, reinterpret_cast<uint4*>(dst));
+  return hipGetLastError();
+}
+
 CodeView code_view(const rq_matrix* W) {
   CodeView v;
   v.codes = W->codes;
-  if (W->codes_layout == RQ_CODES_BLOCKED) {
+  v.packed10 = W->codes_layout == RQ_CODES_PACKED10;
+  if (W->codes_layout != RQ_CODES_ROWS) {
     v.s_blk = 8 * W->rows;
     v.s_row = 8;
   } else {

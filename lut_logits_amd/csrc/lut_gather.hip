@@ -128,7 +128,15 @@ __device__ __forceinline__ float lut_value<float>(const float* e) { return *e; }
 template <>
 __device__ __forceinline__ float lut_value<uint16_t>(const uint16_t* e) { return bf16_to_f32(*e); }
 
+// Code t of a row's 16-byte block: 16-bit layouts hold 8 codes (two per
+// word), RQ_CODES_PACKED10 holds 12 (three 10-bit fields per word).
+template <bool PK>
 __device__ __forceinline__ uint32_t code_of(const uint4& w, int t) {
+  if (PK) {
+    const int wi = t / 3;
+    const uint32_t word = wi == 0 ? w.x : wi == 1 ? w.y : wi == 2 ? w.z : w.w;
+    return (word >> (10 * (t - 3 * wi))) & 0x3ffu;
+  }
   const uint32_t word = (t >> 1) == 0 ? w.x : (t >> 1) == 1 ? w.y : (t >> 1) == 2 ? w.z : w.w;
   return (t & 1) ? (word >> 16) : (word & 0xffffu);
 }
@@ -212,9 +220,11 @@ __device__ __forceinline__ void regs_to_lds(const ChunkRegs& r, u32x4* dst, int 
 // waves per SIMD: the register budget is 128 VGPRs, stated explicitly so the
 // compiler does not trade registers for an occupancy the LDS cannot reach.
 // FD > 0: fused table build (see fused_word); requires LutT float, BT 1, REG.
-template <typename LutT, int BT, int NSTEP, bool REG, int FD = 0>
+// PK: codes in RQ_CODES_PACKED10 (12 pairs per 16-byte block).
+template <typename LutT, int BT, int NSTEP, bool REG, int FD = 0, bool PK = false>
 __global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(1, 4)))
 void gather_kernel(GatherArgs a) {
+  constexpr int PPB = PK ? 12 : 8;         // pairs per code block
   static_assert(FD == 0 || (BT == 1 && REG && sizeof(LutT) == 4 && 4 % FD == 0), "fused build: fp32, B=1, FD | 4");
   constexpr int QL = (BT >= 16) ? 4 : 1;   // lanes per row
   constexpr int BQ = BT / QL;              // batch entries per lane
@@ -268,7 +278,7 @@ void gather_kernel(GatherArgs a) {
   const int pa = g * a.cpg * a.P;                       // this group's pairs [pa, pb)
   const int pb = min(a.NP, (g * a.cpg + a.cpg) * a.P);
 
-  // 16 bytes = the codes of 8 consecutive pairs of one row. Two register
+  // 16 bytes = the codes of PPB consecutive pairs of one row. Two register
   // buffers alternate: while one block is looked up, the next one loads into
   // the other buffer (no register copy, so no wait on the load in flight).
   auto load_block = [&](uint4 (&dst)[NSTEP], int q) {
@@ -282,20 +292,20 @@ void gather_kernel(GatherArgs a) {
   // Lookups of the pairs of block q that lie in [lo, hi), against the chunk staged at p0.
   auto lookup_block = [&](const uint4 (&w)[NSTEP], int q, int lo, int hi, int p0) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int p = 8 * q + t;                 // uniform
+    for (int t = 0; t < PPB; ++t) {
+      const int p = PPB * q + t;               // uniform
       if (p < lo || p >= hi) continue;
       const LutT* base = tab + (size_t)(p - p0) * a.K * BT + rq * BQ;
       if (BQ == 1) {
         // issue every lookup of this pair before adding, so the LDS reads overlap
         float v[NSTEP];
 #pragma unroll
-        for (int st = 0; st < NSTEP; ++st) v[st] = lut_value(base + code_of(w[st], t) * BT);
+        for (int st = 0; st < NSTEP; ++st) v[st] = lut_value(base + code_of<PK>(w[st], t) * BT);
 #pragma unroll
         for (int st = 0; st < NSTEP; ++st) acc[st][0] += v[st];
       } else {
 #pragma unroll
-        for (int st = 0; st < NSTEP; ++st) lookup_add<LutT, BQ>(acc[st], base + code_of(w[st], t) * BT);
+        for (int st = 0; st < NSTEP; ++st) lookup_add<LutT, BQ>(acc[st], base + code_of<PK>(w[st], t) * BT);
       }
     }
   };
@@ -316,12 +326,11 @@ void gather_kernel(GatherArgs a) {
     const int n4 = min(a.P, a.NP - c_begin * a.P) * words_per_pair;
     chunk_to_regs(nxt, lut4 + (size_t)c_begin * a.P * words_per_pair, tid, n4 - 1);
   }
-  for (int c = c_begin; c < c_end; ++c) {
+  // Stage chunk c (uniform): all lookups of the previous chunk are done before
+  // LDS is overwritten, and the next chunk starts loading into registers.
+  auto switch_chunk = [&](int c) {
     const int p0 = c * a.P;
     const int pc = min(a.P, a.NP - p0);
-    const int lo = max(p0, pa), hi = min(p0 + pc, pb);
-    const int q0 = lo >> 3, q1 = (hi + 7) >> 3;
-    load_block(wa, q0);
     __syncthreads();
     if (REG) {
       // words past the chunk were loaded clamped to its last word, so writing
@@ -338,13 +347,38 @@ void gather_kernel(GatherArgs a) {
       stage_chunk<LutT, BT>(tab, lut, p0, pc, a.K, a.B, b0);
     }
     __syncthreads();
-    // The loads are unconditional (past the end they repeat the last block,
-    // a cache hit), so the same count is always in flight.
-    for (int q = q0; q < q1; q += 2) {
-      load_block(wb, min(q + 1, q1 - 1));
-      lookup_block(wa, q, lo, hi, p0);
-      load_block(wa, min(q + 2, q1 - 1));
-      lookup_block(wb, q + 1, lo, hi, p0);
+  };
+  // The loads are unconditional (past the end they repeat the last block, a
+  // cache hit), so the same count is always in flight.
+  if (BT == 1 && a.P % PPB == 0) {
+    // Chunks hold whole code blocks: one flat loop over the group's blocks, so
+    // the next block's codes are already in flight across a chunk switch.
+    // (Batch tiles keep the per-chunk loop: both loops in one kernel spill.)
+    const int bpc = a.P / PPB;
+    const int qa = pa / PPB, qb = (pb + PPB - 1) / PPB;
+    load_block(wa, qa);
+    for (int q = qa; q < qb; q += 2) {
+      if ((q - qa) % bpc == 0) switch_chunk(c_begin + (q - qa) / bpc);
+      load_block(wb, min(q + 1, qb - 1));
+      lookup_block(wa, q, pa, pb, (c_begin + (q - qa) / bpc) * a.P);
+      if (q + 1 < qb && (q + 1 - qa) % bpc == 0) switch_chunk(c_begin + (q + 1 - qa) / bpc);
+      load_block(wa, min(q + 2, qb - 1));
+      lookup_block(wb, q + 1, pa, pb, (c_begin + (q + 1 - qa) / bpc) * a.P);
+    }
+  } else {
+    for (int c = c_begin; c < c_end; ++c) {
+      const int p0 = c * a.P;
+      const int pc = min(a.P, a.NP - p0);
+      const int lo = max(p0, pa), hi = min(p0 + pc, pb);
+      const int q0 = lo / PPB, q1 = (hi + PPB - 1) / PPB;
+      load_block(wa, q0);
+      switch_chunk(c);
+      for (int q = q0; q < q1; q += 2) {
+        load_block(wb, min(q + 1, q1 - 1));
+        lookup_block(wa, q, lo, hi, p0);
+        load_block(wa, min(q + 2, q1 - 1));
+        lookup_block(wb, q + 1, lo, hi, p0);
+      }
     }
   }
   // ---- G > 1: store the partial sums; the finish kernel adds them in group order
@@ -390,13 +424,13 @@ void gather_kernel(GatherArgs a) {
   if (tid < BT && b0 + tid < a.B) a.block_keys[(size_t)(b0 + tid) * a.S + s] = s_keys[tid];
 }
 
-template <typename LutT, int BT, int NSTEP, int FD = 0>
+template <typename LutT, int BT, int NSTEP, int FD = 0, bool PK = false>
 hipError_t launch_gather_typed(const GatherArgs& a, const GatherPlan& plan, hipStream_t stream) {
   const size_t chunk_bytes = (size_t)plan.P * a.K * BT * sizeof(LutT);
   const bool reg = a.B == BT && chunk_bytes % 16 == 0 && chunk_bytes <= (size_t)kRegStage * 16 * kGatherThreads &&
                    ((size_t)a.K * BT * sizeof(LutT)) % 16 == 0;
-  auto kern = FD ? gather_kernel<LutT, BT, NSTEP, true, FD>
-                 : (reg ? gather_kernel<LutT, BT, NSTEP, true> : gather_kernel<LutT, BT, NSTEP, false>);
+  auto kern = FD ? gather_kernel<LutT, BT, NSTEP, true, FD, PK>
+                 : (reg ? gather_kernel<LutT, BT, NSTEP, true, 0, PK> : gather_kernel<LutT, BT, NSTEP, false, 0, PK>);
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget);
   if (e != hipSuccess) return e;
   hipEvent_t before, after;
@@ -626,7 +660,7 @@ double plan_cost_us(int64_t rows, int NP, int K, int B, int es, int BT, int P, i
 // subspace width fused_d (B == 1): a chunk's staged bytes are its codebook
 // rows (4*fused_d per entry, at most 128 KB so they fit the staging
 // registers), and the activation vector (D floats) shares the LDS.
-GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16, int fused_d, int D) {
+GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16, int fused_d, int D, int ppb) {
   const int es = lut_bf16 ? 2 : 4;
   const int stage_es = fused_d ? 4 * fused_d : es;
   GatherPlan best{};
@@ -645,6 +679,11 @@ GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16, int fus
                                    (int64_t)kRegStage * 16 * kGatherThreads / ((int64_t)K * stage_es)});
     if (pmax < 1) return best;
   }
+  // One vector per lane: chunks of at most 24 pairs (whole blocks of both
+  // serving layouts) measured faster than LDS-filling ones -- with the flat
+  // block loop the code stream runs through chunk switches, and smaller
+  // switches stall the workgroup for less time.
+  if (BT == 1 && !fused_d) pmax = std::min(pmax, 24);
   if (pmax < NP && pmax > 1) pmax &= ~1;
   double best_cost = 1e300;
   int tried = 0;
@@ -662,7 +701,7 @@ GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16, int fus
         if (G != G0) continue;
         // prefer aligned chunks (staging outside the block loop) on near-ties
         const double cost = plan_cost_us(rows, NP, K, B, es, BT, P, steps, G, cpg, stage_es) *
-                            ((P % 8 == 0 || chunks == 1) ? 1.0 : 1.03);
+                            ((P % ppb == 0 || chunks == 1) ? 1.0 : 1.03);
         if (cost < best_cost * 0.999) {
           best_cost = cost;
           best.BT = BT; best.P = P; best.chunks = chunks; best.cpg = cpg; best.G = G;
@@ -679,9 +718,10 @@ GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16, int fus
 // off the per-call path.
 struct PlanKey {
   int64_t rows;
-  int NP, K, B, bf16, fused_d, D;
+  int NP, K, B, bf16, fused_d, D, ppb;
   bool operator==(const PlanKey& o) const {
-    return rows == o.rows && NP == o.NP && K == o.K && B == o.B && bf16 == o.bf16 && fused_d == o.fused_d && D == o.D;
+    return rows == o.rows && NP == o.NP && K == o.K && B == o.B && bf16 == o.bf16 && fused_d == o.fused_d &&
+           D == o.D && ppb == o.ppb;
   }
 };
 std::mutex g_plan_mu;
@@ -697,7 +737,7 @@ int g_plan_n = 0, g_plan_next = 0;
 // (partial-sum traffic) and long slabs (loads in flight per lane).
 GatherPlan plan_gather(const rq_matrix* W, int B, int lut_bf16, int fused) {
   const int fd = fused ? W->d : 0;
-  const PlanKey key{W->rows, W->L * W->M, W->K, B, lut_bf16, fd, fused ? W->D : 0};
+  const PlanKey key{W->rows, W->L * W->M, W->K, B, lut_bf16, fd, fused ? W->D : 0, pairs_per_block(W)};
   GatherPlan plan{};
   bool hit = false;
   {
@@ -706,7 +746,7 @@ GatherPlan plan_gather(const rq_matrix* W, int B, int lut_bf16, int fused) {
       if (g_plan_keys[i] == key) { plan = g_plans[i]; hit = true; break; }
   }
   if (!hit) {
-    plan = search_plan(key.rows, key.NP, key.K, B, lut_bf16, fd, key.D);
+    plan = search_plan(key.rows, key.NP, key.K, B, lut_bf16, fd, key.D, key.ppb);
     std::lock_guard<std::mutex> lock(g_plan_mu);
     g_plan_keys[g_plan_next] = key;
     g_plans[g_plan_next] = plan;
@@ -718,6 +758,24 @@ GatherPlan plan_gather(const rq_matrix* W, int B, int lut_bf16, int fused) {
     plan.lds = (size_t)plan.P * W->K * plan.BT * (lut_bf16 ? 2 : 4) + (fd ? (size_t)key.D * 4 : 0);
 #endif
   return plan;
+}
+
+template <bool PK>
+hipError_t dispatch_gather(const GatherArgs& a, const GatherPlan& plan, int d, int lut_bf16, bool fused,
+                           hipStream_t stream) {
+  if (fused) {
+    if (d == 1) return launch_gather_typed<float, 1, 4, 1, PK>(a, plan, stream);
+    if (d == 2) return launch_gather_typed<float, 1, 4, 2, PK>(a, plan, stream);
+    return launch_gather_typed<float, 1, 4, 4, PK>(a, plan, stream);
+  }
+  if (lut_bf16) {
+    if (plan.BT == 1) return launch_gather_typed<uint16_t, 1, 4, 0, PK>(a, plan, stream);
+    if (plan.BT == 4) return launch_gather_typed<uint16_t, 4, 4, 0, PK>(a, plan, stream);
+    return launch_gather_typed<uint16_t, 16, 4, 0, PK>(a, plan, stream);
+  }
+  if (plan.BT == 1) return launch_gather_typed<float, 1, 4, 0, PK>(a, plan, stream);
+  if (plan.BT == 4) return launch_gather_typed<float, 4, 4, 0, PK>(a, plan, stream);
+  return launch_gather_typed<float, 16, 4, 0, PK>(a, plan, stream);
 }
 
 bool fused_build_supported(const rq_matrix* W, int B) {
@@ -744,20 +802,8 @@ hipError_t launch_gather(const rq_matrix* W, const GatherPlan& plan, const void*
   a.out = o.out;
   a.softcap = o.softcap;
   a.block_keys = plan.G == 1 ? o.block_keys : nullptr;
-  hipError_t e;
-  if (fused_act) {
-    if (W->d == 1) e = launch_gather_typed<float, 1, 4, 1>(a, plan, stream);
-    else if (W->d == 2) e = launch_gather_typed<float, 1, 4, 2>(a, plan, stream);
-    else e = launch_gather_typed<float, 1, 4, 4>(a, plan, stream);
-  } else if (lut_bf16) {
-    if (plan.BT == 1) e = launch_gather_typed<uint16_t, 1, 4>(a, plan, stream);
-    else if (plan.BT == 4) e = launch_gather_typed<uint16_t, 4, 4>(a, plan, stream);
-    else e = launch_gather_typed<uint16_t, 16, 4>(a, plan, stream);
-  } else {
-    if (plan.BT == 1) e = launch_gather_typed<float, 1, 4>(a, plan, stream);
-    else if (plan.BT == 4) e = launch_gather_typed<float, 4, 4>(a, plan, stream);
-    else e = launch_gather_typed<float, 16, 4>(a, plan, stream);
-  }
+  hipError_t e = W->codes_layout == RQ_CODES_PACKED10 ? dispatch_gather<true>(a, plan, W->d, lut_bf16, fused_act != nullptr, stream)
+                                                        : dispatch_gather<false>(a, plan, W->d, lut_bf16, fused_act != nullptr, stream);
   if (e != hipSuccess || plan.G == 1) return e;
   return launch_finish(o.partial, plan.G, B, W->rows, o.softcap, o.out, o.block_keys, stream);
 }

@@ -25,11 +25,12 @@
 //     slice of one part of h.
 //   - Lane (i = lane % 16, kg = lane / 16) feeds A row i, slot kg, and receives
 //     C rows 4*kg .. 4*kg+3 of column i.
-// The blocked code layout gives each row 16 bytes per block of 8 (level,
-// subspace) pairs; dword kg of it holds the codes of pairs 2kg and 2kg+1. So a
-// lane loads exactly one dword per row tile and block (a wave reads 16 rows x 16
-// contiguous bytes, no byte twice) and the block is done as two "half-blocks":
-// half s uses pairs {8q + 2kg + s : kg < 4}, the low or high 16 bits.
+// The serving code layouts give each row 16 bytes per block of pairs: 8 pairs
+// of 16-bit codes (dword kg holds pairs 2kg and 2kg+1) or 12 pairs of 10-bit
+// codes (dword kg holds pairs 3kg .. 3kg+2). So a lane loads exactly one dword
+// per row tile and block (a wave reads 16 rows x 16 contiguous bytes, no byte
+// twice) and the block is done as NSUB = 2 or 3 "sub-blocks": sub-block s uses
+// pairs {PPB*q + NSUB*kg + s : kg < 4}, the s-th code field of each dword.
 //
 // Work split: workgroup (group g, slab s, batch tile bt) accumulates 16*NT
 // hidden vectors over slab s's rows (8 waves x T tiles x 16 rows) for group
@@ -100,8 +101,13 @@ struct Staged {
   u32x4 hv[kH];
 };
 
-template <int DS, int NT, int T>
+// NSUB sub-blocks per code block: 2 for 16-bit codes (pairs 2kg, 2kg+1 in
+// dword kg), 3 for RQ_CODES_PACKED10 (pairs 3kg .. 3kg+2, 10 bits each).
+template <int DS, int NT, int T, int NSUB>
 __global__ __launch_bounds__(kMmThreads) void mm_logits_kernel(MmArgs a) {
+  constexpr int PPB = 4 * NSUB;                 // pairs per code block
+  constexpr int CBITS = NSUB == 2 ? 16 : 10;    // bits per code
+  constexpr uint32_t CMASK = (1u << CBITS) - 1u;
   extern __shared__ __align__(16) u32x4 ring[];   // [2][4*K + kParts*4*16*NT]
   const int K = a.K;
   const int cw_entries = 4 * K;
@@ -154,7 +160,7 @@ __global__ __launch_bounds__(kMmThreads) void mm_logits_kernel(MmArgs a) {
       const int c = (tid + u * kMmThreads) % cw_entries;
       const int kk = c / K;
       const int k = c - kk * K;
-      const int p = min(8 * q + 2 * kk + hs, a.NP - 1);
+      const int p = min(PPB * q + NSUB * kk + hs, a.NP - 1);
       const uint32_t* src = reinterpret_cast<const uint32_t*>(a.cb + ((size_t)p * K + k) * DS);
 #pragma unroll
       for (int w = 0; w < DS / 2; ++w) st.cw[u][w] = src[w];
@@ -166,7 +172,7 @@ __global__ __launch_bounds__(kMmThreads) void mm_logits_kernel(MmArgs a) {
       const int rem = e - pr * 4 * n_bt;
       const int kk = rem / n_bt;
       const int n = rem - kk * n_bt;
-      const int p = min(8 * q + 2 * kk + hs, a.NP - 1);
+      const int p = min(PPB * q + NSUB * kk + hs, a.NP - 1);
       const int m = p % a.M;
       st.hv[u] = a.hp[((size_t)pr * a.M + m) * a.Bp + (size_t)bt * n_bt + n];
     }
@@ -176,7 +182,7 @@ __global__ __launch_bounds__(kMmThreads) void mm_logits_kernel(MmArgs a) {
 #pragma unroll
     for (int u = 0; u < kMaxCwPerThread; ++u) {
       const int c = (tid + u * kMmThreads) % cw_entries;
-      const bool live = 8 * q + 2 * (c / K) + hs < a.NP;
+      const bool live = PPB * q + NSUB * (c / K) + hs < a.NP;
       u32x4 v = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int w = 0; w < DS / 2; ++w) v[w] = live ? st.cw[u][w] : 0u;
@@ -187,7 +193,7 @@ __global__ __launch_bounds__(kMmThreads) void mm_logits_kernel(MmArgs a) {
       const int e = (tid + u * kMmThreads) % h_entries;
       const int pr = e / (4 * n_bt);
       const int kk = (e - pr * 4 * n_bt) / n_bt;
-      const bool live = 8 * q + 2 * kk + hs < a.NP;
+      const bool live = PPB * q + NSUB * kk + hs < a.NP;
       const u32x4 z = {0u, 0u, 0u, 0u};
       base[cw_entries + e] = live ? st.hv[u] : z;
     }
@@ -215,7 +221,7 @@ __global__ __launch_bounds__(kMmThreads) void mm_logits_kernel(MmArgs a) {
     bf16x8 av[2][kI];
 #pragma unroll
     for (int u = 0; u < kI; ++u)
-      av[0][u] = __builtin_bit_cast(bf16x8, cwb[(codes[min(u, T - 1)] >> (16 * hs)) & 0xffffu]);
+      av[0][u] = __builtin_bit_cast(bf16x8, cwb[(codes[min(u, T - 1)] >> (CBITS * hs)) & CMASK]);
 #pragma unroll
     for (int gi = 0; gi < kGroups; ++gi) {
       const int cur = gi & 1;
@@ -223,7 +229,7 @@ __global__ __launch_bounds__(kMmThreads) void mm_logits_kernel(MmArgs a) {
 #pragma unroll
         for (int u = 0; u < kI; ++u) {
           const int j = min((gi + 1) * kI + u, T - 1);
-          av[cur ^ 1][u] = __builtin_bit_cast(bf16x8, cwb[(codes[j] >> (16 * hs)) & 0xffffu]);
+          av[cur ^ 1][u] = __builtin_bit_cast(bf16x8, cwb[(codes[j] >> (CBITS * hs)) & CMASK]);
         }
       }
 #pragma unroll
@@ -244,35 +250,27 @@ __global__ __launch_bounds__(kMmThreads) void mm_logits_kernel(MmArgs a) {
     load_codes(ca, q0);
     stage_load(st, q0, 0);
     int slot = 0;
-    for (int q = q0; q < q1; q += 2) {
-      // block q (codes in ca), prefetching block q+1's codes into cbk
-      stage_store(st, slot, q, 0);
-      __syncthreads();
-      stage_load(st, q, 1);
-      __builtin_amdgcn_sched_barrier(0);   // keep the staging loads ahead of the code loads (vmcnt is in order)
-      load_codes(cbk, min(q + 1, q1 - 1));
-      compute(slot, ca, 0);
-      slot ^= 1;
-      stage_store(st, slot, q, 1);
-      __syncthreads();
-      stage_load(st, min(q + 1, q1 - 1), 0);
-      compute(slot, ca, 1);
-      slot ^= 1;
-      if (q + 1 < q1) {
-        // block q+1 (codes in cbk), prefetching block q+2's codes into ca
-        stage_store(st, slot, q + 1, 0);
+    // One code block: its NSUB sub-blocks in turn, each staged in one ring slot
+    // while the next one's codebook loads into registers; the first sub-block
+    // also starts loading the next block's codes (into the other buffer).
+    auto do_block = [&](int q, const uint32_t (&cur)[T], uint32_t (&nxt)[T]) {
+#pragma unroll
+      for (int hs = 0; hs < NSUB; ++hs) {
+        stage_store(st, slot, q, hs);
         __syncthreads();
-        stage_load(st, q + 1, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        load_codes(ca, min(q + 2, q1 - 1));
-        compute(slot, cbk, 0);
-        slot ^= 1;
-        stage_store(st, slot, q + 1, 1);
-        __syncthreads();
-        stage_load(st, min(q + 2, q1 - 1), 0);
-        compute(slot, cbk, 1);
+        if (hs + 1 < NSUB) stage_load(st, q, hs + 1);
+        else stage_load(st, min(q + 1, q1 - 1), 0);
+        if (hs == 0) {
+          __builtin_amdgcn_sched_barrier(0);   // keep the staging loads ahead of the code loads (vmcnt is in order)
+          load_codes(nxt, min(q + 1, q1 - 1));
+        }
+        compute(slot, cur, hs);
         slot ^= 1;
       }
+    };
+    for (int q = q0; q < q1; q += 2) {
+      do_block(q, ca, cbk);
+      if (q + 1 < q1) do_block(q + 1, cbk, ca);
     }
   }
 
@@ -294,25 +292,37 @@ __global__ __launch_bounds__(kMmThreads) void mm_logits_kernel(MmArgs a) {
 
 // Row tiles per wave for NT column tiles: the accumulators (4*T*NT VGPRs), the
 // code registers (2*T) and the staged half-block share a wave's 256 VGPRs.
-constexpr int tiles_for(int NT) {
-  return kMmThreads == 512 ? (NT == 1 ? 16 : NT == 2 ? 8 : 3) : (NT == 1 ? 8 : NT == 2 ? 4 : 2);
+// (Three sub-blocks per code block keep more values live: fewer tiles.)
+constexpr int tiles_for(int NT, int NSUB = 2) {
+  return kMmThreads == 512 ? (NSUB == 2 ? (NT == 1 ? 16 : NT == 2 ? 8 : 3) : (NT == 1 ? 12 : NT == 2 ? 6 : 3))
+                           : (NT == 1 ? 8 : NT == 2 ? 4 : 2);
 }
 
-template <int DS, int NT>
+template <int DS, int NT, int NSUB>
 hipError_t launch_typed(const MmArgs& a, int wgs, size_t lds, hipStream_t stream) {
-  auto kern = mm_logits_kernel<DS, NT, tiles_for(NT)>;
+  auto kern = mm_logits_kernel<DS, NT, tiles_for(NT, NSUB), NSUB>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(kMmThreads), lds, stream, a);
   return hipGetLastError();
 }
 
-template <int DS>
+template <int DS, int NSUB>
 hipError_t launch_ds(const MmArgs& a, const MmPlan& p, hipStream_t stream) {
   const int wgs = p.G * p.S * p.NBT;
-  if (p.NT == 1) return launch_typed<DS, 1>(a, wgs, p.lds, stream);
-  if (p.NT == 2) return launch_typed<DS, 2>(a, wgs, p.lds, stream);
-  return launch_typed<DS, 4>(a, wgs, p.lds, stream);
+  if (p.NT == 1) return launch_typed<DS, 1, NSUB>(a, wgs, p.lds, stream);
+  if (p.NT == 2) return launch_typed<DS, 2, NSUB>(a, wgs, p.lds, stream);
+  return launch_typed<DS, 4, NSUB>(a, wgs, p.lds, stream);
+}
+
+template <int NSUB>
+hipError_t launch_nsub(const MmArgs& a, const MmPlan& p, int d, hipStream_t stream) {
+  switch (d) {
+    case 2: return launch_ds<2, NSUB>(a, p, stream);
+    case 4: return launch_ds<4, NSUB>(a, p, stream);
+    case 6: return launch_ds<6, NSUB>(a, p, stream);
+    default: return launch_ds<8, NSUB>(a, p, stream);
+  }
 }
 
 #ifdef RQ_TUNING
@@ -327,19 +337,20 @@ void mm_tuning_override(MmPlan& p) {
 }  // namespace
 
 bool mm_supported(const rq_matrix* W) {
-  return W->cb_dtype == RQ_BF16 && W->codes_layout == RQ_CODES_BLOCKED && W->d <= 8 && (W->d % 2) == 0 &&
+  return W->cb_dtype == RQ_BF16 && (W->codes_layout == RQ_CODES_BLOCKED || W->codes_layout == RQ_CODES_PACKED10) &&
+         W->d <= 8 && (W->d % 2) == 0 &&
          W->K <= kMmMaxK && ((uintptr_t)W->codebooks % 4) == 0;
 }
 
 MmPlan plan_mm(const rq_matrix* W, int B) {
   MmPlan p{};
   p.NT = B <= 16 ? 1 : (B <= 32 ? 2 : 4);
-  p.T = tiles_for(p.NT);
+  p.T = tiles_for(p.NT, W->codes_layout == RQ_CODES_PACKED10 ? 3 : 2);
   p.NBT = (B + 16 * p.NT - 1) / (16 * p.NT);
   p.Bp = p.NBT * 16 * p.NT;
   const int64_t slab = (int64_t)kMmWaves * p.T * 16;
   p.S = (int)((W->rows + slab - 1) / slab);
-  p.NQ = (W->L * W->M + 7) / 8;
+  p.NQ = (W->L * W->M + pairs_per_block(W) - 1) / pairs_per_block(W);
   // Group count: workgroups run in rounds of one per CU; a round costs the
   // blocks one workgroup handles (about 5.5 us per block for 16 waves' worth of
   // 16x16 tiles, measured at the Gemma head), and every group beyond the first
@@ -351,7 +362,7 @@ MmPlan plan_mm(const rq_matrix* W, int B) {
     const int gg = (p.NQ + qpg - 1) / qpg;
     const int64_t wgs = (int64_t)gg * p.S * p.NBT;
     const double rounds = (double)((wgs + kCUs - 1) / kCUs);
-    const double per_block = 5.5 * (double)(p.T * p.NT) / 16.0;
+    const double per_block = 5.5 * (double)(p.T * p.NT) / 16.0 * (double)pairs_per_block(W) / 8.0;
     const double cost = rounds * qpg * per_block + (gg > 1 ? (double)gg * B * W->rows * 8.0 / 5.0e6 : 0.0);
     if (cost < best * 0.999) { best = cost; G = gg; }
   }
@@ -393,12 +404,7 @@ hipError_t launch_mm_logits(const rq_matrix* W, const MmPlan& p, const float* h,
   hipEvent_t before, after;
   take_stage_events(&before, &after);
   if (before && (e = hipEventRecord(before, stream)) != hipSuccess) return e;
-  switch (W->d) {
-    case 2: e = launch_ds<2>(a, p, stream); break;
-    case 4: e = launch_ds<4>(a, p, stream); break;
-    case 6: e = launch_ds<6>(a, p, stream); break;
-    default: e = launch_ds<8>(a, p, stream); break;
-  }
+  e = W->codes_layout == RQ_CODES_PACKED10 ? launch_nsub<3>(a, p, W->d, stream) : launch_nsub<2>(a, p, W->d, stream);
   if (e != hipSuccess) return e;
   if (after) e = hipEventRecord(after, stream);
   return e;

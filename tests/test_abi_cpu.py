@@ -58,6 +58,7 @@ def call_logits(W, Bn=1, topk=0, lut=0x30000, ws=0x40000, ws_bytes=1 << 40, lut_
     (dict(rows=1 << 29), B.RQ_ERR_SHAPE),
     (dict(cb_dtype=7), B.RQ_ERR_DTYPE),
     (dict(codes_layout=5), B.RQ_ERR_DTYPE),
+    (dict(codes_layout=B.RQ_CODES_PACKED10, K=1025), B.RQ_ERR_SHAPE),   # 10-bit codes need K <= 1024
     (dict(codebooks=0), B.RQ_ERR_NULL),
     (dict(codes=0), B.RQ_ERR_NULL),
     (dict(codes=0x20002), B.RQ_ERR_ALIGN),
@@ -97,6 +98,8 @@ def test_workspace_queries():
     assert lib.rq_blocked_codes_bytes(256000, 2, 384) == 393_216_000
     assert lib.rq_blocked_codes_bytes(10, 1, 5) == 1 * 10 * 16
     assert lib.rq_blocked_codes_bytes(10, 3, 3) == 2 * 10 * 16
+    assert lib.rq_packed10_codes_bytes(256000, 2, 384) == 64 * 256000 * 16   # 1024 bytes per Gemma-head row
+    assert lib.rq_packed10_codes_bytes(10, 1, 13) == 2 * 10 * 16
     Wm = gemma_desc(rows=9216, D=2304, M=1152, d=2, cb_dtype=B.RQ_F32)
     # one vector with fp32 codebooks builds its table while staging: no table in the workspace
     assert 0 < lib.rq_lut_matvec_workspace(ctypes.byref(Wm), 1) < 2 * 1152 * 1024 * 4
@@ -122,6 +125,10 @@ def test_other_entry_points_reject():
     assert lib.rq_pack_codes(None, 10, 2, 3, 0x1000, None) == B.RQ_ERR_NULL
     assert lib.rq_pack_codes(0x1000, 10, 0, 3, 0x1000, None) == B.RQ_ERR_SHAPE
     assert lib.rq_pack_codes(0x1000, 10, 2, 3, 0x1008, None) == B.RQ_ERR_ALIGN
+    assert lib.rq_pack_codes10(None, 10, 2, 3, 0x1000, None) == B.RQ_ERR_NULL
+    assert lib.rq_pack_codes10(0x1000, 10, 0, 3, 0x1000, None) == B.RQ_ERR_SHAPE
+    assert lib.rq_pack_codes10(0x1000, 10, 2, 3, 0x1008, None) == B.RQ_ERR_ALIGN
+    assert lib.rq_pack_codes10(None, 0, 2, 3, None, None) == B.RQ_OK
     assert lib.rq_dense_logits(0x1000, 100, 2300, 0x2000, 1, 30.0, 0x3000, None, None, 0, None) == B.RQ_ERR_SHAPE
     assert lib.rq_dense_logits(0x1000, 100, 2304, 0x2000, 17, 30.0, 0x3000, None, None, 0, None) == B.RQ_ERR_SHAPE
     assert lib.rq_dense_logits(0x1000, 100, 2304, 0x2000, 1, 30.0, 0x3000, 0x4000, None, 0, None) == B.RQ_ERR_WORKSPACE
@@ -143,6 +150,7 @@ def test_logits_method_and_checks():
     assert m(gemma_desc(M=256, d=9), 16) == B.RQ_METHOD_TABLE                  # d > 8
     assert m(gemma_desc(M=768, d=3), 16) == B.RQ_METHOD_TABLE                  # odd d
     assert m(gemma_desc(M=1152, d=2), 16) == B.RQ_METHOD_MATRIX_CORES
+    assert m(gemma_desc(codes_layout=B.RQ_CODES_PACKED10), 16) == B.RQ_METHOD_MATRIX_CORES
     assert m(gemma_desc(D=2305), 16) == B.RQ_ERR_SHAPE
     ws16 = lib.rq_logits_workspace(ctypes.byref(W), 16, 0)
     assert ws16 > 0 and ws16 % 256 == 0

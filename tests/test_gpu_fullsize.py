@@ -16,11 +16,13 @@ pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
 O = oracle.default
 
 
-def test_gemma_head_b1_full():
-    """Gemma-2-2B head at decode: 256000 logits + argmax, and the 64 input rows decoded to bf16."""
+@pytest.mark.parametrize("layout", ["blocked", "packed10"])
+def test_gemma_head_b1_full(layout):
+    """Gemma-2-2B head at decode: 256000 logits + argmax, and the 64 input rows decoded to bf16, from the
+    16-bit blocked codes and from the 10-bit code stream."""
     cfg = synth.CONFIGS["gemma_b1"]
     mat, h, ids = synth.make_head(cfg)
-    W = to_dev(mat)
+    W = to_dev(mat, layout)
     rows = la.decode_rows(W, dev(ids), "bf16")
     assert np.array_equal(host(rows).view(np.uint16),
                           O().decode_rows(mat.codes, mat.codebooks, True, ids, True)[0])
@@ -29,7 +31,7 @@ def test_gemma_head_b1_full():
     _, ref = oracle_head(mat, h, cfg.softcap)
     worst = check_logits(host(lg), ref)
     check_argmax(host(am), host(lg), ref)
-    print(f"gemma B=1: worst |gpu-oracle|/max|oracle| = {worst:.2e}")
+    print(f"gemma B=1 {layout}: worst |gpu-oracle|/max|oracle| = {worst:.2e}")
 
 
 @pytest.mark.parametrize("name", ["gemma_b16", "gemma_b128"])
@@ -46,18 +48,19 @@ def test_gemma_head_batched_full(name):
     print(f"{name}: worst |gpu-oracle|/max|oracle| = {worst:.2e}")
 
 
-@pytest.mark.parametrize("name", ["gemma_b16", "gemma_b128"])
-def test_gemma_head_one_call_full(name):
+@pytest.mark.parametrize("name,layout", [("gemma_b16", "blocked"), ("gemma_b128", "blocked"),
+                                         ("gemma_b16", "packed10")])
+def test_gemma_head_one_call_full(name, layout):
     """rq_logits on the full head at B=16 and B=128 (the matrix-core method): every logit and argmax."""
     cfg = synth.CONFIGS[name]
     mat, h, _ = synth.make_head(cfg)
-    W = to_dev(mat)
+    W = to_dev(mat, layout)
     assert la.logits_method(W, cfg.B) == la.RQ_METHOD_MATRIX_CORES
     lg, am, _, _ = la.logits(W, dev(h), softcap=cfg.softcap)
     _, ref = oracle_head(mat, h, cfg.softcap)
     worst = check_logits(host(lg), ref)
     check_argmax(host(am), host(lg), ref)
-    print(f"{name} one call: worst |gpu-oracle|/max|oracle| = {worst:.2e}")
+    print(f"{name} {layout} one call: worst |gpu-oracle|/max|oracle| = {worst:.2e}")
 
 
 def test_stress_head_full():

@@ -29,11 +29,13 @@ MM_EXACT = [
 
 
 @pytest.mark.parametrize("shape", MM_EXACT, ids=lambda s: "x".join(map(str, s)))
-def test_logits_matrix_cores_exact(shape):
-    """Small-integer inputs: every product and sum is exact in fp32, so z matches the oracle bit for bit."""
+@pytest.mark.parametrize("layout", ["blocked", "packed10"])
+def test_logits_matrix_cores_exact(shape, layout):
+    """Small-integer inputs: every product and sum is exact in fp32, so z matches the oracle bit for bit
+    (16-bit blocked codes: two sub-blocks per code block; 10-bit codes: three)."""
     rows, D, M, K, L, B = shape
     mat, h = synth.gen_exact(rows + 7 * K, rows, D, M, K, L, B, cb_dtype="bf16")
-    W = to_dev(mat)
+    W = to_dev(mat, layout)
     assert la.logits_method(W, B) == la.RQ_METHOD_MATRIX_CORES
     lg, am, _, _ = la.logits(W, dev(h), softcap=0.0)
     z, _ = O().logits(mat.codes, mat.codebooks, True, h, 0.0)

@@ -33,9 +33,23 @@ def test_pack_codes_bit_exact(rows, NP):
     assert np.array_equal(out, want)
 
 
+@pytest.mark.parametrize("rows,NP", [(1, 1), (63, 7), (4097, 34), (130, 768), (65, 1000)])
+def test_pack_codes10_bit_exact(rows, NP):
+    """The 10-bit layout against a host packing: 12 codes per 16-byte block, three per 32-bit word."""
+    rng = np.random.default_rng(7 * rows + NP)
+    codes = rng.integers(0, 1024, size=(rows, NP), dtype=np.uint16)
+    out = host(la.pack_codes10(dev(codes.view(np.int16)), rows, 1, NP)).view(np.uint32)
+    NQ = (NP + 11) // 12
+    padded = np.zeros((rows, 12 * NQ), np.uint32)
+    padded[:, :NP] = codes
+    trip = padded.reshape(rows, NQ, 4, 3)
+    words = trip[..., 0] | (trip[..., 1] << 10) | (trip[..., 2] << 20)        # [rows][NQ][4]
+    assert np.array_equal(out, words.transpose(1, 0, 2).reshape(-1))
+
+
 # ------------------------------------------------------------------ row decode
 
-@pytest.mark.parametrize("layout", ["rows", "blocked"])
+@pytest.mark.parametrize("layout", ["rows", "blocked", "packed10"])
 @pytest.mark.parametrize("L,cb_dtype,out_dtype", [(2, "f32", "f32"), (2, "f32", "bf16"), (2, "bf16", "bf16"),
                                                   (3, "f32", "f32"), (4, "bf16", "f32"), (1, "f32", "f32")])
 def test_decode_rows_bit_exact(layout, L, cb_dtype, out_dtype):
@@ -116,7 +130,7 @@ EXACT_SHAPES = [
 
 
 @pytest.mark.parametrize("shape", EXACT_SHAPES, ids=lambda s: "x".join(map(str, s)))
-@pytest.mark.parametrize("layout", ["rows", "blocked"])
+@pytest.mark.parametrize("layout", ["rows", "blocked", "packed10"])
 def test_lut_logits_exact(shape, layout):
     """Small-integer inputs: every fp32 step is exact, so logits (softcap off) equal the oracle bit for bit."""
     rows, D, M, K, L, B = shape
@@ -146,7 +160,7 @@ def test_tiny_config():
     """The tiny RQ head: V=4096, D=96, M=16, K=256, L=2, fp32 codebooks, softcap 30, argmax, 8 decoded rows."""
     cfg = synth.CONFIGS["tiny"]
     mat, h, ids = synth.make_head(cfg)
-    for layout in ("rows", "blocked"):
+    for layout in ("rows", "blocked", "packed10"):
         W = to_dev(mat, layout)
         lg, am, _, _ = la.lut_logits(W, la.build_lut(W, dev(h)), 1, softcap=cfg.softcap)
         _, ref = oracle_head(mat, h, cfg.softcap)
@@ -255,7 +269,7 @@ def test_lut_matvec_small_chain():
 
 
 @pytest.mark.parametrize("d", [1, 2, 4])
-@pytest.mark.parametrize("layout", ["rows", "blocked"])
+@pytest.mark.parametrize("layout", ["rows", "blocked", "packed10"])
 def test_lut_matvec_fused_build_exact(d, layout):
     """One activation vector with fp32 codebooks: the table is built while staging. Exact inputs, ragged rows
     and (blocked layout) a partly empty last code block: bit-exact against the oracle."""
