@@ -247,8 +247,8 @@ HeadWs head_ws(const rq_matrix* W, int32_t B, int32_t topk, bool logits_out) {
   if (w.mm) {
     w.mp = rq::plan_mm(W, B);
     w.partial = round_up(rq::mm_hp_bytes(W, w.mp), 256);
-    partial_bytes = (size_t)w.mp.G * B * W->rows * sizeof(float);
-    w.nkb = rq::finish_key_blocks(w.mp.G, W->rows);
+    partial_bytes = w.mp.G > 1 ? (size_t)w.mp.G * B * W->rows * sizeof(float) : 0;
+    w.nkb = w.mp.G > 1 ? rq::finish_key_blocks(w.mp.G, W->rows) : w.mp.S;
   } else {
     w.gp = rq::plan_gather(W, B, 0);
     w.partial = round_up(lut_elems(W, B) * sizeof(float), 256);
@@ -300,10 +300,12 @@ rq_status rq_logits(const rq_matrix* W, const float* h, int32_t B, float softcap
   uint64_t* keys = select ? reinterpret_cast<uint64_t*>(base + w.keys) : nullptr;
   hipError_t e;
   if (w.mm) {
-    e = rq::launch_mm_logits(W, w.mp, h, B, base + w.front, partial, stream);
+    e = rq::launch_mm_logits(W, w.mp, h, B, base + w.front, partial, out, softcap, keys, stream);
     if (e != hipSuccess) return launched(e, "rq_logits: matrix-core pass");
-    e = rq::launch_finish(partial, w.mp.G, B, W->rows, softcap, out, keys, stream);
-    if (e != hipSuccess) return launched(e, "rq_logits: finish");
+    if (w.mp.G > 1) {
+      e = rq::launch_finish(partial, w.mp.G, B, W->rows, softcap, out, keys, stream);
+      if (e != hipSuccess) return launched(e, "rq_logits: finish");
+    }
   } else {
     void* lut = base + w.front;
     e = rq::launch_build_lut(W, h, nullptr, RQ_PRO_NONE, B, 0, lut, stream);

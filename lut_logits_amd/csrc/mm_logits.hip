@@ -60,7 +60,10 @@ struct MmArgs {
   const uint16_t* cb;     // bf16 codebooks [NP][K][d]
   const uint16_t* codes;  // RQ_CODES_BLOCKED
   const u32x4* hp;        // [kParts][M][Bp] 8-bf16 vectors (zero past d and past B)
-  float* partial;         // [G][B][rows]
+  float* partial;         // [G][B][rows] (G > 1)
+  float* out;             // G == 1: logits [B][rows] after the softcap, or null
+  float softcap;          // G == 1: <= 0 for none
+  uint64_t* block_keys;   // G == 1: [B][S] best selection key per slab, or null
   int64_t rows;
   int K, M, NP, NQ, B, Bp, G, qpg, S;
 };
@@ -275,18 +278,52 @@ __global__ __launch_bounds__(kMmThreads) void mm_logits_kernel(MmArgs a) {
   }
 
   // acc[j][t][e] = z[batch bt*16NT + 16t + i16][row tile0 + 16j + 4kg + e]
+  if (a.G > 1) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int b = bt * n_bt + 16 * t + i16;
+      if (b >= a.B) continue;
+      float* dst = a.partial + ((size_t)g * a.B + b) * a.rows;
+#pragma unroll
+      for (int j = 0; j < T; ++j) {
+        const int64_t r = tile0 + 16 * j + 4 * kg;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (r + e < a.rows) dst[r + e] = acc[j][t][e];
+      }
+    }
+    return;
+  }
+  // G == 1: the sums are final -- softcap, store, best selection key of this
+  // slab for each hidden vector (the selection kernel reduces the S keys).
+  __shared__ unsigned long long s_keys[16 * NT];
+  if (tid < 16 * NT) s_keys[tid] = 0ull;
+  __syncthreads();
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int b = bt * n_bt + 16 * t + i16;
-    if (b >= a.B) continue;
-    float* dst = a.partial + ((size_t)g * a.B + b) * a.rows;
+    unsigned long long kbest = 0ull;
+    if (b < a.B) {
 #pragma unroll
-    for (int j = 0; j < T; ++j) {
-      const int64_t r = tile0 + 16 * j + 4 * kg;
+      for (int j = 0; j < T; ++j) {
+        const int64_t r = tile0 + 16 * j + 4 * kg;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (r + e < a.rows) dst[r + e] = acc[j][t][e];
+        for (int e = 0; e < 4; ++e) {
+          if (r + e >= a.rows) continue;
+          const float z = acc[j][t][e];
+          const float v = a.softcap > 0.0f ? a.softcap * tanhf(z / a.softcap) : z;
+          if (a.out) a.out[(size_t)b * a.rows + r + e] = v;
+          const unsigned long long k = select_key(v, (uint32_t)(r + e));
+          kbest = k > kbest ? k : kbest;
+        }
+      }
     }
+    if (kbest) atomicMax(&s_keys[16 * t + i16], kbest);   // LDS atomics, this workgroup only
+  }
+  __syncthreads();
+  if (a.block_keys && tid < 16 * NT) {
+    const int b = bt * n_bt + tid;
+    if (b < a.B) a.block_keys[(size_t)b * a.S + s] = s_keys[tid];
   }
 }
 
@@ -352,9 +389,10 @@ MmPlan plan_mm(const rq_matrix* W, int B) {
   p.S = (int)((W->rows + slab - 1) / slab);
   p.NQ = (W->L * W->M + pairs_per_block(W) - 1) / pairs_per_block(W);
   // Group count: workgroups run in rounds of one per CU; a round costs the
-  // blocks one workgroup handles (about 5.5 us per block for 16 waves' worth of
-  // 16x16 tiles, measured at the Gemma head), and every group beyond the first
-  // adds B*rows fp32 partial sums written and read back (at ~5 TB/s).
+  // blocks one workgroup handles (about 3.9 us per block for 8 waves of 16
+  // 16x16 tiles, fitted to this kernel at the Gemma head), and G > 1 adds the
+  // finish pass: G partial sums read and the logits written (~2.2 TB/s, plus a
+  // launch). With G == 1 the kernel writes the logits itself.
   int G = 1;
   double best = 1e30;
   for (int g = 1; g <= std::min(p.NQ, 64); g *= 2) {   // powers of two: g = index mod G keeps XCDs on their groups
@@ -362,8 +400,8 @@ MmPlan plan_mm(const rq_matrix* W, int B) {
     const int gg = (p.NQ + qpg - 1) / qpg;
     const int64_t wgs = (int64_t)gg * p.S * p.NBT;
     const double rounds = (double)((wgs + kCUs - 1) / kCUs);
-    const double per_block = 5.5 * (double)(p.T * p.NT) / 16.0 * (double)pairs_per_block(W) / 8.0;
-    const double cost = rounds * qpg * per_block + (gg > 1 ? (double)gg * B * W->rows * 8.0 / 5.0e6 : 0.0);
+    const double per_block = 3.9 * (double)(p.T * p.NT) / 16.0 * (double)pairs_per_block(W) / 8.0;
+    const double cost = rounds * qpg * per_block + (gg > 1 ? 5.0 + (double)(gg + 1) * B * W->rows * 4.0 / 2.2e6 : 0.0);
     if (cost < best * 0.999) { best = cost; G = gg; }
   }
 #ifdef RQ_TUNING
@@ -380,7 +418,7 @@ MmPlan plan_mm(const rq_matrix* W, int B) {
 size_t mm_hp_bytes(const rq_matrix* W, const MmPlan& p) { return (size_t)kParts * W->M * p.Bp * 16; }
 
 hipError_t launch_mm_logits(const rq_matrix* W, const MmPlan& p, const float* h, int B, void* hp, float* partial,
-                            hipStream_t stream) {
+                            float* out, float softcap, uint64_t* block_keys, hipStream_t stream) {
   const int n = W->M * p.Bp;
   hipLaunchKernelGGL(split_h_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, h, B, W->D, W->M, W->d,
                      p.Bp, static_cast<u32x4*>(hp));
@@ -391,6 +429,9 @@ hipError_t launch_mm_logits(const rq_matrix* W, const MmPlan& p, const float* h,
   a.codes = W->codes;
   a.hp = static_cast<const u32x4*>(hp);
   a.partial = partial;
+  a.out = out;
+  a.softcap = softcap;
+  a.block_keys = block_keys;
   a.rows = W->rows;
   a.K = W->K;
   a.M = W->M;

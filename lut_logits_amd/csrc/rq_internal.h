@@ -150,8 +150,11 @@ struct MmPlan {
 bool mm_supported(const rq_matrix* W);
 MmPlan plan_mm(const rq_matrix* W, int B);
 size_t mm_hp_bytes(const rq_matrix* W, const MmPlan& p);
+// G > 1: partial sums [G][B][rows] (then launch_finish). G == 1: the logits
+// after the softcap go to out (if not null) and the best selection key of each
+// slab to block_keys [B][S] (if not null).
 hipError_t launch_mm_logits(const rq_matrix* W, const MmPlan& p, const float* h, int B, void* hp, float* partial,
-                            hipStream_t stream);
+                            float* out, float softcap, uint64_t* block_keys, hipStream_t stream);
 
 hipError_t launch_decode_rows(const rq_matrix* W, const int32_t* ids, int n, int out_bf16, void* out,
                               int32_t* bad_ids, hipStream_t stream);

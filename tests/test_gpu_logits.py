@@ -120,3 +120,21 @@ def test_logits_ties_and_empty():
     assert np.array_equal(host(ti), np.tile(np.arange(5, dtype=np.int32), (16, 1)))
     lg0, _, _, _ = la.logits(W, torch.zeros((0, 96), device="cuda"), argmax=False)
     assert lg0.shape == (0, 5000)
+
+
+def test_logits_one_group_epilogue_topk():
+    """One code block (L*M = 8) leaves a single group, so the matrix-core kernel applies the softcap and
+    emits the selection keys itself (no finish pass): logits, argmax and top-k against the oracle."""
+    rng = np.random.default_rng(700)
+    mat = synth.gen_matrix(rng, 4000, 48, 8, 256, 1, (0.05,), "bf16")
+    h = synth.gen_hidden(rng, 24, 48)
+    W = to_dev(mat)
+    lg, am, ti, tv = la.logits(W, dev(h), softcap=30.0, topk=7)
+    g = host(lg)
+    _, ref = oracle_head(mat, h, 30.0)
+    check_logits(g, ref)
+    check_argmax(host(am), g, ref)
+    tol = 1e-5 * np.abs(ref).max(axis=1, keepdims=True) * np.ones_like(ref)
+    check_topk(g, host(ti), host(tv), host(am), ref, tol, 7)
+    _, am2, ti2, _ = la.logits(W, dev(h), softcap=30.0, logits=False, topk=7)
+    assert torch.equal(am, am2) and torch.equal(ti, ti2)
