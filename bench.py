@@ -311,7 +311,7 @@ def extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, dev):
     ts = timed(stress, 3, torch)
     res["stress"] = {"ms_per_call": ts, "vocab_rows_per_s": cs.V / (ts * 1e-3),
                      "code_stream_gbs": formats.code_bytes(cs.V, cs.L, cs.M) / (ts * 1e-3) / 1e9,
-                     "method": "table (bf16), 16-vector batch tiles"}
+                     "method": "table (bf16), several batch tiles staged from a batch-tiled copy"}
     del SW, slut, slg, sws
     return res
 

@@ -70,18 +70,28 @@ rq_status check_table_fits(const rq_matrix* W, int lut_bf16) {
 // Workspace of rq_lut_logits, in this order (each part 256-byte aligned):
 //   partial sums [G][B][rows] fp32 (G > 1 only), a logits scratch [B][rows]
 //   fp32 (top-k without a logits output), the per-block selection keys
-//   [B][key_blocks] uint64 and the top-k candidates [B][nblk][topk] uint64.
+//   [B][key_blocks] uint64, the top-k candidates [B][nblk][topk] uint64 and,
+//   with more than one batch tile, the batch-tiled copy of the table.
 struct LogitsWs {
-  size_t partial, scratch, keys, cand, total;
+  size_t partial, scratch, keys, cand, tiled, total;
 };
 
-LogitsWs logits_ws(const rq_matrix* W, const rq::GatherPlan& plan, int32_t B, int32_t topk, bool logits_out) {
+// Bytes of the batch-tiled copy of the table (launch_tile_lut) that a plan
+// with more than one batch tile stages from; 0 otherwise.
+size_t tiled_bytes(const rq_matrix* W, const rq::GatherPlan& plan, bool lut_bf16) {
+  if (plan.NBT <= 1) return 0;
+  return round_up((size_t)plan.NBT * W->L * W->M * W->K * plan.BT * (lut_bf16 ? 2 : 4), 256);
+}
+
+LogitsWs logits_ws(const rq_matrix* W, const rq::GatherPlan& plan, int32_t B, int32_t topk, bool logits_out,
+                   bool lut_bf16) {
   LogitsWs w;
   w.partial = 0;
   w.scratch = w.partial + (plan.G > 1 ? round_up((size_t)plan.G * B * W->rows * sizeof(float), 256) : 0);
   w.keys = w.scratch + (topk > 0 && !logits_out ? round_up((size_t)B * W->rows * sizeof(float), 256) : 0);
   w.cand = w.keys + round_up((size_t)B * rq::key_blocks(plan, W->rows) * sizeof(uint64_t), 256);
-  w.total = w.cand + (topk > 0 ? round_up((size_t)B * rq::epi_blocks(W->rows) * topk * sizeof(uint64_t), 256) : 0);
+  w.tiled = w.cand + (topk > 0 ? round_up((size_t)B * rq::epi_blocks(W->rows) * topk * sizeof(uint64_t), 256) : 0);
+  w.total = w.tiled + tiled_bytes(W, plan, lut_bf16);
   return w;
 }
 
@@ -190,7 +200,7 @@ size_t rq_lut_logits_workspace(const rq_matrix* W, int32_t B, int32_t topk, int3
   if (B == 0 || W->rows == 0) return 0;
   const rq::GatherPlan plan = rq::plan_gather(W, B, lut_dtype == RQ_BF16);
   if (plan.BT == 0) return 0;
-  return logits_ws(W, plan, B, topk, false).total;   // enough with or without a logits output
+  return logits_ws(W, plan, B, topk, false, lut_dtype == RQ_BF16).total;   // enough with or without a logits output
 }
 
 rq_status rq_lut_logits(const rq_matrix* W, const void* lut, int32_t lut_dtype, int32_t B, float softcap,
@@ -209,7 +219,7 @@ rq_status rq_lut_logits(const rq_matrix* W, const void* lut, int32_t lut_dtype, 
     return fail(RQ_ERR_ALIGN, "output misaligned");
   const rq::GatherPlan plan = rq::plan_gather(W, B, lut_dtype == RQ_BF16);
   if (plan.BT == 0) return fail(RQ_ERR_SHAPE, "no table tiling fits on chip for K=%d", W->K);
-  const LogitsWs w = logits_ws(W, plan, B, topk, logits != nullptr);
+  const LogitsWs w = logits_ws(W, plan, B, topk, logits != nullptr, lut_dtype == RQ_BF16);
   if (!ws || ws_bytes < w.total) return fail(RQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, w.total);
   if (!aligned(ws, 256)) return fail(RQ_ERR_ALIGN, "workspace must be 256-byte aligned");
   char* base = static_cast<char*>(ws);
@@ -219,6 +229,13 @@ rq_status rq_lut_logits(const rq_matrix* W, const void* lut, int32_t lut_dtype, 
   o.out = logits ? logits : (topk > 0 ? reinterpret_cast<float*>(base + w.scratch) : nullptr);
   o.softcap = softcap;
   o.block_keys = select ? reinterpret_cast<uint64_t*>(base + w.keys) : nullptr;
+  o.lut_tiled = 0;
+  if (plan.NBT > 1) {   // several batch tiles: stage from a batch-tiled copy with 16-byte copies
+    hipError_t et = rq::launch_tile_lut(lut, lut_dtype == RQ_BF16, W->L * W->M, W->K, B, plan.BT, base + w.tiled, stream);
+    if (et != hipSuccess) return launched(et, "rq_lut_logits: table tiling");
+    lut = base + w.tiled;
+    o.lut_tiled = 1;
+  }
   hipError_t e = rq::launch_gather(W, plan, lut, lut_dtype == RQ_BF16, B, o, stream);
   if (e != hipSuccess) return launched(e, "rq_lut_logits: lookup+sum");
   if (!select) return RQ_OK;
@@ -229,13 +246,15 @@ rq_status rq_lut_logits(const rq_matrix* W, const void* lut, int32_t lut_dtype, 
 
 // Workspace of rq_logits. Matrix-core method: the split hidden vectors, then
 // the partial sums [G][B][rows]; table method: the fp32 table [L][M][K][B], then
-// the partial sums of the lookup+sum. Both end with the logits scratch (top-k
-// without a logits output), the selection keys and the top-k candidates.
+// the partial sums of the lookup+sum. Both continue with the logits scratch
+// (top-k without a logits output), the selection keys and the top-k
+// candidates; the table method with several batch tiles ends with the
+// batch-tiled copy of the table.
 struct HeadWs {
   bool mm;
   rq::MmPlan mp;
   rq::GatherPlan gp;
-  size_t front, partial, scratch, keys, cand, total;
+  size_t front, partial, scratch, keys, cand, tiled, total;
   int nkb;
 };
 
@@ -258,7 +277,8 @@ HeadWs head_ws(const rq_matrix* W, int32_t B, int32_t topk, bool logits_out) {
   w.scratch = w.partial + round_up(partial_bytes, 256);
   w.keys = w.scratch + (topk > 0 && !logits_out ? round_up((size_t)B * W->rows * sizeof(float), 256) : 0);
   w.cand = w.keys + round_up((size_t)B * w.nkb * sizeof(uint64_t), 256);
-  w.total = w.cand + (topk > 0 ? round_up((size_t)B * rq::epi_blocks(W->rows) * topk * sizeof(uint64_t), 256) : 0);
+  w.tiled = w.cand + (topk > 0 ? round_up((size_t)B * rq::epi_blocks(W->rows) * topk * sizeof(uint64_t), 256) : 0);
+  w.total = w.tiled + (w.mm ? 0 : tiled_bytes(W, w.gp, false));
   return w;
 }
 
@@ -315,6 +335,13 @@ rq_status rq_logits(const rq_matrix* W, const float* h, int32_t B, float softcap
     o.out = out;
     o.softcap = softcap;
     o.block_keys = keys;
+    o.lut_tiled = 0;
+    if (w.gp.NBT > 1) {
+      e = rq::launch_tile_lut(lut, 0, W->L * W->M, W->K, B, w.gp.BT, base + w.tiled, stream);
+      if (e != hipSuccess) return launched(e, "rq_logits: table tiling");
+      lut = base + w.tiled;
+      o.lut_tiled = 1;
+    }
     e = rq::launch_gather(W, w.gp, lut, 0, B, o, stream);
     if (e != hipSuccess) return launched(e, "rq_logits: lookup+sum");
   }
@@ -339,11 +366,12 @@ rq_status rq_decode_rows(const rq_matrix* W, const int32_t* ids, int32_t n, int3
 
 // Workspace of rq_lut_matvec. Fused table build (one activation vector, fp32
 // codebooks, d in {1, 2, 4}): the partial sums [G][rows]. Otherwise: the fp32
-// table [L][M][K][B], then the partial sums [G][B][rows] (G > 1).
+// table [L][M][K][B], the partial sums [G][B][rows] (G > 1) and, with more
+// than one batch tile, the batch-tiled copy of the table.
 struct MatvecWs {
   bool fused;
   rq::GatherPlan plan;
-  size_t front, partial, total;
+  size_t front, partial, tiled, total;
 };
 
 MatvecWs matvec_ws(const rq_matrix* W, int32_t B) {
@@ -356,7 +384,8 @@ MatvecWs matvec_ws(const rq_matrix* W, int32_t B) {
   if (!m.fused) m.plan = rq::plan_gather(W, B, 0);
   m.front = 0;
   m.partial = m.fused ? 0 : round_up(lut_elems(W, B) * sizeof(float), 256);
-  m.total = m.partial + (m.plan.G > 1 ? round_up((size_t)m.plan.G * B * W->rows * sizeof(float), 256) : 0);
+  m.tiled = m.partial + (m.plan.G > 1 ? round_up((size_t)m.plan.G * B * W->rows * sizeof(float), 256) : 0);
+  m.total = m.tiled + (m.fused ? 0 : tiled_bytes(W, m.plan, false));
   return m;
 }
 
@@ -385,6 +414,7 @@ rq_status rq_lut_matvec(const rq_matrix* W, const float* x, const float* x2, int
   o.out = y;
   o.softcap = 0.0f;
   o.block_keys = nullptr;
+  o.lut_tiled = 0;
   hipError_t e;
   if (m.fused)
     return launched(rq::launch_gather(W, m.plan, nullptr, 0, B, o, stream, x,
@@ -393,6 +423,12 @@ rq_status rq_lut_matvec(const rq_matrix* W, const float* x, const float* x2, int
   float* lut = reinterpret_cast<float*>(base + m.front);
   e = rq::launch_build_lut(W, x, x2, prologue, B, 0, lut, stream);
   if (e != hipSuccess) return launched(e, "rq_lut_matvec: table build");
+  if (m.plan.NBT > 1) {
+    e = rq::launch_tile_lut(lut, 0, W->L * W->M, W->K, B, m.plan.BT, base + m.tiled, stream);
+    if (e != hipSuccess) return launched(e, "rq_lut_matvec: table tiling");
+    lut = reinterpret_cast<float*>(base + m.tiled);
+    o.lut_tiled = 1;
+  }
   return launched(rq::launch_gather(W, m.plan, lut, 0, B, o, stream), "rq_lut_matvec: lookup+sum");
 }
 

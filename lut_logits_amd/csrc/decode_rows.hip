@@ -31,9 +31,10 @@ __device__ __forceinline__ void out_store<float>(float* p, float v) { *p = v; }
 template <>
 __device__ __forceinline__ void out_store<uint16_t>(uint16_t* p, float v) { *p = f32_to_bf16(v); }
 
-// One thread per (requested row, subspace): it loads the L codes of its
-// subspace, then the L codewords, so every load of the row is in flight at
-// once (two dependent round trips per call, whatever D is).
+// One thread per output element (requested row i, subspace m, component j):
+// it loads the row id, then the L codes of its subspace, then its L codebook
+// entries, so a call is three dependent round trips whatever D is, and
+// consecutive threads store consecutive elements.
 template <typename CbT, typename OutT>
 __global__ __launch_bounds__(kDecodeThreads) void decode_rows_kernel(CodeView cv, const CbT* __restrict__ cb,
                                                                      int64_t rows, int D, int M, int d, int K,
@@ -41,33 +42,32 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_rows_kernel(CodeView cv
                                                                      OutT* __restrict__ out,
                                                                      int32_t* __restrict__ bad) {
   const int64_t t = (int64_t)blockIdx.x * kDecodeThreads + threadIdx.x;
-  if (t >= (int64_t)n * M) return;
-  const int i = (int)(t / M);
-  const int m = (int)(t - (int64_t)i * M);
+  if (t >= (int64_t)n * D) return;
+  const int i = (int)(t / D);
+  const int e = (int)(t - (int64_t)i * D);
+  const int m = e / d;
+  const int j = e - m * d;
   const int64_t id = ids[i];
   const bool ok = id >= 0 && id < rows;
-  if (!ok && m == 0 && bad) atomicAdd(bad, 1);
-  OutT* dst = out + (size_t)i * D + (size_t)m * d;
   if (!ok) {
-    for (int j = 0; j < d; ++j) out_store(dst + j, 0.0f);
+    if (e == 0 && bad) atomicAdd(bad, 1);
+    out_store(out + t, 0.0f);
     return;
   }
   constexpr int kMaxL = RQ_MAX_L;
   uint32_t code[kMaxL];
 #pragma unroll
-  for (int l = 0; l < kMaxL; ++l) {
-    if (l >= L) break;
-    code[l] = code_at(cv, id, l * M + m);
-  }
-  for (int j = 0; j < d; ++j) {
-    double s = 0.0;
+  for (int l = 0; l < kMaxL; ++l)
+    if (l < L) code[l] = code_at(cv, id, l * M + m);
+  double v[kMaxL];
 #pragma unroll
-    for (int l = 0; l < kMaxL; ++l) {
-      if (l >= L) break;
-      s += cb_value(cb + ((size_t)(l * M + m) * K + code[l]) * d + j);
-    }
-    out_store(dst + j, (float)s);
-  }
+  for (int l = 0; l < kMaxL; ++l)
+    if (l < L) v[l] = cb_value(cb + ((size_t)(l * M + m) * K + code[l]) * d + j);
+  double s = 0.0;
+#pragma unroll
+  for (int l = 0; l < kMaxL; ++l)
+    if (l < L) s += v[l];
+  out_store(out + t, (float)s);
 }
 
 // codes[r][p] (uint16, [rows][NP]) -> blocks[q][r] = codes[r][8q .. 8q+8) (16 bytes,
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256) void pack_codes10_kernel(const uint16_t* __res
 
 template <typename CbT, typename OutT>
 hipError_t decode_typed(const rq_matrix* W, const int32_t* ids, int n, void* out, int32_t* bad, hipStream_t stream) {
-  const int64_t threads = (int64_t)n * W->M;
+  const int64_t threads = (int64_t)n * W->D;
   const unsigned blocks = (unsigned)((threads + kDecodeThreads - 1) / kDecodeThreads);
   hipLaunchKernelGGL((decode_rows_kernel<CbT, OutT>), dim3(blocks), dim3(kDecodeThreads), 0, stream, code_view(W),
                      static_cast<const CbT*>(W->codebooks), W->rows, W->D, W->M, W->d, W->K, W->L, ids, n,

@@ -58,6 +58,7 @@ struct GatherArgs {
   float* out;                 // [B][rows] or null (G == 1)
   float softcap;              // <= 0: none
   uint64_t* block_keys;       // [B][S] best selection key per slab, or null (G == 1)
+  int tiled;                  // lut is batch-tiled [NBT][NP][K][BT] (launch_tile_lut)
 };
 
 // Lookup of BQ consecutive batch entries of one table row, accumulated in fp32.
@@ -274,7 +275,8 @@ void gather_kernel(GatherArgs a) {
   const uint32_t blk_bytes = (uint32_t)(a.cv.s_blk * 2);
   const int steps = a.steps;
 
-  const LutT* lut = static_cast<const LutT*>(a.lut);
+  // batch-tiled table: this tile's [NP][K][BT] slice is contiguous
+  const LutT* lut = static_cast<const LutT*>(a.lut) + (a.tiled ? (size_t)bt * a.NP * a.K * BT : 0);
   const int pa = g * a.cpg * a.P;                       // this group's pairs [pa, pb)
   const int pb = min(a.NP, (g * a.cpg + a.cpg) * a.P);
 
@@ -344,7 +346,7 @@ void gather_kernel(GatherArgs a) {
       const int n4n = min(a.P, a.NP - cn * a.P) * words_per_pair;
       chunk_to_regs(nxt, lut4 + (size_t)cn * a.P * words_per_pair, tid, n4n - 1);
     } else {
-      stage_chunk<LutT, BT>(tab, lut, p0, pc, a.K, a.B, b0);
+      stage_chunk<LutT, BT>(tab, lut, p0, pc, a.K, a.tiled ? BT : a.B, a.tiled ? 0 : b0);
     }
     __syncthreads();
   };
@@ -427,7 +429,7 @@ void gather_kernel(GatherArgs a) {
 template <typename LutT, int BT, int NSTEP, int FD = 0, bool PK = false>
 hipError_t launch_gather_typed(const GatherArgs& a, const GatherPlan& plan, hipStream_t stream) {
   const size_t chunk_bytes = (size_t)plan.P * a.K * BT * sizeof(LutT);
-  const bool reg = a.B == BT && chunk_bytes % 16 == 0 && chunk_bytes <= (size_t)kRegStage * 16 * kGatherThreads &&
+  const bool reg = (a.B == BT || a.tiled) && chunk_bytes % 16 == 0 && chunk_bytes <= (size_t)kRegStage * 16 * kGatherThreads &&
                    ((size_t)a.K * BT * sizeof(LutT)) % 16 == 0;
   auto kern = FD ? gather_kernel<LutT, BT, NSTEP, true, FD, PK>
                  : (reg ? gather_kernel<LutT, BT, NSTEP, true, 0, PK> : gather_kernel<LutT, BT, NSTEP, false, 0, PK>);
@@ -554,6 +556,26 @@ __global__ __launch_bounds__(kFinishThreads) void finish_kernel(const float* __r
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelCap = 4096;
+
+// Argmax alone: one wave per batch entry takes the largest of the blocks' best
+// keys (no LDS, no barrier).
+__global__ __launch_bounds__(64) void argmax_kernel(const uint64_t* __restrict__ block_keys, int nkb,
+                                                    int32_t* __restrict__ argmax) {
+  const int b = blockIdx.x;
+  const uint64_t* src = block_keys + (size_t)b * nkb;
+  uint64_t best = 0;
+  int i = threadIdx.x;
+  for (; i + 192 < nkb; i += 256) {   // four loads in flight
+    const uint64_t k0 = src[i], k1 = src[i + 64], k2 = src[i + 128], k3 = src[i + 192];
+    best = k0 > best ? k0 : best;
+    best = k1 > best ? k1 : best;
+    best = k2 > best ? k2 : best;
+    best = k3 > best ? k3 : best;
+  }
+  for (; i < nkb; i += 64) best = src[i] > best ? src[i] : best;
+  best = wave_max_u64(best);
+  if (threadIdx.x == 0) argmax[b] = (int32_t)key_index(best);
+}
 
 // Per batch entry: argmax from the blocks' best keys; top-k by merging the
 // blocks' candidates through a 4096-key LDS buffer that always keeps the best k.
@@ -778,6 +800,32 @@ hipError_t dispatch_gather(const GatherArgs& a, const GatherPlan& plan, int d, i
   return launch_gather_typed<float, 16, 4, 0, PK>(a, plan, stream);
 }
 
+template <typename T>
+__global__ void tile_lut_kernel(const T* __restrict__ src, int64_t NPK, int B, int BT, int NBT, T* __restrict__ dst) {
+  // one thread per (row of the table, batch tile): BT consecutive entries
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= NPK * NBT) return;
+  const int t = (int)(i % NBT);
+  const int64_t pk = i / NBT;
+  const T* s = src + pk * B + (int64_t)t * BT;
+  T* d = dst + ((int64_t)t * NPK + pk) * BT;
+  for (int j = 0; j < BT; ++j) d[j] = (t * BT + j < B) ? s[j] : (T)0;
+}
+
+hipError_t launch_tile_lut(const void* lut, int lut_bf16, int NP, int K, int B, int BT, void* dst, hipStream_t stream) {
+  const int NBT = (B + BT - 1) / BT;
+  const int64_t NPK = (int64_t)NP * K;
+  const int64_t n = NPK * NBT;
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  if (lut_bf16)
+    hipLaunchKernelGGL(tile_lut_kernel<uint16_t>, dim3(blocks), dim3(256), 0, stream, static_cast<const uint16_t*>(lut), NPK,
+                       B, BT, NBT, static_cast<uint16_t*>(dst));
+  else
+    hipLaunchKernelGGL(tile_lut_kernel<float>, dim3(blocks), dim3(256), 0, stream, static_cast<const float*>(lut), NPK, B,
+                       BT, NBT, static_cast<float*>(dst));
+  return hipGetLastError();
+}
+
 bool fused_build_supported(const rq_matrix* W, int B) {
   return B == 1 && W->cb_dtype == RQ_F32 && (W->d == 1 || W->d == 2 || W->d == 4) &&
          ((uintptr_t)W->codebooks % 16) == 0 && ((size_t)W->K * W->d) % 4 == 0;
@@ -802,6 +850,7 @@ hipError_t launch_gather(const rq_matrix* W, const GatherPlan& plan, const void*
   a.out = o.out;
   a.softcap = o.softcap;
   a.block_keys = plan.G == 1 ? o.block_keys : nullptr;
+  a.tiled = o.lut_tiled;
   hipError_t e = W->codes_layout == RQ_CODES_PACKED10 ? dispatch_gather<true>(a, plan, W->d, lut_bf16, fused_act != nullptr, stream)
                                                         : dispatch_gather<false>(a, plan, W->d, lut_bf16, fused_act != nullptr, stream);
   if (e != hipSuccess || plan.G == 1) return e;
@@ -846,6 +895,11 @@ hipError_t launch_select(const uint64_t* block_keys, int nkb, int B, int32_t* ar
                        rows, topk, cand);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+  }
+  if (topk <= 0) {
+    if (!argmax) return hipSuccess;
+    hipLaunchKernelGGL(argmax_kernel, dim3((unsigned)B), dim3(64), 0, stream, block_keys, nkb, argmax);
+    return hipGetLastError();
   }
   hipLaunchKernelGGL(select_kernel, dim3((unsigned)B), dim3(kSelThreads), 0, stream, block_keys, nkb, argmax, ncb,
                      cand, topk, topk_ids, topk_vals);

@@ -108,7 +108,11 @@ struct GatherOut {
   float* out;            // [B][rows] results after the softcap, or null
   float softcap;         // <= 0: none
   uint64_t* block_keys;  // [B][key_blocks()] best selection key per block of rows, or null
+  int lut_tiled;         // the table is in the batch-tiled layout of launch_tile_lut
 };
+// Table [NP][K][B] -> batch-tiled [ceil(B/BT)][NP][K][BT] (zero past B), so that
+// a batch tile's chunk of pairs is contiguous and stages with 16-byte copies.
+hipError_t launch_tile_lut(const void* lut, int lut_bf16, int NP, int K, int B, int BT, void* dst, hipStream_t stream);
 // The lookup+sum pass: the gather kernel, and for G > 1 the finish kernel that
 // adds the partial sums in group order.
 // One-shot events around the next lookup+sum launch of this thread (rq_set_stage_events).
