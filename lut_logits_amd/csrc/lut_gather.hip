@@ -174,10 +174,10 @@ __device__ __forceinline__ void chunk_to_regs(ChunkRegs& r, const u32x4* __restr
 // are computed with the same fmaf chain as the table-build kernel and written
 // to LDS. act sits in LDS after the chunk.
 template <int FD>
-__device__ __forceinline__ void fused_word(const u32x4 w, int i, float* tab, const float* act_s, int p0, int K, int M) {
+__device__ __forceinline__ void fused_word(const u32x4 w, int i, float* tab, const float* act_s, int pl0, int K) {
   constexpr int EPW = 4 / FD;
   const int e0 = i * EPW;                 // entry index within the chunk: (pair - p0) * K + k
-  const int m = (p0 + e0 / K) % M;
+  const int pl = pl0 + e0 / K;            // the pair's index within the group (its activation slice)
   float v[EPW];
 #pragma unroll
   for (int t = 0; t < EPW; ++t) {
@@ -187,7 +187,7 @@ __device__ __forceinline__ void fused_word(const u32x4 w, int i, float* tab, con
       // element to a scalar first: hipcc folds __builtin_bit_cast of a vector
       // element to element 0
       const uint32_t bits = w[t * FD + j];
-      acc = fmaf(act_s[m * FD + j], __uint_as_float(bits), acc);
+      acc = fmaf(act_s[pl * FD + j], __uint_as_float(bits), acc);
     }
     v[t] = acc;
   }
@@ -197,16 +197,16 @@ __device__ __forceinline__ void fused_word(const u32x4 w, int i, float* tab, con
 }
 template <int FD>
 __device__ __forceinline__ void regs_to_lds_fused(const ChunkRegs& r, float* tab, const float* act_s, int tid,
-                                                  int last, int p0, int K, int M) {
+                                                  int last, int pl0, int K) {
   const int T = kGatherThreads;
-  fused_word<FD>(r.w0, min(tid, last), tab, act_s, p0, K, M);
-  fused_word<FD>(r.w1, min(tid + T, last), tab, act_s, p0, K, M);
-  fused_word<FD>(r.w2, min(tid + 2 * T, last), tab, act_s, p0, K, M);
-  fused_word<FD>(r.w3, min(tid + 3 * T, last), tab, act_s, p0, K, M);
-  fused_word<FD>(r.w4, min(tid + 4 * T, last), tab, act_s, p0, K, M);
-  fused_word<FD>(r.w5, min(tid + 5 * T, last), tab, act_s, p0, K, M);
-  fused_word<FD>(r.w6, min(tid + 6 * T, last), tab, act_s, p0, K, M);
-  fused_word<FD>(r.w7, min(tid + 7 * T, last), tab, act_s, p0, K, M);
+  fused_word<FD>(r.w0, min(tid, last), tab, act_s, pl0, K);
+  fused_word<FD>(r.w1, min(tid + T, last), tab, act_s, pl0, K);
+  fused_word<FD>(r.w2, min(tid + 2 * T, last), tab, act_s, pl0, K);
+  fused_word<FD>(r.w3, min(tid + 3 * T, last), tab, act_s, pl0, K);
+  fused_word<FD>(r.w4, min(tid + 4 * T, last), tab, act_s, pl0, K);
+  fused_word<FD>(r.w5, min(tid + 5 * T, last), tab, act_s, pl0, K);
+  fused_word<FD>(r.w6, min(tid + 6 * T, last), tab, act_s, pl0, K);
+  fused_word<FD>(r.w7, min(tid + 7 * T, last), tab, act_s, pl0, K);
 }
 
 __device__ __forceinline__ void regs_to_lds(const ChunkRegs& r, u32x4* dst, int tid, int last) {
@@ -318,10 +318,15 @@ void gather_kernel(GatherArgs a) {
   const u32x4* lut4 = reinterpret_cast<const u32x4*>(lut);
   // REG: 16-byte words per pair (of the table, or with FD of the codebook)
   const int words_per_pair = FD ? a.K * FD / 4 : a.K * BT * (int)sizeof(LutT) / 16;
-  // FD: the activation vector goes to LDS after the chunk, once
+  // FD: the activation slices of this group's pairs [pa, pb) go to LDS after
+  // the chunk, once (pair p uses elements (p % M)*FD .. +FD of the vector)
   float* act_s = reinterpret_cast<float*>(smem + (size_t)a.P * a.K * sizeof(float));
   if (FD)
-    for (int i = tid; i < a.D; i += kGatherThreads) act_s[i] = a.act2 ? gelu_tanh(a.act[i]) * a.act2[i] : a.act[i];
+    for (int i = tid; i < (pb - pa) * FD; i += kGatherThreads) {
+      const int p = pa + i / (FD ? FD : 1);
+      const int src = (p % a.M) * FD + (i - (p - pa) * FD);
+      act_s[i] = a.act2 ? gelu_tanh(a.act[src]) * a.act2[src] : a.act[src];
+    }
   // REG: chunk c's words go to registers with a fixed count of unconditional
   // loads (clamped to the last word of the chunk).
   if (REG) {
@@ -338,8 +343,8 @@ void gather_kernel(GatherArgs a) {
       // words past the chunk were loaded clamped to its last word, so writing
       // them clamped stores that same value again
       if (FD)
-        regs_to_lds_fused<FD ? FD : 1>(nxt, reinterpret_cast<float*>(tab), act_s, tid, pc * words_per_pair - 1, p0, a.K,
-                                       a.M);
+        regs_to_lds_fused<FD ? FD : 1>(nxt, reinterpret_cast<float*>(tab), act_s, tid, pc * words_per_pair - 1, p0 - pa,
+                                       a.K);
       else
         regs_to_lds(nxt, reinterpret_cast<u32x4*>(tab), tid, pc * words_per_pair - 1);
       const int cn = min(c + 1, c_end - 1);
@@ -428,11 +433,15 @@ void gather_kernel(GatherArgs a) {
 
 template <typename LutT, int BT, int NSTEP, int FD = 0, bool PK = false>
 hipError_t launch_gather_typed(const GatherArgs& a, const GatherPlan& plan, hipStream_t stream) {
+  if (plan.steps < 1 || plan.steps > NSTEP) return hipErrorInvalidValue;   // a lane holds NSTEP rows at most
   const size_t chunk_bytes = (size_t)plan.P * a.K * BT * sizeof(LutT);
   const bool reg = (a.B == BT || a.tiled) && chunk_bytes % 16 == 0 && chunk_bytes <= (size_t)kRegStage * 16 * kGatherThreads &&
                    ((size_t)a.K * BT * sizeof(LutT)) % 16 == 0;
-  auto kern = FD ? gather_kernel<LutT, BT, NSTEP, true, FD, PK>
-                 : (reg ? gather_kernel<LutT, BT, NSTEP, true, 0, PK> : gather_kernel<LutT, BT, NSTEP, false, 0, PK>);
+  void (*kern)(GatherArgs);
+  if constexpr (FD != 0)
+    kern = gather_kernel<LutT, BT, NSTEP, true, FD, PK>;
+  else
+    kern = reg ? gather_kernel<LutT, BT, NSTEP, true, 0, PK> : gather_kernel<LutT, BT, NSTEP, false, 0, PK>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget);
   if (e != hipSuccess) return e;
   hipEvent_t before, after;
@@ -656,7 +665,7 @@ namespace {
 // LDS lookups run at ~9 per clock per CU (quad-contiguous 64-byte lookups at
 // ~120 B/clock); G > 1 adds the partial-sum traffic and a finish launch.
 double plan_cost_us(int64_t rows, int NP, int K, int B, int es, int BT, int P, int steps, int G, int cpg,
-                    int stage_es) {
+                    int stage_es, int lane_steps) {
   const int QL = BT >= 16 ? 4 : 1;
   const int rps = kGatherThreads / QL;
   const int64_t S = (rows + (int64_t)steps * rps - 1) / ((int64_t)steps * rps);
@@ -671,7 +680,9 @@ double plan_cost_us(int64_t rows, int NP, int K, int B, int es, int BT, int P, i
   const double per_cu_bw = std::min(150e3, 6.4e6 / (double)active);          // bytes per us
   const double t_codes = slab_rows * pairs * 2.0 / per_cu_bw;
   const double lookups_per_us = BT == 1 ? 9.0 * 2400.0 : (120.0 * 2400.0) / (BT * es);
-  const double t_look = slab_rows * pairs / lookups_per_us;
+  // every lane looks up all lane_steps rows of its kernel, also those past
+  // the slab or the last row
+  const double t_look = (double)lane_steps * rps * pairs / lookups_per_us;
   const double t_wg = t_stage + std::max(t_codes, t_look);
   const double t_stream = (double)rows * NP * 2.0 * NBT / 6.4e6;
   const double t_partial = G > 1 ? 5.0 + (double)G * B * rows * 8.0 / 6.4e6 : 0.0;
@@ -681,8 +692,20 @@ double plan_cost_us(int64_t rows, int NP, int K, int B, int es, int BT, int P, i
 // fused_d > 0: the table is built while staging from fp32 codebooks of
 // subspace width fused_d (B == 1): a chunk's staged bytes are its codebook
 // rows (4*fused_d per entry, at most 128 KB so they fit the staging
-// registers), and the activation vector (D floats) shares the LDS.
-GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16, int fused_d, int D, int ppb) {
+// registers), and the activation slices of the group's pairs share the LDS.
+// Fused d = 2 (the Gemma MLP) has kernels for 2, 3 and 4 rows per lane, so
+// that a slab can cover a short matrix's rows with few idle lanes (more rows
+// per lane spill at 128 VGPRs).
+size_t fused_act_bytes(int P, int cpg, int NP, int fused_d) {
+  return fused_d ? (size_t)std::min(cpg * P, NP) * fused_d * 4 : 0;
+}
+
+bool steps_allowed(int steps, int fused_d) {
+  if (fused_d == 2) return steps >= 2 && steps <= 4;
+  return steps >= 1 && steps <= 4;
+}
+
+GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16, int fused_d, int ppb) {
   const int es = lut_bf16 ? 2 : 4;
   const int stage_es = fused_d ? 4 * fused_d : es;
   GatherPlan best{};
@@ -696,8 +719,7 @@ GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16, int fus
   const int NBT = (B + BT - 1) / BT;
   int pmax = (int)std::min<int64_t>(NP, kLdsBudget / ((size_t)K * BT * es));
   if (fused_d) {
-    const int64_t lds_left = (int64_t)kLdsBudget - (int64_t)D * 4;
-    pmax = (int)std::min<int64_t>({(int64_t)NP, lds_left / ((int64_t)K * 4),
+    pmax = (int)std::min<int64_t>({(int64_t)NP, (int64_t)kLdsBudget / ((int64_t)K * 4),
                                    (int64_t)kRegStage * 16 * kGatherThreads / ((int64_t)K * stage_es)});
     if (pmax < 1) return best;
   }
@@ -714,6 +736,7 @@ GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16, int fus
     ++tried;
     const int chunks = (NP + P - 1) / P;
     for (int steps = nstep; steps >= 1; --steps) {
+      if (!steps_allowed(steps, fused_d)) continue;
       const int64_t S = (rows + (int64_t)steps * rps - 1) / ((int64_t)steps * rps);
       if (S * NBT > (1 << 24)) continue;
       const int64_t gmax = std::max<int64_t>(1, std::min<int64_t>(chunks, 4 * kCUs / (S * NBT) + 1));
@@ -721,8 +744,10 @@ GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16, int fus
         const int cpg = (int)((chunks + G0 - 1) / G0);
         const int G = (chunks + cpg - 1) / cpg;
         if (G != G0) continue;
+        if ((size_t)P * K * 4 + fused_act_bytes(P, cpg, NP, fused_d) > (size_t)kLdsBudget && fused_d) continue;
         // prefer aligned chunks (staging outside the block loop) on near-ties
-        const double cost = plan_cost_us(rows, NP, K, B, es, BT, P, steps, G, cpg, stage_es) *
+        const int lane_steps = fused_d == 2 ? steps : nstep;   // the kernel instances (dispatch_gather)
+        const double cost = plan_cost_us(rows, NP, K, B, es, BT, P, steps, G, cpg, stage_es, lane_steps) *
                             ((P % ppb == 0 || chunks == 1) ? 1.0 : 1.03);
         if (cost < best_cost * 0.999) {
           best_cost = cost;
@@ -732,7 +757,7 @@ GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16, int fus
       }
     }
   }
-  best.lds = (size_t)best.P * K * BT * es + (fused_d ? (size_t)D * 4 : 0);
+  best.lds = (size_t)best.P * K * BT * es + fused_act_bytes(best.P, best.cpg, NP, fused_d);
   return best;
 }
 
@@ -740,10 +765,10 @@ GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16, int fus
 // off the per-call path.
 struct PlanKey {
   int64_t rows;
-  int NP, K, B, bf16, fused_d, D, ppb;
+  int NP, K, B, bf16, fused_d, ppb;
   bool operator==(const PlanKey& o) const {
     return rows == o.rows && NP == o.NP && K == o.K && B == o.B && bf16 == o.bf16 && fused_d == o.fused_d &&
-           D == o.D && ppb == o.ppb;
+           ppb == o.ppb;
   }
 };
 std::mutex g_plan_mu;
@@ -759,7 +784,7 @@ int g_plan_n = 0, g_plan_next = 0;
 // (partial-sum traffic) and long slabs (loads in flight per lane).
 GatherPlan plan_gather(const rq_matrix* W, int B, int lut_bf16, int fused) {
   const int fd = fused ? W->d : 0;
-  const PlanKey key{W->rows, W->L * W->M, W->K, B, lut_bf16, fd, fused ? W->D : 0, pairs_per_block(W)};
+  const PlanKey key{W->rows, W->L * W->M, W->K, B, lut_bf16, fd, pairs_per_block(W)};
   GatherPlan plan{};
   bool hit = false;
   {
@@ -768,7 +793,7 @@ GatherPlan plan_gather(const rq_matrix* W, int B, int lut_bf16, int fused) {
       if (g_plan_keys[i] == key) { plan = g_plans[i]; hit = true; break; }
   }
   if (!hit) {
-    plan = search_plan(key.rows, key.NP, key.K, B, lut_bf16, fd, key.D, key.ppb);
+    plan = search_plan(key.rows, key.NP, key.K, B, lut_bf16, fd, key.ppb);
     std::lock_guard<std::mutex> lock(g_plan_mu);
     g_plan_keys[g_plan_next] = key;
     g_plans[g_plan_next] = plan;
@@ -777,7 +802,7 @@ GatherPlan plan_gather(const rq_matrix* W, int B, int lut_bf16, int fused) {
   }
 #ifdef RQ_TUNING
   if (tuning_override(plan, key.NP, key.rows, B))
-    plan.lds = (size_t)plan.P * W->K * plan.BT * (lut_bf16 ? 2 : 4) + (fd ? (size_t)key.D * 4 : 0);
+    plan.lds = (size_t)plan.P * W->K * plan.BT * (lut_bf16 ? 2 : 4) + fused_act_bytes(plan.P, plan.cpg, key.NP, fd);
 #endif
   return plan;
 }
@@ -787,7 +812,13 @@ hipError_t dispatch_gather(const GatherArgs& a, const GatherPlan& plan, int d, i
                            hipStream_t stream) {
   if (fused) {
     if (d == 1) return launch_gather_typed<float, 1, 4, 1, PK>(a, plan, stream);
-    if (d == 2) return launch_gather_typed<float, 1, 4, 2, PK>(a, plan, stream);
+    if (d == 2) {
+      switch (plan.steps) {
+        case 2: return launch_gather_typed<float, 1, 2, 2, PK>(a, plan, stream);
+        case 3: return launch_gather_typed<float, 1, 3, 2, PK>(a, plan, stream);
+        default: return launch_gather_typed<float, 1, 4, 2, PK>(a, plan, stream);
+      }
+    }
     return launch_gather_typed<float, 1, 4, 4, PK>(a, plan, stream);
   }
   if (lut_bf16) {
