@@ -147,6 +147,9 @@ __device__ __forceinline__ uint32_t code_of(const uint4& w, int t) {
 // loaded into registers while the current one is in use and only written to
 // LDS at the switch -- its HBM/L2 latency is hidden behind a whole chunk.
 constexpr int kRegStage = 8;
+// Pairs whose lookups are issued together in a block that lies wholly in range
+// (fewer for lanes holding four rows).
+constexpr int kLookGroup = 4;
 
 // Cache policy bits of the code-stream loads (0: default).
 #ifndef RQ_CODE_CPOL
@@ -293,6 +296,29 @@ void gather_kernel(GatherArgs a) {
   };
   // Lookups of the pairs of block q that lie in [lo, hi), against the chunk staged at p0.
   auto lookup_block = [&](const uint4 (&w)[NSTEP], int q, int lo, int hi, int p0) {
+    // (not for bf16 tables at 4 rows per lane: that instance would spill)
+    if (BQ == 1 && (sizeof(LutT) == 4 || NSTEP < 4) && PPB * q >= lo && PPB * q + PPB <= hi) {
+      // The whole block is in range (uniform): the lookups of kLookGroup pairs
+      // of every step are issued before any is added, so that many LDS reads
+      // are in flight per wave. Each step still adds its pairs in order.
+      constexpr int LG = NSTEP < 4 ? kLookGroup : kLookGroup / 2;   // 4 rows per lane: 2 pairs (registers)
+      static_assert(PPB % LG == 0, "pairs per block");
+#pragma unroll
+      for (int t0 = 0; t0 < PPB; t0 += LG) {
+        float v[LG][NSTEP];
+#pragma unroll
+        for (int t = 0; t < LG; ++t) {
+          const LutT* base = tab + (size_t)(PPB * q + t0 + t - p0) * a.K * BT + rq * BQ;
+#pragma unroll
+          for (int st = 0; st < NSTEP; ++st) v[t][st] = lut_value(base + code_of<PK>(w[st], t0 + t) * BT);
+        }
+#pragma unroll
+        for (int t = 0; t < LG; ++t)
+#pragma unroll
+          for (int st = 0; st < NSTEP; ++st) acc[st][0] += v[t][st];
+      }
+      return;
+    }
 #pragma unroll
     for (int t = 0; t < PPB; ++t) {
       const int p = PPB * q + t;               // uniform
