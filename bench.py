@@ -87,8 +87,8 @@ def main():
 
     # Instrumented pass of the same steps (kept out of the headline timing: every event record
     # costs the stream a few microseconds): events between the calls and, through
-    # rq_set_stage_events, around the lookup+sum kernel alone, all on the stream the library
-    # launches on.
+    # rq_set_stage_events, the start and end of the lookup+sum kernel's own dispatch, all on the
+    # stream the library launches on.
     n_calls = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_calls)]
     gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_calls)]

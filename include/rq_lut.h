@@ -283,10 +283,12 @@ rq_status rq_dense_logits(const uint16_t* E, int64_t rows, int32_t D, const floa
 
 /*
  * Measurement hook. The next lookup+sum kernel that rq_lut_logits or
- * rq_lut_matvec launches from the calling thread is bracketed by
- * hipEventRecord(before, stream) and hipEventRecord(after, stream), so that
- * hipEventElapsedTime(before, after) is that one kernel's duration on its own
- * stream (the selection/epilogue kernels of the same call fall outside). The
+ * rq_lut_matvec launches from the calling thread is launched with
+ * hipExtLaunchKernelGGL(..., before, after, ...): the events take the start
+ * and end of that kernel's own dispatch on its stream, so that
+ * hipEventElapsedTime(before, after) is that one kernel's duration (the
+ * selection/epilogue kernels of the same call fall outside; like a profiler's
+ * kernel trace, it excludes the cache release at the kernel's end). The
  * hook is one-shot and thread-local: it is cleared when used, and by a call
  * with both events NULL. The events stay owned by the caller and must have
  * been created (hipEventCreate) without hipEventDisableTiming.

@@ -37,6 +37,8 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <hip/hip_ext.h>
+
 #include <algorithm>
 #include <mutex>
 
@@ -142,11 +144,15 @@ __device__ __forceinline__ uint32_t code_of(const uint4& w, int t) {
   return (t & 1) ? (word >> 16) : (word & 0xffffu);
 }
 
-// REG: the table slice of one chunk is contiguous and at most kRegStage
-// 16-byte words per thread (B == BT, chunk <= 128 KB), so the next chunk is
-// loaded into registers while the current one is in use and only written to
-// LDS at the switch -- its HBM/L2 latency is hidden behind a whole chunk.
+// REG: the table slice of one chunk is contiguous and at most reg_stage()
+// 16-byte words per thread (B == BT), so the next chunk is loaded into
+// registers while the current one is in use and only written to LDS at the
+// switch -- its HBM/L2 latency is hidden behind a whole chunk. Eight words
+// (128 KB chunks) for the fused build and batch tiles; six (96 KB, the
+// largest single-vector chunk the planner makes) for the single-vector
+// table, whose lookup loop needs the registers.
 constexpr int kRegStage = 8;
+constexpr int reg_stage(int BT, int FD) { return (FD == 0 && BT == 1) ? 6 : kRegStage; }
 // Pairs whose lookups are issued together in a block that lies wholly in range
 // (fewer for lanes holding four rows).
 constexpr int kLookGroup = 4;
@@ -157,18 +163,17 @@ constexpr int kLookGroup = 4;
 #endif
 constexpr int kCodeCachePolicy = RQ_CODE_CPOL;
 
-// Eight 16-byte words of a chunk held in registers. A native vector type keeps
+// RS 16-byte words of a chunk held in registers. A native vector type keeps
 // the copies first-class values (HIP's uint4 struct is copied through memory).
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+template <int RS>
 struct ChunkRegs {
-  u32x4 w0, w1, w2, w3, w4, w5, w6, w7;
+  u32x4 w[RS];
 };
-__device__ __forceinline__ void chunk_to_regs(ChunkRegs& r, const u32x4* __restrict__ src, int tid, int last) {
-  const int T = kGatherThreads;
-  r.w0 = src[min(tid, last)];         r.w1 = src[min(tid + T, last)];
-  r.w2 = src[min(tid + 2 * T, last)]; r.w3 = src[min(tid + 3 * T, last)];
-  r.w4 = src[min(tid + 4 * T, last)]; r.w5 = src[min(tid + 5 * T, last)];
-  r.w6 = src[min(tid + 6 * T, last)]; r.w7 = src[min(tid + 7 * T, last)];
+template <int RS>
+__device__ __forceinline__ void chunk_to_regs(ChunkRegs<RS>& r, const u32x4* __restrict__ src, int tid, int last) {
+#pragma unroll
+  for (int i = 0; i < RS; ++i) r.w[i] = src[min(tid + i * kGatherThreads, last)];
 }
 // Fused table build (B == 1, fp32 codebooks, subspace width FD dividing 4):
 // the registers hold codebook words instead of table words; each word is 4/FD
@@ -198,26 +203,17 @@ __device__ __forceinline__ void fused_word(const u32x4 w, int i, float* tab, con
   else if (EPW == 2) *reinterpret_cast<float2*>(tab + e0) = make_float2(v[0], v[1 % EPW]);
   else tab[e0] = v[0];
 }
-template <int FD>
-__device__ __forceinline__ void regs_to_lds_fused(const ChunkRegs& r, float* tab, const float* act_s, int tid,
+template <int FD, int RS>
+__device__ __forceinline__ void regs_to_lds_fused(const ChunkRegs<RS>& r, float* tab, const float* act_s, int tid,
                                                   int last, int pl0, int K) {
-  const int T = kGatherThreads;
-  fused_word<FD>(r.w0, min(tid, last), tab, act_s, pl0, K);
-  fused_word<FD>(r.w1, min(tid + T, last), tab, act_s, pl0, K);
-  fused_word<FD>(r.w2, min(tid + 2 * T, last), tab, act_s, pl0, K);
-  fused_word<FD>(r.w3, min(tid + 3 * T, last), tab, act_s, pl0, K);
-  fused_word<FD>(r.w4, min(tid + 4 * T, last), tab, act_s, pl0, K);
-  fused_word<FD>(r.w5, min(tid + 5 * T, last), tab, act_s, pl0, K);
-  fused_word<FD>(r.w6, min(tid + 6 * T, last), tab, act_s, pl0, K);
-  fused_word<FD>(r.w7, min(tid + 7 * T, last), tab, act_s, pl0, K);
+#pragma unroll
+  for (int i = 0; i < RS; ++i) fused_word<FD>(r.w[i], min(tid + i * kGatherThreads, last), tab, act_s, pl0, K);
 }
 
-__device__ __forceinline__ void regs_to_lds(const ChunkRegs& r, u32x4* dst, int tid, int last) {
-  const int T = kGatherThreads;
-  dst[min(tid, last)] = r.w0;         dst[min(tid + T, last)] = r.w1;
-  dst[min(tid + 2 * T, last)] = r.w2; dst[min(tid + 3 * T, last)] = r.w3;
-  dst[min(tid + 4 * T, last)] = r.w4; dst[min(tid + 5 * T, last)] = r.w5;
-  dst[min(tid + 6 * T, last)] = r.w6; dst[min(tid + 7 * T, last)] = r.w7;
+template <int RS>
+__device__ __forceinline__ void regs_to_lds(const ChunkRegs<RS>& r, u32x4* dst, int tid, int last) {
+#pragma unroll
+  for (int i = 0; i < RS; ++i) dst[min(tid + i * kGatherThreads, last)] = r.w[i];
 }
 
 // One 1024-thread workgroup per CU (its LDS chunk fills the CU), i.e. four
@@ -340,7 +336,8 @@ void gather_kernel(GatherArgs a) {
   const int c_begin = g * a.cpg;
   const int c_end = min(a.chunks, c_begin + a.cpg);
   uint4 wa[NSTEP], wb[NSTEP];
-  ChunkRegs nxt;
+  constexpr int RS = reg_stage(BT, FD);
+  ChunkRegs<RS> nxt;
   const u32x4* lut4 = reinterpret_cast<const u32x4*>(lut);
   // REG: 16-byte words per pair (of the table, or with FD of the codebook)
   const int words_per_pair = FD ? a.K * FD / 4 : a.K * BT * (int)sizeof(LutT) / 16;
@@ -369,7 +366,7 @@ void gather_kernel(GatherArgs a) {
       // words past the chunk were loaded clamped to its last word, so writing
       // them clamped stores that same value again
       if (FD)
-        regs_to_lds_fused<FD ? FD : 1>(nxt, reinterpret_cast<float*>(tab), act_s, tid, pc * words_per_pair - 1, p0 - pa,
+        regs_to_lds_fused<FD ? FD : 1, RS>(nxt, reinterpret_cast<float*>(tab), act_s, tid, pc * words_per_pair - 1, p0 - pa,
                                        a.K);
       else
         regs_to_lds(nxt, reinterpret_cast<u32x4*>(tab), tid, pc * words_per_pair - 1);
@@ -461,7 +458,8 @@ template <typename LutT, int BT, int NSTEP, int FD = 0, bool PK = false>
 hipError_t launch_gather_typed(const GatherArgs& a, const GatherPlan& plan, hipStream_t stream) {
   if (plan.steps < 1 || plan.steps > NSTEP) return hipErrorInvalidValue;   // a lane holds NSTEP rows at most
   const size_t chunk_bytes = (size_t)plan.P * a.K * BT * sizeof(LutT);
-  const bool reg = (a.B == BT || a.tiled) && chunk_bytes % 16 == 0 && chunk_bytes <= (size_t)kRegStage * 16 * kGatherThreads &&
+  const bool reg = (a.B == BT || a.tiled) && chunk_bytes % 16 == 0 &&
+                   chunk_bytes <= (size_t)reg_stage(BT, FD) * 16 * kGatherThreads &&
                    ((size_t)a.K * BT * sizeof(LutT)) % 16 == 0;
   void (*kern)(GatherArgs);
   if constexpr (FD != 0)
@@ -472,11 +470,14 @@ hipError_t launch_gather_typed(const GatherArgs& a, const GatherPlan& plan, hipS
   if (e != hipSuccess) return e;
   hipEvent_t before, after;
   take_stage_events(&before, &after);
-  if (before && (e = hipEventRecord(before, stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)plan.wgs()), dim3(kGatherThreads), plan.lds, stream, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (after) e = hipEventRecord(after, stream);
-  return e;
+  if (before || after) {
+    // the events take the start and end of this kernel's own dispatch
+    hipExtLaunchKernelGGL(kern, dim3((unsigned)plan.wgs()), dim3(kGatherThreads), plan.lds, stream, before, after, 0,
+                          a);
+  } else {
+    hipLaunchKernelGGL(kern, dim3((unsigned)plan.wgs()), dim3(kGatherThreads), plan.lds, stream, a);
+  }
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ top-k
