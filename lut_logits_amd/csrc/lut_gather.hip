@@ -61,6 +61,7 @@ struct GatherArgs {
   float softcap;              // <= 0: none
   uint64_t* block_keys;       // [B][S] best selection key per slab, or null (G == 1)
   int tiled;                  // lut is batch-tiled [NBT][NP][K][BT] (launch_tile_lut)
+  int xcd_contiguous;         // give each XCD a contiguous range of workgroups (see gather_kernel)
 };
 
 // Lookup of BQ consecutive batch entries of one table row, accumulated in fp32.
@@ -233,11 +234,13 @@ void gather_kernel(GatherArgs a) {
   LutT* tab = reinterpret_cast<LutT*>(smem);
   __shared__ unsigned long long s_keys[BT];
 
-  // XCD-aware numbering: consecutive workgroup ids land on different XCDs, so
-  // give each XCD a contiguous range of logical ids (same chunk group).
+  // XCD-aware numbering (when the host asks for it): workgroups are dealt to
+  // the 8 XCDs round robin, so give each XCD a contiguous range of logical ids
+  // (the same chunk groups, whose tables then stay in that XCD's L2). With N
+  // workgroups the first N % 8 XCDs get one more than the others.
   const int total = a.G * a.S * a.NBT;
-  int li = blockIdx.x;
-  if ((total & 7) == 0) li = (li & 7) * (total >> 3) + (li >> 3);
+  const int xcd = blockIdx.x & 7;
+  int li = a.xcd_contiguous ? xcd * (total >> 3) + min(xcd, total & 7) + (blockIdx.x >> 3) : (int)blockIdx.x;
   const int bt = li % a.NBT;
   li /= a.NBT;
   const int s = li % a.S;
@@ -341,8 +344,15 @@ void gather_kernel(GatherArgs a) {
   const u32x4* lut4 = reinterpret_cast<const u32x4*>(lut);
   // REG: 16-byte words per pair (of the table, or with FD of the codebook)
   const int words_per_pair = FD ? a.K * FD / 4 : a.K * BT * (int)sizeof(LutT) / 16;
+  // REG: chunk c's words go to registers with a fixed count of unconditional
+  // loads (clamped to the last word of the chunk).
+  if (REG) {
+    const int n4 = min(a.P, a.NP - c_begin * a.P) * words_per_pair;
+    chunk_to_regs(nxt, lut4 + (size_t)c_begin * a.P * words_per_pair, tid, n4 - 1);
+  }
   // FD: the activation slices of this group's pairs [pa, pb) go to LDS after
-  // the chunk, once (pair p uses elements (p % M)*FD .. +FD of the vector)
+  // the chunk, once (pair p uses elements (p % M)*FD .. +FD of the vector).
+  // Their loads follow the first chunk's, so the two latencies overlap.
   float* act_s = reinterpret_cast<float*>(smem + (size_t)a.P * a.K * sizeof(float));
   if (FD)
     for (int i = tid; i < (pb - pa) * FD; i += kGatherThreads) {
@@ -350,12 +360,6 @@ void gather_kernel(GatherArgs a) {
       const int src = (p % a.M) * FD + (i - (p - pa) * FD);
       act_s[i] = a.act2 ? gelu_tanh(a.act[src]) * a.act2[src] : a.act[src];
     }
-  // REG: chunk c's words go to registers with a fixed count of unconditional
-  // loads (clamped to the last word of the chunk).
-  if (REG) {
-    const int n4 = min(a.P, a.NP - c_begin * a.P) * words_per_pair;
-    chunk_to_regs(nxt, lut4 + (size_t)c_begin * a.P * words_per_pair, tid, n4 - 1);
-  }
   // Stage chunk c (uniform): all lookups of the previous chunk are done before
   // LDS is overwritten, and the next chunk starts loading into registers.
   auto switch_chunk = [&](int c) {
@@ -909,6 +913,15 @@ hipError_t launch_gather(const rq_matrix* W, const GatherPlan& plan, const void*
   a.softcap = o.softcap;
   a.block_keys = plan.G == 1 ? o.block_keys : nullptr;
   a.tiled = o.lut_tiled;
+  // Contiguous per-XCD ranges let the few slabs of one group share its staged
+  // chunks in one L2 (gate/up of the Gemma MLP: 3 slabs, 24.5 -> 18.5 us).
+  // With many slabs per group (the head: 63) the workgroups of an XCD would
+  // all switch to the same chunks at once, which measured slower (69 -> 74 us),
+  // so dispatch order is kept there.
+  a.xcd_contiguous = plan.S >= 2 && plan.S <= 8;
+#ifdef RQ_TUNING
+  if (const char* xm = getenv("RQ_XCD_MAP")) a.xcd_contiguous = atoi(xm);
+#endif
   hipError_t e = W->codes_layout == RQ_CODES_PACKED10 ? dispatch_gather<true>(a, plan, W->d, lut_bf16, fused_act != nullptr, stream)
                                                         : dispatch_gather<false>(a, plan, W->d, lut_bf16, fused_act != nullptr, stream);
   if (e != hipSuccess || plan.G == 1) return e;
