@@ -10,7 +10,8 @@
  *   - input rows reconstructed on demand, a handful per prompt
  *                                      -> rq_decode_rows
  * and the non-materialising path for RQ-coded MLP weights that the Gemma-2-2B
- * MLP RQ page names as its natural follow-up   -> rq_lut_matvec.
+ * MLP RQ page names as its natural follow-up   -> rq_lut_matvec (one matrix)
+ *                                                 and rq_lut_mlp (a whole block).
  *
  * The coded matrix. W[rows][D] with D = M*d is split into M contiguous
  * subspaces of width d; row r's subvector in subspace m is the sum over L
@@ -264,6 +265,29 @@ size_t rq_lut_matvec_workspace(const rq_matrix* W, int32_t B);
  */
 rq_status rq_lut_matvec(const rq_matrix* W, const float* x, const float* x2, int32_t prologue,
                         int32_t B, float* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * A whole Gemma-2 MLP block with RQ-coded weights (MLP RQ page, final
+ * paragraphs: the three projections as LUT matvecs):
+ *     y = down( gelu_tanh(gate(x)) * up(x) )
+ * with the arithmetic of the three rq_lut_matvec calls. With one activation
+ * vector and fused table builds (fp32 codebooks, d in {1, 2, 4}) it takes
+ * three launches instead of six: gate and up in one lookup+sum launch, down
+ * with its activation summed straight from their partial sums in the finish
+ * pass's order, then down's finish. Gate and up may then be split into a
+ * different (fixed) number of partial sums than a single call would use, so
+ * the result agrees with the three calls to fp32 rounding (exactly when no sum
+ * rounds) and is deterministic. Otherwise it runs the three matvecs.
+ *   gate, up  same rows, D, M, d, K, L, codebook dtype and code layout
+ *   down      down->D == gate->rows
+ *   x         device fp32 [B][gate->D];  y  device fp32 [B][down->rows]
+ *   ws        device workspace of at least rq_lut_mlp_workspace() bytes,
+ *             256-byte aligned
+ * Shape mismatches return RQ_ERR_SHAPE; other checks as rq_lut_matvec.
+ */
+size_t rq_lut_mlp_workspace(const rq_matrix* gate, const rq_matrix* up, const rq_matrix* down, int32_t B);
+rq_status rq_lut_mlp(const rq_matrix* gate, const rq_matrix* up, const rq_matrix* down, const float* x,
+                     int32_t B, float* y, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Comparison baseline: the standard dense path with the head stored as a

@@ -10,7 +10,7 @@ from .binding import (RQ_BF16, RQ_CODES_BLOCKED, RQ_CODES_PACKED10, RQ_CODES_ROW
                       RQ_PRO_GELU_TANH_MUL,  # noqa: F401
                       RQ_PRO_NONE, DeviceMatrix, RQError, build_lut, logits, logits_method, logits_workspace, decode_rows, dense_logits, dense_logits_workspace, lib,
                       lut_bytes,
-                      lut_logits, lut_logits_workspace, lut_matvec, lut_matvec_workspace, pack_codes, pack_codes10, packed10_codes_bytes,
+                      lut_logits, lut_logits_workspace, lut_matvec, lut_matvec_workspace, lut_mlp, lut_mlp_workspace, pack_codes, pack_codes10, packed10_codes_bytes,
                       set_stage_events,
                       to_device, workspace)
 

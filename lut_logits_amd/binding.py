@@ -23,7 +23,7 @@ RQ_METHOD_TABLE, RQ_METHOD_MATRIX_CORES = 0, 1
 # Every symbol include/rq_lut.h declares.
 EXPORTS = ("rq_blocked_codes_bytes", "rq_pack_codes", "rq_packed10_codes_bytes", "rq_pack_codes10", "rq_lut_bytes", "rq_build_lut", "rq_lut_logits_workspace",
            "rq_lut_logits", "rq_logits_method", "rq_logits_workspace", "rq_logits", "rq_decode_rows", "rq_lut_matvec_workspace", "rq_lut_matvec",
-           "rq_dense_logits_workspace", "rq_dense_logits", "rq_set_stage_events", "rq_status_string", "rq_last_error", "rq_version")
+           "rq_lut_mlp_workspace", "rq_lut_mlp", "rq_dense_logits_workspace", "rq_dense_logits", "rq_set_stage_events", "rq_status_string", "rq_last_error", "rq_version")
 
 
 class RQError(RuntimeError):
@@ -65,6 +65,8 @@ def lib():
             "rq_decode_rows": (_i32, [_MP, _vp, _i32, _i32, _vp, _vp, _vp]),
             "rq_lut_matvec_workspace": (_sz, [_MP, _i32]),
             "rq_lut_matvec": (_i32, [_MP, _vp, _vp, _i32, _i32, _vp, _vp, _sz, _vp]),
+            "rq_lut_mlp_workspace": (_sz, [_MP, _MP, _MP, _i32]),
+            "rq_lut_mlp": (_i32, [_MP, _MP, _MP, _vp, _i32, _vp, _vp, _sz, _vp]),
             "rq_dense_logits_workspace": (_sz, [_i64, _i32]),
             "rq_dense_logits": (_i32, [_vp, _i64, _i32, _vp, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
             "rq_set_stage_events": (_i32, [_vp, _vp]),
@@ -240,6 +242,20 @@ def lut_matvec(W, x, x2=None, prologue=RQ_PRO_NONE, ws=None, out=None):
     if ws is None:
         ws = workspace(lut_matvec_workspace(W, B), x.device)
     check(lib().rq_lut_matvec(W.ref, _ptr(x), _ptr(x2), prologue, B, _ptr(y), _ptr(ws), ws.numel(), _stream()))
+    return y
+
+
+def lut_mlp_workspace(gate, up, down, B):
+    return lib().rq_lut_mlp_workspace(gate.ref, up.ref, down.ref, B)
+
+
+def lut_mlp(gate, up, down, x, ws=None, out=None):
+    """rq_lut_mlp: y [B][down.rows] = down(gelu_tanh(gate(x)) * up(x))."""
+    B = x.shape[0]
+    y = out if out is not None else torch.empty((B, down.rows), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = workspace(lut_mlp_workspace(gate, up, down, B), x.device)
+    check(lib().rq_lut_mlp(gate.ref, up.ref, down.ref, _ptr(x), B, _ptr(y), _ptr(ws), ws.numel(), _stream()))
     return y
 
 

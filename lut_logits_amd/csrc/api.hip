@@ -5,6 +5,7 @@
 // synchronisation: everything is enqueued on the caller's stream.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 
 #include <algorithm>
 
@@ -258,7 +259,7 @@ struct HeadWs {
   int nkb;
 };
 
-HeadWs head_ws(const rq_matrix* W, int32_t B, int32_t topk, bool logits_out) {
+static HeadWs head_ws(const rq_matrix* W, int32_t B, int32_t topk, bool logits_out) {
   HeadWs w{};
   w.mm = B >= RQ_MM_MIN_B && rq::mm_supported(W);
   size_t partial_bytes;
@@ -374,7 +375,7 @@ struct MatvecWs {
   size_t front, partial, tiled, total;
 };
 
-MatvecWs matvec_ws(const rq_matrix* W, int32_t B) {
+static MatvecWs matvec_ws(const rq_matrix* W, int32_t B) {
   MatvecWs m{};
   m.fused = rq::fused_build_supported(W, B);
   if (m.fused) {
@@ -430,6 +431,92 @@ rq_status rq_lut_matvec(const rq_matrix* W, const float* x, const float* x2, int
     o.lut_tiled = 1;
   }
   return launched(rq::launch_gather(W, m.plan, lut, 0, B, o, stream), "rq_lut_matvec: lookup+sum");
+}
+
+// Workspace of rq_lut_mlp. Fused route: the partial sums of gate and up
+// [2][Gg][rows] (their sums when Gg == 1), then down's partial sums
+// [Gd][down rows] (Gd > 1). Otherwise: g and u [2][B][rows], then one
+// rq_lut_matvec workspace large enough for the three calls.
+struct MlpWs {
+  bool fused;
+  rq::GatherPlan pgu, pd;
+  size_t down_part, mv, total;
+};
+
+static rq_status check_mlp(const rq_matrix* gate, const rq_matrix* up, const rq_matrix* down, int32_t B) {
+  rq_status s = check_lut_call(gate, B, RQ_F32);
+  if (s == RQ_OK) s = check_lut_call(up, B, RQ_F32);
+  if (s == RQ_OK) s = check_lut_call(down, B, RQ_F32);
+  if (s != RQ_OK) return s;
+  if (gate->rows != up->rows || gate->D != up->D || gate->M != up->M || gate->d != up->d || gate->K != up->K ||
+      gate->L != up->L || gate->cb_dtype != up->cb_dtype || gate->codes_layout != up->codes_layout)
+    return fail(RQ_ERR_SHAPE, "lut_mlp: gate and up differ in shape, codebook dtype or code layout");
+  if ((int64_t)down->D != gate->rows)
+    return fail(RQ_ERR_SHAPE, "lut_mlp: down->D=%d != gate->rows=%lld", down->D, (long long)gate->rows);
+  return RQ_OK;
+}
+
+static MlpWs mlp_ws(const rq_matrix* gate, const rq_matrix* up, const rq_matrix* down, int32_t B) {
+  MlpWs w{};
+  w.fused = rq::fused_build_supported(gate, B) && rq::fused_build_supported(up, B) &&
+            rq::fused_build_supported(down, B);
+  if (w.fused) {
+    int pair_mats = 2;
+#ifdef RQ_TUNING
+    if (const char* pm = getenv("RQ_MLP_PAIR_MATS")) pair_mats = atoi(pm);
+#endif
+    w.pgu = rq::plan_gather(gate, B, 0, 1, pair_mats);
+    w.pd = rq::plan_gather(down, B, 0, 1);
+    w.fused = w.pgu.BT != 0 && w.pd.BT != 0 && rq::gather_pro_lds(down, w.pd, w.pgu.G) <= (size_t)rq::kLdsBudget;
+  }
+  if (w.fused) {
+    w.down_part = round_up((size_t)2 * w.pgu.G * gate->rows * sizeof(float), 256);
+    w.total = w.down_part + (w.pd.G > 1 ? round_up((size_t)w.pd.G * down->rows * sizeof(float), 256) : 0);
+    return w;
+  }
+  w.mv = round_up((size_t)2 * B * gate->rows * sizeof(float), 256);
+  const MatvecWs mg = matvec_ws(gate, B), mu = matvec_ws(up, B), md = matvec_ws(down, B);
+  if (mg.plan.BT == 0 || mu.plan.BT == 0 || md.plan.BT == 0) return w;   // total 0: no tiling fits
+  w.total = w.mv + std::max(mg.total, std::max(mu.total, md.total));
+  return w;
+}
+
+size_t rq_lut_mlp_workspace(const rq_matrix* gate, const rq_matrix* up, const rq_matrix* down, int32_t B) {
+  if (check_mlp(gate, up, down, B) != RQ_OK || B == 0 || down->rows == 0) return 0;
+  return mlp_ws(gate, up, down, B).total;
+}
+
+rq_status rq_lut_mlp(const rq_matrix* gate, const rq_matrix* up, const rq_matrix* down, const float* x, int32_t B,
+                     float* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  rq_status s = check_mlp(gate, up, down, B);
+  if (s != RQ_OK) return s;
+  if (B == 0 || down->rows == 0) return RQ_OK;
+  if (!x || !y) return fail(RQ_ERR_NULL, "lut_mlp: NULL buffer");
+  if (!aligned(x, 4) || !aligned(y, 4)) return fail(RQ_ERR_ALIGN, "lut_mlp: misaligned buffer");
+  const MlpWs w = mlp_ws(gate, up, down, B);
+  if (w.total == 0) return fail(RQ_ERR_SHAPE, "no table tiling fits on chip for K=%d", gate->K);
+  if (!ws || ws_bytes < w.total) return fail(RQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, w.total);
+  if (!aligned(ws, 256)) return fail(RQ_ERR_ALIGN, "workspace must be 256-byte aligned");
+  char* base = static_cast<char*>(ws);
+  if (w.fused) {
+    float* pg = reinterpret_cast<float*>(base);
+    float* pu = pg + (size_t)w.pgu.G * gate->rows;
+    hipError_t e = rq::launch_gather_pair(gate, up, w.pgu, x, pg, pu, stream);
+    if (e != hipSuccess) return launched(e, "rq_lut_mlp: gate and up lookup+sum");
+    rq::GatherOut o{};
+    o.partial = reinterpret_cast<float*>(base + w.down_part);
+    o.out = y;
+    return launched(rq::launch_gather_pro(down, w.pd, pg, w.pgu.G, gate->rows, o, stream),
+                    "rq_lut_mlp: down lookup+sum");
+  }
+  float* g = reinterpret_cast<float*>(base);
+  float* u = g + (size_t)B * gate->rows;
+  void* mws = base + w.mv;
+  const size_t mbytes = ws_bytes - w.mv;
+  s = rq_lut_matvec(gate, x, nullptr, RQ_PRO_NONE, B, g, mws, mbytes, stream);
+  if (s == RQ_OK) s = rq_lut_matvec(up, x, nullptr, RQ_PRO_NONE, B, u, mws, mbytes, stream);
+  if (s == RQ_OK) s = rq_lut_matvec(down, g, u, RQ_PRO_GELU_TANH_MUL, B, y, mws, mbytes, stream);
+  return s;
 }
 
 size_t rq_dense_logits_workspace(int64_t rows, int32_t B) {

@@ -58,10 +58,23 @@ struct GatherArgs {
   int P, chunks, cpg, G, steps, S, NBT;
   float* partial;             // [G][B][rows] (G > 1)
   float* out;                 // [B][rows] or null (G == 1)
+  float* out2;                // second matrix of a two-matrix launch: its out
   float softcap;              // <= 0: none
   uint64_t* block_keys;       // [B][S] best selection key per slab, or null (G == 1)
   int tiled;                  // lut is batch-tiled [NBT][NP][K][BT] (launch_tile_lut)
   int xcd_contiguous;         // give each XCD a contiguous range of workgroups (see gather_kernel)
+  int mats;                   // host side: 1, or 2 for a two-matrix launch (gridDim.y)
+  // gridDim.y == 2: a second matrix of the same shape and plan (cv2, lut2),
+  // its partial sums to partial2 (the Gemma MLP's gate and up in one launch)
+  CodeView cv2;
+  const void* lut2;
+  float* partial2;
+  // Fused build with pro_partial set: the activation is gelu_tanh(g) * u with
+  // g and u summed from partial sums [2][pro_G][pro_rows] (g's, then u's, B = 1)
+  // in the finish kernel's order (pro_tpr parts), instead of read from act/act2.
+  const float* pro_partial;
+  int pro_G, pro_tpr;
+  int64_t pro_rows;
 };
 
 // Lookup of BQ consecutive batch entries of one table row, accumulated in fp32.
@@ -235,12 +248,19 @@ void gather_kernel(GatherArgs a) {
   __shared__ unsigned long long s_keys[BT];
 
   // XCD-aware numbering (when the host asks for it): workgroups are dealt to
-  // the 8 XCDs round robin, so give each XCD a contiguous range of logical ids
-  // (the same chunk groups, whose tables then stay in that XCD's L2). With N
-  // workgroups the first N % 8 XCDs get one more than the others.
+  // the 8 XCDs round robin in dispatch order, so give each XCD a contiguous
+  // range of logical ids (the same chunk groups, whose tables then stay in
+  // that XCD's L2). With N workgroups the first N % 8 XCDs get one more than
+  // the others. With two matrices the logical ids run over both.
   const int total = a.G * a.S * a.NBT;
-  const int xcd = blockIdx.x & 7;
-  int li = a.xcd_contiguous ? xcd * (total >> 3) + min(xcd, total & 7) + (blockIdx.x >> 3) : (int)blockIdx.x;
+  const int all = total * (int)gridDim.y;
+  const int idx = (int)(blockIdx.y * gridDim.x + blockIdx.x);
+  const int xcd = idx & 7;
+  int li = a.xcd_contiguous ? xcd * (all >> 3) + min(xcd, all & 7) + (idx >> 3) : idx;
+  const bool second = li >= total;   // uniform: the second matrix of a two-matrix launch
+  if (second) li -= total;
+  const CodeView cv = second ? a.cv2 : a.cv;
+  float* const partial = second ? a.partial2 : a.partial;
   const int bt = li % a.NBT;
   li /= a.NBT;
   const int s = li % a.S;
@@ -267,18 +287,18 @@ void gather_kernel(GatherArgs a) {
 #pragma unroll
   for (int st = 0; st < NSTEP; ++st) {
     const int64_t r = min(row0 + (int64_t)(st < a.steps ? st : 0) * RPS, a.rows - 1);
-    roff[st] = (uint32_t)(r * a.cv.s_row * 2);
+    roff[st] = (uint32_t)(r * cv.s_row * 2);
   }
   // The code stream is read with buffer loads: a scalar resource, the row
   // offset in a VGPR and the block offset in an SGPR, so the hot loop holds no
   // 64-bit per-lane addresses. (The host keeps the code array below 4 GiB.)
   const __amdgpu_buffer_rsrc_t code_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)a.cv.codes, (short)0, (int)0xffffffffu, 0x00020000);
-  const uint32_t blk_bytes = (uint32_t)(a.cv.s_blk * 2);
+      __builtin_amdgcn_make_buffer_rsrc((void*)cv.codes, (short)0, (int)0xffffffffu, 0x00020000);
+  const uint32_t blk_bytes = (uint32_t)(cv.s_blk * 2);
   const int steps = a.steps;
 
   // batch-tiled table: this tile's [NP][K][BT] slice is contiguous
-  const LutT* lut = static_cast<const LutT*>(a.lut) + (a.tiled ? (size_t)bt * a.NP * a.K * BT : 0);
+  const LutT* lut = static_cast<const LutT*>(second ? a.lut2 : a.lut) + (a.tiled ? (size_t)bt * a.NP * a.K * BT : 0);
   const int pa = g * a.cpg * a.P;                       // this group's pairs [pa, pb)
   const int pb = min(a.NP, (g * a.cpg + a.cpg) * a.P);
 
@@ -354,12 +374,48 @@ void gather_kernel(GatherArgs a) {
   // the chunk, once (pair p uses elements (p % M)*FD .. +FD of the vector).
   // Their loads follow the first chunk's, so the two latencies overlap.
   float* act_s = reinterpret_cast<float*>(smem + (size_t)a.P * a.K * sizeof(float));
-  if (FD)
+  if (FD && a.pro_partial) {
+    // g and u of each element: pro_tpr parts per element and matrix, part t
+    // adding groups t, t+pro_tpr, ... in order, then the parts in order -- the
+    // finish kernel's arithmetic, so the activation is bit-identical to
+    // finishing g and u first.
+    const int E = (pb - pa) * FD;
+    const int TPR = a.pro_tpr;
+    float* pro_s = act_s + (size_t)min(a.cpg * a.P, a.NP) * FD;   // [2][E][TPR]
+    for (int task = tid; task < 2 * E * TPR; task += kGatherThreads) {
+      const int mat = task / (E * TPR);
+      const int rem = task - mat * E * TPR;
+      const int i = rem / TPR;
+      const int part = rem - i * TPR;
+      const int p = pa + i / FD;
+      const int src = (p % a.M) * FD + (i - (p - pa) * FD);
+      const float* col = a.pro_partial + ((size_t)mat * a.pro_G) * a.pro_rows + src;
+      float z = 0.0f;
+      int gg = part;
+      for (; gg + 3 * TPR < a.pro_G; gg += 4 * TPR) {
+        const float v0 = col[(size_t)gg * a.pro_rows], v1 = col[(size_t)(gg + TPR) * a.pro_rows];
+        const float v2 = col[(size_t)(gg + 2 * TPR) * a.pro_rows], v3 = col[(size_t)(gg + 3 * TPR) * a.pro_rows];
+        z += v0; z += v1; z += v2; z += v3;
+      }
+      for (; gg < a.pro_G; gg += TPR) z += col[(size_t)gg * a.pro_rows];
+      pro_s[(size_t)(mat * E + i) * TPR + part] = z;
+    }
+    __syncthreads();
+    for (int i = tid; i < E; i += kGatherThreads) {
+      float gv = pro_s[(size_t)i * TPR], uv = pro_s[(size_t)(E + i) * TPR];
+      for (int t = 1; t < TPR; ++t) {
+        gv += pro_s[(size_t)i * TPR + t];
+        uv += pro_s[(size_t)(E + i) * TPR + t];
+      }
+      act_s[i] = gelu_tanh(gv) * uv;
+    }
+  } else if (FD) {
     for (int i = tid; i < (pb - pa) * FD; i += kGatherThreads) {
       const int p = pa + i / (FD ? FD : 1);
       const int src = (p % a.M) * FD + (i - (p - pa) * FD);
       act_s[i] = a.act2 ? gelu_tanh(a.act[src]) * a.act2[src] : a.act[src];
     }
+  }
   // Stage chunk c (uniform): all lookups of the previous chunk are done before
   // LDS is overwritten, and the next chunk starts loading into registers.
   auto switch_chunk = [&](int c) {
@@ -424,7 +480,7 @@ void gather_kernel(GatherArgs a) {
 #pragma unroll
       for (int i = 0; i < BQ; ++i) {
         const int b = b0 + rq * BQ + i;
-        if (b < a.B) a.partial[((size_t)g * a.B + b) * a.rows + r] = acc[st][i];
+        if (b < a.B) partial[((size_t)g * a.B + b) * a.rows + r] = acc[st][i];
       }
     }
     return;
@@ -444,7 +500,8 @@ void gather_kernel(GatherArgs a) {
       if (b >= a.B) continue;
       const float z = acc[st][i];
       const float v = a.softcap > 0.0f ? a.softcap * tanhf(z / a.softcap) : z;
-      if (a.out) a.out[(size_t)b * a.rows + r] = v;
+      float* const outp = second ? a.out2 : a.out;
+      if (outp) outp[(size_t)b * a.rows + r] = v;
       kbest[i] = umax64(kbest[i], select_key(v, (uint32_t)r));
     }
   }
@@ -476,10 +533,10 @@ hipError_t launch_gather_typed(const GatherArgs& a, const GatherPlan& plan, hipS
   take_stage_events(&before, &after);
   if (before || after) {
     // the events take the start and end of this kernel's own dispatch
-    hipExtLaunchKernelGGL(kern, dim3((unsigned)plan.wgs()), dim3(kGatherThreads), plan.lds, stream, before, after, 0,
-                          a);
+    hipExtLaunchKernelGGL(kern, dim3((unsigned)plan.wgs(), (unsigned)a.mats), dim3(kGatherThreads), plan.lds, stream,
+                          before, after, 0, a);
   } else {
-    hipLaunchKernelGGL(kern, dim3((unsigned)plan.wgs()), dim3(kGatherThreads), plan.lds, stream, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)plan.wgs(), (unsigned)a.mats), dim3(kGatherThreads), plan.lds, stream, a);
   }
   return hipGetLastError();
 }
@@ -696,12 +753,12 @@ namespace {
 // LDS lookups run at ~9 per clock per CU (quad-contiguous 64-byte lookups at
 // ~120 B/clock); G > 1 adds the partial-sum traffic and a finish launch.
 double plan_cost_us(int64_t rows, int NP, int K, int B, int es, int BT, int P, int steps, int G, int cpg,
-                    int stage_es, int lane_steps) {
+                    int stage_es, int lane_steps, int mats) {
   const int QL = BT >= 16 ? 4 : 1;
   const int rps = kGatherThreads / QL;
   const int64_t S = (rows + (int64_t)steps * rps - 1) / ((int64_t)steps * rps);
   const int NBT = (B + BT - 1) / BT;
-  const int64_t wgs = (int64_t)G * S * NBT;
+  const int64_t wgs = (int64_t)G * S * NBT * mats;
   const int64_t rounds = (wgs + kCUs - 1) / kCUs;
   const int64_t active = std::min<int64_t>(wgs, kCUs);
   const double slab_rows = (double)std::min<int64_t>(rows, (int64_t)steps * rps);
@@ -715,8 +772,8 @@ double plan_cost_us(int64_t rows, int NP, int K, int B, int es, int BT, int P, i
   // the slab or the last row
   const double t_look = (double)lane_steps * rps * pairs / lookups_per_us;
   const double t_wg = t_stage + std::max(t_codes, t_look);
-  const double t_stream = (double)rows * NP * 2.0 * NBT / 6.4e6;
-  const double t_partial = G > 1 ? 5.0 + (double)G * B * rows * 8.0 / 6.4e6 : 0.0;
+  const double t_stream = (double)rows * NP * 2.0 * NBT * mats / 6.4e6;
+  const double t_partial = G > 1 ? 5.0 + (double)G * B * rows * 8.0 * mats / 6.4e6 : 0.0;
   return std::max(t_stream, (double)rounds * t_wg) + t_partial;
 }
 
@@ -736,7 +793,7 @@ bool steps_allowed(int steps, int fused_d) {
   return steps >= 1 && steps <= 4;
 }
 
-GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16, int fused_d, int ppb) {
+GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16, int fused_d, int ppb, int mats) {
   const int es = lut_bf16 ? 2 : 4;
   const int stage_es = fused_d ? 4 * fused_d : es;
   GatherPlan best{};
@@ -770,7 +827,7 @@ GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16, int fus
       if (!steps_allowed(steps, fused_d)) continue;
       const int64_t S = (rows + (int64_t)steps * rps - 1) / ((int64_t)steps * rps);
       if (S * NBT > (1 << 24)) continue;
-      const int64_t gmax = std::max<int64_t>(1, std::min<int64_t>(chunks, 4 * kCUs / (S * NBT) + 1));
+      const int64_t gmax = std::max<int64_t>(1, std::min<int64_t>(chunks, 4 * kCUs / (S * NBT * mats) + 1));
       for (int64_t G0 = 1; G0 <= gmax; ++G0) {
         const int cpg = (int)((chunks + G0 - 1) / G0);
         const int G = (chunks + cpg - 1) / cpg;
@@ -778,7 +835,7 @@ GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16, int fus
         if ((size_t)P * K * 4 + fused_act_bytes(P, cpg, NP, fused_d) > (size_t)kLdsBudget && fused_d) continue;
         // prefer aligned chunks (staging outside the block loop) on near-ties
         const int lane_steps = fused_d == 2 ? steps : nstep;   // the kernel instances (dispatch_gather)
-        const double cost = plan_cost_us(rows, NP, K, B, es, BT, P, steps, G, cpg, stage_es, lane_steps) *
+        const double cost = plan_cost_us(rows, NP, K, B, es, BT, P, steps, G, cpg, stage_es, lane_steps, mats) *
                             ((P % ppb == 0 || chunks == 1) ? 1.0 : 1.03);
         if (cost < best_cost * 0.999) {
           best_cost = cost;
@@ -796,10 +853,10 @@ GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16, int fus
 // off the per-call path.
 struct PlanKey {
   int64_t rows;
-  int NP, K, B, bf16, fused_d, ppb;
+  int NP, K, B, bf16, fused_d, ppb, mats;
   bool operator==(const PlanKey& o) const {
     return rows == o.rows && NP == o.NP && K == o.K && B == o.B && bf16 == o.bf16 && fused_d == o.fused_d &&
-           ppb == o.ppb;
+           ppb == o.ppb && mats == o.mats;
   }
 };
 std::mutex g_plan_mu;
@@ -813,9 +870,9 @@ int g_plan_n = 0, g_plan_next = 0;
 // and G are, so P is taken as large as LDS allows; then (steps, G) are chosen
 // to fill every CU with one workgroup per round, preferring few groups
 // (partial-sum traffic) and long slabs (loads in flight per lane).
-GatherPlan plan_gather(const rq_matrix* W, int B, int lut_bf16, int fused) {
+GatherPlan plan_gather(const rq_matrix* W, int B, int lut_bf16, int fused, int mats) {
   const int fd = fused ? W->d : 0;
-  const PlanKey key{W->rows, W->L * W->M, W->K, B, lut_bf16, fd, pairs_per_block(W)};
+  const PlanKey key{W->rows, W->L * W->M, W->K, B, lut_bf16, fd, pairs_per_block(W), mats};
   GatherPlan plan{};
   bool hit = false;
   {
@@ -824,7 +881,7 @@ GatherPlan plan_gather(const rq_matrix* W, int B, int lut_bf16, int fused) {
       if (g_plan_keys[i] == key) { plan = g_plans[i]; hit = true; break; }
   }
   if (!hit) {
-    plan = search_plan(key.rows, key.NP, key.K, B, lut_bf16, fd, key.ppb);
+    plan = search_plan(key.rows, key.NP, key.K, B, lut_bf16, fd, key.ppb, mats);
     std::lock_guard<std::mutex> lock(g_plan_mu);
     g_plan_keys[g_plan_next] = key;
     g_plans[g_plan_next] = plan;
@@ -893,9 +950,11 @@ bool fused_build_supported(const rq_matrix* W, int B) {
          ((uintptr_t)W->codebooks % 16) == 0 && ((size_t)W->K * W->d) % 4 == 0;
 }
 
-hipError_t launch_gather(const rq_matrix* W, const GatherPlan& plan, const void* lut, int lut_bf16, int B,
-                         const GatherOut& o, hipStream_t stream, const float* fused_act, const float* fused_x2) {
-  GatherArgs a;
+namespace {
+
+GatherArgs gather_args(const rq_matrix* W, const GatherPlan& plan, const void* lut, int B, const GatherOut& o,
+                       const float* fused_act, const float* fused_x2) {
+  GatherArgs a{};
   a.cv = code_view(W);
   a.lut = fused_act ? W->codebooks : lut;
   a.act = fused_act;
@@ -913,6 +972,7 @@ hipError_t launch_gather(const rq_matrix* W, const GatherPlan& plan, const void*
   a.softcap = o.softcap;
   a.block_keys = plan.G == 1 ? o.block_keys : nullptr;
   a.tiled = o.lut_tiled;
+  a.mats = 1;
   // Contiguous per-XCD ranges let the few slabs of one group share its staged
   // chunks in one L2 (gate/up of the Gemma MLP: 3 slabs, 24.5 -> 18.5 us).
   // With many slabs per group (the head: 63) the workgroups of an XCD would
@@ -922,10 +982,57 @@ hipError_t launch_gather(const rq_matrix* W, const GatherPlan& plan, const void*
 #ifdef RQ_TUNING
   if (const char* xm = getenv("RQ_XCD_MAP")) a.xcd_contiguous = atoi(xm);
 #endif
-  hipError_t e = W->codes_layout == RQ_CODES_PACKED10 ? dispatch_gather<true>(a, plan, W->d, lut_bf16, fused_act != nullptr, stream)
-                                                        : dispatch_gather<false>(a, plan, W->d, lut_bf16, fused_act != nullptr, stream);
+  return a;
+}
+
+hipError_t dispatch(const rq_matrix* W, const GatherArgs& a, const GatherPlan& plan, int lut_bf16, bool fused,
+                    hipStream_t stream) {
+  return W->codes_layout == RQ_CODES_PACKED10 ? dispatch_gather<true>(a, plan, W->d, lut_bf16, fused, stream)
+                                              : dispatch_gather<false>(a, plan, W->d, lut_bf16, fused, stream);
+}
+
+}  // namespace
+
+hipError_t launch_gather(const rq_matrix* W, const GatherPlan& plan, const void* lut, int lut_bf16, int B,
+                         const GatherOut& o, hipStream_t stream, const float* fused_act, const float* fused_x2) {
+  const GatherArgs a = gather_args(W, plan, lut, B, o, fused_act, fused_x2);
+  hipError_t e = dispatch(W, a, plan, lut_bf16, fused_act != nullptr, stream);
   if (e != hipSuccess || plan.G == 1) return e;
   return launch_finish(o.partial, plan.G, B, W->rows, o.softcap, o.out, o.block_keys, stream);
+}
+
+hipError_t launch_gather_pair(const rq_matrix* W1, const rq_matrix* W2, const GatherPlan& plan, const float* x,
+                              float* part1, float* part2, hipStream_t stream) {
+  GatherOut o{};
+  o.partial = part1;
+  o.out = plan.G == 1 ? part1 : nullptr;   // one group: the sums themselves
+  GatherArgs a = gather_args(W1, plan, nullptr, 1, o, x, nullptr);
+  a.cv2 = code_view(W2);
+  a.lut2 = W2->codebooks;
+  a.partial2 = part2;
+  a.out2 = plan.G == 1 ? part2 : nullptr;
+  a.mats = 2;
+  return dispatch(W1, a, plan, 0, true, stream);
+}
+
+size_t gather_pro_lds(const rq_matrix* W, const GatherPlan& plan, int pro_G) {
+  const size_t E = (size_t)std::min(plan.cpg * plan.P, W->L * W->M) * W->d;
+  return plan.lds + 2 * E * finish_parts(pro_G) * sizeof(float);
+}
+
+hipError_t launch_gather_pro(const rq_matrix* W, const GatherPlan& plan, const float* pro_partial, int pro_G,
+                             int64_t pro_rows, const GatherOut& o, hipStream_t stream) {
+  GatherPlan p = plan;
+  p.lds = gather_pro_lds(W, plan, pro_G);
+  if (p.lds > (size_t)kLdsBudget) return hipErrorInvalidValue;
+  GatherArgs a = gather_args(W, p, nullptr, 1, o, pro_partial, nullptr);
+  a.pro_partial = pro_partial;
+  a.pro_G = pro_G;
+  a.pro_tpr = finish_parts(pro_G);
+  a.pro_rows = pro_rows;
+  hipError_t e = dispatch(W, a, p, 0, true, stream);
+  if (e != hipSuccess || p.G == 1) return e;
+  return launch_finish(o.partial, p.G, 1, W->rows, o.softcap, o.out, o.block_keys, stream);
 }
 
 int finish_parts(int G) { return G <= 8 ? 1 : (G <= 64 ? 4 : 16); }

@@ -94,7 +94,8 @@ struct GatherPlan {
   int64_t wgs() const { return (int64_t)G * S * NBT; }
 };
 // fused != 0: the table is built while staging (fused_build_supported).
-GatherPlan plan_gather(const rq_matrix* W, int B, int lut_bf16, int fused = 0);
+// mats = 2: one launch covers two matrices of W's shape (launch_gather_pair).
+GatherPlan plan_gather(const rq_matrix* W, int B, int lut_bf16, int fused = 0, int mats = 1);
 // Whether the lookup+sum can build the table itself while staging: one
 // activation vector, fp32 codebooks with d in {1, 2, 4}, 16-byte aligned.
 bool fused_build_supported(const rq_matrix* W, int B);
@@ -124,6 +125,19 @@ void take_stage_events(hipEvent_t* before, hipEvent_t* after);
 hipError_t launch_gather(const rq_matrix* W, const GatherPlan& plan, const void* lut, int lut_bf16, int B,
                          const GatherOut& o, hipStream_t stream, const float* fused_act = nullptr,
                          const float* fused_x2 = nullptr);
+// Two matrices of the same shape (W1, W2) and one activation vector x, with
+// the fused table build, in one launch (plan from plan_gather(W1, 1, 0, 1, 2)):
+// each writes its partial sums [G][1][rows] (G > 1), or with G == 1 its sums,
+// to part1 / part2. No finish pass.
+hipError_t launch_gather_pair(const rq_matrix* W1, const rq_matrix* W2, const GatherPlan& plan, const float* x,
+                              float* part1, float* part2, hipStream_t stream);
+// Fused table build whose activation is gelu_tanh(g) * u, g and u summed from
+// the partial sums [2][pro_G][pro_rows] of launch_gather_pair in the finish
+// pass's order (bit-identical to finishing them first); then as launch_gather.
+// Returns hipErrorInvalidValue when the extra LDS does not fit.
+hipError_t launch_gather_pro(const rq_matrix* W, const GatherPlan& plan, const float* pro_partial, int pro_G,
+                             int64_t pro_rows, const GatherOut& o, hipStream_t stream);
+size_t gather_pro_lds(const rq_matrix* W, const GatherPlan& plan, int pro_G);
 int key_blocks(const GatherPlan& plan, int64_t rows);
 // argmax from the per-block keys (argmax may be null) and, with topk > 0, the
 // top-k of the logits (cand: [B][epi_blocks(rows)][topk] scratch).
@@ -134,6 +148,7 @@ hipError_t launch_select(const uint64_t* block_keys, int nkb, int B, int32_t* ar
 // applies the softcap, writes out [B][rows] and one selection key per block of
 // rows (block_keys [B][finish_key_blocks(G, rows)], or null).
 int finish_key_blocks(int G, int64_t rows);
+int finish_parts(int G);   // threads per row of the finish pass (its summation order)
 hipError_t launch_finish(const float* partial, int G, int B, int64_t rows, float softcap, float* out,
                          uint64_t* block_keys, hipStream_t stream);
 

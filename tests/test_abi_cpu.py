@@ -167,3 +167,25 @@ def test_logits_method_and_checks():
     assert call(topk=3, ids=0) == B.RQ_ERR_NULL
     assert call(Bn=-2) == B.RQ_ERR_SHAPE
     assert call(Bn=0, h=0, ws=0, ws_bytes=0) == B.RQ_OK
+
+
+def test_mlp_workspace_and_rejects():
+    """rq_lut_mlp: the fused route's workspace holds partial sums only (no tables); mismatched shapes and
+    missing buffers are rejected on the host before any launch."""
+    lib = B.lib()
+    gate = gemma_desc(rows=9216, D=2304, M=1152, d=2, cb_dtype=B.RQ_F32)
+    up = gemma_desc(rows=9216, D=2304, M=1152, d=2, cb_dtype=B.RQ_F32, codebooks=0x30000, codes=0x40000)
+    down = gemma_desc(rows=2304, D=9216, M=4608, d=2, cb_dtype=B.RQ_F32, codebooks=0x50000, codes=0x60000)
+    g, u, d = (ctypes.byref(m) for m in (gate, up, down))
+    ws1 = lib.rq_lut_mlp_workspace(g, u, d, 1)
+    assert 0 < ws1 < 2 * 1152 * 1024 * 4 and ws1 % 256 == 0          # no table in the fused route
+    assert lib.rq_lut_mlp_workspace(g, u, d, 2) >= 2 * 2 * 9216 * 4      # g and u, then matvec workspaces
+    assert lib.rq_lut_mlp_workspace(g, u, d, 0) == 0
+    bad_up = gemma_desc(rows=9215, D=2304, M=1152, d=2, cb_dtype=B.RQ_F32)
+    assert lib.rq_lut_mlp(g, ctypes.byref(bad_up), d, 0x1000, 1, 0x2000, 0x100000, 1 << 30, None) == B.RQ_ERR_SHAPE
+    bad_down = gemma_desc(rows=2304, D=9214, M=4607, d=2, cb_dtype=B.RQ_F32)
+    assert lib.rq_lut_mlp(g, u, ctypes.byref(bad_down), 0x1000, 1, 0x2000, 0x100000, 1 << 30, None) == B.RQ_ERR_SHAPE
+    assert lib.rq_lut_mlp(g, u, d, None, 1, 0x2000, 0x100000, 1 << 30, None) == B.RQ_ERR_NULL
+    assert lib.rq_lut_mlp(g, u, d, 0x1000, 1, 0x2000, 0x100000, 16, None) == B.RQ_ERR_WORKSPACE
+    assert lib.rq_lut_mlp(g, u, d, 0x1000, 1, 0x2000, 0x100008, 1 << 30, None) == B.RQ_ERR_ALIGN
+    assert lib.rq_lut_mlp(g, u, d, None, 0, None, None, 0, None) == B.RQ_OK

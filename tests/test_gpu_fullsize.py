@@ -81,7 +81,8 @@ def test_stress_head_full():
 
 
 def test_mlp_26_layers_full():
-    """All 26 Gemma-2-2B MLP layers (independent codes and codebooks, the same x): g, u and y of every layer."""
+    """All 26 Gemma-2-2B MLP layers (independent codes and codebooks, the same x): g, u and y of every layer,
+    and rq_lut_mlp's y against the three calls."""
     x = synth.make_mlp_x()
     xd = dev(x)
     for i in range(synth.MLP_LAYERS):
@@ -90,6 +91,7 @@ def test_mlp_26_layers_full():
         g = la.lut_matvec(Wg, xd)
         u = la.lut_matvec(Wu, xd)
         y = la.lut_matvec(Wd, g, x2=u, prologue=la.RQ_PRO_GELU_TANH_MUL)
+        check_logits(host(la.lut_mlp(Wg, Wu, Wd, xd)), host(y).astype(np.float64))   # the fused block
         og, ou, _, oy = O().mlp((gate.codes, gate.codebooks, False), (up.codes, up.codebooks, False),
                                 (down.codes, down.codebooks, False), x)
         check_logits(host(g), og)
