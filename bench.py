@@ -320,6 +320,37 @@ def extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, dev):
                      "code_stream_gbs": formats.code_bytes(cs.V, cs.L, cs.M) / (ts * 1e-3) / 1e9,
                      "method": "table (bf16), several batch tiles staged from a batch-tiled copy"}
     del SW, slut, slg, sws
+    torch.cuda.empty_cache()
+
+    # per-token composite: the token's embedding row, 26 distinct MLP layers chained (rq_lut_mlp) and the
+    # head's argmax, fed back as the next token on the device; 80 tokens
+    from lut_logits_amd.composite import DecodeLoop
+    layers = []
+    for i in range(synth.MLP_LAYERS):
+        layers.append(tuple(la.to_device(m) for m in synth.make_mlp_layer(i)))
+    loop = DecodeLoop(Ws[0], layers, softcap=cfg.softcap, max_tokens=80)
+    loop.run(1, 8)
+    torch.cuda.synchronize()
+    ntok = 80
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    loop.run(1, ntok)
+    e1.record()
+    torch.cuda.synchronize()
+    tt = e0.elapsed_time(e1) / ntok
+    def cbb(m):
+        return m.codebooks.numel() * m.codebooks.element_size()
+
+    mlp_bytes = synth.MLP_LAYERS * sum(formats.code_bytes(m.rows, m.L, m.M) + cbb(m) for m in layers[0])
+    head_bytes = formats.code_bytes(V, cfg.L, cfg.M) + cbb(Ws[0])
+    res["per_token_composite"] = {
+        "ms_per_token": tt, "tokens_per_s": 1e3 / tt, "tokens": ntok, "mlp_layers": synth.MLP_LAYERS,
+        "bytes_per_token": mlp_bytes + head_bytes, "gbs": (mlp_bytes + head_bytes) / (tt * 1e-3) / 1e9,
+        "resident_bytes": sum(m.resident_bytes() for lay in layers for m in lay) + Ws[0].resident_bytes(),
+        "distinct_tokens": int(torch.unique(loop.ids[:ntok + 1]).numel()),
+        "what": "embedding row (x sqrt(D)) -> 26 RQ MLP blocks chained -> RQ head softcap+argmax; no attention"}
+    del loop, layers
+    torch.cuda.empty_cache()
     return res
 
 

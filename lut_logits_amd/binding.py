@@ -175,7 +175,7 @@ def lut_logits_workspace(W, B, topk=0, lut_dtype="f32"):
 
 
 def workspace(nbytes, device="cuda"):
-    """A workspace buffer: zero-filled once, as the library requires before first use."""
+    """A 256-byte aligned device workspace (the library needs no particular initial contents)."""
     return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
