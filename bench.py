@@ -302,6 +302,28 @@ def extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, dev):
     del dl, wsm, wsf, g, u, y
     torch.cuda.empty_cache()
 
+    # the MLP RQ page's second-attempt layer: d=8, K=1024 for gate/up (10-bit codes), K=256 for down
+    # (8-bit codes), fp32 codebooks
+    v2 = [synth.make_mlp_v2_layer(i) for i in range(2)]
+    dv2 = [(la.to_device(a, "packed10"), la.to_device(b, "packed10"), la.to_device(c, "packed8")) for a, b, c in v2]
+    wsv2 = la.workspace(la.lut_mlp_workspace(*dv2[0], 1), dev)
+
+    def mlp_v2(i=0):
+        la.lut_mlp(*dv2[i & 1], x, ws=wsv2, out=y2)
+
+    y2 = torch.empty((1, synth.MLP_HIDDEN), device=dev)
+    tv2 = timed(mlp_v2, 20, torch)
+    code_v2 = sum(m.codes.numel() * m.codes.element_size() for m in dv2[0])
+    cb_v2 = sum(m.codebooks.nbytes for m in v2[0])
+    res["mlp_v2_layer"] = {
+        "ms": tv2, "code_bytes": code_v2, "codebook_bytes": cb_v2,
+        "gbs_codes_plus_codebooks": (code_v2 + cb_v2) / (tv2 * 1e-3) / 1e9,
+        "bits_per_param": formats.mlp_average_bpp(synth.MLP_HIDDEN, synth.MLP_INTER, synth.MLP_V2_D_SUB,
+                                                  synth.MLP_V2_K_GATE_UP, synth.MLP_V2_K_DOWN, synth.MLP_L),
+        "what": "d=8; gate/up K=1024 (10-bit codes), down K=256 (8-bit codes); fp32 codebooks; rq_lut_mlp"}
+    del v2, dv2, wsv2, y2
+    torch.cuda.empty_cache()
+
     # stress head: K=4096, L=4, B=64, bf16 table, softcap 30, top-50 (one call pair: build + logits)
     cs = synth.CONFIGS["stress"]
     smat, sh, _ = synth.make_head(cs)

@@ -89,16 +89,21 @@ typedef enum rq_prologue {
  *                     behind the runtime-compression page's 265 MB artifact,
  *                     laid out so every load stays 16-byte aligned and every
  *                     code is one bit-field extract.
- * Every entry point reads all three. BLOCKED and PACKED10 are serving layouts:
+ *   RQ_CODES_PACKED8  the 8-bit code stream (K <= 256): [ceil(NP/16)][rows]
+ *                     of 16 bytes; in block q, byte i of a row holds the code
+ *                     of pair 16q + i (unused slots are 0). The uint8 codes of
+ *                     the MLP RQ page's K=256 down projections.
+ * Every entry point reads all four. BLOCKED and PACKED10 are serving layouts:
  * a wave loads 64 rows x 16 bytes as one contiguous 1 KB run, whatever chunk of
- * pairs it works on. rq_pack_codes and rq_pack_codes10 convert ROWS to them
- * once, at load. With RQ_CODES_ROWS, rq_lut_logits and rq_lut_matvec need
+ * pairs it works on. rq_pack_codes, rq_pack_codes10 and rq_pack_codes8 convert
+ * ROWS to them once, at load. With RQ_CODES_ROWS, rq_lut_logits and rq_lut_matvec need
  * NP % 8 == 0.
  */
 typedef enum rq_codes_layout {
   RQ_CODES_ROWS = 0,
   RQ_CODES_BLOCKED = 1,
-  RQ_CODES_PACKED10 = 2
+  RQ_CODES_PACKED10 = 2,
+  RQ_CODES_PACKED8 = 3
 } rq_codes_layout;
 
 /*
@@ -109,7 +114,8 @@ typedef enum rq_codes_layout {
  *   K             codewords per codebook, 1 <= K <= 65536 (but see RQ_MAX_K_F32)
  *   L             residual levels, 1 <= L <= RQ_MAX_L
  *   cb_dtype      RQ_F32 or RQ_BF16, the storage type of the codebooks
- *   codes_layout  RQ_CODES_ROWS, RQ_CODES_BLOCKED or RQ_CODES_PACKED10 (K <= 1024)
+ *   codes_layout  RQ_CODES_ROWS, RQ_CODES_BLOCKED, RQ_CODES_PACKED10 (K <= 1024)
+ *                 or RQ_CODES_PACKED8 (K <= 256)
  *   codebooks     device [L][M][K][d] of cb_dtype
  *   codes         device uint16 in codes_layout, 16-byte aligned
  */
@@ -144,6 +150,18 @@ size_t rq_packed10_codes_bytes(int64_t rows, int32_t L, int32_t M);
  */
 rq_status rq_pack_codes10(const uint16_t* src, int64_t rows, int32_t L, int32_t M, uint16_t* dst,
                           hipStream_t stream);
+
+/* Bytes of the RQ_CODES_PACKED8 layout: ceil(L*M/16) * rows * 16. */
+size_t rq_packed8_codes_bytes(int64_t rows, int32_t L, int32_t M);
+
+/*
+ * Convert codes from RQ_CODES_ROWS (src, uint16 [rows][L*M]) to
+ * RQ_CODES_PACKED8 (dst, rq_packed8_codes_bytes bytes). Codes must be below
+ * 256 (a precondition: the bits above the eighth are dropped). src and dst
+ * must not overlap.
+ */
+rq_status rq_pack_codes8(const uint16_t* src, int64_t rows, int32_t L, int32_t M, uint16_t* dst,
+                         hipStream_t stream);
 
 /* Largest K whose per-subspace table (K entries) fits the kernels' on-chip
  * staging: 32768 for fp32 tables, 65536 for bf16 tables. */

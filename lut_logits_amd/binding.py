@@ -16,12 +16,14 @@ LIB_PATH = os.path.join(HERE, "librq_lut.so")
 RQ_OK, RQ_ERR_NULL, RQ_ERR_SHAPE, RQ_ERR_DTYPE, RQ_ERR_ALIGN, RQ_ERR_WORKSPACE, RQ_ERR_HIP = 0, -1, -2, -3, -4, -5, -6
 RQ_F32, RQ_BF16 = 0, 1
 RQ_PRO_NONE, RQ_PRO_GELU_TANH_MUL = 0, 1
-RQ_CODES_ROWS, RQ_CODES_BLOCKED, RQ_CODES_PACKED10 = 0, 1, 2
-_LAYOUTS = {"rows": RQ_CODES_ROWS, "blocked": RQ_CODES_BLOCKED, "packed10": RQ_CODES_PACKED10}
+RQ_CODES_ROWS, RQ_CODES_BLOCKED, RQ_CODES_PACKED10, RQ_CODES_PACKED8 = 0, 1, 2, 3
+_LAYOUTS = {"rows": RQ_CODES_ROWS, "blocked": RQ_CODES_BLOCKED, "packed10": RQ_CODES_PACKED10,
+            "packed8": RQ_CODES_PACKED8}
 RQ_METHOD_TABLE, RQ_METHOD_MATRIX_CORES = 0, 1
 
 # Every symbol include/rq_lut.h declares.
-EXPORTS = ("rq_blocked_codes_bytes", "rq_pack_codes", "rq_packed10_codes_bytes", "rq_pack_codes10", "rq_lut_bytes", "rq_build_lut", "rq_lut_logits_workspace",
+EXPORTS = ("rq_blocked_codes_bytes", "rq_pack_codes", "rq_packed10_codes_bytes", "rq_pack_codes10",
+           "rq_packed8_codes_bytes", "rq_pack_codes8", "rq_lut_bytes", "rq_build_lut", "rq_lut_logits_workspace",
            "rq_lut_logits", "rq_logits_method", "rq_logits_workspace", "rq_logits", "rq_decode_rows", "rq_lut_matvec_workspace", "rq_lut_matvec",
            "rq_lut_mlp_workspace", "rq_lut_mlp", "rq_dense_logits_workspace", "rq_dense_logits", "rq_set_stage_events", "rq_status_string", "rq_last_error", "rq_version")
 
@@ -55,6 +57,8 @@ def lib():
             "rq_pack_codes": (_i32, [_vp, _i64, _i32, _i32, _vp, _vp]),
             "rq_packed10_codes_bytes": (_sz, [_i64, _i32, _i32]),
             "rq_pack_codes10": (_i32, [_vp, _i64, _i32, _i32, _vp, _vp]),
+            "rq_packed8_codes_bytes": (_sz, [_i64, _i32, _i32]),
+            "rq_pack_codes8": (_i32, [_vp, _i64, _i32, _i32, _vp, _vp]),
             "rq_lut_bytes": (_sz, [_MP, _i32, _i32]),
             "rq_build_lut": (_i32, [_MP, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
             "rq_lut_logits_workspace": (_sz, [_MP, _i32, _i32, _i32]),
@@ -127,7 +131,7 @@ def to_device(mat, layout="blocked", device="cuda"):
     rows_codes = torch.from_numpy(np.ascontiguousarray(mat.codes).view(np.int16)).to(device)
     if layout == "rows":
         return DeviceMatrix(mat.rows, mat.D, mat.M, mat.K, mat.L, mat.cb_dtype, cb, rows_codes, "rows")
-    packer = pack_codes10 if layout == "packed10" else pack_codes
+    packer = {"packed10": pack_codes10, "packed8": pack_codes8}.get(layout, pack_codes)
     packed = packer(rows_codes, mat.rows, mat.L, mat.M)
     del rows_codes
     return DeviceMatrix(mat.rows, mat.D, mat.M, mat.K, mat.L, mat.cb_dtype, cb, packed, layout)
@@ -142,6 +146,17 @@ def pack_codes(rows_codes, rows, L, M):
     nbytes = blocked_codes_bytes(rows, L, M)
     dst = torch.empty(nbytes // 2, dtype=torch.int16, device=rows_codes.device)
     check(lib().rq_pack_codes(_ptr(rows_codes), rows, L, M, _ptr(dst), _stream()))
+    return dst
+
+
+def packed8_codes_bytes(rows, L, M):
+    return lib().rq_packed8_codes_bytes(rows, L, M)
+
+
+def pack_codes8(rows_codes, rows, L, M):
+    """rq_pack_codes8: [rows][L*M] uint16 (codes < 256) -> the 8-bit layout (an int16 tensor)."""
+    dst = torch.empty(packed8_codes_bytes(rows, L, M) // 2, dtype=torch.int16, device=rows_codes.device)
+    check(lib().rq_pack_codes8(_ptr(rows_codes), rows, L, M, _ptr(dst), _stream()))
     return dst
 
 

@@ -46,10 +46,12 @@ rq_status check_matrix(const rq_matrix* W, bool need_codes) {
   if ((int64_t)W->L * W->M > (1 << 24)) return fail(RQ_ERR_SHAPE, "L*M=%lld too large", (long long)W->L * W->M);
   if (!valid_dtype(W->cb_dtype)) return fail(RQ_ERR_DTYPE, "unknown codebook dtype %d", W->cb_dtype);
   if (W->codes_layout != RQ_CODES_ROWS && W->codes_layout != RQ_CODES_BLOCKED &&
-      W->codes_layout != RQ_CODES_PACKED10)
+      W->codes_layout != RQ_CODES_PACKED10 && W->codes_layout != RQ_CODES_PACKED8)
     return fail(RQ_ERR_DTYPE, "unknown codes layout %d", W->codes_layout);
   if (W->codes_layout == RQ_CODES_PACKED10 && W->K > 1024)
     return fail(RQ_ERR_SHAPE, "10-bit packed codes need K <= 1024 (K=%d)", W->K);
+  if (W->codes_layout == RQ_CODES_PACKED8 && W->K > 256)
+    return fail(RQ_ERR_SHAPE, "8-bit packed codes need K <= 256 (K=%d)", W->K);
   if (!W->codebooks) return fail(RQ_ERR_NULL, "codebooks is NULL");
   if (!aligned(W->codebooks, W->cb_dtype == RQ_F32 ? 4 : 2)) return fail(RQ_ERR_ALIGN, "codebooks misaligned");
   if (need_codes) {
@@ -176,6 +178,21 @@ rq_status rq_pack_codes10(const uint16_t* src, int64_t rows, int32_t L, int32_t 
   if (!src || !dst) return fail(RQ_ERR_NULL, "pack10: NULL buffer");
   if (!aligned(src, 2) || !aligned(dst, 16)) return fail(RQ_ERR_ALIGN, "pack10: misaligned buffer");
   return launched(rq::launch_pack_codes10(src, rows, L * M, dst, stream), "rq_pack_codes10");
+}
+
+size_t rq_packed8_codes_bytes(int64_t rows, int32_t L, int32_t M) {
+  if (rows < 0 || L < 1 || M < 1) return 0;
+  return (size_t)(((int64_t)L * M + 15) / 16) * (size_t)rows * 16;
+}
+
+rq_status rq_pack_codes8(const uint16_t* src, int64_t rows, int32_t L, int32_t M, uint16_t* dst,
+                         hipStream_t stream) {
+  if (rows < 0 || rows >= ((int64_t)1 << 29) || L < 1 || L > RQ_MAX_L || M < 1 || (int64_t)L * M > (1 << 24))
+    return fail(RQ_ERR_SHAPE, "bad pack shape rows=%lld L=%d M=%d", (long long)rows, L, M);
+  if (rows == 0) return RQ_OK;
+  if (!src || !dst) return fail(RQ_ERR_NULL, "pack8: NULL buffer");
+  if (!aligned(src, 2) || !aligned(dst, 16)) return fail(RQ_ERR_ALIGN, "pack8: misaligned buffer");
+  return launched(rq::launch_pack_codes8(src, rows, L * M, dst, stream), "rq_pack_codes8");
 }
 
 size_t rq_lut_bytes(const rq_matrix* W, int32_t B, int32_t lut_dtype) {

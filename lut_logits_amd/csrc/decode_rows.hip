@@ -121,6 +121,21 @@ __global__ __launch_bounds__(256) void pack_codes10_kernel(const uint16_t* __res
   dst[(int64_t)q * rows + r] = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// codes[r][p] (uint16, [rows][NP]) -> RQ_CODES_PACKED8: thread (block q, row r)
+// packs codes 16q .. 16q+15 of row r, one byte each (zero past NP).
+__global__ __launch_bounds__(256) void pack_codes8_kernel(const uint16_t* __restrict__ src, int64_t rows, int NP,
+                                                          uint4* __restrict__ dst) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int q = blockIdx.y;
+  if (r >= rows) return;
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  for (int t = 0; t < 16; ++t) {
+    const int p = 16 * q + t;
+    if (p < NP) w[t >> 2] |= ((uint32_t)src[r * NP + p] & 0xffu) << (8 * (t & 3));
+  }
+  dst[(int64_t)q * rows + r] = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 template <typename CbT, typename OutT>
 hipError_t decode_typed(const rq_matrix* W, const int32_t* ids, int n, void* out, int32_t* bad, hipStream_t stream) {
   const int64_t threads = (int64_t)n * W->D;
@@ -156,10 +171,17 @@ hipError_t launch_pack_codes10(const uint16_t* src, int64_t rows, int NP, uint16
   return hipGetLastError();
 }
 
+hipError_t launch_pack_codes8(const uint16_t* src, int64_t rows, int NP, uint16_t* dst, hipStream_t stream) {
+  const int NQ = (NP + 15) / 16;
+  dim3 grid((unsigned)((rows + 255) / 256), (unsigned)NQ);
+  hipLaunchKernelGGL(pack_codes8_kernel, grid, dim3(256), 0, stream, src, rows, NP, reinterpret_cast<uint4*>(dst));
+  return hipGetLastError();
+}
+
 CodeView code_view(const rq_matrix* W) {
   CodeView v;
   v.codes = W->codes;
-  v.packed10 = W->codes_layout == RQ_CODES_PACKED10;
+  v.cbits = W->codes_layout == RQ_CODES_PACKED10 ? 10 : (W->codes_layout == RQ_CODES_PACKED8 ? 8 : 16);
   if (W->codes_layout != RQ_CODES_ROWS) {
     v.s_blk = 8 * W->rows;
     v.s_row = 8;

@@ -145,14 +145,19 @@ __device__ __forceinline__ float lut_value<float>(const float* e) { return *e; }
 template <>
 __device__ __forceinline__ float lut_value<uint16_t>(const uint16_t* e) { return bf16_to_f32(*e); }
 
-// Code t of a row's 16-byte block: 16-bit layouts hold 8 codes (two per
-// word), RQ_CODES_PACKED10 holds 12 (three 10-bit fields per word).
-template <bool PK>
+// Code t of a row's 16-byte block, by code width CB: 16-bit layouts hold 8
+// codes (two per word), RQ_CODES_PACKED10 12 (three 10-bit fields per word),
+// RQ_CODES_PACKED8 16 (four bytes per word).
+template <int CB>
 __device__ __forceinline__ uint32_t code_of(const uint4& w, int t) {
-  if (PK) {
+  if (CB == 10) {
     const int wi = t / 3;
     const uint32_t word = wi == 0 ? w.x : wi == 1 ? w.y : wi == 2 ? w.z : w.w;
     return (word >> (10 * (t - 3 * wi))) & 0x3ffu;
+  }
+  if (CB == 8) {
+    const uint32_t word = (t >> 2) == 0 ? w.x : (t >> 2) == 1 ? w.y : (t >> 2) == 2 ? w.z : w.w;
+    return (word >> (8 * (t & 3))) & 0xffu;
   }
   const uint32_t word = (t >> 1) == 0 ? w.x : (t >> 1) == 1 ? w.y : (t >> 1) == 2 ? w.z : w.w;
   return (t & 1) ? (word >> 16) : (word & 0xffffu);
@@ -234,11 +239,12 @@ __device__ __forceinline__ void regs_to_lds(const ChunkRegs<RS>& r, u32x4* dst, 
 // waves per SIMD: the register budget is 128 VGPRs, stated explicitly so the
 // compiler does not trade registers for an occupancy the LDS cannot reach.
 // FD > 0: fused table build (see fused_word); requires LutT float, BT 1, REG.
-// PK: codes in RQ_CODES_PACKED10 (12 pairs per 16-byte block).
-template <typename LutT, int BT, int NSTEP, bool REG, int FD = 0, bool PK = false>
+// CB: code width of the layout (16, 10 for RQ_CODES_PACKED10, 8 for
+// RQ_CODES_PACKED8): 8, 12 or 16 pairs per 16-byte block.
+template <typename LutT, int BT, int NSTEP, bool REG, int FD = 0, int CB = 16>
 __global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(1, 4)))
 void gather_kernel(GatherArgs a) {
-  constexpr int PPB = PK ? 12 : 8;         // pairs per code block
+  constexpr int PPB = CB == 10 ? 12 : (CB == 8 ? 16 : 8);   // pairs per code block
   static_assert(FD == 0 || (BT == 1 && REG && sizeof(LutT) == 4 && 4 % FD == 0), "fused build: fp32, B=1, FD | 4");
   constexpr int QL = (BT >= 16) ? 4 : 1;   // lanes per row
   constexpr int BQ = BT / QL;              // batch entries per lane
@@ -329,7 +335,7 @@ void gather_kernel(GatherArgs a) {
         for (int t = 0; t < LG; ++t) {
           const LutT* base = tab + (size_t)(PPB * q + t0 + t - p0) * a.K * BT + rq * BQ;
 #pragma unroll
-          for (int st = 0; st < NSTEP; ++st) v[t][st] = lut_value(base + code_of<PK>(w[st], t0 + t) * BT);
+          for (int st = 0; st < NSTEP; ++st) v[t][st] = lut_value(base + code_of<CB>(w[st], t0 + t) * BT);
         }
 #pragma unroll
         for (int t = 0; t < LG; ++t)
@@ -347,12 +353,12 @@ void gather_kernel(GatherArgs a) {
         // issue every lookup of this pair before adding, so the LDS reads overlap
         float v[NSTEP];
 #pragma unroll
-        for (int st = 0; st < NSTEP; ++st) v[st] = lut_value(base + code_of<PK>(w[st], t) * BT);
+        for (int st = 0; st < NSTEP; ++st) v[st] = lut_value(base + code_of<CB>(w[st], t) * BT);
 #pragma unroll
         for (int st = 0; st < NSTEP; ++st) acc[st][0] += v[st];
       } else {
 #pragma unroll
-        for (int st = 0; st < NSTEP; ++st) lookup_add<LutT, BQ>(acc[st], base + code_of<PK>(w[st], t) * BT);
+        for (int st = 0; st < NSTEP; ++st) lookup_add<LutT, BQ>(acc[st], base + code_of<CB>(w[st], t) * BT);
       }
     }
   };
@@ -515,7 +521,7 @@ void gather_kernel(GatherArgs a) {
   if (tid < BT && b0 + tid < a.B) a.block_keys[(size_t)(b0 + tid) * a.S + s] = s_keys[tid];
 }
 
-template <typename LutT, int BT, int NSTEP, int FD = 0, bool PK = false>
+template <typename LutT, int BT, int NSTEP, int FD = 0, int CB = 16>
 hipError_t launch_gather_typed(const GatherArgs& a, const GatherPlan& plan, hipStream_t stream) {
   if (plan.steps < 1 || plan.steps > NSTEP) return hipErrorInvalidValue;   // a lane holds NSTEP rows at most
   const size_t chunk_bytes = (size_t)plan.P * a.K * BT * sizeof(LutT);
@@ -524,9 +530,9 @@ hipError_t launch_gather_typed(const GatherArgs& a, const GatherPlan& plan, hipS
                    ((size_t)a.K * BT * sizeof(LutT)) % 16 == 0;
   void (*kern)(GatherArgs);
   if constexpr (FD != 0)
-    kern = gather_kernel<LutT, BT, NSTEP, true, FD, PK>;
+    kern = gather_kernel<LutT, BT, NSTEP, true, FD, CB>;
   else
-    kern = reg ? gather_kernel<LutT, BT, NSTEP, true, 0, PK> : gather_kernel<LutT, BT, NSTEP, false, 0, PK>;
+    kern = reg ? gather_kernel<LutT, BT, NSTEP, true, 0, CB> : gather_kernel<LutT, BT, NSTEP, false, 0, CB>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget);
   if (e != hipSuccess) return e;
   hipEvent_t before, after;
@@ -895,28 +901,28 @@ GatherPlan plan_gather(const rq_matrix* W, int B, int lut_bf16, int fused, int m
   return plan;
 }
 
-template <bool PK>
+template <int CB>
 hipError_t dispatch_gather(const GatherArgs& a, const GatherPlan& plan, int d, int lut_bf16, bool fused,
                            hipStream_t stream) {
   if (fused) {
-    if (d == 1) return launch_gather_typed<float, 1, 4, 1, PK>(a, plan, stream);
+    if (d == 1) return launch_gather_typed<float, 1, 4, 1, CB>(a, plan, stream);
     if (d == 2) {
       switch (plan.steps) {
-        case 2: return launch_gather_typed<float, 1, 2, 2, PK>(a, plan, stream);
-        case 3: return launch_gather_typed<float, 1, 3, 2, PK>(a, plan, stream);
-        default: return launch_gather_typed<float, 1, 4, 2, PK>(a, plan, stream);
+        case 2: return launch_gather_typed<float, 1, 2, 2, CB>(a, plan, stream);
+        case 3: return launch_gather_typed<float, 1, 3, 2, CB>(a, plan, stream);
+        default: return launch_gather_typed<float, 1, 4, 2, CB>(a, plan, stream);
       }
     }
-    return launch_gather_typed<float, 1, 4, 4, PK>(a, plan, stream);
+    return launch_gather_typed<float, 1, 4, 4, CB>(a, plan, stream);
   }
   if (lut_bf16) {
-    if (plan.BT == 1) return launch_gather_typed<uint16_t, 1, 4, 0, PK>(a, plan, stream);
-    if (plan.BT == 4) return launch_gather_typed<uint16_t, 4, 4, 0, PK>(a, plan, stream);
-    return launch_gather_typed<uint16_t, 16, 4, 0, PK>(a, plan, stream);
+    if (plan.BT == 1) return launch_gather_typed<uint16_t, 1, 4, 0, CB>(a, plan, stream);
+    if (plan.BT == 4) return launch_gather_typed<uint16_t, 4, 4, 0, CB>(a, plan, stream);
+    return launch_gather_typed<uint16_t, 16, 4, 0, CB>(a, plan, stream);
   }
-  if (plan.BT == 1) return launch_gather_typed<float, 1, 4, 0, PK>(a, plan, stream);
-  if (plan.BT == 4) return launch_gather_typed<float, 4, 4, 0, PK>(a, plan, stream);
-  return launch_gather_typed<float, 16, 4, 0, PK>(a, plan, stream);
+  if (plan.BT == 1) return launch_gather_typed<float, 1, 4, 0, CB>(a, plan, stream);
+  if (plan.BT == 4) return launch_gather_typed<float, 4, 4, 0, CB>(a, plan, stream);
+  return launch_gather_typed<float, 16, 4, 0, CB>(a, plan, stream);
 }
 
 template <typename T>
@@ -987,8 +993,9 @@ GatherArgs gather_args(const rq_matrix* W, const GatherPlan& plan, const void* l
 
 hipError_t dispatch(const rq_matrix* W, const GatherArgs& a, const GatherPlan& plan, int lut_bf16, bool fused,
                     hipStream_t stream) {
-  return W->codes_layout == RQ_CODES_PACKED10 ? dispatch_gather<true>(a, plan, W->d, lut_bf16, fused, stream)
-                                              : dispatch_gather<false>(a, plan, W->d, lut_bf16, fused, stream);
+  if (W->codes_layout == RQ_CODES_PACKED10) return dispatch_gather<10>(a, plan, W->d, lut_bf16, fused, stream);
+  if (W->codes_layout == RQ_CODES_PACKED8) return dispatch_gather<8>(a, plan, W->d, lut_bf16, fused, stream);
+  return dispatch_gather<16>(a, plan, W->d, lut_bf16, fused, stream);
 }
 
 }  // namespace

@@ -44,20 +44,26 @@ __device__ __forceinline__ float gelu_tanh(float t) {
   return 0.5f * t * (1.0f + tanhf(k * (t + 0.044715f * t * t * t)));
 }
 
-// Code of pair p for row r. 16-bit layouts: codes[(p >> 3) * s_blk + r * s_row
-// + (p & 7)]; RQ_CODES_ROWS: s_blk = 8, s_row = NP; RQ_CODES_BLOCKED: s_blk =
-// 8 * rows, s_row = 8. RQ_CODES_PACKED10 (packed10 != 0): blocks of 12 pairs,
-// s_blk = 8 * rows and s_row = 8 in 16-bit units; pair 12q + 3w + i sits at
-// bits [10i, 10i+10) of the row's 32-bit word w of block q.
+// Code of pair p for row r. 16-bit layouts (cbits 16): codes[(p >> 3) * s_blk
+// + r * s_row + (p & 7)]; RQ_CODES_ROWS: s_blk = 8, s_row = NP;
+// RQ_CODES_BLOCKED: s_blk = 8 * rows, s_row = 8. RQ_CODES_PACKED10 (cbits 10):
+// blocks of 12 pairs, s_blk = 8 * rows and s_row = 8 in 16-bit units; pair
+// 12q + 3w + i sits at bits [10i, 10i+10) of the row's 32-bit word w of block
+// q. RQ_CODES_PACKED8 (cbits 8): blocks of 16 pairs, same strides; pair
+// 16q + i is byte i of the row's 16 bytes of block q.
 struct CodeView {
   const uint16_t* codes;
   int64_t s_blk;
   int64_t s_row;
-  int packed10;
+  int cbits;
 };
 
 __device__ __forceinline__ uint32_t code_at(const CodeView& cv, int64_t r, int p) {
-  if (cv.packed10) {
+  if (cv.cbits == 8) {
+    const int q = p >> 4;
+    return reinterpret_cast<const uint8_t*>(cv.codes + q * cv.s_blk + r * cv.s_row)[p & 15];
+  }
+  if (cv.cbits == 10) {
     const int q = p / 12;
     const int t = p - 12 * q;
     const int w = t / 3;
@@ -68,7 +74,9 @@ __device__ __forceinline__ uint32_t code_at(const CodeView& cv, int64_t r, int p
 }
 
 // Pairs per 16-byte code block of a serving layout.
-inline int pairs_per_block(const rq_matrix* W) { return W->codes_layout == RQ_CODES_PACKED10 ? 12 : 8; }
+inline int pairs_per_block(const rq_matrix* W) {
+  return W->codes_layout == RQ_CODES_PACKED10 ? 12 : (W->codes_layout == RQ_CODES_PACKED8 ? 16 : 8);
+}
 
 // ---------------------------------------------------------------- host side
 
@@ -179,6 +187,7 @@ hipError_t launch_decode_rows(const rq_matrix* W, const int32_t* ids, int n, int
                               int32_t* bad_ids, hipStream_t stream);
 hipError_t launch_pack_codes(const uint16_t* src, int64_t rows, int NP, uint16_t* dst, hipStream_t stream);
 hipError_t launch_pack_codes10(const uint16_t* src, int64_t rows, int NP, uint16_t* dst, hipStream_t stream);
+hipError_t launch_pack_codes8(const uint16_t* src, int64_t rows, int NP, uint16_t* dst, hipStream_t stream);
 hipError_t launch_dense_logits(const uint16_t* E, int64_t rows, int D, const float* h, int B, float softcap,
                                float* logits, uint64_t* block_keys, hipStream_t stream);
 

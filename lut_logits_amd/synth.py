@@ -152,6 +152,24 @@ def make_mlp_layer(i, inter=MLP_INTER, hidden=MLP_HIDDEN):
     return gate, up, down
 
 
+# The MLP RQ page's second attempt: subspaces of 8 values, K chosen per matrix (1024 for gate/up,
+# 256 for down, whose codes fit 8 bits), fp32 codebooks, two levels.
+MLP_V2_D_SUB = 8
+MLP_V2_K_GATE_UP = 1024
+MLP_V2_K_DOWN = 256
+
+
+def make_mlp_v2_layer(i, inter=MLP_INTER, hidden=MLP_HIDDEN):
+    """(gate, up, down) RQ matrices of layer i in the second-attempt shapes (seed 5000+i)."""
+    rng = np.random.default_rng(5000 + i)
+    m_in = hidden // MLP_V2_D_SUB
+    m_mid = inter // MLP_V2_D_SUB
+    gate = gen_matrix(rng, inter, hidden, m_in, MLP_V2_K_GATE_UP, MLP_L, MLP_SIGMAS, "f32")
+    up = gen_matrix(rng, inter, hidden, m_in, MLP_V2_K_GATE_UP, MLP_L, MLP_SIGMAS, "f32")
+    down = gen_matrix(rng, hidden, inter, m_mid, MLP_V2_K_DOWN, MLP_L, MLP_SIGMAS, "f32")
+    return gate, up, down
+
+
 def make_mlp_x(B=1, hidden=MLP_HIDDEN):
     return gen_hidden(np.random.default_rng(MLP_X_SEED), B, hidden)
 

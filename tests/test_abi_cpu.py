@@ -189,3 +189,20 @@ def test_mlp_workspace_and_rejects():
     assert lib.rq_lut_mlp(g, u, d, 0x1000, 1, 0x2000, 0x100000, 16, None) == B.RQ_ERR_WORKSPACE
     assert lib.rq_lut_mlp(g, u, d, 0x1000, 1, 0x2000, 0x100008, 1 << 30, None) == B.RQ_ERR_ALIGN
     assert lib.rq_lut_mlp(g, u, d, None, 0, None, None, 0, None) == B.RQ_OK
+
+
+def test_packed8_layout_checks():
+    """The 8-bit layout: byte counts, pack argument checks, and K <= 256 enforced on every entry point."""
+    lib = B.lib()
+    assert lib.rq_packed8_codes_bytes(256000, 2, 384) == 48 * 256000 * 16   # 768 bytes per Gemma-head row
+    assert lib.rq_packed8_codes_bytes(10, 1, 17) == 2 * 10 * 16
+    assert lib.rq_pack_codes8(None, 10, 2, 3, 0x1000, None) == B.RQ_ERR_NULL
+    assert lib.rq_pack_codes8(0x1000, 10, 0, 3, 0x1000, None) == B.RQ_ERR_SHAPE
+    assert lib.rq_pack_codes8(0x1000, 10, 2, 3, 0x1008, None) == B.RQ_ERR_ALIGN
+    assert lib.rq_pack_codes8(None, 0, 2, 3, None, None) == B.RQ_OK
+    W = gemma_desc(codes_layout=B.RQ_CODES_PACKED8)                        # K = 1024: too large
+    assert lib.rq_lut_logits_workspace(ctypes.byref(W), 1, 0, B.RQ_F32) == 0
+    assert call_logits(W) == B.RQ_ERR_SHAPE
+    W = gemma_desc(codes_layout=B.RQ_CODES_PACKED8, K=256)
+    assert lib.rq_lut_logits_workspace(ctypes.byref(W), 1, 0, B.RQ_F32) > 0
+    assert lib.rq_logits_method(ctypes.byref(W), 16) == B.RQ_METHOD_TABLE  # no matrix-core staging of 8-bit codes

@@ -107,6 +107,21 @@ def test_logits_table_method_matches_two_call_form():
         assert torch.equal(lg, lg2) and torch.equal(am, am2)
 
 
+def test_logits_packed8_uses_the_table_method():
+    """8-bit codes (K <= 256) are not staged for the matrix cores: rq_logits takes the table method at any B
+    and gives the two-call form's bits."""
+    rng = np.random.default_rng(800)
+    mat = synth.gen_matrix(rng, 3000, 96, 16, 256, 2, (0.02, 0.005), "bf16")
+    h = synth.gen_hidden(rng, 16, 96)
+    W, hd = to_dev(mat, "packed8"), dev(h)
+    assert la.logits_method(W, 16) == la.RQ_METHOD_TABLE
+    lg, am, _, _ = la.logits(W, hd, softcap=30.0)
+    lg2, am2, _, _ = la.lut_logits(W, la.build_lut(W, hd), 16, softcap=30.0)
+    assert torch.equal(lg, lg2) and torch.equal(am, am2)
+    _, ref = oracle_head(mat, h, 30.0)
+    check_logits(host(lg), ref)
+
+
 def test_logits_ties_and_empty():
     """K = 1: every logit ties and the argmax is row 0 on the matrix cores too; B = 0 is a no-op."""
     rng = np.random.default_rng(600)

@@ -88,3 +88,21 @@ def test_lut_mlp_exact_inputs_gemma_shape():
     g = la.lut_matvec(Wg, xd)
     assert np.array_equal(host(g).astype(np.float64), O().matvec(gate.codes, gate.codebooks, False, x))
     assert torch.equal(la.lut_mlp(Wg, Wu, Wd, xd), _three_calls(Wg, Wu, Wd, xd))
+
+
+def test_lut_mlp_second_attempt_shapes():
+    """The MLP RQ page's second-attempt layer: d=8 throughout, K=1024 for gate/up (10-bit codes), K=256 for
+    down (8-bit codes), fp32 codebooks. The table is built by the separate kernel (d=8), so the block is the
+    three matvecs: equal to them bit for bit, and close to the oracle."""
+    gate, up, down = synth.make_mlp_v2_layer(0)
+    x = synth.make_mlp_x()
+    Wg, Wu, Wd = to_dev(gate, "packed10"), to_dev(up, "packed10"), to_dev(down, "packed8")
+    xd = dev(x)
+    y = la.lut_mlp(Wg, Wu, Wd, xd)
+    assert torch.equal(y, _three_calls(Wg, Wu, Wd, xd))
+    og, ou, _, oy = O().mlp((gate.codes, gate.codebooks, False), (up.codes, up.codebooks, False),
+                            (down.codes, down.codebooks, False), x)
+    check_logits(host(la.lut_matvec(Wg, xd)), og)
+    check_logits(host(y), oy)
+    # the 8-bit stream is half the 16-bit one: 2304 rows x 2304 pairs
+    assert Wd.codes.numel() * 2 == 2304 * 2304

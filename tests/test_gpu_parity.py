@@ -47,9 +47,21 @@ def test_pack_codes10_bit_exact(rows, NP):
     assert np.array_equal(out, words.transpose(1, 0, 2).reshape(-1))
 
 
+@pytest.mark.parametrize("rows,NP", [(1, 1), (63, 7), (4097, 34), (130, 768), (65, 1000)])
+def test_pack_codes8_bit_exact(rows, NP):
+    """The 8-bit layout against a host packing: 16 codes per 16-byte block, one byte each."""
+    rng = np.random.default_rng(11 * rows + NP)
+    codes = rng.integers(0, 256, size=(rows, NP), dtype=np.uint16)
+    out = host(la.pack_codes8(dev(codes.view(np.int16)), rows, 1, NP)).view(np.uint8)
+    NQ = (NP + 15) // 16
+    padded = np.zeros((rows, 16 * NQ), np.uint8)
+    padded[:, :NP] = codes
+    assert np.array_equal(out, padded.reshape(rows, NQ, 16).transpose(1, 0, 2).reshape(-1))
+
+
 # ------------------------------------------------------------------ row decode
 
-@pytest.mark.parametrize("layout", ["rows", "blocked", "packed10"])
+@pytest.mark.parametrize("layout", ["rows", "blocked", "packed10", "packed8"])
 @pytest.mark.parametrize("L,cb_dtype,out_dtype", [(2, "f32", "f32"), (2, "f32", "bf16"), (2, "bf16", "bf16"),
                                                   (3, "f32", "f32"), (4, "bf16", "f32"), (1, "f32", "f32")])
 def test_decode_rows_bit_exact(layout, L, cb_dtype, out_dtype):
@@ -130,12 +142,14 @@ EXACT_SHAPES = [
 
 
 @pytest.mark.parametrize("shape", EXACT_SHAPES, ids=lambda s: "x".join(map(str, s)))
-@pytest.mark.parametrize("layout", ["rows", "blocked", "packed10"])
+@pytest.mark.parametrize("layout", ["rows", "blocked", "packed10", "packed8"])
 def test_lut_logits_exact(shape, layout):
     """Small-integer inputs: every fp32 step is exact, so logits (softcap off) equal the oracle bit for bit."""
     rows, D, M, K, L, B = shape
     if layout == "rows" and (L * M) % 8:
         pytest.skip("row-major codes need L*M % 8 == 0")
+    if (layout == "packed10" and K > 1024) or (layout == "packed8" and K > 256):
+        pytest.skip("K too large for the packed layout")
     mat, h = synth.gen_exact(rows + K, rows, D, M, K, L, B)
     W = to_dev(mat, layout)
     lut = la.build_lut(W, dev(h))
@@ -160,7 +174,7 @@ def test_tiny_config():
     """The tiny RQ head: V=4096, D=96, M=16, K=256, L=2, fp32 codebooks, softcap 30, argmax, 8 decoded rows."""
     cfg = synth.CONFIGS["tiny"]
     mat, h, ids = synth.make_head(cfg)
-    for layout in ("rows", "blocked", "packed10"):
+    for layout in ("rows", "blocked", "packed10", "packed8"):
         W = to_dev(mat, layout)
         lg, am, _, _ = la.lut_logits(W, la.build_lut(W, dev(h)), 1, softcap=cfg.softcap)
         _, ref = oracle_head(mat, h, cfg.softcap)
@@ -269,7 +283,7 @@ def test_lut_matvec_small_chain():
 
 
 @pytest.mark.parametrize("d", [1, 2, 4])
-@pytest.mark.parametrize("layout", ["rows", "blocked", "packed10"])
+@pytest.mark.parametrize("layout", ["rows", "blocked", "packed10", "packed8"])
 def test_lut_matvec_fused_build_exact(d, layout):
     """One activation vector with fp32 codebooks: the table is built while staging. Exact inputs, ragged rows
     and (blocked layout) a partly empty last code block: bit-exact against the oracle."""
