@@ -289,7 +289,7 @@ rq_status rq_lut_matvec(const rq_matrix* W, const float* x, const float* x2, int
  * paragraphs: the three projections as LUT matvecs):
  *     y = down( gelu_tanh(gate(x)) * up(x) )
  * with the arithmetic of the three rq_lut_matvec calls. With one activation
- * vector and fused table builds (fp32 codebooks, d in {1, 2, 4}) it takes
+ * vector and fused table builds (fp32 codebooks, d in {1, 2, 4, 8}) it takes
  * three launches instead of six: gate and up in one lookup+sum launch, down
  * with its activation summed straight from their partial sums in the finish
  * pass's order, then down's finish. Gate and up may then be split into a

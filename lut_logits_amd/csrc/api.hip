@@ -383,7 +383,7 @@ rq_status rq_decode_rows(const rq_matrix* W, const int32_t* ids, int32_t n, int3
 }
 
 // Workspace of rq_lut_matvec. Fused table build (one activation vector, fp32
-// codebooks, d in {1, 2, 4}): the partial sums [G][rows]. Otherwise: the fp32
+// codebooks, d in {1, 2, 4, 8}): the partial sums [G][rows]. Otherwise: the fp32
 // table [L][M][K][B], the partial sums [G][B][rows] (G > 1) and, with more
 // than one batch tile, the batch-tiled copy of the table.
 struct MatvecWs {
@@ -397,7 +397,7 @@ static MatvecWs matvec_ws(const rq_matrix* W, int32_t B) {
   m.fused = rq::fused_build_supported(W, B);
   if (m.fused) {
     m.plan = rq::plan_gather(W, B, 0, 1);
-    if (m.plan.BT == 0) m.fused = false;
+    if (m.plan.BT == 0 || !rq::plan_covers_blocks(W, m.plan)) m.fused = false;
   }
   if (!m.fused) m.plan = rq::plan_gather(W, B, 0);
   m.front = 0;
@@ -452,12 +452,14 @@ rq_status rq_lut_matvec(const rq_matrix* W, const float* x, const float* x2, int
 
 // Workspace of rq_lut_mlp. Fused route: the partial sums of gate and up
 // [2][Gg][rows] (their sums when Gg == 1), then down's partial sums
-// [Gd][down rows] (Gd > 1). Otherwise: g and u [2][B][rows], then one
-// rq_lut_matvec workspace large enough for the three calls.
+// [Gd][down rows] (Gd > 1), then -- when gate and up do not build their
+// tables while staging (pair_tables) -- their two fp32 tables. Otherwise: g
+// and u [2][B][rows], then one rq_lut_matvec workspace large enough for the
+// three calls.
 struct MlpWs {
-  bool fused;
+  bool fused, pair_tables;
   rq::GatherPlan pgu, pd;
-  size_t down_part, mv, total;
+  size_t down_part, tables, mv, total;
 };
 
 static rq_status check_mlp(const rq_matrix* gate, const rq_matrix* up, const rq_matrix* down, int32_t B) {
@@ -483,12 +485,18 @@ static MlpWs mlp_ws(const rq_matrix* gate, const rq_matrix* up, const rq_matrix*
     if (const char* pm = getenv("RQ_MLP_PAIR_MATS")) pair_mats = atoi(pm);
 #endif
     w.pgu = rq::plan_gather(gate, B, 0, 1, pair_mats);
+    if (w.pgu.BT != 0 && !rq::plan_covers_blocks(gate, w.pgu)) {   // gate and up from tables built first
+      w.pair_tables = true;
+      w.pgu = rq::plan_gather(gate, B, 0, 0, pair_mats);
+    }
     w.pd = rq::plan_gather(down, B, 0, 1);
-    w.fused = w.pgu.BT != 0 && w.pd.BT != 0 && rq::gather_pro_lds(down, w.pd, w.pgu.G) <= (size_t)rq::kLdsBudget;
+    w.fused = w.pgu.BT != 0 && w.pd.BT != 0 && rq::plan_covers_blocks(down, w.pd) &&
+              rq::gather_pro_lds(down, w.pd, w.pgu.G) <= (size_t)rq::kLdsBudget;
   }
   if (w.fused) {
     w.down_part = round_up((size_t)2 * w.pgu.G * gate->rows * sizeof(float), 256);
-    w.total = w.down_part + (w.pd.G > 1 ? round_up((size_t)w.pd.G * down->rows * sizeof(float), 256) : 0);
+    w.tables = w.down_part + (w.pd.G > 1 ? round_up((size_t)w.pd.G * down->rows * sizeof(float), 256) : 0);
+    w.total = w.tables + (w.pair_tables ? 2 * round_up(lut_elems(gate, B) * sizeof(float), 256) : 0);
     return w;
   }
   w.mv = round_up((size_t)2 * B * gate->rows * sizeof(float), 256);
@@ -518,7 +526,17 @@ rq_status rq_lut_mlp(const rq_matrix* gate, const rq_matrix* up, const rq_matrix
   if (w.fused) {
     float* pg = reinterpret_cast<float*>(base);
     float* pu = pg + (size_t)w.pgu.G * gate->rows;
-    hipError_t e = rq::launch_gather_pair(gate, up, w.pgu, x, pg, pu, stream);
+    hipError_t e;
+    if (w.pair_tables) {
+      float* tg = reinterpret_cast<float*>(base + w.tables);
+      float* tu = reinterpret_cast<float*>(base + w.tables + round_up(lut_elems(gate, B) * sizeof(float), 256));
+      e = rq::launch_build_lut(gate, x, nullptr, RQ_PRO_NONE, B, 0, tg, stream);
+      if (e == hipSuccess) e = rq::launch_build_lut(up, x, nullptr, RQ_PRO_NONE, B, 0, tu, stream);
+      if (e != hipSuccess) return launched(e, "rq_lut_mlp: gate and up tables");
+      e = rq::launch_gather_pair(gate, up, w.pgu, nullptr, tg, tu, pg, pu, stream);
+    } else {
+      e = rq::launch_gather_pair(gate, up, w.pgu, x, nullptr, nullptr, pg, pu, stream);
+    }
     if (e != hipSuccess) return launched(e, "rq_lut_mlp: gate and up lookup+sum");
     rq::GatherOut o{};
     o.partial = reinterpret_cast<float*>(base + w.down_part);

@@ -189,20 +189,51 @@ template <int RS>
 struct ChunkRegs {
   u32x4 w[RS];
 };
-template <int RS>
+// Word i of a chunk whose last word is `last`: words past the end repeat the
+// last one. With PAIRS (a codeword spread over two words, fused d = 8) an
+// even index clamps to last - 1 and an odd one to last, so the two lanes that
+// hold one codeword's halves keep holding one codeword (last is odd then).
+template <bool PAIRS>
+__device__ __forceinline__ int clamp_word(int i, int last) {
+  return PAIRS ? min(i, last - 1 + (i & 1)) : min(i, last);
+}
+template <int RS, bool PAIRS = false>
 __device__ __forceinline__ void chunk_to_regs(ChunkRegs<RS>& r, const u32x4* __restrict__ src, int tid, int last) {
 #pragma unroll
-  for (int i = 0; i < RS; ++i) r.w[i] = src[min(tid + i * kGatherThreads, last)];
+  for (int i = 0; i < RS; ++i) r.w[i] = src[clamp_word<PAIRS>(tid + i * kGatherThreads, last)];
 }
-// Fused table build (B == 1, fp32 codebooks, subspace width FD dividing 4):
+// Fused table build (B == 1, fp32 codebooks, subspace width FD in {1, 2, 4, 8}):
 // the registers hold codebook words instead of table words; each word is 4/FD
-// codewords of one pair, whose table entries
+// codewords of one pair (FD = 8: half a codeword), whose table entries
 //     LUT[p][k] = sum_{j<FD} act[m*FD + j] * C[p][k][j]      (m = p mod M)
 // are computed with the same fmaf chain as the table-build kernel and written
 // to LDS. act sits in LDS after the chunk.
 template <int FD>
 __device__ __forceinline__ void fused_word(const u32x4 w, int i, float* tab, const float* act_s, int pl0, int K) {
-  constexpr int EPW = 4 / FD;
+  if constexpr (FD == 8) {
+    // Words 2e and 2e+1 (codeword e) sit in adjacent lanes: the even lane runs
+    // the chain over values 0..3, hands its sum to the odd lane, which runs it
+    // on over values 4..7 -- one sequential chain, as in the table build.
+    const int e = i >> 1;
+    const int pl = pl0 + e / K;
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t bits = w[j];
+      acc = fmaf(act_s[pl * 8 + j], __uint_as_float(bits), acc);
+    }
+    acc = __shfl_xor(acc, 1, 64);
+    if (i & 1) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t bits = w[j];
+        acc = fmaf(act_s[pl * 8 + 4 + j], __uint_as_float(bits), acc);
+      }
+      tab[e] = acc;
+    }
+    return;
+  }
+  constexpr int EPW = 4 / (FD == 8 ? 4 : FD);
   const int e0 = i * EPW;                 // entry index within the chunk: (pair - p0) * K + k
   const int pl = pl0 + e0 / K;            // the pair's index within the group (its activation slice)
   float v[EPW];
@@ -226,7 +257,8 @@ template <int FD, int RS>
 __device__ __forceinline__ void regs_to_lds_fused(const ChunkRegs<RS>& r, float* tab, const float* act_s, int tid,
                                                   int last, int pl0, int K) {
 #pragma unroll
-  for (int i = 0; i < RS; ++i) fused_word<FD>(r.w[i], min(tid + i * kGatherThreads, last), tab, act_s, pl0, K);
+  for (int i = 0; i < RS; ++i)
+    fused_word<FD>(r.w[i], clamp_word<FD == 8>(tid + i * kGatherThreads, last), tab, act_s, pl0, K);
 }
 
 template <int RS>
@@ -245,7 +277,8 @@ template <typename LutT, int BT, int NSTEP, bool REG, int FD = 0, int CB = 16>
 __global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(1, 4)))
 void gather_kernel(GatherArgs a) {
   constexpr int PPB = CB == 10 ? 12 : (CB == 8 ? 16 : 8);   // pairs per code block
-  static_assert(FD == 0 || (BT == 1 && REG && sizeof(LutT) == 4 && 4 % FD == 0), "fused build: fp32, B=1, FD | 4");
+  static_assert(FD == 0 || (BT == 1 && REG && sizeof(LutT) == 4 && (4 % FD == 0 || FD == 8)),
+                "fused build: fp32, B=1, FD in {1, 2, 4, 8}");
   constexpr int QL = (BT >= 16) ? 4 : 1;   // lanes per row
   constexpr int BQ = BT / QL;              // batch entries per lane
   constexpr int RPS = kGatherThreads / QL; // rows per step
@@ -374,7 +407,7 @@ void gather_kernel(GatherArgs a) {
   // loads (clamped to the last word of the chunk).
   if (REG) {
     const int n4 = min(a.P, a.NP - c_begin * a.P) * words_per_pair;
-    chunk_to_regs(nxt, lut4 + (size_t)c_begin * a.P * words_per_pair, tid, n4 - 1);
+    chunk_to_regs<RS, FD == 8>(nxt, lut4 + (size_t)c_begin * a.P * words_per_pair, tid, n4 - 1);
   }
   // FD: the activation slices of this group's pairs [pa, pb) go to LDS after
   // the chunk, once (pair p uses elements (p % M)*FD .. +FD of the vector).
@@ -438,7 +471,7 @@ void gather_kernel(GatherArgs a) {
         regs_to_lds(nxt, reinterpret_cast<u32x4*>(tab), tid, pc * words_per_pair - 1);
       const int cn = min(c + 1, c_end - 1);
       const int n4n = min(a.P, a.NP - cn * a.P) * words_per_pair;
-      chunk_to_regs(nxt, lut4 + (size_t)cn * a.P * words_per_pair, tid, n4n - 1);
+      chunk_to_regs<RS, FD == 8>(nxt, lut4 + (size_t)cn * a.P * words_per_pair, tid, n4n - 1);
     } else {
       stage_chunk<LutT, BT>(tab, lut, p0, pc, a.K, a.tiled ? BT : a.B, a.tiled ? 0 : b0);
     }
@@ -787,15 +820,16 @@ double plan_cost_us(int64_t rows, int NP, int K, int B, int es, int BT, int P, i
 // subspace width fused_d (B == 1): a chunk's staged bytes are its codebook
 // rows (4*fused_d per entry, at most 128 KB so they fit the staging
 // registers), and the activation slices of the group's pairs share the LDS.
-// Fused d = 2 (the Gemma MLP) has kernels for 2, 3 and 4 rows per lane, so
-// that a slab can cover a short matrix's rows with few idle lanes (more rows
-// per lane spill at 128 VGPRs).
+// Fused d = 2 (the Gemma MLP) has kernels for 2, 3 and 4 rows per lane, d = 8
+// (its second attempt) for 2 and 3, so that a slab can cover a short matrix's
+// rows with few idle lanes (more rows per lane spill at 128 VGPRs).
 size_t fused_act_bytes(int P, int cpg, int NP, int fused_d) {
   return fused_d ? (size_t)std::min(cpg * P, NP) * fused_d * 4 : 0;
 }
 
 bool steps_allowed(int steps, int fused_d) {
   if (fused_d == 2) return steps >= 2 && steps <= 4;
+  if (fused_d == 8) return steps == 2 || steps == 3;
   return steps >= 1 && steps <= 4;
 }
 
@@ -827,6 +861,9 @@ GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16, int fus
   int tried = 0;
   for (int P = pmax; P >= 1 && P >= pmax / 2 && tried < 8; --P) {
     if (P < NP && P > 1 && (P & 1)) continue;
+    // a chunk smaller than a code block loads every block once per chunk it
+    // touches: only when nothing larger fits
+    if (P < ppb && P < NP && pmax >= ppb) continue;
     ++tried;
     const int chunks = (NP + P - 1) / P;
     for (int steps = nstep; steps >= 1; --steps) {
@@ -840,7 +877,7 @@ GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16, int fus
         if (G != G0) continue;
         if ((size_t)P * K * 4 + fused_act_bytes(P, cpg, NP, fused_d) > (size_t)kLdsBudget && fused_d) continue;
         // prefer aligned chunks (staging outside the block loop) on near-ties
-        const int lane_steps = fused_d == 2 ? steps : nstep;   // the kernel instances (dispatch_gather)
+        const int lane_steps = (fused_d == 2 || fused_d == 8) ? steps : nstep;   // the kernel instances (dispatch_gather)
         const double cost = plan_cost_us(rows, NP, K, B, es, BT, P, steps, G, cpg, stage_es, lane_steps, mats) *
                             ((P % ppb == 0 || chunks == 1) ? 1.0 : 1.03);
         if (cost < best_cost * 0.999) {
@@ -913,6 +950,9 @@ hipError_t dispatch_gather(const GatherArgs& a, const GatherPlan& plan, int d, i
         default: return launch_gather_typed<float, 1, 4, 2, CB>(a, plan, stream);
       }
     }
+    if (d == 8)   // 2 or 3 rows per lane (4 would spill)
+      return plan.steps == 2 ? launch_gather_typed<float, 1, 2, 8, CB>(a, plan, stream)
+                             : launch_gather_typed<float, 1, 3, 8, CB>(a, plan, stream);
     return launch_gather_typed<float, 1, 4, 4, CB>(a, plan, stream);
   }
   if (lut_bf16) {
@@ -952,7 +992,7 @@ hipError_t launch_tile_lut(const void* lut, int lut_bf16, int NP, int K, int B, 
 }
 
 bool fused_build_supported(const rq_matrix* W, int B) {
-  return B == 1 && W->cb_dtype == RQ_F32 && (W->d == 1 || W->d == 2 || W->d == 4) &&
+  return B == 1 && W->cb_dtype == RQ_F32 && (W->d == 1 || W->d == 2 || W->d == 4 || W->d == 8) &&
          ((uintptr_t)W->codebooks % 16) == 0 && ((size_t)W->K * W->d) % 4 == 0;
 }
 
@@ -1009,17 +1049,17 @@ hipError_t launch_gather(const rq_matrix* W, const GatherPlan& plan, const void*
 }
 
 hipError_t launch_gather_pair(const rq_matrix* W1, const rq_matrix* W2, const GatherPlan& plan, const float* x,
-                              float* part1, float* part2, hipStream_t stream) {
+                              const float* lut1, const float* lut2, float* part1, float* part2, hipStream_t stream) {
   GatherOut o{};
   o.partial = part1;
   o.out = plan.G == 1 ? part1 : nullptr;   // one group: the sums themselves
-  GatherArgs a = gather_args(W1, plan, nullptr, 1, o, x, nullptr);
+  GatherArgs a = gather_args(W1, plan, lut1, 1, o, x, nullptr);
   a.cv2 = code_view(W2);
-  a.lut2 = W2->codebooks;
+  a.lut2 = x ? W2->codebooks : static_cast<const void*>(lut2);
   a.partial2 = part2;
   a.out2 = plan.G == 1 ? part2 : nullptr;
   a.mats = 2;
-  return dispatch(W1, a, plan, 0, true, stream);
+  return dispatch(W1, a, plan, 0, x != nullptr, stream);
 }
 
 size_t gather_pro_lds(const rq_matrix* W, const GatherPlan& plan, int pro_G) {

@@ -105,7 +105,7 @@ struct GatherPlan {
 // mats = 2: one launch covers two matrices of W's shape (launch_gather_pair).
 GatherPlan plan_gather(const rq_matrix* W, int B, int lut_bf16, int fused = 0, int mats = 1);
 // Whether the lookup+sum can build the table itself while staging: one
-// activation vector, fp32 codebooks with d in {1, 2, 4}, 16-byte aligned.
+// activation vector, fp32 codebooks with d in {1, 2, 4, 8}, 16-byte aligned.
 bool fused_build_supported(const rq_matrix* W, int B);
 
 // Launchers: return hipSuccess or the launch error. All enqueue on `stream`.
@@ -133,12 +133,20 @@ void take_stage_events(hipEvent_t* before, hipEvent_t* after);
 hipError_t launch_gather(const rq_matrix* W, const GatherPlan& plan, const void* lut, int lut_bf16, int B,
                          const GatherOut& o, hipStream_t stream, const float* fused_act = nullptr,
                          const float* fused_x2 = nullptr);
-// Two matrices of the same shape (W1, W2) and one activation vector x, with
-// the fused table build, in one launch (plan from plan_gather(W1, 1, 0, 1, 2)):
-// each writes its partial sums [G][1][rows] (G > 1), or with G == 1 its sums,
-// to part1 / part2. No finish pass.
+// Whether a plan's chunks span at least one 16-byte code block (or the matrix
+// is one chunk). A fused build whose register stage holds fewer pairs than a
+// block (d = 8 at K = 1024: 4 pairs) loads every block once per chunk it
+// touches, and measured slower than building the table first.
+inline bool plan_covers_blocks(const rq_matrix* W, const GatherPlan& p) {
+  return p.chunks == 1 || p.P >= pairs_per_block(W);
+}
+// Two matrices of the same shape (W1, W2) and one activation vector, in one
+// launch: with x != null the fused table build (plan from plan_gather(W1, 1, 0,
+// 1, 2)), else the fp32 tables lut1 / lut2 (plan from plan_gather(W1, 1, 0, 0,
+// 2)). Each writes its partial sums [G][1][rows] (G > 1), or with G == 1 its
+// sums, to part1 / part2. No finish pass.
 hipError_t launch_gather_pair(const rq_matrix* W1, const rq_matrix* W2, const GatherPlan& plan, const float* x,
-                              float* part1, float* part2, hipStream_t stream);
+                              const float* lut1, const float* lut2, float* part1, float* part2, hipStream_t stream);
 // Fused table build whose activation is gelu_tanh(g) * u, g and u summed from
 // the partial sums [2][pro_G][pro_rows] of launch_gather_pair in the finish
 // pass's order (bit-identical to finishing them first); then as launch_gather.

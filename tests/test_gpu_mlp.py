@@ -24,6 +24,8 @@ SHAPES = [
     (64, 200, 1, 128, 1),      # d=1
     (1024, 3000, 2, 256, 1),   # more groups: the finish order with 4 parts per row
     (96, 160, 2, 64, 2),       # two activation vectors: the three-call route
+    (128, 256, 8, 256, 1),     # d=8: codewords over two staged words
+    (96, 200, 8, 64, 1),       # d=8, ragged rows
 ]
 
 
@@ -92,17 +94,29 @@ def test_lut_mlp_exact_inputs_gemma_shape():
 
 def test_lut_mlp_second_attempt_shapes():
     """The MLP RQ page's second-attempt layer: d=8 throughout, K=1024 for gate/up (10-bit codes), K=256 for
-    down (8-bit codes), fp32 codebooks. The table is built by the separate kernel (d=8), so the block is the
-    three matvecs: equal to them bit for bit, and close to the oracle."""
+    down (8-bit codes), fp32 codebooks: close to the three matvecs and to the oracle."""
     gate, up, down = synth.make_mlp_v2_layer(0)
     x = synth.make_mlp_x()
     Wg, Wu, Wd = to_dev(gate, "packed10"), to_dev(up, "packed10"), to_dev(down, "packed8")
     xd = dev(x)
     y = la.lut_mlp(Wg, Wu, Wd, xd)
-    assert torch.equal(y, _three_calls(Wg, Wu, Wd, xd))
+    check_logits(host(y), host(_three_calls(Wg, Wu, Wd, xd)).astype(np.float64))
     og, ou, _, oy = O().mlp((gate.codes, gate.codebooks, False), (up.codes, up.codebooks, False),
                             (down.codes, down.codebooks, False), x)
     check_logits(host(la.lut_matvec(Wg, xd)), og)
     check_logits(host(y), oy)
     # the 8-bit stream is half the 16-bit one: 2304 rows x 2304 pairs
     assert Wd.codes.numel() * 2 == 2304 * 2304
+
+
+def test_lut_mlp_second_attempt_exact_inputs():
+    """Exact inputs at the second-attempt shapes (d=8, gate/up K=1024 on 10-bit codes, down K=256 on 8-bit
+    codes): gate's fused d=8 build is bit-exact against the oracle, and the block equals the three calls."""
+    gate, x = synth.gen_exact(81, 9216, 2304, 288, 1024, 2, 1)
+    up, _ = synth.gen_exact(82, 9216, 2304, 288, 1024, 2, 1)
+    down, _ = synth.gen_exact(83, 2304, 9216, 1152, 256, 2, 1)
+    Wg, Wu, Wd = to_dev(gate, "packed10"), to_dev(up, "packed10"), to_dev(down, "packed8")
+    xd = dev(x)
+    g = la.lut_matvec(Wg, xd)
+    assert np.array_equal(host(g).astype(np.float64), O().matvec(gate.codes, gate.codebooks, False, x))
+    assert torch.equal(la.lut_mlp(Wg, Wu, Wd, xd), _three_calls(Wg, Wu, Wd, xd))

@@ -282,7 +282,7 @@ def test_lut_matvec_small_chain():
     check_logits(host(y), oy)
 
 
-@pytest.mark.parametrize("d", [1, 2, 4])
+@pytest.mark.parametrize("d", [1, 2, 4, 8])
 @pytest.mark.parametrize("layout", ["rows", "blocked", "packed10", "packed8"])
 def test_lut_matvec_fused_build_exact(d, layout):
     """One activation vector with fp32 codebooks: the table is built while staging. Exact inputs, ragged rows
