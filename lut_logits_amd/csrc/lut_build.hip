@@ -44,6 +44,17 @@ __device__ __forceinline__ float activation(const float* x, const float* x2, int
   return gelu ? gelu_tanh(v) * x2[i] : v;
 }
 
+// 16 bytes of table entries (8 bf16 or 4 fp32) from fp32 values, stored at once.
+__device__ __forceinline__ void store16(float* p, const float* v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store16(uint16_t* p, const float* v) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f32_to_bf16(v[2 * i]) | ((uint32_t)f32_to_bf16(v[2 * i + 1]) << 16);
+  *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 template <typename CbT, typename OutT>
 __global__ __launch_bounds__(kBuildThreads) void build_lut_kernel(const CbT* __restrict__ cb,
                                                                   const float* __restrict__ x,
@@ -70,6 +81,25 @@ __global__ __launch_bounds__(kBuildThreads) void build_lut_kernel(const CbT* __r
     float cw[kMaxRegD];
 #pragma unroll
     for (int j = 0; j < kMaxRegD; ++j) cw[j] = (j < d) ? cb_load(c + j) : 0.0f;
+    // B a multiple of VEC: a codeword's B entries are whole 16-byte units (the
+    // table is 16-byte aligned), written one unit at a time
+    constexpr int VEC = 16 / (int)sizeof(OutT);
+    if (B % VEC == 0) {
+      for (int b0 = 0; b0 < B; b0 += VEC) {
+        float v[VEC];
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          const float* a = act + (b0 + i) * d;
+          float acc = 0.0f;
+#pragma unroll
+          for (int j = 0; j < kMaxRegD; ++j)
+            if (j < d) acc = fmaf(a[j], cw[j], acc);
+          v[i] = acc;
+        }
+        store16(out + b0, v);
+      }
+      return;
+    }
     for (int b = 0; b < B; ++b) {
       const float* a = act + b * d;
       float acc = 0.0f;

@@ -977,9 +977,46 @@ __global__ void tile_lut_kernel(const T* __restrict__ src, int64_t NPK, int B, i
   for (int j = 0; j < BT; ++j) d[j] = (t * BT + j < B) ? s[j] : (T)0;
 }
 
+// The same transposition through LDS, in 4-byte units (B and BT of 4-byte
+// multiples): a workgroup reads R whole table rows contiguously, then writes
+// each batch tile's R-row run contiguously (zero past B). Rows sit in LDS
+// with one unit of padding, so the column reads do not collide in banks.
+constexpr int kTileThreads = 256;
+__global__ __launch_bounds__(kTileThreads) void tile_lut_lds_kernel(const uint32_t* __restrict__ src, int64_t NPK,
+                                                                    int UB, int UT, int NBT, int R,
+                                                                    uint32_t* __restrict__ dst) {
+  extern __shared__ uint32_t rowbuf[];   // [R][UB + 1]
+  const int64_t r0 = (int64_t)blockIdx.x * R;
+  const int rows = (int)min<int64_t>(R, NPK - r0);
+  for (int u = threadIdx.x; u < rows * UB; u += kTileThreads) {
+    const int row = u / UB;
+    rowbuf[row * (UB + 1) + (u - row * UB)] = src[(r0 + row) * UB + (u - row * UB)];
+  }
+  __syncthreads();
+  const int per_tile = rows * UT;
+  for (int v = threadIdx.x; v < NBT * per_tile; v += kTileThreads) {
+    const int t = v / per_tile;
+    const int rem = v - t * per_tile;
+    const int row = rem / UT;
+    const int c = rem - row * UT;
+    const int col = t * UT + c;
+    dst[((int64_t)t * NPK + r0 + row) * UT + c] = col < UB ? rowbuf[row * (UB + 1) + col] : 0u;
+  }
+}
+
 hipError_t launch_tile_lut(const void* lut, int lut_bf16, int NP, int K, int B, int BT, void* dst, hipStream_t stream) {
   const int NBT = (B + BT - 1) / BT;
   const int64_t NPK = (int64_t)NP * K;
+  const int es = lut_bf16 ? 2 : 4;
+  if ((B * es) % 4 == 0 && (BT * es) % 4 == 0) {
+    const int UB = B * es / 4, UT = BT * es / 4;
+    const int R = std::max(1, std::min(64, 16384 / (UB + 1)));   // at most 64 KB of LDS
+    const size_t lds = (size_t)R * (UB + 1) * 4;
+    const unsigned blocks = (unsigned)((NPK + R - 1) / R);
+    hipLaunchKernelGGL(tile_lut_lds_kernel, dim3(blocks), dim3(kTileThreads), lds, stream,
+                       static_cast<const uint32_t*>(lut), NPK, UB, UT, NBT, R, static_cast<uint32_t*>(dst));
+    return hipGetLastError();
+  }
   const int64_t n = NPK * NBT;
   const unsigned blocks = (unsigned)((n + 255) / 256);
   if (lut_bf16)
