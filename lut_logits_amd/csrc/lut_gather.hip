@@ -690,6 +690,50 @@ __global__ __launch_bounds__(kFinishThreads) void finish_kernel(const float* __r
   if (threadIdx.x == 0) block_keys[(size_t)b * gridDim.x + blk] = s_best;
 }
 
+// finish_kernel<1> for many batch vectors (B >= 8: grid.y alone fills the
+// chip): the same 1024-row blocks and keys, with 256 threads of 4 rows each,
+// so every thread has the loads of four rows in flight. Each row adds its G
+// partial sums in group order, as finish_kernel<1> does.
+constexpr int kFinish4Threads = 256;
+__global__ __launch_bounds__(kFinish4Threads) void finish4_kernel(const float* __restrict__ partial, int G, int B,
+                                                                  int64_t rows, float softcap, float* __restrict__ out,
+                                                                  uint64_t* __restrict__ block_keys) {
+  __shared__ unsigned long long s_best;
+  const int blk = blockIdx.x;
+  const int b = blockIdx.y;
+  if (threadIdx.x == 0) s_best = 0ull;
+  const float* src = partial + (size_t)b * rows;
+  const size_t gstride = (size_t)B * rows;
+  int64_t r[4];
+  float z[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    r[k] = (int64_t)blk * kFinishThreads + threadIdx.x + k * kFinish4Threads;
+    z[k] = 0.0f;
+  }
+  for (int g = 0; g < G; ++g) {
+    float v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = r[k] < rows ? src[(size_t)g * gstride + r[k]] : 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) z[k] += v[k];
+  }
+  unsigned long long key = 0ull;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (r[k] >= rows) continue;
+    const float v = softcap > 0.0f ? softcap * tanhf(z[k] / softcap) : z[k];
+    if (out) out[(size_t)b * rows + r[k]] = v;
+    key = umax64(key, select_key(v, (uint32_t)r[k]));
+  }
+  if (!block_keys) return;   // uniform: a kernel argument
+  __syncthreads();
+  const uint64_t w = wave_max_u64(key);
+  if ((threadIdx.x & 63) == 0) atomicMax(&s_best, (unsigned long long)w);
+  __syncthreads();
+  if (threadIdx.x == 0) block_keys[(size_t)b * gridDim.x + blk] = s_best;
+}
+
 constexpr int kSelThreads = 1024;
 constexpr int kSelCap = 4096;
 
@@ -1127,7 +1171,10 @@ hipError_t launch_finish(const float* partial, int G, int B, int64_t rows, float
   const int tpr = finish_parts(G);
   const int rpb = kFinishThreads / tpr;
   dim3 grid((unsigned)((rows + rpb - 1) / rpb), (unsigned)B);
-  if (tpr == 1)
+  if (tpr == 1 && B >= 8)
+    hipLaunchKernelGGL(finish4_kernel, grid, dim3(kFinish4Threads), 0, stream, partial, G, B, rows, softcap, out,
+                       block_keys);
+  else if (tpr == 1)
     hipLaunchKernelGGL(finish_kernel<1>, grid, dim3(kFinishThreads), 0, stream, partial, G, B, rows, softcap, out,
                        block_keys);
   else if (tpr == 4)
