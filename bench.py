@@ -45,8 +45,9 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the head shards over the vocabulary with one tiny all-gather; see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported: the library has no multi-GPU "
+              "path (the head would shard over the vocabulary and merge the per-shard maxima with one small "
+              "all-gather)", file=sys.stderr)
         sys.exit(2)
 
     import torch
