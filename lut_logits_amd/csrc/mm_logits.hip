@@ -267,7 +267,15 @@ __global__ __launch_bounds__(kMmThreads) void mm_logits_kernel(MmArgs a) {
           __builtin_amdgcn_sched_barrier(0);   // keep the staging loads ahead of the code loads (vmcnt is in order)
           load_codes(nxt, min(q + 1, q1 - 1));
         }
+        // Left alone, the scheduler sinks the code loads to the end of a long
+        // compute and hoists the next sub-block's LDS stores (with their waits
+        // on the loads just issued) into it, so both loads get a fraction of a
+        // compute phase to land. With many tiles the compute is fenced on both
+        // sides (B=16 head: 266 -> 253 us per call); a short one (few tiles)
+        // gains from the overlap and is left to the scheduler.
+        if constexpr (T >= 8) __builtin_amdgcn_sched_barrier(0);
         compute(slot, cur, hs);
+        if constexpr (T >= 8) __builtin_amdgcn_sched_barrier(0);
         slot ^= 1;
       }
     };
