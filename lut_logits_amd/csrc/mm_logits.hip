@@ -139,15 +139,44 @@ __global__ __launch_bounds__(kMmThreads) void mm_logits_kernel(MmArgs a) {
   const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc((void*)a.codes, (short)0, (int)0xffffffffu,
                                                                         0x00020000);
   const uint32_t blk_bytes = (uint32_t)a.rows * 16u;
-  uint32_t voff[T];
+  // Code loads. Every vector-memory instruction costs the CU's load pipe about
+  // the same whatever its width, so with T a multiple of 4 a lane loads whole
+  // 16-byte rows: load v gives lane (i16, kg) row i16 of tile 4v + kg, and a
+  // 4 x 4 transpose across the wave's four 16-lane rows (two 32-lane and two
+  // 16-lane swaps) leaves dword kg of tile 4v + t's row i16 in codes[4v + t],
+  // as a one-dword load per tile would. A quarter of the instructions.
+  constexpr bool kWide = T % 4 == 0;
+  constexpr int NV = kWide ? T / 4 : T;
+  uint32_t voff[NV];
 #pragma unroll
-  for (int j = 0; j < T; ++j) {
-    const int64_t r = min(tile0 + 16 * j + i16, a.rows - 1);
-    voff[j] = (uint32_t)r * 16u + (uint32_t)kg * 4u;
+  for (int v = 0; v < NV; ++v) {
+    const int64_t r = min(tile0 + 16 * (kWide ? 4 * v + kg : v) + i16, a.rows - 1);
+    voff[v] = (uint32_t)r * 16u + (kWide ? 0u : (uint32_t)kg * 4u);
   }
   auto load_codes = [&](uint32_t (&dst)[T], int q) {
 #pragma unroll
-    for (int j = 0; j < T; ++j) dst[j] = __builtin_amdgcn_raw_buffer_load_b32(crs, voff[j], (uint32_t)q * blk_bytes, 0);
+    for (int v = 0; v < NV; ++v) {
+      if constexpr (kWide) {
+        const u32x4 w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(crs, voff[v], (uint32_t)q * blk_bytes, 0));
+        dst[4 * v + 0] = w[0]; dst[4 * v + 1] = w[1]; dst[4 * v + 2] = w[2]; dst[4 * v + 3] = w[3];
+      } else {
+        dst[v] = __builtin_amdgcn_raw_buffer_load_b32(crs, voff[v], (uint32_t)q * blk_bytes, 0);
+      }
+    }
+  };
+  // After a wide load: row-of-lanes k holds tile 4v + k's row; give every row
+  // of lanes its own dword of each tile instead.
+  auto arrange_codes = [&](uint32_t (&c)[T]) {
+    if constexpr (kWide) {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const auto x02 = __builtin_amdgcn_permlane32_swap(c[4 * v + 0], c[4 * v + 2], false, false);
+        const auto x13 = __builtin_amdgcn_permlane32_swap(c[4 * v + 1], c[4 * v + 3], false, false);
+        const auto y01 = __builtin_amdgcn_permlane16_swap(x02[0], x13[0], false, false);
+        const auto y23 = __builtin_amdgcn_permlane16_swap(x02[1], x13[1], false, false);
+        c[4 * v + 0] = y01[0]; c[4 * v + 1] = y01[1]; c[4 * v + 2] = y23[0]; c[4 * v + 3] = y23[1];
+      }
+    }
   };
 
   // ---- staging of one half-block into registers, then into a ring slot
@@ -256,7 +285,8 @@ __global__ __launch_bounds__(kMmThreads) void mm_logits_kernel(MmArgs a) {
     // One code block: its NSUB sub-blocks in turn, each staged in one ring slot
     // while the next one's codebook loads into registers; the first sub-block
     // also starts loading the next block's codes (into the other buffer).
-    auto do_block = [&](int q, const uint32_t (&cur)[T], uint32_t (&nxt)[T]) {
+    auto do_block = [&](int q, uint32_t (&cur)[T], uint32_t (&nxt)[T]) {
+      arrange_codes(cur);
 #pragma unroll
       for (int hs = 0; hs < NSUB; ++hs) {
         stage_store(st, slot, q, hs);
