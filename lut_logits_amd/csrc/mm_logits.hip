@@ -367,9 +367,10 @@ __global__ __launch_bounds__(kMmThreads) void mm_logits_kernel(MmArgs a) {
 
 // Row tiles per wave for NT column tiles: the accumulators (4*T*NT VGPRs), the
 // code registers (2*T) and the staged half-block share a wave's 256 VGPRs.
-// (Three sub-blocks per code block keep more values live: fewer tiles.)
+// (Three sub-blocks per code block keep more values live: fewer tiles.) A
+// multiple of 4 takes the wide code loads; 4 at NT = 4 uses 254 VGPRs.
 constexpr int tiles_for(int NT, int NSUB = 2) {
-  return kMmThreads == 512 ? (NSUB == 2 ? (NT == 1 ? 16 : NT == 2 ? 8 : 3) : (NT == 1 ? 12 : NT == 2 ? 6 : 3))
+  return kMmThreads == 512 ? (NSUB == 2 ? (NT == 1 ? 16 : NT == 2 ? 8 : 4) : (NT == 1 ? 12 : NT == 2 ? 6 : 3))
                            : (NT == 1 ? 8 : NT == 2 ? 4 : 2);
 }
 
