@@ -804,9 +804,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const uint64_t* __r
 int nstep_for(int BT) { return 4; }
 
 #ifdef RQ_TUNING
-// Tuning builds only: RQ_GATHER_PLAN="P,steps,G[,BT]" replaces the heuristic's choice.
-bool tuning_override(GatherPlan& p, int NP, int64_t rows, int B) {
-  const char* s = getenv("RQ_GATHER_PLAN");
+// Tuning builds only: RQ_GATHER_PLAN="P,steps,G[,BT]" replaces the heuristic's choice
+// (RQ_GATHER_PLAN2 for two-matrix launches).
+bool tuning_override(GatherPlan& p, int NP, int64_t rows, int B, int mats) {
+  const char* s = getenv(mats == 2 ? "RQ_GATHER_PLAN2" : "RQ_GATHER_PLAN");
   if (!s) return false;
   int P, steps, G, BT = 0;
   if (sscanf(s, "%d,%d,%d,%d", &P, &steps, &G, &BT) < 3) return false;
@@ -976,7 +977,7 @@ GatherPlan plan_gather(const rq_matrix* W, int B, int lut_bf16, int fused, int m
     if (g_plan_n < 32) ++g_plan_n;
   }
 #ifdef RQ_TUNING
-  if (tuning_override(plan, key.NP, key.rows, B))
+  if (tuning_override(plan, key.NP, key.rows, B, mats))
     plan.lds = (size_t)plan.P * W->K * plan.BT * (lut_bf16 ? 2 : 4) + fused_act_bytes(plan.P, plan.cpg, key.NP, fd);
 #endif
   return plan;
