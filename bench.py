@@ -114,6 +114,7 @@ def main():
     lut_b = formats.lut_bytes(1, L, M, K)
     algo_bytes = code_bytes + lut_b                # what the lookup+sum kernel must read once
     achieved = algo_bytes / (t_gather * 1e-3) / 1e9
+    ceiling = stream_ceiling(la, torch, [W.codes for W in Ws])
 
     out = {
         "metric": METRIC,
@@ -134,7 +135,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "gather_kernel (lookup+sum of rq_lut_logits, B=1)",
-                     "kernel_ms": t_gather, "algorithmic_bytes": algo_bytes},
+                     "kernel_ms": t_gather, "algorithmic_bytes": algo_bytes,
+                     "stream_ceiling_gbs": ceiling["gbs"], "frac_of_stream_ceiling": achieved / ceiling["gbs"],
+                     "stream_ceiling": ceiling},
         "calls_ms": {"decode_rows_64": t_dec, "build_lut": t_build, "lut_logits": t_logits,
                      "lut_logits_median": t_logits_med, "lut_logits_gather_kernel": t_gather},
         "resident_bytes": {"lut_head": Ws[0].resident_bytes() + lut_b + ws.numel(),
@@ -176,6 +179,29 @@ def measured_traffic():
     if h.hexdigest() != rec["sources_sha256"]:
         return None
     return rec["traffic_bytes_per_launch"]
+
+
+def stream_ceiling(la, torch, bufs, reps=10):
+    """The HBM stream-read ceiling on this GPU: rq_stream_read (one read of a buffer with 16-byte loads and
+    nothing else) over the resident code arrays, alternating them so the Infinity Cache cannot serve repeats,
+    in each grid configuration, each launch timed by its own dispatch (rq_set_stage_events, as the lookup+sum
+    kernel is); the fastest configuration's mean, in GB/s (decimal)."""
+    nbytes = bufs[0].numel() * bufs[0].element_size()
+    best = None
+    for config in range(la.stream_read_configs()):
+        sink = la.stream_read(bufs[0], config)
+        for i in range(2):
+            la.stream_read(bufs[i & 1], config, sink)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i in range(reps):
+            la.set_stage_events(*ev[i])
+            la.stream_read(bufs[i & 1], config, sink)
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in ev) / reps
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        if best is None or gbs > best["gbs"]:
+            best = {"gbs": gbs, "config": config, "workgroups": int(sink.numel()), "bytes": nbytes, "kernel_ms": ms}
+    return best
 
 
 def timed(fn, n, torch):

@@ -324,8 +324,28 @@ rq_status rq_dense_logits(const uint16_t* E, int64_t rows, int32_t D, const floa
                           hipStream_t stream);
 
 /*
+ * Measurement aid, not part of the method: reads bytes [src, src + bytes)
+ * once with 16-byte loads and nothing else, so that its rate is the HBM
+ * stream-read ceiling this GPU reaches; the lookup+sum pass's bandwidth is
+ * reported against it as well as against the specification.
+ *   config  0 .. rq_stream_read_configs()-1: a grid size (256 to 2048
+ *           workgroups of 1024 threads) and a count of loads each thread
+ *           keeps in flight (1, 2, 4 or 8); the caller keeps the fastest
+ *   src     device buffer, 16-byte aligned; bytes a multiple of 16
+ *   sink    device uint32 [rq_stream_read_sink_words(config)]: word w is
+ *           the XOR of every 32-bit word workgroup w read, so the XOR of
+ *           all sink words is the XOR of every word of the buffer
+ * bytes == 0 is a no-op. NULL buffers return RQ_ERR_NULL, misalignment
+ * RQ_ERR_ALIGN, an unknown config RQ_ERR_SHAPE.
+ */
+int32_t rq_stream_read_configs(void);
+size_t rq_stream_read_sink_words(int32_t config);
+rq_status rq_stream_read(const void* src, size_t bytes, int32_t config, uint32_t* sink, hipStream_t stream);
+
+/*
  * Measurement hook. The next lookup+sum kernel that rq_lut_logits or
- * rq_lut_matvec launches from the calling thread is launched with
+ * rq_lut_matvec launches from the calling thread (or the next
+ * rq_stream_read kernel) is launched with
  * hipExtLaunchKernelGGL(..., before, after, ...): the events take the start
  * and end of that kernel's own dispatch on its stream, so that
  * hipEventElapsedTime(before, after) is that one kernel's duration (the

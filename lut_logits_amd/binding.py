@@ -25,7 +25,8 @@ RQ_METHOD_TABLE, RQ_METHOD_MATRIX_CORES = 0, 1
 EXPORTS = ("rq_blocked_codes_bytes", "rq_pack_codes", "rq_packed10_codes_bytes", "rq_pack_codes10",
            "rq_packed8_codes_bytes", "rq_pack_codes8", "rq_lut_bytes", "rq_build_lut", "rq_lut_logits_workspace",
            "rq_lut_logits", "rq_logits_method", "rq_logits_workspace", "rq_logits", "rq_decode_rows", "rq_lut_matvec_workspace", "rq_lut_matvec",
-           "rq_lut_mlp_workspace", "rq_lut_mlp", "rq_dense_logits_workspace", "rq_dense_logits", "rq_set_stage_events", "rq_status_string", "rq_last_error", "rq_version")
+           "rq_lut_mlp_workspace", "rq_lut_mlp", "rq_dense_logits_workspace", "rq_dense_logits", "rq_stream_read_configs",
+           "rq_stream_read_sink_words", "rq_stream_read", "rq_set_stage_events", "rq_status_string", "rq_last_error", "rq_version")
 
 
 class RQError(RuntimeError):
@@ -73,6 +74,9 @@ def lib():
             "rq_lut_mlp": (_i32, [_MP, _MP, _MP, _vp, _i32, _vp, _vp, _sz, _vp]),
             "rq_dense_logits_workspace": (_sz, [_i64, _i32]),
             "rq_dense_logits": (_i32, [_vp, _i64, _i32, _vp, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
+            "rq_stream_read_configs": (_i32, []),
+            "rq_stream_read_sink_words": (_sz, [_i32]),
+            "rq_stream_read": (_i32, [_vp, _sz, _i32, _vp, _vp]),
             "rq_set_stage_events": (_i32, [_vp, _vp]),
             "rq_status_string": (ctypes.c_char_p, [_i32]),
             "rq_last_error": (ctypes.c_char_p, []),
@@ -272,6 +276,20 @@ def lut_mlp(gate, up, down, x, ws=None, out=None):
         ws = workspace(lut_mlp_workspace(gate, up, down, B), x.device)
     check(lib().rq_lut_mlp(gate.ref, up.ref, down.ref, _ptr(x), B, _ptr(y), _ptr(ws), ws.numel(), _stream()))
     return y
+
+
+def stream_read_configs():
+    """rq_stream_read_configs: number of grid configurations of the stream-read probe."""
+    return lib().rq_stream_read_configs()
+
+
+def stream_read(buf, config, sink=None):
+    """rq_stream_read: one read of the whole of `buf` (a device tensor, 16-byte aligned, nbytes % 16 == 0)
+    with 16-byte loads; returns the uint32 sink (one XOR per workgroup) as an int32 tensor."""
+    if sink is None:
+        sink = torch.empty(lib().rq_stream_read_sink_words(config), dtype=torch.int32, device=buf.device)
+    check(lib().rq_stream_read(_ptr(buf), buf.numel() * buf.element_size(), config, _ptr(sink), _stream()))
+    return sink
 
 
 def dense_logits_workspace(rows, B):

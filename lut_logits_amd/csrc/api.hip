@@ -582,4 +582,21 @@ rq_status rq_dense_logits(const uint16_t* E, int64_t rows, int32_t D, const floa
                   "rq_dense_logits: argmax");
 }
 
+int32_t rq_stream_read_configs(void) { return rq::stream_read_configs(); }
+
+size_t rq_stream_read_sink_words(int32_t config) {
+  if (config < 0 || config >= rq::stream_read_configs()) return 0;
+  return rq::stream_read_sink_words(config);
+}
+
+rq_status rq_stream_read(const void* src, size_t bytes, int32_t config, uint32_t* sink, hipStream_t stream) {
+  if (config < 0 || config >= rq::stream_read_configs())
+    return fail(RQ_ERR_SHAPE, "stream_read: config %d outside [0, %d)", config, rq::stream_read_configs());
+  if (bytes == 0) return RQ_OK;
+  if (!src || !sink) return fail(RQ_ERR_NULL, "stream_read: NULL buffer");
+  if (!aligned(src, 16) || bytes % 16 != 0 || !aligned(sink, 4))
+    return fail(RQ_ERR_ALIGN, "stream_read: src must be 16-byte aligned and bytes a multiple of 16");
+  return launched(rq::launch_stream_read(src, bytes, config, sink, stream), "rq_stream_read");
+}
+
 }  // extern "C"

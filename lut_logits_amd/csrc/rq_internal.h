@@ -191,6 +191,12 @@ size_t mm_hp_bytes(const rq_matrix* W, const MmPlan& p);
 hipError_t launch_mm_logits(const rq_matrix* W, const MmPlan& p, const float* h, int B, void* hp, float* partial,
                             float* out, float softcap, uint64_t* block_keys, hipStream_t stream);
 
+// Measurement aid: one read of [src, src + bytes) with 16-byte loads; one
+// 32-bit XOR per workgroup to sink (stream_read_sink_words(config) words).
+int stream_read_configs();
+size_t stream_read_sink_words(int config);
+hipError_t launch_stream_read(const void* src, size_t bytes, int config, uint32_t* sink, hipStream_t stream);
+
 hipError_t launch_decode_rows(const rq_matrix* W, const int32_t* ids, int n, int out_bf16, void* out,
                               int32_t* bad_ids, hipStream_t stream);
 hipError_t launch_pack_codes(const uint16_t* src, int64_t rows, int NP, uint16_t* dst, hipStream_t stream);

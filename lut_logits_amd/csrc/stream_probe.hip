@@ -1,0 +1,82 @@
+// stream_probe.hip -- a measurement aid, not part of the method: reads a
+// buffer once with 16-byte loads and nothing else, so that its rate is the
+// HBM stream-read ceiling this GPU reaches. The lookup+sum pass is a code
+// stream plus table lookups; its achieved bandwidth is reported against this
+// ceiling as well as against the 8 TB/s specification.
+//
+// Workgroups of 1024 threads stride over the buffer as one grid: in every
+// round the grid's loads cover one contiguous span, and each thread keeps U
+// 16-byte loads in flight. The configurations differ in grid size (one to
+// eight workgroups per CU) and U (1, 2, 4 or 8); the caller keeps the fastest.
+#include <hip/hip_ext.h>
+
+#include "rq_internal.h"
+
+namespace rq {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kStreamThreads = 1024;
+struct StreamConfig {
+  int wgs, unroll;
+};
+constexpr StreamConfig kStreamConfig[] = {{256, 4}, {512, 4}, {1024, 4}, {2048, 4},
+                                          {256, 8}, {512, 8}, {256, 2}, {512, 2}, {256, 1}, {512, 1}};
+constexpr int kStreamConfigs = sizeof(kStreamConfig) / sizeof(kStreamConfig[0]);
+
+template <int kStreamUnroll>
+__global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(const u32x4* __restrict__ src, size_t n16,
+                                                                     uint32_t* __restrict__ sink) {
+  const size_t stride = (size_t)gridDim.x * kStreamThreads;
+  size_t i = (size_t)blockIdx.x * kStreamThreads + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + (kStreamUnroll - 1) * stride < n16; i += kStreamUnroll * stride) {
+    u32x4 v[kStreamUnroll];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) v[u] = src[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 v = src[i];
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  // XOR of the workgroup's words (so the loads cannot be dropped, and the
+  // sink's XOR over all workgroups is the XOR of every word of the buffer)
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o, 64);
+  __shared__ uint32_t s_acc[kStreamThreads / 64];
+  if ((threadIdx.x & 63) == 0) s_acc[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int k = 0; k < kStreamThreads / 64; ++k) w ^= s_acc[k];
+    sink[blockIdx.x] = w;
+  }
+}
+
+}  // namespace
+
+int stream_read_configs() { return kStreamConfigs; }
+size_t stream_read_sink_words(int config) { return (size_t)kStreamConfig[config].wgs; }
+
+hipError_t launch_stream_read(const void* src, size_t bytes, int config, uint32_t* sink, hipStream_t stream) {
+  const dim3 grid((unsigned)kStreamConfig[config].wgs);
+  const int unroll = kStreamConfig[config].unroll;
+  auto kern = unroll == 1   ? stream_read_kernel<1>
+              : unroll == 2 ? stream_read_kernel<2>
+              : unroll == 8 ? stream_read_kernel<8>
+                            : stream_read_kernel<4>;
+  const u32x4* s16 = static_cast<const u32x4*>(src);
+  hipEvent_t before, after;
+  take_stage_events(&before, &after);
+  if (before || after)   // timed like the lookup+sum kernel: its own dispatch's start and end
+    hipExtLaunchKernelGGL(kern, grid, dim3(kStreamThreads), 0, stream, before, after, 0, s16, bytes / 16, sink);
+  else
+    hipLaunchKernelGGL(kern, grid, dim3(kStreamThreads), 0, stream, s16, bytes / 16, sink);
+  return hipGetLastError();
+}
+
+}  // namespace rq

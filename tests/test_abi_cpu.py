@@ -206,3 +206,20 @@ def test_packed8_layout_checks():
     W = gemma_desc(codes_layout=B.RQ_CODES_PACKED8, K=256)
     assert lib.rq_lut_logits_workspace(ctypes.byref(W), 1, 0, B.RQ_F32) > 0
     assert lib.rq_logits_method(ctypes.byref(W), 16) == B.RQ_METHOD_TABLE  # no matrix-core staging of 8-bit codes
+
+
+def test_stream_read_checks():
+    """The stream-read probe (a measurement aid): configurations, sink sizes and host-side rejections
+    (no launch)."""
+    lib = B.lib()
+    n = lib.rq_stream_read_configs()
+    assert n >= 1
+    assert all(lib.rq_stream_read_sink_words(c) in (256, 512, 1024, 2048) for c in range(n))
+    assert lib.rq_stream_read_sink_words(-1) == 0 and lib.rq_stream_read_sink_words(n) == 0
+    assert lib.rq_stream_read(0x1000, 4096, n, 0x2000, None) == B.RQ_ERR_SHAPE
+    assert lib.rq_stream_read(0x1000, 4096, -1, 0x2000, None) == B.RQ_ERR_SHAPE
+    assert lib.rq_stream_read(None, 4096, 0, 0x2000, None) == B.RQ_ERR_NULL
+    assert lib.rq_stream_read(0x1000, 4096, 0, None, None) == B.RQ_ERR_NULL
+    assert lib.rq_stream_read(0x1008, 4096, 0, 0x2000, None) == B.RQ_ERR_ALIGN
+    assert lib.rq_stream_read(0x1000, 4100, 0, 0x2000, None) == B.RQ_ERR_ALIGN
+    assert lib.rq_stream_read(None, 0, 0, None, None) == B.RQ_OK
