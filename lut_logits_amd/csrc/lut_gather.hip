@@ -616,21 +616,89 @@ __device__ void bitonic_sort_desc(uint64_t* s, int n) {
   }
 }
 
-// The k best selection keys of each 1024-row block of the logits.
+// The k best selection keys of each 1024-row block of the logits, in any order
+// (the merge sorts them). Selection keys are distinct (the row index is part
+// of every key), so the block's k-th largest key T splits it exactly: the k
+// keys >= T. T is found most significant byte first: a 256-bin histogram of
+// the keys that agree with the bytes fixed so far, then the bin where the
+// count from the top reaches the number still needed; it stops as soon as the
+// keys that agree with the prefix are exactly the ones still needed (for
+// random logits after two or three bytes). Rows past the end carry key 0,
+// below every real key: a block with no more real keys than k gives all of
+// them and zeros.
 __global__ __launch_bounds__(kTopkThreads) void topk_block_kernel(const float* __restrict__ logits, int64_t rows,
                                                                   int topk, uint64_t* __restrict__ cand) {
-  __shared__ uint64_t keys[kEpiRowsPerBlock];
+  constexpr int KPT = kEpiRowsPerBlock / kTopkThreads;   // keys per thread
+  static_assert(kTopkThreads >= 256, "one thread per histogram bin");
+  __shared__ unsigned int hist[256];
+  __shared__ unsigned int s_digit, s_above, s_out;
+  const int tid = threadIdx.x;
   const int blk = blockIdx.x;
   const int b = blockIdx.y;
-  const int nblk = gridDim.x;
-  for (int local = threadIdx.x; local < kEpiRowsPerBlock; local += kTopkThreads) {
-    const int64_t r = (int64_t)blk * kEpiRowsPerBlock + local;
-    keys[local] = r < rows ? select_key(logits[(size_t)b * rows + r], (uint32_t)r) : 0ull;
+  const int64_t r0 = (int64_t)blk * kEpiRowsPerBlock;
+  const int n_real = (int)min<int64_t>(kEpiRowsPerBlock, rows - r0);
+  uint64_t* dst = cand + ((size_t)b * gridDim.x + blk) * topk;
+  uint64_t key[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int local = tid + j * kTopkThreads;
+    key[j] = local < n_real ? select_key(logits[(size_t)b * rows + r0 + local], (uint32_t)(r0 + local)) : 0ull;
   }
-  __syncthreads();
-  bitonic_sort_desc(keys, kEpiRowsPerBlock);
-  uint64_t* dst = cand + ((size_t)b * nblk + blk) * topk;
-  for (int i = threadIdx.x; i < topk; i += kTopkThreads) dst[i] = keys[i];
+  if (n_real <= topk) {   // uniform
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int local = tid + j * kTopkThreads;
+      if (local < topk) dst[local] = key[j];
+    }
+    return;
+  }
+  if (tid == 0) s_out = 0u;
+  uint64_t prefix = 0ull, pmask = 0ull;
+  unsigned int need = (unsigned int)topk;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    if (tid < 256) hist[tid] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      if ((key[j] & pmask) == prefix) atomicAdd(&hist[(unsigned int)(key[j] >> shift) & 255u], 1u);
+    __syncthreads();
+    if (tid < 64) {
+      // lane l holds bins 255-4l .. 252-4l; an exclusive scan from the top
+      unsigned int h[4], lsum = 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        h[i] = hist[255 - 4 * tid - i];
+        lsum += h[i];
+      }
+      unsigned int incl = lsum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const unsigned int t = (unsigned int)__shfl_up((int)incl, o, 64);
+        if (tid >= o) incl += t;
+      }
+      unsigned int cum = incl - lsum;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (cum < need && need <= cum + h[i]) {
+          s_digit = 255u - 4u * tid - i;
+          s_above = cum;
+        }
+        cum += h[i];
+      }
+    }
+    __syncthreads();
+    const unsigned int d = s_digit;
+    need -= s_above;
+    prefix |= (uint64_t)d << shift;
+    pmask |= (uint64_t)0xff << shift;
+    const bool done = hist[d] == need;   // uniform: read from LDS
+    __syncthreads();                      // before the next byte clears the histogram
+    if (done) break;
+  }
+  // the keys whose fixed bytes are at or above the prefix: exactly k of them
+#pragma unroll
+  for (int j = 0; j < KPT; ++j)
+    if ((key[j] & pmask) >= prefix) dst[atomicAdd(&s_out, 1u)] = key[j];
 }
 
 constexpr int kFinishThreads = 1024;

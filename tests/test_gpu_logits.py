@@ -153,3 +153,25 @@ def test_logits_one_group_epilogue_topk():
     check_topk(g, host(ti), host(tv), host(am), ref, tol, 7)
     _, am2, ti2, _ = la.logits(W, dev(h), softcap=30.0, logits=False, topk=7)
     assert torch.equal(am, am2) and torch.equal(ti, ti2)
+
+
+@pytest.mark.parametrize("B", [3, 9])
+@pytest.mark.parametrize("k", [1, 50, 1000, 1024])
+def test_topk_exact_ties_ragged(B, k):
+    """Top-k on exact small-integer inputs (many equal logits, so the order among ties is decided by the id)
+    over 3000 rows (a last 1024-row block of 952): the ids are exactly the first k of the GPU's own logits
+    sorted by (value desc, id asc), including k above a block's rows (1000, 1024) and k = 1; B=3 runs the
+    table method, B=9 the matrix cores."""
+    rows = 3000
+    mat, h = synth.gen_exact(500 + B, rows, 96, 16, 64, 2, B, cb_dtype="bf16", cmax=2, hmax=1)
+    W = to_dev(mat)
+    lg, am, ti, tv = la.logits(W, dev(h), softcap=0.0, topk=k)
+    g, ids, vals = host(lg), host(ti), host(tv)
+    z, _ = O().logits(mat.codes, mat.codebooks, True, h, 0.0)
+    assert np.array_equal(g.astype(np.float64), z)
+    for b in range(B):
+        order = np.lexsort((np.arange(rows), -g[b]))[:k]
+        assert len(np.unique(g[b])) < rows // 4          # ties everywhere
+        assert np.array_equal(ids[b], order), (b, k)
+        assert np.array_equal(vals[b], g[b, order])
+        assert host(am)[b] == order[0]
