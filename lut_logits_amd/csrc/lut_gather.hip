@@ -803,7 +803,7 @@ __global__ __launch_bounds__(kFinish4Threads) void finish4_kernel(const float* _
 }
 
 constexpr int kSelThreads = 1024;
-constexpr int kSelCap = 4096;
+constexpr int kSelCap = 1024;   // the largest k the entry points accept
 
 // Argmax alone: one wave per batch entry takes the largest of the blocks' best
 // keys (no LDS, no barrier).
@@ -825,8 +825,12 @@ __global__ __launch_bounds__(64) void argmax_kernel(const uint64_t* __restrict__
   if (threadIdx.x == 0) argmax[b] = (int32_t)key_index(best);
 }
 
-// Per batch entry: argmax from the blocks' best keys; top-k by merging the
-// blocks' candidates through a 4096-key LDS buffer that always keeps the best k.
+// Per batch entry: argmax from the blocks' best keys; top-k from the blocks'
+// candidates: the k-th largest candidate T by the same most-significant-byte
+// radix select as the per-block pass (the candidates stay in global memory,
+// read once per byte), then the k candidates >= T sorted in LDS. The k-th
+// largest is a real key (rows >= k), so the zero keys of short blocks never
+// reach the selection.
 __global__ __launch_bounds__(kSelThreads) void select_kernel(const uint64_t* __restrict__ block_keys, int nkb,
                                                              int32_t* __restrict__ argmax, int ncb,
                                                              const uint64_t* __restrict__ cand, int topk,
@@ -851,16 +855,65 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const uint64_t* __r
   if (topk <= 0) return;
   const uint64_t* src = cand + (size_t)b * ncb * topk;
   const size_t total = (size_t)ncb * topk;
-  const int room = kSelCap - topk;
-  for (int i = threadIdx.x; i < topk; i += kSelThreads) buf[i] = 0;
-  for (size_t start = 0; start < total; start += room) {
-    for (int i = threadIdx.x; i < room; i += kSelThreads) {
-      const size_t j = start + i;
-      buf[topk + i] = j < total ? src[j] : 0;
+  __shared__ unsigned int hist[256];
+  __shared__ unsigned int s_digit, s_above, s_out;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_out = 0u;
+  uint64_t prefix = 0ull, pmask = 0ull;
+  unsigned int need = (unsigned int)topk;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    if (tid < 256) hist[tid] = 0u;
+    __syncthreads();
+    for (size_t i = tid; i < total; i += kSelThreads) {
+      const uint64_t k = src[i];
+      if ((k & pmask) == prefix) atomicAdd(&hist[(unsigned int)(k >> shift) & 255u], 1u);
     }
     __syncthreads();
-    bitonic_sort_desc(buf, kSelCap);
+    if (tid < 64) {
+      unsigned int h[4], lsum = 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        h[i] = hist[255 - 4 * tid - i];
+        lsum += h[i];
+      }
+      unsigned int incl = lsum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const unsigned int t = (unsigned int)__shfl_up((int)incl, o, 64);
+        if (tid >= o) incl += t;
+      }
+      unsigned int cum = incl - lsum;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (cum < need && need <= cum + h[i]) {
+          s_digit = 255u - 4u * tid - i;
+          s_above = cum;
+        }
+        cum += h[i];
+      }
+    }
+    __syncthreads();
+    const unsigned int d = s_digit;
+    need -= s_above;
+    prefix |= (uint64_t)d << shift;
+    pmask |= (uint64_t)0xff << shift;
+    const bool done = hist[d] == need;   // uniform: read from LDS
+    __syncthreads();                      // before the next byte clears the histogram
+    if (done) break;
   }
+  // the k candidates at or above the threshold, then sorted (value desc, id asc)
+  for (size_t i = tid; i < total; i += kSelThreads) {
+    const uint64_t k = src[i];
+    if ((k & pmask) >= prefix) {
+      const unsigned int slot = atomicAdd(&s_out, 1u);
+      if (slot < (unsigned int)topk) buf[slot] = k;   // exactly k for distinct nonzero keys
+    }
+  }
+  int n2 = 1;
+  while (n2 < topk) n2 <<= 1;
+  for (int i = topk + tid; i < n2; i += kSelThreads) buf[i] = 0ull;
+  __syncthreads();
+  bitonic_sort_desc(buf, n2);
   for (int i = threadIdx.x; i < topk; i += kSelThreads) {
     topk_ids[(size_t)b * topk + i] = (int32_t)key_index(buf[i]);
     if (topk_vals) topk_vals[(size_t)b * topk + i] = key_value(buf[i]);
