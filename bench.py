@@ -329,6 +329,19 @@ def extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, dev):
     del dl, wsm, wsf, g, u, y
     torch.cuda.empty_cache()
 
+    # the same layer with its codes stored at 10 bits (the RQ_CODES_PACKED10 layout: 10 bits per code,
+    # so 10 bits/param at d=2 and L=2)
+    dp = [[la.to_device(m, "packed10") for m in lay] for lay in layers]
+    wsp = la.workspace(la.lut_mlp_workspace(*dp[0], 1), dev)
+    yp = torch.empty((1, synth.MLP_HIDDEN), device=dev)
+    tp = timed(lambda i=0: la.lut_mlp(*dp[i & 1], x, ws=wsp, out=yp), 20, torch)
+    code_p = sum(la.packed10_codes_bytes(m.rows, m.L, m.M) for m in layers[0])
+    gbs_p = (code_p + cb_b) / (tp * 1e-3) / 1e9
+    res["mlp_layer_packed10"] = {"ms": tp, "code_bytes": code_p, "codebook_bytes": cb_b,
+                                 "gbs_codes_plus_codebooks": gbs_p, "hbm_frac": gbs_p / HBM_PEAK_GBS}
+    del dp, wsp, yp
+    torch.cuda.empty_cache()
+
     # the MLP RQ page's second-attempt layer: d=8, K=1024 for gate/up (10-bit codes), K=256 for down
     # (8-bit codes), fp32 codebooks
     v2 = [synth.make_mlp_v2_layer(i) for i in range(2)]
@@ -414,8 +427,18 @@ def cpu_baseline(mat, h, cfg):
         o.logits(mat.codes, mat.codebooks, mat.cb_is_bf16, h, cfg.softcap, nthreads=nt)
         passes += 1
     dt = time.time() - t0
+    # the same oracle on one core, over the first 16,000 rows (about 4 s)
+    rows1 = 16000
+    codes1 = mat.codes[:rows1]
+    p1, t1 = 0, time.time()
+    while p1 < 50 and (p1 == 0 or time.time() - t1 < 4.0):
+        o.logits(codes1, mat.codebooks, mat.cb_is_bf16, h, cfg.softcap, nthreads=1)
+        p1 += 1
+    dt1 = time.time() - t1
     return {"value": passes * cfg.V / dt, "unit": "vocab-rows/s", "cores": nt, "kind": "oracle",
-            "sample": f"full 256000-row head at B=1 (decode+matmul+softcap in fp64), {passes} passes, {dt:.1f} s"}
+            "sample": f"full 256000-row head at B=1 (decode+matmul+softcap in fp64), {passes} passes, {dt:.1f} s",
+            "one_core": {"value": p1 * rows1 / dt1, "unit": "vocab-rows/s", "cores": 1,
+                         "sample": f"first {rows1} rows of the same head, {p1} passes, {dt1:.1f} s"}}
 
 
 if __name__ == "__main__":
