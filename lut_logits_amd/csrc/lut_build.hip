@@ -120,6 +120,68 @@ __global__ __launch_bounds__(kBuildThreads) void build_lut_kernel(const CbT* __r
   }
 }
 
+// The same table for B a multiple of VEC (16 bytes of entries) with B / VEC
+// dividing the workgroup: the B / VEC lanes of one codeword each own one
+// 16-byte chunk of its B entries, so a wave's store covers whole consecutive
+// codewords -- one contiguous 1 KB span -- instead of 16 bytes in each of 64
+// lines (the per-codeword loop above, whose partial-line writes the memory
+// system does not merge: 3.4x the table's bytes reached HBM at B=64). The
+// workgroup's 256 codewords are first copied to LDS with 4-byte loads (one
+// per lane per 1 KB, not d loads per lane per codeword), and each lane keeps
+// its chunk's activation slices in registers; entries are computed in the
+// same order as above, so the tables are bit-identical.
+template <typename CbT, typename OutT>
+__global__ __launch_bounds__(kBuildThreads) void build_lut_wide_kernel(const CbT* __restrict__ cb,
+                                                                       const float* __restrict__ x,
+                                                                       const float* __restrict__ x2, int gelu,
+                                                                       int B, int D, int M, int d, int K, int ktiles,
+                                                                       OutT* __restrict__ lut) {
+  constexpr int VEC = 16 / (int)sizeof(OutT);
+  __shared__ float act[kActStage];
+  __shared__ uint32_t cws[kBuildThreads * kMaxRegD * sizeof(CbT) / 4];   // this tile's codewords
+  const int p = blockIdx.x / ktiles;
+  const int m = p % M;
+  const int kt = blockIdx.x - p * ktiles;
+  const size_t col0 = (size_t)m * d;
+  for (int i = threadIdx.x; i < B * d; i += kBuildThreads) {
+    const int b = i / d;
+    act[i] = activation(x, x2, gelu, (size_t)b * D + col0 + (i - b * d));
+  }
+  // the tile's n codewords are n*d consecutive elements; the host guarantees
+  // 4-byte alignment of their start and a whole number of words in every tile
+  const int n = min(kBuildThreads, K - kt * kBuildThreads);
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(cb + ((size_t)p * K + (size_t)kt * kBuildThreads) * d);
+  const int words = n * d * (int)sizeof(CbT) / 4;
+  for (int i = threadIdx.x; i < words; i += kBuildThreads) cws[i] = src[i];
+  __syncthreads();
+  const CbT* cwt = reinterpret_cast<const CbT*>(cws);
+  const int cpc = B / VEC;                       // lanes per codeword
+  const int bc = threadIdx.x % cpc;              // this lane's 16-byte chunk of the B entries
+  const int per_iter = kBuildThreads / cpc;      // codewords per pass of the workgroup
+  float a[VEC][kMaxRegD];
+#pragma unroll
+  for (int i = 0; i < VEC; ++i)
+#pragma unroll
+    for (int j = 0; j < kMaxRegD; ++j) a[i][j] = (j < d) ? act[(bc * VEC + i) * d + j] : 0.0f;
+  for (int kk = threadIdx.x / cpc; kk < kBuildThreads; kk += per_iter) {
+    const int k = kt * kBuildThreads + kk;
+    if (k >= K) break;
+    float cw[kMaxRegD];
+#pragma unroll
+    for (int j = 0; j < kMaxRegD; ++j) cw[j] = (j < d) ? cb_load(cwt + kk * d + j) : 0.0f;
+    float v[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kMaxRegD; ++j)
+        if (j < d) acc = fmaf(a[i][j], cw[j], acc);
+      v[i] = acc;
+    }
+    store16(lut + ((size_t)p * K + k) * B + bc * VEC, v);
+  }
+}
+
 constexpr int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
 
 // Fast path for one activation vector and a small compile-time subspace width:
@@ -185,6 +247,19 @@ hipError_t launch_typed(const rq_matrix* W, const float* x, const float* x2, int
   const int NP = W->L * W->M;
   const int ktiles = (W->K + kBuildThreads - 1) / kBuildThreads;
   const int64_t blocks = (int64_t)NP * ktiles;
+  constexpr int VEC = 16 / (int)sizeof(OutT);
+  const int cpc = B / VEC;
+  // whole 4-byte words per codeword tile: K*d*sizeof(CbT) and the last tile's
+  // bytes multiples of 4 (a full tile of 256 codewords always is)
+  const size_t es = sizeof(CbT);
+  const bool words = ((uintptr_t)W->codebooks & 3) == 0 && ((size_t)W->K * W->d * es) % 4 == 0 &&
+                     ((size_t)(W->K % kBuildThreads) * W->d * es) % 4 == 0;
+  if (W->d <= kMaxRegD && (int64_t)B * W->d <= kActStage && B % VEC == 0 && cpc <= kBuildThreads &&
+      kBuildThreads % cpc == 0 && ((uintptr_t)lut & 15) == 0 && words) {
+    hipLaunchKernelGGL((build_lut_wide_kernel<CbT, OutT>), dim3((unsigned)blocks), dim3(kBuildThreads), 0, stream,
+                       static_cast<const CbT*>(W->codebooks), x, x2, gelu, B, W->D, W->M, W->d, W->K, ktiles, lut);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((build_lut_kernel<CbT, OutT>), dim3((unsigned)blocks), dim3(kBuildThreads), 0, stream,
                      static_cast<const CbT*>(W->codebooks), x, x2, gelu, B, W->D, W->M, W->d, W->K, ktiles, lut);
   return hipGetLastError();

@@ -114,6 +114,26 @@ def test_build_lut_exact_and_bf16_table():
     assert np.array_equal(lutb, synth.f32_to_bf16_bits(ref.astype(np.float32)))
 
 
+@pytest.mark.parametrize("cb_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("lut_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("B,d,K", [(8, 6, 300), (24, 3, 300), (64, 6, 300), (12, 8, 300), (16, 3, 301)])
+def test_build_lut_batched_exact(cb_dtype, lut_dtype, B, d, K):
+    """Batched tables on exact inputs, with a partial last tile of codewords (K=300, 301 over tiles of 256): the
+    fp32 table equals the oracle's and the bf16 one is its single rounding (nearest even). B=8, 64 and 16 fill whole
+    16-byte units of entries per lane of a codeword (both table types); B=24 and B=12 do not divide the workgroup
+    that way and take the per-codeword loop, as do bf16 codebooks at d=3, K=301, whose tiles are not whole 4-byte
+    words."""
+    M = 96 // d
+    mat, h = synth.gen_exact(60 + B + d + K, rows=4, D=96, M=M, K=K, L=2, B=B, cb_dtype=cb_dtype)
+    W = to_dev(mat)
+    lut = host(la.build_lut(W, dev(h), lut_dtype=lut_dtype))
+    ref = O().build_lut(mat.codebooks, mat.cb_is_bf16, h).transpose(1, 2, 3, 0)   # [L][M][K][B]
+    if lut_dtype == "f32":
+        assert np.array_equal(lut.reshape(2, M, K, B), ref)
+    else:
+        assert np.array_equal(lut.view(np.uint16).reshape(2, M, K, B), synth.f32_to_bf16_bits(ref.astype(np.float32)))
+
+
 def test_build_lut_gelu_prologue():
     mat, rng = _rand(50, 8, 96, 48, 64, 2)
     g = synth.gen_hidden(rng, 2, 96) * np.float32(2.0)
