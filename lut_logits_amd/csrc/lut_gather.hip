@@ -1179,6 +1179,45 @@ __global__ __launch_bounds__(kTileThreads) void tile_lut_lds_kernel(const uint32
   }
 }
 
+// The same copy in 16-byte units, for whole 16-byte table rows (UB % 4 == 0)
+// and 16-byte runs per tile (R * UT % 4 == 0): a tile's R rows are one
+// contiguous run of R * UT units in the destination, so each lane gathers
+// four consecutive units of a run from LDS and stores them at once. A quarter
+// of the memory instructions of the 4-byte copy.
+__global__ __launch_bounds__(kTileThreads) void tile_lut_lds16_kernel(const uint32_t* __restrict__ src, int64_t NPK,
+                                                                      int UB, int UT, int NBT, int R,
+                                                                      uint32_t* __restrict__ dst) {
+  extern __shared__ uint32_t rowbuf[];   // [R][UB + 1]
+  const int64_t r0 = (int64_t)blockIdx.x * R;
+  const int rows = (int)min<int64_t>(R, NPK - r0);
+  const int UB4 = UB / 4;
+  const u32x4* s4 = reinterpret_cast<const u32x4*>(src + r0 * UB);
+  for (int u = threadIdx.x; u < rows * UB4; u += kTileThreads) {
+    const int row = u / UB4;
+    const int c = (u - row * UB4) * 4;
+    const u32x4 v = s4[u];
+    uint32_t* b = rowbuf + row * (UB + 1) + c;
+    b[0] = v[0]; b[1] = v[1]; b[2] = v[2]; b[3] = v[3];
+  }
+  __syncthreads();
+  const int run = rows * UT;              // this block's units of one tile
+  const int run4 = run / 4;               // whole 16-byte groups (rows * UT % 4 == 0 by the host's choice of R)
+  for (int v = threadIdx.x; v < NBT * run4; v += kTileThreads) {
+    const int t = v / run4;
+    const int w0 = (v - t * run4) * 4;    // first unit of the group within the run
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (w0 + i) / UT;
+      const int col = t * UT + (w0 + i - row * UT);
+      w[i] = col < UB ? rowbuf[row * (UB + 1) + col] : 0u;
+    }
+    u32x4 o;
+    o[0] = w[0]; o[1] = w[1]; o[2] = w[2]; o[3] = w[3];
+    *reinterpret_cast<u32x4*>(dst + ((int64_t)t * NPK + r0) * UT + w0) = o;
+  }
+}
+
 hipError_t launch_tile_lut(const void* lut, int lut_bf16, int NP, int K, int B, int BT, void* dst, hipStream_t stream) {
   const int NBT = (B + BT - 1) / BT;
   const int64_t NPK = (int64_t)NP * K;
@@ -1188,6 +1227,15 @@ hipError_t launch_tile_lut(const void* lut, int lut_bf16, int NP, int K, int B, 
     const int R = std::max(1, std::min(64, 16384 / (UB + 1)));   // at most 64 KB of LDS
     const size_t lds = (size_t)R * (UB + 1) * 4;
     const unsigned blocks = (unsigned)((NPK + R - 1) / R);
+    // 16-byte units: whole 16-byte table rows, every block's run per tile (the
+    // last block's too) a whole number of 16-byte units, 16-byte aligned ends
+    const int64_t last_rows = NPK - (int64_t)(blocks - 1) * R;
+    if (UB % 4 == 0 && ((int64_t)R * UT) % 4 == 0 && (last_rows * UT) % 4 == 0 && (NPK * UT) % 4 == 0 &&
+        ((uintptr_t)lut & 15) == 0 && ((uintptr_t)dst & 15) == 0) {
+      hipLaunchKernelGGL(tile_lut_lds16_kernel, dim3(blocks), dim3(kTileThreads), lds, stream,
+                         static_cast<const uint32_t*>(lut), NPK, UB, UT, NBT, R, static_cast<uint32_t*>(dst));
+      return hipGetLastError();
+    }
     hipLaunchKernelGGL(tile_lut_lds_kernel, dim3(blocks), dim3(kTileThreads), lds, stream,
                        static_cast<const uint32_t*>(lut), NPK, UB, UT, NBT, R, static_cast<uint32_t*>(dst));
     return hipGetLastError();

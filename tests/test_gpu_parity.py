@@ -188,6 +188,24 @@ def test_lut_logits_bf16_codebooks_exact():
     assert np.array_equal(host(lg).astype(np.float64), z)
 
 
+@pytest.mark.parametrize("lut_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("B", [20, 24, 40])
+def test_lut_logits_batch_tiled_exact(B, lut_dtype):
+    """Batches the lookup+sum splits into batch tiles (fp32 tables: 16 + the rest; bf16 tables: tiles of 4), so
+    the call first copies the table into the batch-tiled layout: 16-byte units where a table row is whole 16-byte
+    units (all but B=20 with a bf16 table, which takes the 4-byte copy), a last block of 32 of 64 table rows
+    (K=501), and zero columns past B. Exact inputs: every table entry is exact in bf16 too, so the logits equal the
+    oracle's bit for bit."""
+    mat, h = synth.gen_exact(900 + B, 1500, 96, 16, 501, 2, B)
+    W = to_dev(mat)
+    lut = la.build_lut(W, dev(h), lut_dtype=lut_dtype)
+    lg, am, _, _ = la.lut_logits(W, lut, B, softcap=0.0, lut_dtype=lut_dtype)
+    z, _ = O().logits(mat.codes, mat.codebooks, False, h, 0.0)
+    got = host(lg)
+    assert np.array_equal(got.astype(np.float64), z)
+    assert np.array_equal(host(am), np.argmax(got, axis=1).astype(np.int32))
+
+
 # ------------------------------------------------------------------ logits: float parity
 
 def test_tiny_config():
