@@ -273,7 +273,12 @@ __device__ __forceinline__ void regs_to_lds(const ChunkRegs<RS>& r, u32x4* dst, 
 // FD > 0: fused table build (see fused_word); requires LutT float, BT 1, REG.
 // CB: code width of the layout (16, 10 for RQ_CODES_PACKED10, 8 for
 // RQ_CODES_PACKED8): 8, 12 or 16 pairs per 16-byte block.
-template <typename LutT, int BT, int NSTEP, bool REG, int FD = 0, int CB = 16>
+// RSET: row sets per workgroup. Each staged chunk serves RSET sets of
+// steps x RPS rows one after the other (the code registers are reused, the
+// sums of every set stay in registers), so a slab of RSET times the rows
+// stages each chunk once: with several batch tiles the table restaging, not
+// the code stream, bounds the pass.
+template <typename LutT, int BT, int NSTEP, bool REG, int FD = 0, int CB = 16, int RSET = 1>
 __global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(1, 4)))
 void gather_kernel(GatherArgs a) {
   constexpr int PPB = CB == 10 ? 12 : (CB == 8 ? 16 : 8);   // pairs per code block
@@ -309,25 +314,29 @@ void gather_kernel(GatherArgs a) {
   const int rq = tid % QL;
   const int rl = tid / QL;
   const int b0 = bt * BT;
-  const int64_t row0 = (int64_t)s * a.steps * RPS + rl;
+  const int64_t row0 = (int64_t)s * RSET * a.steps * RPS + rl;
 
-  float acc[NSTEP][BQ];
+  float acc[RSET][NSTEP][BQ];
 #pragma unroll
-  for (int st = 0; st < NSTEP; ++st)
+  for (int rs = 0; rs < RSET; ++rs)
 #pragma unroll
-    for (int i = 0; i < BQ; ++i) acc[st][i] = 0.0f;
+    for (int st = 0; st < NSTEP; ++st)
+#pragma unroll
+      for (int i = 0; i < BQ; ++i) acc[rs][st][i] = 0.0f;
 
   // Byte offsets of this lane's rows inside one block of codes. Rows past the
   // end read the last row (in bounds); their sums are never stored.
   // Steps beyond the slab repeat step 0's row, so every load is issued
   // unconditionally (a fixed number of loads per block keeps the wait counts
   // exact) without touching other slabs' codes.
-  uint32_t roff[NSTEP];
+  uint32_t roff[RSET][NSTEP];
 #pragma unroll
-  for (int st = 0; st < NSTEP; ++st) {
-    const int64_t r = min(row0 + (int64_t)(st < a.steps ? st : 0) * RPS, a.rows - 1);
-    roff[st] = (uint32_t)(r * cv.s_row * 2);
-  }
+  for (int rs = 0; rs < RSET; ++rs)
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st) {
+      const int64_t r = min(row0 + (int64_t)(rs * a.steps + (st < a.steps ? st : 0)) * RPS, a.rows - 1);
+      roff[rs][st] = (uint32_t)(r * cv.s_row * 2);
+    }
   // The code stream is read with buffer loads: a scalar resource, the row
   // offset in a VGPR and the block offset in an SGPR, so the hot loop holds no
   // 64-bit per-lane addresses. (The host keeps the code array below 4 GiB.)
@@ -344,16 +353,16 @@ void gather_kernel(GatherArgs a) {
   // 16 bytes = the codes of PPB consecutive pairs of one row. Two register
   // buffers alternate: while one block is looked up, the next one loads into
   // the other buffer (no register copy, so no wait on the load in flight).
-  auto load_block = [&](uint4 (&dst)[NSTEP], int q) {
+  auto load_block = [&](uint4 (&dst)[NSTEP], int q, int rs = 0) {
     const uint32_t boff = (uint32_t)q * blk_bytes;
 #pragma unroll
     for (int st = 0; st < NSTEP; ++st) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(code_rsrc, (int)roff[st], (int)boff, kCodeCachePolicy);
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(code_rsrc, (int)roff[rs][st], (int)boff, kCodeCachePolicy);
       dst[st] = make_uint4(v[0], v[1], v[2], v[3]);
     }
   };
   // Lookups of the pairs of block q that lie in [lo, hi), against the chunk staged at p0.
-  auto lookup_block = [&](const uint4 (&w)[NSTEP], int q, int lo, int hi, int p0) {
+  auto lookup_block = [&](const uint4 (&w)[NSTEP], int q, int lo, int hi, int p0, int rs = 0) {
     // (not for bf16 tables at 4 rows per lane: that instance would spill)
     if (BQ == 1 && (sizeof(LutT) == 4 || NSTEP < 4) && PPB * q >= lo && PPB * q + PPB <= hi) {
       // The whole block is in range (uniform): the lookups of kLookGroup pairs
@@ -373,7 +382,7 @@ void gather_kernel(GatherArgs a) {
 #pragma unroll
         for (int t = 0; t < LG; ++t)
 #pragma unroll
-          for (int st = 0; st < NSTEP; ++st) acc[st][0] += v[t][st];
+          for (int st = 0; st < NSTEP; ++st) acc[rs][st][0] += v[t][st];
       }
       return;
     }
@@ -388,10 +397,10 @@ void gather_kernel(GatherArgs a) {
 #pragma unroll
         for (int st = 0; st < NSTEP; ++st) v[st] = lut_value(base + code_of<CB>(w[st], t) * BT);
 #pragma unroll
-        for (int st = 0; st < NSTEP; ++st) acc[st][0] += v[st];
+        for (int st = 0; st < NSTEP; ++st) acc[rs][st][0] += v[st];
       } else {
 #pragma unroll
-        for (int st = 0; st < NSTEP; ++st) lookup_add<LutT, BQ>(acc[st], base + code_of<CB>(w[st], t) * BT);
+        for (int st = 0; st < NSTEP; ++st) lookup_add<LutT, BQ>(acc[rs][st], base + code_of<CB>(w[st], t) * BT);
       }
     }
   };
@@ -479,7 +488,7 @@ void gather_kernel(GatherArgs a) {
   };
   // The loads are unconditional (past the end they repeat the last block, a
   // cache hit), so the same count is always in flight.
-  if (BT == 1 && a.P % PPB == 0) {
+  if (RSET == 1 && BT == 1 && a.P % PPB == 0) {
     // Chunks hold whole code blocks: one flat loop over the group's blocks, so
     // the next block's codes are already in flight across a chunk switch.
     // (Batch tiles keep the per-chunk loop: both loops in one kernel spill.)
@@ -502,26 +511,32 @@ void gather_kernel(GatherArgs a) {
       const int q0 = lo / PPB, q1 = (hi + PPB - 1) / PPB;
       load_block(wa, q0);
       switch_chunk(c);
-      for (int q = q0; q < q1; q += 2) {
-        load_block(wb, min(q + 1, q1 - 1));
-        lookup_block(wa, q, lo, hi, p0);
-        load_block(wa, min(q + 2, q1 - 1));
-        lookup_block(wb, q + 1, lo, hi, p0);
+#pragma unroll
+      for (int rs = 0; rs < RSET; ++rs) {
+        if (rs > 0) load_block(wa, q0, rs);
+        for (int q = q0; q < q1; q += 2) {
+          load_block(wb, min(q + 1, q1 - 1), rs);
+          lookup_block(wa, q, lo, hi, p0, rs);
+          load_block(wa, min(q + 2, q1 - 1), rs);
+          lookup_block(wb, q + 1, lo, hi, p0, rs);
+        }
       }
     }
   }
   // ---- G > 1: store the partial sums; the finish kernel adds them in group order
   if (a.G > 1) {
 #pragma unroll
-    for (int st = 0; st < NSTEP; ++st) {
-      const int64_t r = row0 + (int64_t)st * RPS;
-      if (st >= steps || r >= a.rows) continue;
+    for (int rs = 0; rs < RSET; ++rs)
 #pragma unroll
-      for (int i = 0; i < BQ; ++i) {
-        const int b = b0 + rq * BQ + i;
-        if (b < a.B) partial[((size_t)g * a.B + b) * a.rows + r] = acc[st][i];
+      for (int st = 0; st < NSTEP; ++st) {
+        const int64_t r = row0 + (int64_t)(rs * steps + st) * RPS;
+        if (st >= steps || r >= a.rows) continue;
+#pragma unroll
+        for (int i = 0; i < BQ; ++i) {
+          const int b = b0 + rq * BQ + i;
+          if (b < a.B) partial[((size_t)g * a.B + b) * a.rows + r] = acc[rs][st][i];
+        }
       }
-    }
     return;
   }
 
@@ -530,14 +545,16 @@ void gather_kernel(GatherArgs a) {
 #pragma unroll
   for (int i = 0; i < BQ; ++i) kbest[i] = 0ull;
 #pragma unroll
+  for (int rs = 0; rs < RSET; ++rs)
+#pragma unroll
   for (int st = 0; st < NSTEP; ++st) {
-    const int64_t r = row0 + (int64_t)st * RPS;
+    const int64_t r = row0 + (int64_t)(rs * steps + st) * RPS;
     if (st >= steps || r >= a.rows) continue;
 #pragma unroll
     for (int i = 0; i < BQ; ++i) {
       const int b = b0 + rq * BQ + i;
       if (b >= a.B) continue;
-      const float z = acc[st][i];
+      const float z = acc[rs][st][i];
       const float v = a.softcap > 0.0f ? a.softcap * tanhf(z / a.softcap) : z;
       float* const outp = second ? a.out2 : a.out;
       if (outp) outp[(size_t)b * a.rows + r] = v;
@@ -554,9 +571,10 @@ void gather_kernel(GatherArgs a) {
   if (tid < BT && b0 + tid < a.B) a.block_keys[(size_t)(b0 + tid) * a.S + s] = s_keys[tid];
 }
 
-template <typename LutT, int BT, int NSTEP, int FD = 0, int CB = 16>
+template <typename LutT, int BT, int NSTEP, int FD = 0, int CB = 16, int RSET = 1>
 hipError_t launch_gather_typed(const GatherArgs& a, const GatherPlan& plan, hipStream_t stream) {
   if (plan.steps < 1 || plan.steps > NSTEP) return hipErrorInvalidValue;   // a lane holds NSTEP rows at most
+  if (plan.rset != RSET) return hipErrorInvalidValue;                       // slabs are sized for this many row sets
   const size_t chunk_bytes = (size_t)plan.P * a.K * BT * sizeof(LutT);
   const bool reg = (a.B == BT || a.tiled) && chunk_bytes % 16 == 0 &&
                    chunk_bytes <= (size_t)reg_stage(BT, FD) * 16 * kGatherThreads &&
@@ -565,7 +583,7 @@ hipError_t launch_gather_typed(const GatherArgs& a, const GatherPlan& plan, hipS
   if constexpr (FD != 0)
     kern = gather_kernel<LutT, BT, NSTEP, true, FD, CB>;
   else
-    kern = reg ? gather_kernel<LutT, BT, NSTEP, true, 0, CB> : gather_kernel<LutT, BT, NSTEP, false, 0, CB>;
+    kern = reg ? gather_kernel<LutT, BT, NSTEP, true, 0, CB, RSET> : gather_kernel<LutT, BT, NSTEP, false, 0, CB, RSET>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget);
   if (e != hipSuccess) return e;
   hipEvent_t before, after;
@@ -942,7 +960,9 @@ bool tuning_override(GatherPlan& p, int NP, int64_t rows, int B, int mats) {
   p.steps = std::min(steps, nstep_for(p.BT));
   p.cpg = (p.chunks + G - 1) / G;
   p.G = (p.chunks + p.cpg - 1) / p.cpg;
-  p.S = (int)((rows + (int64_t)p.steps * p.rps - 1) / ((int64_t)p.steps * p.rps));
+  int rset = 0;
+  if (sscanf(s, "%*d,%*d,%*d,%*d,%d", &rset) == 1 && (rset == 1 || rset == 2)) p.rset = rset;
+  p.S = (int)((rows + (int64_t)p.rset * p.steps * p.rps - 1) / ((int64_t)p.rset * p.steps * p.rps));
   return true;
 }
 #endif
@@ -1063,6 +1083,13 @@ GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16, int fus
     best.cpg = (best.chunks + 7) / 8;
     best.G = (best.chunks + best.cpg - 1) / best.cpg;
   }
+  // Several bf16 batch tiles of 4: two row sets per workgroup, so every staged
+  // chunk serves twice the rows (the kernel's time there falls as 1/rows per
+  // slab: the table restaging bounds it).
+  if (best.BT == 4 && best.NBT > 1 && lut_bf16 && !fused_d && best.S >= 2) {
+    best.rset = 2;
+    best.S = (int)((rows + 2 * (int64_t)best.steps * best.rps - 1) / (2 * (int64_t)best.steps * best.rps));
+  }
   best.lds = (size_t)best.P * K * BT * es + fused_act_bytes(best.P, best.cpg, NP, fused_d);
   return best;
 }
@@ -1132,7 +1159,9 @@ hipError_t dispatch_gather(const GatherArgs& a, const GatherPlan& plan, int d, i
   }
   if (lut_bf16) {
     if (plan.BT == 1) return launch_gather_typed<uint16_t, 1, 4, 0, CB>(a, plan, stream);
-    if (plan.BT == 4) return launch_gather_typed<uint16_t, 4, 4, 0, CB>(a, plan, stream);
+    if (plan.BT == 4)
+      return plan.rset == 2 ? launch_gather_typed<uint16_t, 4, 4, 0, CB, 2>(a, plan, stream)
+                            : launch_gather_typed<uint16_t, 4, 4, 0, CB>(a, plan, stream);
     return launch_gather_typed<uint16_t, 16, 4, 0, CB>(a, plan, stream);
   }
   if (plan.BT == 1) return launch_gather_typed<float, 1, 4, 0, CB>(a, plan, stream);

@@ -94,9 +94,10 @@ struct GatherPlan {
   int chunks;    // ceil(NP / P)
   int cpg;       // chunks per group
   int G;         // groups: partial sums per output, reduced in a fixed order
-  int steps;     // row steps per slab
+  int steps;     // row steps per row set
   int rps;       // rows per step
-  int S;         // row slabs
+  int S;         // row slabs of rset * steps * rps rows
+  int rset = 1;  // row sets per workgroup (2: bf16 tables in several batch tiles of 4)
   int NBT;       // batch tiles
   size_t lds;    // dynamic LDS bytes per workgroup
   int64_t wgs() const { return (int64_t)G * S * NBT; }

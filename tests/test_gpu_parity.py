@@ -206,6 +206,21 @@ def test_lut_logits_batch_tiled_exact(B, lut_dtype):
     assert np.array_equal(host(am), np.argmax(got, axis=1).astype(np.int32))
 
 
+@pytest.mark.parametrize("B,rows", [(24, 20000), (40, 9000), (4, 12000)])
+def test_lut_logits_row_sets_exact(B, rows):
+    """bf16 tables in several batch tiles of 4 over more than two slabs of 4,096 rows: each workgroup runs two row
+    sets per staged chunk (slabs of 8,192 rows, the last one ragged), and B=4 (a single tile) keeps one. Exact
+    inputs: the logits equal the oracle's bit for bit."""
+    mat, h = synth.gen_exact(700 + B, rows, 96, 16, 301, 2, B)
+    W = to_dev(mat)
+    lut = la.build_lut(W, dev(h), lut_dtype="bf16")
+    lg, am, _, _ = la.lut_logits(W, lut, B, softcap=0.0, lut_dtype="bf16")
+    z, _ = O().logits(mat.codes, mat.codebooks, False, h, 0.0)
+    got = host(lg)
+    assert np.array_equal(got.astype(np.float64), z)
+    assert np.array_equal(host(am), np.argmax(got, axis=1).astype(np.int32))
+
+
 # ------------------------------------------------------------------ logits: float parity
 
 def test_tiny_config():
