@@ -139,6 +139,12 @@ class Oracle:
         _check(self.lib.oracle_topk(_ptr(logits, _dp), B, V, k, _ptr(ids, _i32p), _ptr(vals, _dp)))
         return ids, vals
 
+    def check_codes(self, codes, K):
+        """0 when every code of [rows][L][M] is below K, else the oracle's error status."""
+        codes = np.ascontiguousarray(codes, dtype=np.uint16)
+        rows, L, M = codes.shape
+        return self.lib.oracle_check_codes(rows, M, K, L, _ptr(codes, _u16p))
+
     def decode_rows(self, codes, cb, cb_bf16, ids, out_bf16):
         """Rows [n][D]: fp32 (out_bf16 False) or bf16 bits as uint16; plus the bad-id count."""
         codes, cb, V, L, M, K, d = self._mat(codes, cb, cb_bf16)

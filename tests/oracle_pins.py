@@ -233,6 +233,85 @@ def pin_decode_rows(o):
     assert out.shape == (3, M * d)
 
 
+def _round_to_f32(q):
+    """Correct rounding (to nearest, ties to even) of an exact rational to fp32, in integer
+    arithmetic: no intermediate float, so no double rounding."""
+    if q == 0:
+        return np.float32(0.0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()   # 2^e <= a < 2^(e+2)
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    ulp = Fraction(2) ** max(e - 23, -149)
+    n, rem = divmod(a, ulp)
+    n = int(n)
+    if rem * 2 > ulp or (rem * 2 == ulp and n % 2 == 1):
+        n += 1
+    return np.float32(sign * float(n * ulp))   # n * ulp is an fp32 value: float() is exact
+
+
+def pin_decode_rows_many_levels(o):
+    """Decoded rows for L >= 3 are the correctly rounded fp32 value of the exact level sum (one
+    rounding; Python Fractions), not a level-by-level fp32 sum: a hand case where the two differ
+    (1 + 2^-24 + 2^-24: fp32 sum 1, exact 1 + 2^-23), then random codebooks at L=3 and L=4 with
+    codewords of very different scales, where at least one element tells the two readings apart.
+    bf16 output is the nearest-even bf16 of that fp32 value."""
+    cb = np.zeros((3, 1, 2, 1), np.float32)
+    cb[:, 0, 0, 0] = [1.0, 2.0 ** -24, 2.0 ** -24]
+    cb[:, 0, 1, 0] = [2.0 ** -24, 2.0 ** -24, 1.0]
+    codes = np.zeros((2, 3, 1), np.uint16)
+    codes[1] = 1
+    out, _ = o.decode_rows(codes, cb, False, np.array([0, 1], np.int32), False)
+    assert out[0, 0] == np.float32(1.0 + 2.0 ** -23) and out[1, 0] == np.float32(1.0 + 2.0 ** -23)
+    differ = 0
+    for L, seed in ((3, 31), (4, 32)):
+        sig = (0.5, 3e-5, 2e-9, 1e-6)[:L]
+        mat, _ = _random_matrix(seed, 40, 12, 4, 6, L, sigmas=sig)
+        ids = np.arange(40, dtype=np.int32)
+        got, _ = o.decode_rows(mat.codes, mat.codebooks, False, ids, False)
+        gotb, _ = o.decode_rows(mat.codes, mat.codebooks, False, ids, True)
+        d = mat.d
+        for i in ids:
+            for m in range(mat.M):
+                for j in range(d):
+                    vals = [mat.codebooks[l, m, mat.codes[i, l, m], j] for l in range(L)]
+                    want = _round_to_f32(sum(Fraction(float(v)) for v in vals))
+                    assert got[i, m * d + j] == want, (L, i, m, j)
+                    seq = np.float32(0.0)
+                    for v in vals:
+                        seq = np.float32(seq + v)
+                    differ += int(seq != want)
+        wantb = torch.from_numpy(got).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(gotb, wantb)
+    assert differ > 0, "no element separates one rounding from a level-by-level fp32 sum"
+
+
+def pin_code_range(o):
+    """Codes index codewords 0 .. K-1 (a code is a codeword number): the largest valid code
+    K-1 is accepted and decodes to codeword K-1; a code equal to K is refused by the code
+    check and by every operation that reads codes."""
+    K = 5
+    cb = np.arange(2 * 3 * K * 2, dtype=np.float32).reshape(2, 3, K, 2)
+    codes = np.full((4, 2, 3), K - 1, np.uint16)
+    assert o.check_codes(codes, K) == 0
+    out, _ = o.decode_rows(codes, cb, False, np.array([2], np.int32), False)
+    assert np.array_equal(out[0], cb[0, :, K - 1].reshape(-1) + cb[1, :, K - 1].reshape(-1))
+    bad = codes.copy()
+    bad[3, 1, 2] = K
+    assert o.check_codes(bad, K) != 0
+    for call in (lambda: o.decode_rows(bad, cb, False, np.array([3], np.int32), False),
+                 lambda: o.matvec(bad, cb, False, np.ones((1, 6))),
+                 lambda: o.logits(bad, cb, False, np.ones((1, 6), np.float32), 30.0)):
+        try:
+            call()
+        except ValueError:
+            continue
+        raise AssertionError("a code equal to K was accepted")
+
+
 def pin_bf16_rounding(o):
     """Round-to-nearest-even ties on hand-checked values (1 + 2^-8 -> 1; 1 + 3*2^-8 -> 1 + 2^-6)."""
     cb = np.zeros((1, 1, 4, 1), np.float32)

@@ -56,6 +56,15 @@ MUTANTS = {
     "lut_sum_level0_only": (
         "acc += lut[(((size_t)b * L + l) * M + m) * (size_t)K + k];",
         "acc += lut[(((size_t)b * L + 0) * M + m) * (size_t)K + k];"),
+    "decode_levels_summed_in_fp32": (
+        "s += codebook_value(cb, cb_is_bf16, cb_pos(l, m, k, j, M, K, d));",
+        "s = (float)(s + codebook_value(cb, cb_is_bf16, cb_pos(l, m, k, j, M, K, d)));"),
+    "code_check_admits_k": (
+        "if (codes[i] >= K) return OR_ERR_CODE;",
+        "if (codes[i] > K) return OR_ERR_CODE;"),
+    "decode_code_check_admits_k": (
+        "if (codes[code_pos(r, l, m, L, M)] >= K) { free(w); return OR_ERR_CODE; }",
+        "if (codes[code_pos(r, l, m, L, M)] > K) { free(w); return OR_ERR_CODE; }"),
     "lut_sum_first_code_of_row": (
         "int k = codes[code_pos(r, l, m, L, M)];\n          acc +=",
         "int k = codes[code_pos(r, l, 0, L, M)];\n          acc +="),
