@@ -24,18 +24,19 @@
  * Conventions for every entry point:
  *   - Memory. All array pointers are DEVICE pointers owned by the caller. The
  *     library allocates nothing, keeps no state between calls (apart from the
- *     thread-local text behind rq_last_error and the one-shot events of
- *     rq_set_stage_events) and never synchronises: work is
- *     enqueued on `stream` and completes asynchronously.
+ *     thread-local text behind rq_last_error) and never synchronises: work is
+ *     enqueued on `stream` and completes asynchronously. (The measurement
+ *     aids of rq_lut_measure.h are outside these serving calls.)
  *   - Errors. Arguments are checked on the host before anything is launched;
  *     a failed check returns a negative rq_status and enqueues nothing. A
  *     failed launch returns RQ_ERR_HIP. rq_last_error() describes the last
  *     failure on the calling thread.
  *   - Empty work. B == 0, n == 0 or rows == 0 return RQ_OK and enqueue
  *     nothing.
- *   - Codes must be < K; a larger code is a precondition violation that the
- *     kernels do not check (it reads a neighbouring table entry; results are
- *     undefined, memory outside the library's own buffers is never touched).
+ *   - Codes must be < K. A larger code breaks that precondition: the lookup
+ *     kernels then read some other entry of their on-chip table or codebook
+ *     copy (the result is undefined) and rq_decode_rows reads it as K-1; no
+ *     call reads or writes memory outside the arrays it is given.
  *   - Alignment. codes and lut must be 16-byte aligned, other arrays 4-byte
  *     aligned, workspaces 256-byte aligned (torch allocations satisfy this).
  *   - Workspaces hold per-call scratch only (no state carries over between
@@ -323,39 +324,6 @@ rq_status rq_dense_logits(const uint16_t* E, int64_t rows, int32_t D, const floa
                           float softcap, float* logits, int32_t* argmax, void* ws, size_t ws_bytes,
                           hipStream_t stream);
 
-/*
- * Measurement aid, not part of the method: reads bytes [src, src + bytes)
- * once with 16-byte loads and nothing else, so that its rate is the HBM
- * stream-read ceiling this GPU reaches; the lookup+sum pass's bandwidth is
- * reported against it as well as against the specification.
- *   config  0 .. rq_stream_read_configs()-1: a grid size (256 to 2048
- *           workgroups of 1024 threads) and a count of loads each thread
- *           keeps in flight (1, 2, 4 or 8); the caller keeps the fastest
- *   src     device buffer, 16-byte aligned; bytes a multiple of 16
- *   sink    device uint32 [rq_stream_read_sink_words(config)]: word w is
- *           the XOR of every 32-bit word workgroup w read, so the XOR of
- *           all sink words is the XOR of every word of the buffer
- * bytes == 0 is a no-op. NULL buffers return RQ_ERR_NULL, misalignment
- * RQ_ERR_ALIGN, an unknown config RQ_ERR_SHAPE.
- */
-int32_t rq_stream_read_configs(void);
-size_t rq_stream_read_sink_words(int32_t config);
-rq_status rq_stream_read(const void* src, size_t bytes, int32_t config, uint32_t* sink, hipStream_t stream);
-
-/*
- * Measurement hook. The next lookup+sum kernel that rq_lut_logits or
- * rq_lut_matvec launches from the calling thread (or the next
- * rq_stream_read kernel) is launched with
- * hipExtLaunchKernelGGL(..., before, after, ...): the events take the start
- * and end of that kernel's own dispatch on its stream, so that
- * hipEventElapsedTime(before, after) is that one kernel's duration (the
- * selection/epilogue kernels of the same call fall outside; like a profiler's
- * kernel trace, it excludes the cache release at the kernel's end). The
- * hook is one-shot and thread-local: it is cleared when used, and by a call
- * with both events NULL. The events stay owned by the caller and must have
- * been created (hipEventCreate) without hipEventDisableTiming.
- */
-rq_status rq_set_stage_events(hipEvent_t before, hipEvent_t after);
 
 /* Static text for a status code. */
 const char* rq_status_string(rq_status s);

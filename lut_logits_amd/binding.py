@@ -26,7 +26,8 @@ EXPORTS = ("rq_blocked_codes_bytes", "rq_pack_codes", "rq_packed10_codes_bytes",
            "rq_packed8_codes_bytes", "rq_pack_codes8", "rq_lut_bytes", "rq_build_lut", "rq_lut_logits_workspace",
            "rq_lut_logits", "rq_logits_method", "rq_logits_workspace", "rq_logits", "rq_decode_rows", "rq_lut_matvec_workspace", "rq_lut_matvec",
            "rq_lut_mlp_workspace", "rq_lut_mlp", "rq_dense_logits_workspace", "rq_dense_logits", "rq_stream_read_configs",
-           "rq_stream_read_sink_words", "rq_stream_read", "rq_set_stage_events", "rq_status_string", "rq_last_error", "rq_version")
+           "rq_stream_read_sink_words", "rq_stream_read", "rq_set_stage_events", "rq_lut_logits_plan", "rq_status_string",
+           "rq_last_error", "rq_version")
 
 
 class RQError(RuntimeError):
@@ -78,6 +79,7 @@ def lib():
             "rq_stream_read_sink_words": (_sz, [_i32]),
             "rq_stream_read": (_i32, [_vp, _sz, _i32, _vp, _vp]),
             "rq_set_stage_events": (_i32, [_vp, _vp]),
+            "rq_lut_logits_plan": (_i32, [_MP, _i32, _i32, ctypes.POINTER(_i32)]),
             "rq_status_string": (ctypes.c_char_p, [_i32]),
             "rq_last_error": (ctypes.c_char_p, []),
             "rq_version": (ctypes.c_char_p, []),
@@ -104,6 +106,48 @@ def _stream():
 
 def _dtype_code(name):
     return {"f32": RQ_F32, "bf16": RQ_BF16}[name]
+
+
+def _arg(t, name, dtype, shape=None, numel=None, min_numel=None):
+    """Validate a tensor argument before its pointer reaches the library: dtype, shape (or element
+    count), contiguity and device. The library sees only pointers and sizes, so a tensor of the
+    wrong type or size here would otherwise be read or written out of its bounds."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name}: {t.numel()} elements, expected {numel}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name}: {t.numel()} elements, at least {min_numel} needed")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return t
+
+
+def _gpu(**tensors):
+    """Every tensor argument of a call must live on the GPU (checked after the per-argument checks)."""
+    for name, t in tensors.items():
+        if t is not None and t.device.type != "cuda":
+            raise ValueError(f"{name}: must be a GPU tensor (device {t.device})")
+
+
+_LUT_TORCH = {"f32": torch.float32, "bf16": torch.int16}
+
+
+def _lut_dtype_of(lut, lut_dtype):
+    """The table's dtype name from its tensor (float32: fp32 entries, int16: bf16 bit patterns);
+    an explicit lut_dtype must agree with it."""
+    if not isinstance(lut, torch.Tensor):
+        raise TypeError("lut: expected a torch.Tensor")
+    have = {torch.float32: "f32", torch.int16: "bf16"}.get(lut.dtype)
+    if have is None:
+        raise ValueError(f"lut: dtype {lut.dtype}; tables are float32 (fp32) or int16 (bf16 bits)")
+    if lut_dtype is not None and lut_dtype != have:
+        raise ValueError(f"lut_dtype={lut_dtype!r} but the table tensor holds {have} entries ({lut.dtype})")
+    return have
 
 
 class DeviceMatrix:
@@ -181,10 +225,15 @@ def lut_bytes(W, B, lut_dtype="f32"):
 
 def build_lut(W, x, lut_dtype="f32", x2=None, prologue=RQ_PRO_NONE, out=None):
     """rq_build_lut: the [L][M][K][B] table of the rows of x (fp32 [B][D])."""
-    B = x.shape[0]
+    B = x.shape[0] if x.dim() == 2 else -1
+    _arg(x, "x", torch.float32, shape=(B, W.D))
+    if x2 is not None:
+        _arg(x2, "x2", torch.float32, shape=(B, W.D))
+    n = lut_bytes(W, B, lut_dtype) // (2 if lut_dtype == "bf16" else 4)
     if out is None:
-        n = lut_bytes(W, B, lut_dtype) // (2 if lut_dtype == "bf16" else 4)
-        out = torch.empty(n, dtype=torch.int16 if lut_dtype == "bf16" else torch.float32, device=x.device)
+        out = torch.empty(n, dtype=_LUT_TORCH[lut_dtype], device=x.device)
+    _arg(out, "out", _LUT_TORCH[lut_dtype], numel=n)
+    _gpu(x=x, x2=x2, out=out)
     check(lib().rq_build_lut(W.ref, _ptr(x), _ptr(x2), prologue, B, _dtype_code(lut_dtype), _ptr(out), _stream()))
     return out
 
@@ -198,16 +247,36 @@ def workspace(nbytes, device="cuda"):
     return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
-def lut_logits(W, lut, B, softcap=30.0, lut_dtype="f32", logits=True, argmax=True, topk=0, ws=None, out=None,
-               argmax_out=None):
-    """rq_lut_logits: returns (logits [B][rows] | None, argmax [B] | None, topk_ids | None, topk_vals | None)."""
-    dev = lut.device
-    lg = (out if out is not None else torch.empty((B, W.rows), dtype=torch.float32, device=dev)) if logits else None
-    am = (argmax_out if argmax_out is not None else torch.empty(B, dtype=torch.int32, device=dev)) if argmax else None
+def _outputs(W, B, topk, dev, logits, argmax, out, argmax_out):
+    """Logits, argmax and top-k output tensors of a head call (the caller's, checked, or new ones)."""
+    lg = am = None
+    if logits:
+        lg = out if out is not None else torch.empty((B, W.rows), dtype=torch.float32, device=dev)
+        _arg(lg, "out", torch.float32, numel=B * W.rows)
+    if argmax:
+        am = argmax_out if argmax_out is not None else torch.empty(B, dtype=torch.int32, device=dev)
+        _arg(am, "argmax_out", torch.int32, numel=B)
     ti = torch.empty((B, topk), dtype=torch.int32, device=dev) if topk else None
     tv = torch.empty((B, topk), dtype=torch.float32, device=dev) if topk else None
+    return lg, am, ti, tv
+
+
+def _ws(ws, need, dev):
     if ws is None:
-        ws = workspace(lut_logits_workspace(W, B, topk, lut_dtype), dev)
+        return workspace(need, dev)
+    return _arg(ws, "ws", torch.uint8, min_numel=need)
+
+
+def lut_logits(W, lut, B, softcap=30.0, lut_dtype=None, logits=True, argmax=True, topk=0, ws=None, out=None,
+               argmax_out=None):
+    """rq_lut_logits: returns (logits [B][rows] | None, argmax [B] | None, topk_ids | None, topk_vals | None).
+    The table's dtype is taken from the tensor (float32 or int16 bf16 bits); lut_dtype, if given, must agree."""
+    lut_dtype = _lut_dtype_of(lut, lut_dtype)
+    _arg(lut, "lut", lut.dtype, numel=lut_bytes(W, B, lut_dtype) // lut.element_size())
+    dev = lut.device
+    lg, am, ti, tv = _outputs(W, B, topk, dev, logits, argmax, out, argmax_out)
+    ws = _ws(ws, lut_logits_workspace(W, B, topk, lut_dtype), dev)
+    _gpu(lut=lut, out=lg, argmax_out=am, ws=ws)
     check(lib().rq_lut_logits(W.ref, _ptr(lut), _dtype_code(lut_dtype), B, softcap, _ptr(lg), _ptr(am), topk,
                               _ptr(ti), _ptr(tv), _ptr(ws), ws.numel(), _stream()))
     return lg, am, ti, tv
@@ -228,14 +297,12 @@ def logits_workspace(W, B, topk=0):
 def logits(W, h, softcap=30.0, logits=True, argmax=True, topk=0, ws=None, out=None, argmax_out=None):
     """rq_logits (one call from the hidden vectors h [B][D] fp32): returns
     (logits [B][rows] | None, argmax [B] | None, topk_ids | None, topk_vals | None)."""
-    B = h.shape[0]
+    B = h.shape[0] if h.dim() == 2 else -1
+    _arg(h, "h", torch.float32, shape=(B, W.D))
     dev = h.device
-    lg = (out if out is not None else torch.empty((B, W.rows), dtype=torch.float32, device=dev)) if logits else None
-    am = (argmax_out if argmax_out is not None else torch.empty(B, dtype=torch.int32, device=dev)) if argmax else None
-    ti = torch.empty((B, topk), dtype=torch.int32, device=dev) if topk else None
-    tv = torch.empty((B, topk), dtype=torch.float32, device=dev) if topk else None
-    if ws is None:
-        ws = workspace(logits_workspace(W, B, topk), dev)
+    lg, am, ti, tv = _outputs(W, B, topk, dev, logits, argmax, out, argmax_out)
+    ws = _ws(ws, logits_workspace(W, B, topk), dev)
+    _gpu(h=h, out=lg, argmax_out=am, ws=ws)
     check(lib().rq_logits(W.ref, _ptr(h), B, softcap, _ptr(lg), _ptr(am), topk, _ptr(ti), _ptr(tv), _ptr(ws),
                           ws.numel(), _stream()))
     return lg, am, ti, tv
@@ -243,9 +310,15 @@ def logits(W, h, softcap=30.0, logits=True, argmax=True, topk=0, ws=None, out=No
 
 def decode_rows(W, ids, out_dtype="f32", bad_ids=None, out=None):
     """rq_decode_rows: rows [n][D] (fp32, or bf16 bit patterns as int16)."""
-    n = ids.shape[0]
+    n = ids.shape[0] if ids.dim() == 1 else -1
+    _arg(ids, "ids", torch.int32, shape=(n,))
+    if bad_ids is not None:
+        _arg(bad_ids, "bad_ids", torch.int32, min_numel=1)
+    odt = torch.int16 if out_dtype == "bf16" else torch.float32
     if out is None:
-        out = torch.empty((n, W.D), dtype=torch.int16 if out_dtype == "bf16" else torch.float32, device=ids.device)
+        out = torch.empty((n, W.D), dtype=odt, device=ids.device)
+    _arg(out, "out", odt, numel=n * W.D)
+    _gpu(ids=ids, bad_ids=bad_ids, out=out)
     check(lib().rq_decode_rows(W.ref, _ptr(ids), n, _dtype_code(out_dtype), _ptr(out), _ptr(bad_ids), _stream()))
     return out
 
@@ -256,10 +329,14 @@ def lut_matvec_workspace(W, B):
 
 def lut_matvec(W, x, x2=None, prologue=RQ_PRO_NONE, ws=None, out=None):
     """rq_lut_matvec: y [B][rows] = W a, a = x or gelu_tanh(x) * x2."""
-    B = x.shape[0]
+    B = x.shape[0] if x.dim() == 2 else -1
+    _arg(x, "x", torch.float32, shape=(B, W.D))
+    if x2 is not None:
+        _arg(x2, "x2", torch.float32, shape=(B, W.D))
     y = out if out is not None else torch.empty((B, W.rows), dtype=torch.float32, device=x.device)
-    if ws is None:
-        ws = workspace(lut_matvec_workspace(W, B), x.device)
+    _arg(y, "out", torch.float32, numel=B * W.rows)
+    ws = _ws(ws, lut_matvec_workspace(W, B), x.device)
+    _gpu(x=x, x2=x2, out=y, ws=ws)
     check(lib().rq_lut_matvec(W.ref, _ptr(x), _ptr(x2), prologue, B, _ptr(y), _ptr(ws), ws.numel(), _stream()))
     return y
 
@@ -270,10 +347,12 @@ def lut_mlp_workspace(gate, up, down, B):
 
 def lut_mlp(gate, up, down, x, ws=None, out=None):
     """rq_lut_mlp: y [B][down.rows] = down(gelu_tanh(gate(x)) * up(x))."""
-    B = x.shape[0]
+    B = x.shape[0] if x.dim() == 2 else -1
+    _arg(x, "x", torch.float32, shape=(B, gate.D))
     y = out if out is not None else torch.empty((B, down.rows), dtype=torch.float32, device=x.device)
-    if ws is None:
-        ws = workspace(lut_mlp_workspace(gate, up, down, B), x.device)
+    _arg(y, "out", torch.float32, numel=B * down.rows)
+    ws = _ws(ws, lut_mlp_workspace(gate, up, down, B), x.device)
+    _gpu(x=x, out=y, ws=ws)
     check(lib().rq_lut_mlp(gate.ref, up.ref, down.ref, _ptr(x), B, _ptr(y), _ptr(ws), ws.numel(), _stream()))
     return y
 
@@ -286,8 +365,13 @@ def stream_read_configs():
 def stream_read(buf, config, sink=None):
     """rq_stream_read: one read of the whole of `buf` (a device tensor, 16-byte aligned, nbytes % 16 == 0)
     with 16-byte loads; returns the uint32 sink (one XOR per workgroup) as an int32 tensor."""
+    if not buf.is_contiguous() or buf.device.type != "cuda":
+        raise ValueError("buf: must be a contiguous GPU tensor")
+    words = lib().rq_stream_read_sink_words(config)
     if sink is None:
-        sink = torch.empty(lib().rq_stream_read_sink_words(config), dtype=torch.int32, device=buf.device)
+        sink = torch.empty(words, dtype=torch.int32, device=buf.device)
+    _arg(sink, "sink", torch.int32, min_numel=words)
+    _gpu(sink=sink)
     check(lib().rq_stream_read(_ptr(buf), buf.numel() * buf.element_size(), config, _ptr(sink), _stream()))
     return sink
 
@@ -298,15 +382,31 @@ def dense_logits_workspace(rows, B):
 
 def dense_logits(E, h, softcap=30.0, argmax=True, ws=None, out=None):
     """rq_dense_logits: the dense bf16 comparison head; E is [rows][D] bf16 bits (int16 tensor)."""
+    if E.dim() != 2:
+        raise ValueError("E: expected [rows][D] bf16 bits")
     rows, D = E.shape
-    B = h.shape[0]
+    _arg(E, "E", torch.int16, shape=(rows, D))
+    B = h.shape[0] if h.dim() == 2 else -1
+    _arg(h, "h", torch.float32, shape=(B, D))
     lg = out if out is not None else torch.empty((B, rows), dtype=torch.float32, device=h.device)
+    _arg(lg, "out", torch.float32, numel=B * rows)
     am = torch.empty(B, dtype=torch.int32, device=h.device) if argmax else None
-    if ws is None and argmax:
-        ws = workspace(dense_logits_workspace(rows, B), h.device)
+    if argmax:
+        ws = _ws(ws, dense_logits_workspace(rows, B), h.device)
+    _gpu(E=E, h=h, out=lg, ws=ws)
     check(lib().rq_dense_logits(_ptr(E), rows, D, _ptr(h), B, softcap, _ptr(lg), _ptr(am), _ptr(ws),
                                 ws.numel() if ws is not None else 0, _stream()))
     return lg, am
+
+
+PLAN_FIELDS = ("BT", "P", "chunks", "cpg", "G", "steps", "rps", "S", "rset", "NBT")
+
+
+def lut_logits_plan(W, B, lut_dtype="f32"):
+    """rq_lut_logits_plan: the tiling rq_lut_logits uses, as a dict of PLAN_FIELDS."""
+    buf = (_i32 * 10)()
+    check(lib().rq_lut_logits_plan(W.ref, B, _dtype_code(lut_dtype), buf))
+    return dict(zip(PLAN_FIELDS, list(buf)))
 
 
 def set_stage_events(before, after):

@@ -17,12 +17,15 @@ from . import binding as B
 class DecodeLoop:
     """head: DeviceMatrix of the tied embedding / head; layers: list of (gate, up, down) DeviceMatrix."""
 
-    def __init__(self, head, layers, softcap=30.0, max_tokens=128, device="cuda"):
+    def __init__(self, head, layers, softcap=30.0, max_tokens=128, device="cuda", keep_layers=False):
+        """keep_layers: keep every block's output of the last step (xs[i] is block i's input,
+        xs[i + 1] its output) instead of two alternating buffers."""
         self.head, self.layers, self.softcap = head, list(layers), softcap
         self.scale = math.sqrt(head.D)
         self.ids = torch.zeros(max_tokens + 1, dtype=torch.int32, device=device)
         self.row = torch.empty((1, head.D), dtype=torch.float32, device=device)
-        self.xs = [torch.empty((1, head.D), dtype=torch.float32, device=device) for _ in range(2)]
+        nbuf = len(self.layers) + 1 if keep_layers else 2
+        self.xs = [torch.empty((1, head.D), dtype=torch.float32, device=device) for _ in range(nbuf)]
         self.lut = torch.empty(B.lut_bytes(head, 1) // 4, dtype=torch.float32, device=device)
         mlp_ws = max([B.lut_mlp_workspace(*lay, 1) for lay in self.layers] + [256])
         self.ws_mlp = B.workspace(mlp_ws, device)
@@ -34,7 +37,7 @@ class DecodeLoop:
         x = self.xs[0]
         torch.mul(self.row, self.scale, out=x)
         for i, (gate, up, down) in enumerate(self.layers):
-            y = self.xs[(i + 1) & 1]
+            y = self.xs[(i + 1) % len(self.xs)]
             B.lut_mlp(gate, up, down, x, ws=self.ws_mlp, out=y)
             x = y
         B.build_lut(self.head, x, out=self.lut)

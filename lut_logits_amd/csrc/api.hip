@@ -480,10 +480,7 @@ static MlpWs mlp_ws(const rq_matrix* gate, const rq_matrix* up, const rq_matrix*
   w.fused = rq::fused_build_supported(gate, B) && rq::fused_build_supported(up, B) &&
             rq::fused_build_supported(down, B);
   if (w.fused) {
-    int pair_mats = 2;
-#ifdef RQ_TUNING
-    if (const char* pm = getenv("RQ_MLP_PAIR_MATS")) pair_mats = atoi(pm);
-#endif
+    const int pair_mats = 2;
     w.pgu = rq::plan_gather(gate, B, 0, 1, pair_mats);
     if (w.pgu.BT != 0 && !rq::plan_covers_blocks(gate, w.pgu)) {   // gate and up from tables built first
       w.pair_tables = true;
@@ -580,6 +577,18 @@ rq_status rq_dense_logits(const uint16_t* E, int64_t rows, int32_t D, const floa
   return launched(rq::launch_select(keys, rq::dense_blocks(rows), B, argmax, logits, rows, 0, nullptr, nullptr,
                                     nullptr, stream),
                   "rq_dense_logits: argmax");
+}
+
+rq_status rq_lut_logits_plan(const rq_matrix* W, int32_t B, int32_t lut_dtype, int32_t plan[10]) {
+  rq_status s = check_lut_call(W, B, lut_dtype);
+  if (s != RQ_OK) return s;
+  if (!plan) return fail(RQ_ERR_NULL, "plan is NULL");
+  if (B < 1 || W->rows == 0) return fail(RQ_ERR_SHAPE, "a plan needs B >= 1 and rows >= 1");
+  const rq::GatherPlan p = rq::plan_gather(W, B, lut_dtype == RQ_BF16);
+  if (p.BT == 0) return fail(RQ_ERR_SHAPE, "no table tiling fits on chip for K=%d", W->K);
+  const int32_t v[10] = {p.BT, p.P, p.chunks, p.cpg, p.G, p.steps, p.rps, p.S, p.rset, p.NBT};
+  for (int i = 0; i < 10; ++i) plan[i] = v[i];
+  return RQ_OK;
 }
 
 int32_t rq_stream_read_configs(void) { return rq::stream_read_configs(); }

@@ -56,9 +56,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_rows_kernel(CodeView cv
   }
   constexpr int kMaxL = RQ_MAX_L;
   uint32_t code[kMaxL];
+  // A code >= K breaks the precondition; it is read as K-1 so that the
+  // codebook load stays inside the caller's array.
 #pragma unroll
   for (int l = 0; l < kMaxL; ++l)
-    if (l < L) code[l] = code_at(cv, id, l * M + m);
+    if (l < L) code[l] = min(code_at(cv, id, l * M + m), (uint32_t)(K - 1));
   double v[kMaxL];
 #pragma unroll
   for (int l = 0; l < kMaxL; ++l)

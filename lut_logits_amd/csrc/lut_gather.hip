@@ -176,11 +176,9 @@ constexpr int reg_stage(int BT, int FD) { return (FD == 0 && BT == 1) ? 6 : kReg
 // (fewer for lanes holding four rows).
 constexpr int kLookGroup = 4;
 
-// Cache policy bits of the code-stream loads (0: default).
-#ifndef RQ_CODE_CPOL
-#define RQ_CODE_CPOL 0
-#endif
-constexpr int kCodeCachePolicy = RQ_CODE_CPOL;
+// Cache policy bits of the code-stream loads: the default (non-temporal
+// policies measured no faster).
+constexpr int kCodeCachePolicy = 0;
 
 // RS 16-byte words of a chunk held in registers. A native vector type keeps
 // the copies first-class values (HIP's uint4 struct is copied through memory).
@@ -942,30 +940,6 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const uint64_t* __r
 
 int nstep_for(int BT) { return 4; }
 
-#ifdef RQ_TUNING
-// Tuning builds only: RQ_GATHER_PLAN="P,steps,G[,BT]" replaces the heuristic's choice
-// (RQ_GATHER_PLAN2 for two-matrix launches).
-bool tuning_override(GatherPlan& p, int NP, int64_t rows, int B, int mats) {
-  const char* s = getenv(mats == 2 ? "RQ_GATHER_PLAN2" : "RQ_GATHER_PLAN");
-  if (!s) return false;
-  int P, steps, G, BT = 0;
-  if (sscanf(s, "%d,%d,%d,%d", &P, &steps, &G, &BT) < 3) return false;
-  if (BT == 1 || BT == 4 || BT == 16) {
-    p.BT = BT;
-    p.rps = kGatherThreads / (BT >= 16 ? 4 : 1);
-    p.NBT = (B + BT - 1) / BT;
-  }
-  p.P = std::min(P, NP);
-  p.chunks = (NP + p.P - 1) / p.P;
-  p.steps = std::min(steps, nstep_for(p.BT));
-  p.cpg = (p.chunks + G - 1) / G;
-  p.G = (p.chunks + p.cpg - 1) / p.cpg;
-  int rset = 0;
-  if (sscanf(s, "%*d,%*d,%*d,%*d,%d", &rset) == 1 && (rset == 1 || rset == 2)) p.rset = rset;
-  p.S = (int)((rows + (int64_t)p.rset * p.steps * p.rps - 1) / ((int64_t)p.rset * p.steps * p.rps));
-  return true;
-}
-#endif
 
 }  // namespace
 
@@ -1146,10 +1120,6 @@ GatherPlan plan_gather(const rq_matrix* W, int B, int lut_bf16, int fused, int m
     g_plan_next = (g_plan_next + 1) % 32;
     if (g_plan_n < 32) ++g_plan_n;
   }
-#ifdef RQ_TUNING
-  if (tuning_override(plan, key.NP, key.rows, B, mats))
-    plan.lds = (size_t)plan.P * W->K * plan.BT * (lut_bf16 ? 2 : 4) + fused_act_bytes(plan.P, plan.cpg, key.NP, fd);
-#endif
   return plan;
 }
 
@@ -1328,9 +1298,6 @@ GatherArgs gather_args(const rq_matrix* W, const GatherPlan& plan, const void* l
   // all switch to the same chunks at once, which measured slower (69 -> 74 us),
   // so dispatch order is kept there.
   a.xcd_contiguous = plan.S >= 2 && plan.S <= 8;
-#ifdef RQ_TUNING
-  if (const char* xm = getenv("RQ_XCD_MAP")) a.xcd_contiguous = atoi(xm);
-#endif
   return a;
 }
 

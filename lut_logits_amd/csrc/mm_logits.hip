@@ -48,10 +48,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-#ifndef RQ_MM_THREADS
-#define RQ_MM_THREADS 512
-#endif
-constexpr int kMmThreads = RQ_MM_THREADS;   // one workgroup per CU (LDS); 512: 2 waves per SIMD, 256 VGPRs each
+constexpr int kMmThreads = 512;   // one workgroup per CU (LDS); 512: 2 waves per SIMD, 256 VGPRs each
 constexpr int kMmWaves = kMmThreads / 64;
 constexpr int kParts = 3;           // bf16 parts of each hidden value
 constexpr int kMaxCwPerThread = 4 * kMmMaxK / kMmThreads;   // codewords of a half-block per thread
@@ -401,15 +398,6 @@ hipError_t launch_nsub(const MmArgs& a, const MmPlan& p, int d, hipStream_t stre
   }
 }
 
-#ifdef RQ_TUNING
-// Tuning builds only: RQ_MM_PLAN="G" replaces the planner's group count.
-void mm_tuning_override(MmPlan& p) {
-  const char* s = getenv("RQ_MM_PLAN");
-  int G;
-  if (s && sscanf(s, "%d", &G) == 1 && G >= 1) p.G = G;
-}
-#endif
-
 }  // namespace
 
 bool mm_supported(const rq_matrix* W) {
@@ -443,11 +431,6 @@ MmPlan plan_mm(const rq_matrix* W, int B) {
     const double cost = rounds * qpg * per_block + (gg > 1 ? 5.0 + (double)(gg + 1) * B * W->rows * 4.0 / 2.2e6 : 0.0);
     if (cost < best * 0.999) { best = cost; G = gg; }
   }
-#ifdef RQ_TUNING
-  p.G = G;
-  mm_tuning_override(p);
-  G = std::max(1, std::min(p.G, p.NQ));
-#endif
   p.qpg = (p.NQ + G - 1) / G;
   p.G = (p.NQ + p.qpg - 1) / p.qpg;
   p.lds = (size_t)2 * (4 * (size_t)W->K + (size_t)kParts * 4 * 16 * p.NT) * 16;

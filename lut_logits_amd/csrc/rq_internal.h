@@ -11,6 +11,7 @@
 #include <stdint.h>
 
 #include "rq_lut.h"
+#include "rq_lut_measure.h"
 
 namespace rq {
 
@@ -97,7 +98,7 @@ struct GatherPlan {
   int steps;     // row steps per row set
   int rps;       // rows per step
   int S;         // row slabs of rset * steps * rps rows
-  int rset = 1;  // row sets per workgroup (2: bf16 tables in several batch tiles of 4)
+  int rset = 1;  // row sets per workgroup (2: bf16 tables in several batch tiles of 4, fp32 tables of 16 vectors)
   int NBT;       // batch tiles
   size_t lds;    // dynamic LDS bytes per workgroup
   int64_t wgs() const { return (int64_t)G * S * NBT; }

@@ -91,10 +91,65 @@ def test_mlp_26_layers_full():
         g = la.lut_matvec(Wg, xd)
         u = la.lut_matvec(Wu, xd)
         y = la.lut_matvec(Wd, g, x2=u, prologue=la.RQ_PRO_GELU_TANH_MUL)
-        check_logits(host(la.lut_mlp(Wg, Wu, Wd, xd)), host(y).astype(np.float64))   # the fused block
+        yf = host(la.lut_mlp(Wg, Wu, Wd, xd))   # the fused block
+        check_logits(yf, host(y).astype(np.float64))
         og, ou, _, oy = O().mlp((gate.codes, gate.codebooks, False), (up.codes, up.codebooks, False),
                                 (down.codes, down.codebooks, False), x)
         check_logits(host(g), og)
         check_logits(host(u), ou)
         check_logits(host(y), oy)
+        check_logits(yf, oy)
         del Wg, Wu, Wd
+
+
+@pytest.mark.parametrize("layer", [0, 1, 25])
+def test_mlp_layer_packed10_full(layer):
+    """The benchmarked 10-bit MLP layer (gate/up/down codes in RQ_CODES_PACKED10, d=2, K=1024, fp32
+    codebooks) under the planner's Gemma-shape plans: the fused block and the three matvecs against the
+    oracle; a repeated call gives the same bits."""
+    x = synth.make_mlp_x()
+    xd = dev(x)
+    gate, up, down = synth.make_mlp_layer(layer)
+    P = [to_dev(m, "packed10") for m in (gate, up, down)]
+    y = host(la.lut_mlp(*P, xd))
+    g = la.lut_matvec(P[0], xd)
+    u = la.lut_matvec(P[1], xd)
+    y3 = host(la.lut_matvec(P[2], g, x2=u, prologue=la.RQ_PRO_GELU_TANH_MUL))
+    og, ou, _, oy = O().mlp((gate.codes, gate.codebooks, False), (up.codes, up.codebooks, False),
+                            (down.codes, down.codebooks, False), x)
+    check_logits(host(g), og)
+    check_logits(host(u), ou)
+    check_logits(y3, oy)
+    check_logits(y, oy)
+    assert np.array_equal(host(la.lut_mlp(*P, xd)), y)   # deterministic
+
+
+def test_composite_gemma_shapes_teacher_forced():
+    """The per-token loop at the Gemma-2-2B shapes (the 256000 x 2304 head, 26 MLP blocks of 9216 x 2304 /
+    2304 x 9216) for three tokens, teacher-forced: for every token and block, the block's GPU output against
+    the oracle's block on the GPU's input to it; the embedding row against the oracle's decode; the next
+    token within 2t of the oracle head's maximum on the GPU's last hidden vector."""
+    from lut_logits_amd.composite import DecodeLoop
+    cfg = synth.CONFIGS["gemma_b1"]
+    head, _, _ = synth.make_head(cfg)
+    layers = [synth.make_mlp_layer(i) for i in range(synth.MLP_LAYERS)]
+    loop = DecodeLoop(to_dev(head), [tuple(to_dev(m) for m in lay) for lay in layers], softcap=cfg.softcap,
+                      max_tokens=4, keep_layers=True)
+    loop.ids[0] = 1234
+    o = O()
+    scale = np.float32(np.sqrt(cfg.D))
+    tok = 1234
+    for t in range(3):
+        loop.step(t)
+        xs = [host(v) for v in loop.xs]
+        nxt = int(loop.ids[t + 1].item())
+        row, _ = o.decode_rows(head.codes, head.codebooks, True, np.array([tok], np.int32), False)
+        assert np.array_equal(xs[0], row.astype(np.float32) * scale)
+        for i, (gate, up, down) in enumerate(layers):
+            _, _, _, oy = o.mlp((gate.codes, gate.codebooks, False), (up.codes, up.codebooks, False),
+                                (down.codes, down.codebooks, False), xs[i])
+            check_logits(xs[i + 1], oy)
+        _, ref = o.logits(head.codes, head.codebooks, True, xs[-1], cfg.softcap)
+        tol = 1e-5 * np.abs(ref).max()
+        assert ref[0, nxt] >= ref[0].max() - 2 * tol, f"token {t}: {nxt} is not a maximum of the oracle head"
+        tok = nxt

@@ -87,6 +87,24 @@ def test_decode_rows_gemma_shape():
     assert nbad == 0 and np.array_equal(out, want)
 
 
+@pytest.mark.parametrize("layout", ["rows", "blocked"])
+def test_decode_rows_code_out_of_range(layout):
+    """A code equal to K (a broken precondition) decodes as codeword K-1 instead of reading past the
+    codebook: placed only at pair (0, 0) of one row, so even an unclamped read would stay inside the
+    codebook array. Every other element and row is the oracle's."""
+    mat, rng = _rand(41, 256, 96, 16, 64, 2, "f32")
+    bad_codes = mat.codes.copy()
+    bad_codes[5, 0, 0] = mat.K
+    bad = synth.RQMatrix(mat.rows, mat.D, mat.M, mat.d, mat.K, mat.L, mat.cb_dtype, mat.codebooks, bad_codes)
+    W = to_dev(bad, layout)
+    ids = np.array([5, 6], np.int32)
+    out = host(la.decode_rows(W, dev(ids)))
+    fixed = bad_codes.copy()
+    fixed[5, 0, 0] = mat.K - 1
+    want, _ = O().decode_rows(fixed, mat.codebooks, False, ids, False)
+    assert np.array_equal(out, want)
+
+
 # ------------------------------------------------------------------ table build
 
 @pytest.mark.parametrize("cb_dtype", ["f32", "bf16"])
@@ -215,6 +233,25 @@ def test_lut_logits_row_sets_exact(B, rows):
     W = to_dev(mat)
     lut = la.build_lut(W, dev(h), lut_dtype="bf16")
     lg, am, _, _ = la.lut_logits(W, lut, B, softcap=0.0, lut_dtype="bf16")
+    z, _ = O().logits(mat.codes, mat.codebooks, False, h, 0.0)
+    got = host(lg)
+    assert np.array_equal(got.astype(np.float64), z)
+    assert np.array_equal(host(am), np.argmax(got, axis=1).astype(np.int32))
+
+
+@pytest.mark.parametrize("B", [16, 17])
+def test_lut_logits_fp32_row_sets_exact(B):
+    """fp32 tables of 16 vectors: two row sets per workgroup (slabs of 2 x 4 x 256 rows) with groups of pairs
+    added to keep a workgroup per CU. 5000 rows span three slabs, the last one ragged; B=17 adds a second,
+    one-vector batch tile. The plan query confirms the route; exact inputs make the logits the oracle's bit
+    for bit."""
+    mat, h = synth.gen_exact(750 + B, 5000, 96, 16, 301, 2, B)
+    W = to_dev(mat)
+    plan = la.lut_logits_plan(W, B, "f32")
+    assert plan["BT"] == 16 and plan["rset"] == 2 and plan["G"] > 1 and plan["S"] == 3, plan
+    assert plan["NBT"] == (B + 15) // 16
+    lut = la.build_lut(W, dev(h))
+    lg, am, _, _ = la.lut_logits(W, lut, B, softcap=0.0)
     z, _ = O().logits(mat.codes, mat.codebooks, False, h, 0.0)
     got = host(lg)
     assert np.array_equal(got.astype(np.float64), z)
