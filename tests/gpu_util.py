@@ -2,7 +2,7 @@
 
 Comparison rules (the tolerances the tests enforce):
   - integer and byte work (packed codes, decoded rows, ids) is compared bit for bit;
-  - fp32-table logits: |gpu - oracle| <= 1e-5 * max|oracle| for each batch entry;
+  - fp32-table logits: |gpu - oracle| <= 1e-5 * max|oracle| for each batch entry, all values finite;
   - bf16-table logits: per element 2^-8 * sum_{l,m} |LUT64 entry used| + 1e-5 * max|oracle|
     (twice the bf16 rounding bound of every looked-up entry; the softcap's slope <= 1 keeps it);
   - argmax: the GPU id is the lowest index of the maximum of the GPU's own logits, and its oracle
@@ -35,6 +35,8 @@ def oracle_head(mat, h, softcap):
 def check_logits(gpu, ref, tol=None):
     """Per batch entry: max |gpu - ref| <= tol (default 1e-5 * max|ref|). Returns the worst relative error."""
     gpu = np.asarray(gpu, np.float64)
+    assert np.isfinite(ref).all(), "the oracle's values are not all finite"
+    assert np.isfinite(gpu).all(), f"{int((~np.isfinite(gpu)).sum())} GPU values are not finite"
     worst = 0.0
     for b in range(ref.shape[0]):
         scale = max(np.abs(ref[b]).max(), 1e-30)

@@ -2,7 +2,8 @@
 
 The loop feeds each argmax back as the next token on the device. The oracle is run teacher-forced: for
 every step it takes the token the GPU chose, rebuilds that token's embedding row, the sqrt(D) scale, the
-MLP chain (fp64) and the head, and the GPU's hidden vector and next token must agree with it."""
+blocks (fp64) on the GPU's inputs to them and the head, and the GPU's blocks and next token must agree
+with it."""
 import numpy as np
 import pytest
 import torch
@@ -18,6 +19,31 @@ pytestmark = pytest.mark.gpu
 O = oracle.default
 
 
+def _rms(v):
+    v = np.asarray(v, np.float64)
+    return v / np.sqrt((v * v).mean(axis=-1, keepdims=True) + 1e-6)
+
+
+def check_loop_step(o, head, layers, loop, tok, softcap):
+    """One step of the loop, teacher-forced: every block's GPU output against the oracle's block on the
+    GPU's input to it, the norms and residual stream (torch glue) against numpy to fp32 rounding, and the
+    next token within 2t of the oracle head's maximum on the GPU's final hidden vector. Returns it."""
+    row, _ = o.decode_rows(head.codes, head.codebooks, head.cb_is_bf16, np.array([tok], np.int32), False)
+    h = row.astype(np.float64) * np.sqrt(head.D)
+    for i, (gate, up, down) in enumerate(layers):
+        x = host(loop.ins[i])
+        assert np.allclose(x, _rms(h), rtol=0, atol=1e-5 * np.abs(_rms(h)).max()), f"block {i}: pre-norm"
+        _, _, _, oy = o.mlp(*((m.codes, m.codebooks, False) for m in (gate, up, down)), x)
+        y = host(loop.outs[i])
+        check_logits(y, oy)
+        h = h + _rms(y)
+    last = host(loop.last)
+    assert np.allclose(last, _rms(h), rtol=0, atol=1e-4 * np.abs(_rms(h)).max()), "final norm"
+    _, ref = o.logits(head.codes, head.codebooks, head.cb_is_bf16, last, softcap)
+    assert np.isfinite(ref).all()
+    return ref
+
+
 def test_decode_loop_teacher_forced():
     cfg = synth.CONFIGS["tiny"]
     head, _, _ = synth.make_head(cfg)
@@ -30,21 +56,15 @@ def test_decode_loop_teacher_forced():
         down = synth.gen_matrix(rng, hid, inter, inter // d, K, 2, (0.02, 0.005), "f32")
         layers.append((gate, up, down))
     Wh = to_dev(head)
-    loop = DecodeLoop(Wh, [tuple(to_dev(m) for m in lay) for lay in layers], softcap=cfg.softcap, max_tokens=8)
+    loop = DecodeLoop(Wh, [tuple(to_dev(m) for m in lay) for lay in layers], softcap=cfg.softcap, max_tokens=8,
+                      keep_layers=True)
     loop.ids[0] = 7
     o = O()
-    scale = np.float32(np.sqrt(cfg.D))
     tokens = [7]
     for t in range(8):
-        x_gpu = host(loop.step(t))
+        loop.step(t)
         nxt = int(loop.ids[t + 1].item())
-        # oracle, teacher-forced on the GPU's token t
-        row, _ = o.decode_rows(head.codes, head.codebooks, head.cb_is_bf16, np.array([tokens[-1]], np.int32), False)
-        y = row.astype(np.float32) * scale              # the loop's fp32 scaling of the fp32 row
-        for gate, up, down in layers:
-            _, _, _, y = o.mlp(*((m.codes, m.codebooks, False) for m in (gate, up, down)), y)
-        check_logits(x_gpu, y)
-        _, ref = o.logits(head.codes, head.codebooks, head.cb_is_bf16, x_gpu, cfg.softcap)
+        ref = check_loop_step(o, head, layers, loop, tokens[-1], cfg.softcap)
         tol = 1e-5 * np.abs(ref).max()
         assert ref[0, nxt] >= ref[0].max() - 2 * tol, f"step {t}: token {nxt} is not a maximum of the oracle"
         tokens.append(nxt)
