@@ -223,6 +223,25 @@ rq_status rq_lut_logits(const rq_matrix* W, const void* lut, int32_t lut_dtype, 
                         hipStream_t stream);
 
 /*
+ * rq_lut_logits for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, kernels and results as rq_lut_logits, without the
+ * workspace: the call uses a scratch array of RQ_STATIC_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on (allocated with the code object, kept
+ * until the process ends) and calls no allocator.
+ *   - A call that needs more scratch than that (rq_lut_logits_workspace is
+ *     the measure; the B=1 Gemma head with top-50 needs about 4.2 MB) returns
+ *     RQ_ERR_WORKSPACE and enqueues nothing.
+ *   - The scratch is per GPU (the calling thread's current device, which must
+ *     own `stream`) and shared by every call on it: calls that overlap in time
+ *     on one GPU race, whatever their streams. Nothing in it must start at zero.
+ */
+#define RQ_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+rq_status rq_lut_logits_static(const rq_matrix* W, const void* lut, int32_t lut_dtype, int32_t B,
+                               float softcap, float* logits, int32_t* argmax, int32_t topk,
+                               int32_t* topk_ids, float* topk_vals, hipStream_t stream);
+
+/*
  * One-call head: the same logits, argmax and top-k as rq_build_lut followed by
  * rq_lut_logits with an fp32 table, computed from the hidden vectors directly
  * (runtime-compression page, LUT-serving paragraph; the sum is regrouped by

@@ -24,7 +24,7 @@ RQ_METHOD_TABLE, RQ_METHOD_MATRIX_CORES = 0, 1
 # Every symbol include/rq_lut.h declares.
 EXPORTS = ("rq_blocked_codes_bytes", "rq_pack_codes", "rq_packed10_codes_bytes", "rq_pack_codes10",
            "rq_packed8_codes_bytes", "rq_pack_codes8", "rq_lut_bytes", "rq_build_lut", "rq_lut_logits_workspace",
-           "rq_lut_logits", "rq_logits_method", "rq_logits_workspace", "rq_logits", "rq_decode_rows", "rq_lut_matvec_workspace", "rq_lut_matvec",
+           "rq_lut_logits", "rq_lut_logits_static", "rq_logits_method", "rq_logits_workspace", "rq_logits", "rq_decode_rows", "rq_lut_matvec_workspace", "rq_lut_matvec",
            "rq_lut_mlp_workspace", "rq_lut_mlp", "rq_dense_logits_workspace", "rq_dense_logits", "rq_stream_read_configs",
            "rq_stream_read_sink_words", "rq_stream_read", "rq_set_stage_events", "rq_lut_logits_plan", "rq_status_string",
            "rq_last_error", "rq_version")
@@ -65,6 +65,7 @@ def lib():
             "rq_build_lut": (_i32, [_MP, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
             "rq_lut_logits_workspace": (_sz, [_MP, _i32, _i32, _i32]),
             "rq_lut_logits": (_i32, [_MP, _vp, _i32, _i32, _f32, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
+            "rq_lut_logits_static": (_i32, [_MP, _vp, _i32, _i32, _f32, _vp, _vp, _i32, _vp, _vp, _vp]),
             "rq_logits_method": (_i32, [_MP, _i32]),
             "rq_logits_workspace": (_sz, [_MP, _i32, _i32]),
             "rq_logits": (_i32, [_MP, _vp, _i32, _f32, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
@@ -279,6 +280,19 @@ def lut_logits(W, lut, B, softcap=30.0, lut_dtype=None, logits=True, argmax=True
     _gpu(lut=lut, out=lg, argmax_out=am, ws=ws)
     check(lib().rq_lut_logits(W.ref, _ptr(lut), _dtype_code(lut_dtype), B, softcap, _ptr(lg), _ptr(am), topk,
                               _ptr(ti), _ptr(tv), _ptr(ws), ws.numel(), _stream()))
+    return lg, am, ti, tv
+
+
+def lut_logits_static(W, lut, B, softcap=30.0, lut_dtype=None, logits=True, argmax=True, topk=0, out=None,
+                      argmax_out=None):
+    """rq_lut_logits_static: rq_lut_logits on the library's own per-GPU scratch (no workspace, no allocation
+    inside the call; the outputs are allocated here unless given)."""
+    lut_dtype = _lut_dtype_of(lut, lut_dtype)
+    _arg(lut, "lut", lut.dtype, numel=lut_bytes(W, B, lut_dtype) // lut.element_size())
+    lg, am, ti, tv = _outputs(W, B, topk, lut.device, logits, argmax, out, argmax_out)
+    _gpu(lut=lut, out=lg, argmax_out=am)
+    check(lib().rq_lut_logits_static(W.ref, _ptr(lut), _dtype_code(lut_dtype), B, softcap, _ptr(lg), _ptr(am), topk,
+                                     _ptr(ti), _ptr(tv), _stream()))
     return lg, am, ti, tv
 
 

@@ -8,8 +8,15 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "rq_internal.h"
+
+// The scratch of rq_lut_logits_static: one copy per GPU the library runs on,
+// held until the process ends. Host code uses the device address that
+// hipGetSymbolAddress gives for the current device (static_scratch below),
+// never this name, which on the host is only a stand-in for the symbol.
+__device__ __align__(256) unsigned char scratch[RQ_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -589,6 +596,58 @@ rq_status rq_lut_logits_plan(const rq_matrix* W, int32_t B, int32_t lut_dtype, i
   const int32_t v[10] = {p.BT, p.P, p.chunks, p.cpg, p.G, p.steps, p.rps, p.S, p.rset, p.NBT};
   for (int i = 0; i < 10; ++i) plan[i] = v[i];
   return RQ_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Device address of this GPU's copy of `scratch`, resolved once per device
+// with that device current (the calling thread's current device).
+rq_status static_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(RQ_ERR_HIP, "rq_lut_logits_static: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(RQ_ERR_HIP, "rq_lut_logits_static: device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(RQ_ERR_HIP, "rq_lut_logits_static: hipGetSymbolAddress: %s", hipGetErrorString(e));
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
+  return RQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rq_status rq_lut_logits_static(const rq_matrix* W, const void* lut, int32_t lut_dtype, int32_t B, float softcap,
+                               float* logits, int32_t* argmax, int32_t topk, int32_t* topk_ids, float* topk_vals,
+                               hipStream_t stream) {
+  rq_status s = check_lut_call(W, B, lut_dtype);
+  if (s != RQ_OK) return s;
+  if (topk < 0 || topk > 1024 || (W->rows > 0 && topk > W->rows))
+    return fail(RQ_ERR_SHAPE, "topk=%d outside [0, min(rows, 1024)]", topk);
+  if (B == 0 || W->rows == 0) return RQ_OK;
+  const rq::GatherPlan plan = rq::plan_gather(W, B, lut_dtype == RQ_BF16);
+  if (plan.BT == 0) return fail(RQ_ERR_SHAPE, "no table tiling fits on chip for K=%d", W->K);
+  const size_t need = logits_ws(W, plan, B, topk, logits != nullptr, lut_dtype == RQ_BF16).total;
+  if (need > (size_t)RQ_STATIC_SCRATCH_BYTES)
+    return fail(RQ_ERR_WORKSPACE, "rq_lut_logits_static: this call needs %zu bytes of scratch, more than the %zu the "
+                "library holds (use rq_lut_logits with a workspace)", need, (size_t)RQ_STATIC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  s = static_scratch(&ws);
+  if (s != RQ_OK) return s;
+  return rq_lut_logits(W, lut, lut_dtype, B, softcap, logits, argmax, topk, topk_ids, topk_vals, ws,
+                       (size_t)RQ_STATIC_SCRATCH_BYTES, stream);
 }
 
 int32_t rq_stream_read_configs(void) { return rq::stream_read_configs(); }
