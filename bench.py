@@ -109,6 +109,11 @@ def main():
     t_build = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     t_logits = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
     t_logits_med = float(np.median([e[2].elapsed_time(e[3]) for e in ev]))
+    # spread of single steps in the instrumented pass (each step bracketed by events: a few
+    # microseconds slower than the headline mean, which has none)
+    step_inst = np.array([e[0].elapsed_time(e[3]) for e in ev])
+    spread = {"p10": float(np.percentile(step_inst, 10)), "p50": float(np.percentile(step_inst, 50)),
+              "p90": float(np.percentile(step_inst, 90)), "steps": len(step_inst)}
 
     code_bytes = formats.code_bytes(V, L, M)       # 1536 B per vocab row
     lut_b = formats.lut_bytes(1, L, M, K)
@@ -140,6 +145,7 @@ def main():
                      "stream_ceiling": ceiling},
         "calls_ms": {"decode_rows_64": t_dec, "build_lut": t_build, "lut_logits": t_logits,
                      "lut_logits_median": t_logits_med, "lut_logits_gather_kernel": t_gather},
+        "step_ms_instrumented": spread,
         "resident_bytes": {"lut_head": Ws[0].resident_bytes() + lut_b + ws.numel(),
                            "dense_bf16_head": formats.dense_bytes(V, D)},
     }
@@ -153,7 +159,7 @@ def main():
         out["copy_calibration_bytes"] = src.numel()
 
     if not args.no_extras:
-        out.update(extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, dev))
+        out.update(extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, dev, ms_step))
     del Ws, lut, ws
     torch.cuda.empty_cache()
 
@@ -218,7 +224,7 @@ def timed(fn, n, torch):
     return a.elapsed_time(b) / n
 
 
-def extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, dev):
+def extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, dev, ms_step_b1):
     res = {}
     V = cfg.V
     # the same B=1 step on the 10-bit code stream (1024 bytes per row instead of 1536)
@@ -289,13 +295,19 @@ def extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, dev):
     E = la.decode_rows(Ws[0], torch.arange(V, dtype=torch.int32, device=dev), "bf16")
     E2 = E.clone()
     Es = [E, E2]
-    lgd = torch.empty((16, V), dtype=torch.float32, device=dev)
-    wsd = la.workspace(la.dense_logits_workspace(V, 16), dev)
-    td1 = timed(lambda i=0: la.dense_logits(Es[i & 1], ht, 30.0, ws=wsd, out=lgd[:1]), 50, torch)
-    td16 = timed(lambda i=0: la.dense_logits(Es[i & 1], h16, 30.0, ws=wsd, out=lgd), 20, torch)
-    res["dense_bf16"] = {"ms_b1": td1, "ms_b16": td16, "gbs_b1": formats.dense_bytes(V, cfg.D) / (td1 * 1e-3) / 1e9,
-                         "resident_bytes": formats.dense_bytes(V, cfg.D)}
-    del E, E2, Es, lgd, wsd
+    lgd = torch.empty((128, V), dtype=torch.float32, device=dev)
+    wsd = la.workspace(la.dense_logits_workspace(V, 128), dev)
+    h128 = torch.from_numpy(synth.gen_hidden(np.random.default_rng(c16.seed), 128, cfg.D)).to(dev)
+    dense = {"resident_bytes": formats.dense_bytes(V, cfg.D)}
+    for B, hB, n in ((1, ht, 50), (16, h16, 20), (128, h128, 10)):
+        tdB = timed(lambda i=0: la.dense_logits(Es[i & 1], hB, 30.0, ws=wsd, out=lgd[:B]), n, torch)
+        gbs = formats.dense_bytes(V, cfg.D) / (tdB * 1e-3) / 1e9
+        dense[f"b{B}"] = {"ms": tdB, "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+                          "mfma_tflops": 2.0 * B * V * cfg.D / (tdB * 1e-3) / 1e12}
+        lut_ms = res[f"b{B}"]["ms_per_call"] if B > 1 else ms_step_b1
+        dense[f"b{B}"]["lut_over_dense_time"] = lut_ms / tdB
+    res["dense_bf16"] = dense
+    del E, E2, Es, lgd, wsd, h128
 
     # one Gemma-2-2B MLP layer: the fused block (rq_lut_mlp), and the three rq_lut_matvec calls
     # (gate, up, down with the gelu_tanh*up prologue) it replaces

@@ -331,12 +331,14 @@ rq_status rq_lut_mlp(const rq_matrix* gate, const rq_matrix* up, const rq_matrix
  * Comparison baseline: the standard dense path with the head stored as a
  * dense bf16 matrix E[rows][D] (row-major), as deployed before LUT serving
  * (runtime-compression page, variant table "Uncompressed" row):
- *     logits[b][r] = softcap(sum_i E[r][i] * h[b][i]) in fp32, plus argmax.
- *   E       device bf16 bit patterns [rows][D], 16-byte aligned, D % 8 == 0
- *   h       device fp32 [B][D], 1 <= B <= 16
+ *     logits[b][r] = softcap(sum_i E[r][i] * bf16(h[b][i])) in fp32, plus argmax
+ * (a GEMV at B=1, a GEMM on the matrix cores for larger batches).
+ *   E       device bf16 bit patterns [rows][D], 16-byte aligned, D % 8 == 0,
+ *           8 <= D <= 4096
+ *   h       device fp32 [B][D], 0 <= B <= 128
  *   logits  device fp32 [B][rows] (required); argmax device int32 [B] or NULL
  *   ws      device workspace of at least rq_dense_logits_workspace() bytes
- *           (only used when argmax != NULL)
+ *           (the bf16 copy of h and the per-block selection keys)
  */
 size_t rq_dense_logits_workspace(int64_t rows, int32_t B);
 rq_status rq_dense_logits(const uint16_t* E, int64_t rows, int32_t D, const float* h, int32_t B,

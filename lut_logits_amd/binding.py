@@ -405,8 +405,7 @@ def dense_logits(E, h, softcap=30.0, argmax=True, ws=None, out=None):
     lg = out if out is not None else torch.empty((B, rows), dtype=torch.float32, device=h.device)
     _arg(lg, "out", torch.float32, numel=B * rows)
     am = torch.empty(B, dtype=torch.int32, device=h.device) if argmax else None
-    if argmax:
-        ws = _ws(ws, dense_logits_workspace(rows, B), h.device)
+    ws = _ws(ws, dense_logits_workspace(rows, B), h.device)
     _gpu(E=E, h=h, out=lg, ws=ws)
     check(lib().rq_dense_logits(_ptr(E), rows, D, _ptr(h), B, softcap, _ptr(lg), _ptr(am), _ptr(ws),
                                 ws.numel() if ws is not None else 0, _stream()))

@@ -558,28 +558,29 @@ rq_status rq_lut_mlp(const rq_matrix* gate, const rq_matrix* up, const rq_matrix
   return s;
 }
 
+// Workspace of rq_dense_logits: the bf16 copy of h (padded to 16-vector tiles),
+// then the per-block selection keys [B][dense_blocks].
 size_t rq_dense_logits_workspace(int64_t rows, int32_t B) {
-  if (rows <= 0 || B < 1 || B > 16) return 0;
-  return round_up((size_t)B * rq::dense_blocks(rows) * sizeof(uint64_t), 256);
+  if (rows <= 0 || B < 1 || B > 128) return 0;
+  return round_up(rq::dense_hb_bytes(4096, B), 256) + round_up((size_t)B * rq::dense_blocks(rows) * sizeof(uint64_t), 256);
 }
 
 rq_status rq_dense_logits(const uint16_t* E, int64_t rows, int32_t D, const float* h, int32_t B, float softcap,
                           float* logits, int32_t* argmax, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (rows < 0 || rows >= ((int64_t)1 << 31)) return fail(RQ_ERR_SHAPE, "rows out of range");
   if (D < 8 || D % 8 != 0 || D > 4096) return fail(RQ_ERR_SHAPE, "dense head needs D %% 8 == 0 and 8 <= D <= 4096");
-  if (B < 0 || B > 16) return fail(RQ_ERR_SHAPE, "dense head supports 0 <= B <= 16");
+  if (B < 0 || B > 128) return fail(RQ_ERR_SHAPE, "dense head supports 0 <= B <= 128");
   if (rows == 0 || B == 0) return RQ_OK;
   if (!E || !h || !logits) return fail(RQ_ERR_NULL, "dense_logits: NULL buffer");
   if (!aligned(E, 16) || !aligned(h, 4) || !aligned(logits, 4) || (argmax && !aligned(argmax, 4)))
     return fail(RQ_ERR_ALIGN, "dense_logits: misaligned buffer");
-  uint64_t* keys = nullptr;
-  if (argmax) {
-    const size_t need = rq_dense_logits_workspace(rows, B);
-    if (!ws || ws_bytes < need) return fail(RQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
-    if (!aligned(ws, 256)) return fail(RQ_ERR_ALIGN, "workspace must be 256-byte aligned");
-    keys = static_cast<uint64_t*>(ws);
-  }
-  hipError_t e = rq::launch_dense_logits(E, rows, D, h, B, softcap, logits, keys, stream);
+  const size_t need = rq_dense_logits_workspace(rows, B);
+  if (!ws || ws_bytes < need) return fail(RQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (!aligned(ws, 256)) return fail(RQ_ERR_ALIGN, "workspace must be 256-byte aligned");
+  uint16_t* hb = static_cast<uint16_t*>(ws);
+  uint64_t* keys = argmax ? reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + round_up(rq::dense_hb_bytes(4096, B), 256))
+                          : nullptr;
+  hipError_t e = rq::launch_dense_logits(E, rows, D, h, B, softcap, logits, keys, hb, stream);
   if (e != hipSuccess || !argmax) return launched(e, "rq_dense_logits");
   return launched(rq::launch_select(keys, rq::dense_blocks(rows), B, argmax, logits, rows, 0, nullptr, nullptr,
                                     nullptr, stream),

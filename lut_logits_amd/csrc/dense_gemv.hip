@@ -3,15 +3,27 @@
 // The pages' standard path keeps the head as a full bf16 matrix and computes
 // logits with one matmul (Gemma-2-2B runtime-compression page, variant
 // table, "Uncompressed" row). This kernel is that path on the same GPU, so the
-// LUT head can be timed against it: E[rows][D] bf16 times up to 16 hidden
+// LUT head can be timed against it: E[rows][D] bf16 times up to 128 hidden
 // vectors rounded to bf16, accumulated in fp32 on the matrix cores
 // (v_mfma_f32_16x16x32_bf16), then the same softcap and argmax selection as
-// the LUT head (best key per block, reduced by the selection kernel).
+// the LUT head (best key per block of rows, reduced by the selection kernel).
 //
-// A wave owns 16 rows at a time: each lane loads 16 bytes (8 bf16) of one row
-// per k-step, so a wave-wide load is 16 rows x 64 contiguous bytes, and the
-// hidden vectors (as bf16, padded to 16 columns) sit in LDS. Bound: HBM
-// (2*D bytes per row); the matrix cores idle most of the time.
+// Mapping: C[b][r] = sum_k h[b][k] * E[r][k], with A = 16 hidden vectors x 32
+// k (from LDS) and B = 32 k x 16 rows of E (from HBM). Lane (i16, kg) loads 16
+// bytes (8 bf16) of row i16 of its tile per k-step, so a wave-wide load is 16
+// rows x 64 contiguous bytes, and receives C[4kg .. 4kg+3][row i16]: a store of
+// one batch entry covers 16 consecutive rows (64 contiguous bytes). The hidden
+// vectors are rounded to bf16 once, by a small kernel, into the workspace.
+//
+// Work split: a workgroup owns 256 rows (4 waves x 4 tiles of 16) and all
+// hidden vectors (NT tiles of 16). The hidden vectors are staged in LDS as
+// bf16 in chunks of KC columns (all of D when it fits); each wave keeps the E
+// loads of the next k-steps in flight while the matrix cores work on the
+// current ones. Bound: HBM (2*D bytes per row) for every B up to 128; the
+// matrix cores need 2*B*D flops per row (151 GFLOP at B=128 on the Gemma
+// head, about 60 us at the bf16 peak). Two waves per SIMD are asked for (the
+// accumulators of eight column tiles then stay in the 256 registers beside the
+// load buffers) so that two workgroups share a CU.
 #include "rq_internal.h"
 
 namespace rq {
@@ -19,84 +31,184 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kDenseThreads = 256;
-constexpr int kTilesPerWave = kDenseRowsPerBlock / 16 / (kDenseThreads / 64);
-constexpr int kKUnroll = 8;
+constexpr int kDenseWaves = kDenseThreads / 64;
+constexpr int kTilesPerWave = kDenseRowsPerBlock / 16 / kDenseWaves;   // 4
+static_assert(kTilesPerWave * 16 * kDenseWaves == kDenseRowsPerBlock, "rows per block");
 
-__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
-  const uint4 v = *reinterpret_cast<const uint4*>(p);
-  return __builtin_bit_cast(bf16x8, v);
+// k-steps (of 32 columns) whose E loads are issued together, per column-tile count.
+constexpr int unroll_for(int NT) { return NT <= 2 ? 4 : 2; }
+// Columns of h staged per chunk: the whole row for 16 vectors, else a chunk of
+// at most 64 KB of bf16 (so two workgroups share a CU).
+inline int chunk_cols(int D, int NT) {
+  const int kc = NT == 1 ? D : 2048 / NT;
+  return std::min(D, kc);
 }
 
-__global__ __launch_bounds__(kDenseThreads) void dense_logits_kernel(const uint16_t* __restrict__ E, int64_t rows,
-                                                                     int D, const float* __restrict__ h, int B,
-                                                                     float softcap, float* __restrict__ logits,
-                                                                     uint64_t* __restrict__ block_keys) {
-  extern __shared__ __align__(16) uint16_t hs[];   // [16][Dp] bf16
-  __shared__ unsigned long long bmax[16];
-  const int Dp = D + 8;
-  for (int i = threadIdx.x; i < 16 * D; i += kDenseThreads) {
-    const int b = i / D;
-    const int c = i - b * D;
-    hs[b * Dp + c] = b < B ? f32_to_bf16(h[(size_t)b * D + c]) : (uint16_t)0;
-  }
-  if (threadIdx.x < 16) bmax[threadIdx.x] = 0ull;
-  __syncthreads();
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int i16 = lane & 15;   // A: row within the tile; B and C: batch column
-  const int kg = lane >> 4;    // which 8 of the 32 k-values this lane feeds
+// hb[n][c] = bf16(h[n][c]) (round to nearest even), zero for n >= B: Bp x D.
+__global__ void dense_h_kernel(const float* __restrict__ h, int B, int D, int Bp, uint16_t* __restrict__ hb) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)Bp * D) return;
+  const int n = (int)(i / D);
+  hb[i] = n < B ? f32_to_bf16(h[i]) : (uint16_t)0;
+}
+
+template <int NT>
+__global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void dense_logits_kernel(const uint16_t* __restrict__ E, int64_t rows, int D, const uint16_t* __restrict__ hb,
+                         int B, int KC, float softcap, float* __restrict__ logits, uint64_t* __restrict__ block_keys) {
+  constexpr int T = kTilesPerWave;
+  constexpr int U = unroll_for(NT);
+  constexpr int Bp = 16 * NT;
+  extern __shared__ __align__(16) uint16_t hs[];   // [Bp][KC + 8] bf16
+  __shared__ unsigned long long bmax[Bp];
+  const int ldh = KC + 8;   // row stride of 2*(KC+8) bytes: lanes of one k-group hit different banks
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int i16 = lane & 15;   // A: batch row within a tile; B and C: row of E within a tile
+  const int kg = lane >> 4;    // which 8 of the 32 k-values this lane feeds; C rows 4kg .. 4kg+3
+  if (tid < Bp) bmax[tid] = 0ull;
+
+  int64_t rbase[T];
+  const uint16_t* erow[T];
+  bool rvalid[T];
+#pragma unroll
+  for (int j = 0; j < T; ++j) {
+    rbase[j] = (int64_t)blockIdx.x * kDenseRowsPerBlock + (int64_t)(wave * T + j) * 16;
+    const int64_t r = rbase[j] + i16;
+    rvalid[j] = r < rows;
+    erow[j] = E + (rvalid[j] ? r : 0) * (int64_t)D;
+  }
+  floatx4 acc[T][NT];
+#pragma unroll
+  for (int j = 0; j < T; ++j)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[j][t] = floatx4{0.f, 0.f, 0.f, 0.f};
   const bf16x8 zero = {};
-  for (int tile = 0; tile < kTilesPerWave; ++tile) {
-    const int64_t row_base = (int64_t)blockIdx.x * kDenseRowsPerBlock + (int64_t)(wave * kTilesPerWave + tile) * 16;
-    const int64_t row = row_base + i16;
-    const bool rvalid = row < rows;
-    const uint16_t* erow = E + (rvalid ? row : 0) * (int64_t)D;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < D; k0 += 32 * kKUnroll) {
-      bf16x8 a[kKUnroll];
+
+  for (int k0 = 0; k0 < D; k0 += KC) {
+    const int kc = min(KC, D - k0);
+    // Groups of U k-steps, two register buffers used ping-pong: the E loads of
+    // the next group are in flight while the matrix cores work on this one.
+    // Loads are unconditional (columns past the chunk re-read its last 8 and
+    // are zeroed by a select, rows past the end read row 0 and are never
+    // stored), so no branch makes the compiler wait on the loads in flight.
+    auto load = [&](bf16x8 (&a)[U][T], int s) {
 #pragma unroll
-      for (int u = 0; u < kKUnroll; ++u) {
-        const int col = k0 + u * 32 + 8 * kg;
-        a[u] = (rvalid && col < D) ? load_bf16x8(erow + col) : zero;
-      }
+      for (int u = 0; u < U; ++u) {
+        const int col = s + 32 * u + 8 * kg;
+        const int cc = min(col, kc - 8);
 #pragma unroll
-      for (int u = 0; u < kKUnroll; ++u) {
-        const int col = k0 + u * 32 + 8 * kg;
-        const bf16x8 bv = col < D ? *reinterpret_cast<const bf16x8*>(hs + i16 * Dp + col) : zero;
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], bv, acc, 0, 0, 0);
+        for (int j = 0; j < T; ++j) {
+          const bf16x8 v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(erow[j] + k0 + cc));
+          a[u][j] = col < kc ? v : zero;
+        }
       }
+    };
+    auto compute = [&](const bf16x8 (&a)[U][T], int s) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int col = min(s + 32 * u + 8 * kg, kc - 8);   // past the chunk: any in-bounds h, times zeros of E
+        bf16x8 hv[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) hv[t] = *reinterpret_cast<const bf16x8*>(hs + (16 * t + i16) * ldh + col);
+#pragma unroll
+        for (int j = 0; j < T; ++j)
+#pragma unroll
+          for (int t = 0; t < NT; ++t) acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hv[t], a[u][j], acc[j][t], 0, 0, 0);
+      }
+    };
+    bf16x8 b0[U][T], b1[U][T];
+    load(b0, 0);   // in flight during the staging of this chunk of h
+    // stage hb[:, k0 .. k0+kc) (bf16, zero rows past B) with 16-byte copies
+    __syncthreads();
+    const int n8 = kc >> 3;
+    for (int i = tid; i < Bp * n8; i += kDenseThreads) {
+      const int b = i / n8;
+      const int c = (i - b * n8) * 8;
+      *reinterpret_cast<u32x4*>(hs + b * ldh + c) = *reinterpret_cast<const u32x4*>(hb + (size_t)b * D + k0 + c);
     }
-    // acc[t] = C[row_base + 4*kg + t][batch i16]
+    __syncthreads();
+    for (int s0 = 0; s0 < kc; s0 += 64 * U) {
+      load(b1, s0 + 32 * U);
+      compute(b0, s0);
+      load(b0, s0 + 64 * U);
+      if (s0 + 32 * U < kc) compute(b1, s0 + 32 * U);   // (uniform)
+    }
+  }
+
+  // acc[j][t][e] = C[batch 16t + 4kg + e][row rbase[j] + i16]: softcap, store, and the
+  // best key of each batch entry over this wave's rows (max over tiles in registers,
+  // then over the 16 lanes of a k-group), one LDS atomic per batch entry and wave.
+  const int64_t r_of = i16;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int64_t r = row_base + 4 * kg + t;
-      if (r < rows && i16 < B) {
-        const float z = acc[t];
-        const float v = softcap > 0.0f ? softcap * tanhf(z / softcap) : z;
-        logits[(size_t)i16 * rows + r] = v;
-        if (block_keys) atomicMax(&bmax[i16], (unsigned long long)select_key(v, (uint32_t)r));
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int b = 16 * t + 4 * kg + e;
+      uint64_t kb = 0ull;
+      if (b < B) {
+#pragma unroll
+        for (int j = 0; j < T; ++j) {
+          const int64_t r = rbase[j] + r_of;
+          if (r >= rows) continue;
+          const float z = acc[j][t][e];
+          const float v = softcap > 0.0f ? softcap * tanhf(z / softcap) : z;
+          logits[(size_t)b * rows + r] = v;
+          kb = max_u64(kb, select_key(v, (uint32_t)r));
+        }
+      }
+      if (block_keys) {   // (uniform: a kernel argument)
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) {   // within the 16 lanes of this k-group
+          const uint32_t lo = __shfl_xor((unsigned)(uint32_t)kb, m, 64);
+          const uint32_t hi = __shfl_xor((unsigned)(uint32_t)(kb >> 32), m, 64);
+          kb = max_u64(kb, ((uint64_t)hi << 32) | lo);
+        }
+        if (i16 == 0 && b < B) atomicMax(&bmax[b], (unsigned long long)kb);
       }
     }
   }
   if (!block_keys) return;
   __syncthreads();
-  if (threadIdx.x < B) block_keys[(size_t)threadIdx.x * gridDim.x + blockIdx.x] = bmax[threadIdx.x];
+  if (tid < B) block_keys[(size_t)tid * gridDim.x + blockIdx.x] = bmax[tid];
+}
+
+template <int NT>
+hipError_t launch_nt(const uint16_t* E, int64_t rows, int D, const float* h, int B, float softcap, float* logits,
+                     uint64_t* block_keys, uint16_t* hb, hipStream_t stream) {
+  const int Bp = 16 * NT;
+  const int64_t n = (int64_t)Bp * D;
+  hipLaunchKernelGGL(dense_h_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, h, B, D, Bp, hb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int KC = chunk_cols(D, NT);
+  const size_t lds = (size_t)16 * NT * (KC + 8) * sizeof(uint16_t);
+  auto kern = dense_logits_kernel<NT>;
+  e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)dense_blocks(rows)), dim3(kDenseThreads), lds, stream, E, rows, D,
+                     (const uint16_t*)hb, B, KC, softcap, logits, block_keys);
+  return hipGetLastError();
 }
 
 }  // namespace
 
+// Column tiles of 16 vectors the kernel runs for B vectors.
+static int dense_nt(int B) { return B <= 16 ? 1 : (B <= 32 ? 2 : (B <= 64 ? 4 : 8)); }
+size_t dense_hb_bytes(int D, int B) { return (size_t)16 * dense_nt(B) * D * sizeof(uint16_t); }
+
 hipError_t launch_dense_logits(const uint16_t* E, int64_t rows, int D, const float* h, int B, float softcap,
-                               float* logits, uint64_t* block_keys, hipStream_t stream) {
-  const size_t lds = (size_t)16 * (D + 8) * sizeof(uint16_t);
-  hipError_t e = hipFuncSetAttribute((const void*)dense_logits_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(dense_logits_kernel, dim3((unsigned)dense_blocks(rows)), dim3(kDenseThreads), lds, stream, E,
-                     rows, D, h, B, softcap, logits, block_keys);
-  return hipGetLastError();
+                               float* logits, uint64_t* block_keys, uint16_t* hb, hipStream_t stream) {
+  if (B <= 16) return launch_nt<1>(E, rows, D, h, B, softcap, logits, block_keys, hb, stream);
+  if (B <= 32) return launch_nt<2>(E, rows, D, h, B, softcap, logits, block_keys, hb, stream);
+  if (B <= 64) return launch_nt<4>(E, rows, D, h, B, softcap, logits, block_keys, hb, stream);
+  return launch_nt<8>(E, rows, D, h, B, softcap, logits, block_keys, hb, stream);
 }
 
 }  // namespace rq

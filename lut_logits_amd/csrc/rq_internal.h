@@ -204,8 +204,11 @@ hipError_t launch_decode_rows(const rq_matrix* W, const int32_t* ids, int n, int
 hipError_t launch_pack_codes(const uint16_t* src, int64_t rows, int NP, uint16_t* dst, hipStream_t stream);
 hipError_t launch_pack_codes10(const uint16_t* src, int64_t rows, int NP, uint16_t* dst, hipStream_t stream);
 hipError_t launch_pack_codes8(const uint16_t* src, int64_t rows, int NP, uint16_t* dst, hipStream_t stream);
+// Dense comparator: hb is a bf16 copy of h padded to whole 16-vector tiles
+// (dense_hb_bytes), written first by the same call.
+size_t dense_hb_bytes(int D, int B);
 hipError_t launch_dense_logits(const uint16_t* E, int64_t rows, int D, const float* h, int B, float softcap,
-                               float* logits, uint64_t* block_keys, hipStream_t stream);
+                               float* logits, uint64_t* block_keys, uint16_t* hb, hipStream_t stream);
 
 constexpr int kEpiRowsPerBlock = 1024;   // rows per epilogue workgroup
 inline int epi_blocks(int64_t rows) { return (int)((rows + kEpiRowsPerBlock - 1) / kEpiRowsPerBlock); }

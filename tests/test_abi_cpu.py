@@ -108,7 +108,7 @@ def test_workspace_queries():
     assert 0 < lib.rq_lut_matvec_workspace(ctypes.byref(Wm), 1) < 2 * 1152 * 1024 * 4
     assert lib.rq_lut_matvec_workspace(ctypes.byref(Wm), 2) >= 2 * 1152 * 1024 * 4 * 2
     assert lib.rq_dense_logits_workspace(256000, 1) > 0
-    assert lib.rq_dense_logits_workspace(256000, 17) == 0
+    assert lib.rq_dense_logits_workspace(256000, 129) == 0
 
 
 def test_other_entry_points_reject():
@@ -133,7 +133,7 @@ def test_other_entry_points_reject():
     assert lib.rq_pack_codes10(0x1000, 10, 2, 3, 0x1008, None) == B.RQ_ERR_ALIGN
     assert lib.rq_pack_codes10(None, 0, 2, 3, None, None) == B.RQ_OK
     assert lib.rq_dense_logits(0x1000, 100, 2300, 0x2000, 1, 30.0, 0x3000, None, None, 0, None) == B.RQ_ERR_SHAPE
-    assert lib.rq_dense_logits(0x1000, 100, 2304, 0x2000, 17, 30.0, 0x3000, None, None, 0, None) == B.RQ_ERR_SHAPE
+    assert lib.rq_dense_logits(0x1000, 100, 2304, 0x2000, 129, 30.0, 0x3000, None, None, 0, None) == B.RQ_ERR_SHAPE
     assert lib.rq_dense_logits(0x1000, 100, 2304, 0x2000, 1, 30.0, 0x3000, 0x4000, None, 0, None) == B.RQ_ERR_WORKSPACE
 
 

@@ -423,15 +423,19 @@ def test_mlp_layer_gemma_shapes():
 
 # ------------------------------------------------------------------ dense comparison head
 
-def test_dense_comparator():
-    """The dense bf16 head against an fp64 numpy product of the same bf16 values."""
-    mat, rng = _rand(110, 5000, 96, 16, 256, 2, "bf16")
-    h = synth.gen_hidden(rng, 3, 96)
+@pytest.mark.parametrize("B,D", [(1, 96), (3, 96), (16, 96), (17, 96), (40, 200), (128, 96), (128, 600)])
+def test_dense_comparator(B, D):
+    """The dense bf16 head (GEMV at B=1, matrix-core GEMM up to B=128, with h staged in chunks of columns for
+    B > 16) against an fp64 numpy product of the same bf16 values, over 5000 rows (a ragged last block of
+    256): every logit, the softcap, and the argmax as the first maximum of the GPU's own logits."""
+    M = D // 6 if D % 6 == 0 else D // 8
+    mat, rng = _rand(110 + B, 5000, D, M, 256, 2, "bf16")
+    h = synth.gen_hidden(rng, B, D)
     W = to_dev(mat)
     E = la.decode_rows(W, torch.arange(5000, dtype=torch.int32, device="cuda"), "bf16")
-    lg, am = la.dense_logits(E, dev(h), softcap=0.0)
+    lg, am = la.dense_logits(E, dev(h), softcap=30.0)
     Ef = synth.bf16_bits_to_f32(host(E).view(np.uint16)).astype(np.float64)
     hb = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(h)).astype(np.float64)
-    ref = hb @ Ef.T
+    ref = 30.0 * np.tanh((hb @ Ef.T) / 30.0)
     check_logits(host(lg), ref)
     assert np.array_equal(host(am), np.argmax(host(lg), axis=1).astype(np.int32))
