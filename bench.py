@@ -210,6 +210,24 @@ def stream_ceiling(la, torch, bufs, reps=10):
     return best
 
 
+def lds_roof(la, torch, reps=500, runs=5):
+    """The LDS random-gather roof: rq_lds_gather (random entries of 128 KB of LDS, every CU) for entry widths of
+    2, 4, 8 and 16 bytes, each launch timed by its own dispatch; mean TB/s (decimal) per width."""
+    out = {}
+    for width in (2, 4, 8, 16):
+        sink = la.lds_gather(width, 1)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(runs)]
+        for i in range(runs):
+            la.set_stage_events(*ev[i])
+            la.lds_gather(width, reps, sink)
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in ev) / runs
+        lookups = la.lib().rq_lds_gather_sink_words() * 1024 * 8 * reps
+        out[f"w{width}"] = {"tbs": lookups * width / (ms * 1e-3) / 1e12, "lookups_per_clk_per_cu": lookups / (ms * 1e-3) / 2.4e9 / 256,
+                            "bytes_per_clk_per_cu": lookups * width / (ms * 1e-3) / 2.4e9 / 256}
+    return out
+
+
 def timed(fn, n, torch):
     """Mean milliseconds of fn() over n calls (HIP events on the current stream) after 3 warm-up calls."""
     for _ in range(3):
@@ -227,6 +245,8 @@ def timed(fn, n, torch):
 def extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, dev, ms_step_b1):
     res = {}
     V = cfg.V
+    roof = lds_roof(la, torch)
+    res["lds_roof"] = roof
     # the same B=1 step on the 10-bit code stream (1024 bytes per row instead of 1536)
     P10 = [la.to_device(mat, layout="packed10"), la.to_device(mat, layout="packed10")]
     lut10 = la.build_lut(P10[0], ht)
@@ -270,7 +290,10 @@ def extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, dev, ms_step_b1):
         # 16x16x32 bf16 MFMA per level and per bf16 part of h (3): dense-equivalent flops at 2.5 PFLOP/s
         n_mfma = (V // 16) * ((B + 15) // 16) * (cfg.L * cfg.M // 4) * 3
         mfma_tflops = n_mfma * 16 * 16 * 32 * 2 / (tB * 1e-3) / 1e12
+        # LDS work of the matrix-core method: one 16-byte codeword read per (row, pair, 16-vector tile)
+        lds_b = V * cfg.L * cfg.M * 16 * ((B + 63) // 64 if B > 32 else 1)
         res[f"b{B}"] = {"ms_per_call": tB, "vocab_rows_per_s": V / (tB * 1e-3), "token_rows_per_s": B * V / (tB * 1e-3),
+                        "lds_bytes": lds_b, "lds_frac": lds_b / (tB * 1e-3) / (roof["w16"]["tbs"] * 1e12),
                         "method": "matrix_cores" if mm else "table",
                         "code_stream_gbs": formats.code_bytes(V, cfg.L, cfg.M) / (tB * 1e-3) / 1e9,
                         "mfma_tflops": mfma_tflops if mm else None,
@@ -288,7 +311,10 @@ def extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, dev, ms_step_b1):
         la.lut_logits(W, lut16, 16, softcap=30.0, out=lg16, ws=ws16)
 
     t16 = timed(head16, 10, torch)
-    res["b16_table"] = {"ms_per_call": t16, "vocab_rows_per_s": V / (t16 * 1e-3)}
+    # LDS work of the table method at 16 vectors: 4 lanes x 16 bytes per (row, pair)
+    lds16 = V * cfg.L * cfg.M * 64
+    res["b16_table"] = {"ms_per_call": t16, "vocab_rows_per_s": V / (t16 * 1e-3), "lds_bytes": lds16,
+                        "lds_frac": lds16 / (t16 * 1e-3) / (roof["w16"]["tbs"] * 1e12)}
     del lut16, lg16, ws16, hb
 
     # dense bf16 head on the same GPU: E = bf16(decode(all rows)), built by rq_decode_rows
@@ -390,7 +416,10 @@ def extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, dev, ms_step_b1):
         la.lut_logits(SW, slut, cs.B, softcap=cs.softcap, lut_dtype="bf16", topk=cs.topk, out=slg, ws=sws)
 
     ts = timed(stress, 3, torch)
-    res["stress"] = {"ms_per_call": ts, "vocab_rows_per_s": cs.V / (ts * 1e-3),
+    # LDS work of the bf16 table in batch tiles of 4: one 8-byte read per (row, pair, tile)
+    lds_s = cs.V * cs.L * cs.M * ((cs.B + 3) // 4) * 8
+    res["stress"] = {"ms_per_call": ts, "vocab_rows_per_s": cs.V / (ts * 1e-3), "lds_bytes": lds_s,
+                     "lds_frac": lds_s / (ts * 1e-3) / (roof["w8"]["tbs"] * 1e12),
                      "code_stream_gbs": formats.code_bytes(cs.V, cs.L, cs.M) / (ts * 1e-3) / 1e9,
                      "method": "table (bf16), several batch tiles staged from a batch-tiled copy"}
     del SW, slut, slg, sws

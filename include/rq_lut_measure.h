@@ -2,7 +2,8 @@
  * rq_lut_measure.h -- measurement aids exported by librq_lut.so. None of them is
  * part of the method or of the serving calls in rq_lut.h: they exist so that a
  * benchmark can time one kernel by its own dispatch, measure the HBM
- * stream-read ceiling of this GPU, and report which tiling a call will use.
+ * stream-read ceiling and the LDS random-gather roof of this GPU, and report
+ * which tiling a call will use.
  *
  * rq_set_stage_events keeps a one-shot, thread-local hook (the only state the
  * library holds between calls); the other functions are stateless.
@@ -38,7 +39,7 @@ rq_status rq_stream_read(const void* src, size_t bytes, int32_t config, uint32_t
 /*
  * Measurement hook. The next lookup+sum kernel that rq_lut_logits or
  * rq_lut_matvec launches from the calling thread (or the next
- * rq_stream_read kernel) is launched with
+ * rq_stream_read or rq_lds_gather kernel) is launched with
  * hipExtLaunchKernelGGL(..., before, after, ...): the events take the start
  * and end of that kernel's own dispatch on its stream, so that
  * hipEventElapsedTime(before, after) is that one kernel's duration (the
@@ -49,6 +50,21 @@ rq_status rq_stream_read(const void* src, size_t bytes, int32_t config, uint32_t
  * been created (hipEventCreate) without hipEventDisableTiming.
  */
 rq_status rq_set_stage_events(hipEvent_t before, hipEvent_t after);
+
+/*
+ * Measurement aid: the LDS random-gather roof. One workgroup of 1024 threads
+ * per CU (256) fills 128 KB of LDS with 32-bit word i = i * 2654435761 (mod
+ * 2^32), then each thread runs 8 independent sequences x <- x * 1664525 +
+ * 1013904223 (mod 2^32), seeded x = 8 * (1024 * workgroup + thread) + chain,
+ * and for each of `reps` steps of every sequence reads the `width`-byte entry
+ * (2, 4, 8 or 16) whose index is the top log2(128 KB / width) bits of the new
+ * x, XOR-folding its 32-bit words (a 2-byte entry: its 16 bits) into one
+ * accumulator. sink[w] (rq_lds_gather_sink_words() words) is the XOR of the
+ * accumulators of workgroup w's threads. 256 * 1024 * 8 * reps lookups in all.
+ * Bad width or reps < 0: RQ_ERR_SHAPE; NULL sink: RQ_ERR_NULL.
+ */
+size_t rq_lds_gather_sink_words(void);
+rq_status rq_lds_gather(int32_t width, int32_t reps, uint32_t* sink, hipStream_t stream);
 
 /*
  * The tiling rq_lut_logits uses for this matrix, batch and table dtype (a pure

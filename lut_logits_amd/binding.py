@@ -26,7 +26,8 @@ EXPORTS = ("rq_blocked_codes_bytes", "rq_pack_codes", "rq_packed10_codes_bytes",
            "rq_packed8_codes_bytes", "rq_pack_codes8", "rq_lut_bytes", "rq_build_lut", "rq_lut_logits_workspace",
            "rq_lut_logits", "rq_lut_logits_static", "rq_logits_method", "rq_logits_workspace", "rq_logits", "rq_decode_rows", "rq_lut_matvec_workspace", "rq_lut_matvec",
            "rq_lut_mlp_workspace", "rq_lut_mlp", "rq_dense_logits_workspace", "rq_dense_logits", "rq_stream_read_configs",
-           "rq_stream_read_sink_words", "rq_stream_read", "rq_set_stage_events", "rq_lut_logits_plan", "rq_status_string",
+           "rq_stream_read_sink_words", "rq_stream_read", "rq_lds_gather_sink_words", "rq_lds_gather",
+           "rq_set_stage_events", "rq_lut_logits_plan", "rq_status_string",
            "rq_last_error", "rq_version")
 
 
@@ -79,6 +80,8 @@ def lib():
             "rq_stream_read_configs": (_i32, []),
             "rq_stream_read_sink_words": (_sz, [_i32]),
             "rq_stream_read": (_i32, [_vp, _sz, _i32, _vp, _vp]),
+            "rq_lds_gather_sink_words": (_sz, []),
+            "rq_lds_gather": (_i32, [_i32, _i32, _vp, _vp]),
             "rq_set_stage_events": (_i32, [_vp, _vp]),
             "rq_lut_logits_plan": (_i32, [_MP, _i32, _i32, ctypes.POINTER(_i32)]),
             "rq_status_string": (ctypes.c_char_p, [_i32]),
@@ -387,6 +390,17 @@ def stream_read(buf, config, sink=None):
     _arg(sink, "sink", torch.int32, min_numel=words)
     _gpu(sink=sink)
     check(lib().rq_stream_read(_ptr(buf), buf.numel() * buf.element_size(), config, _ptr(sink), _stream()))
+    return sink
+
+
+def lds_gather(width, reps, sink=None):
+    """rq_lds_gather: the LDS random-gather probe; returns its sink (one word per workgroup) as int32."""
+    words = lib().rq_lds_gather_sink_words()
+    if sink is None:
+        sink = torch.empty(words, dtype=torch.int32, device="cuda")
+    _arg(sink, "sink", torch.int32, min_numel=words)
+    _gpu(sink=sink)
+    check(lib().rq_lds_gather(width, reps, _ptr(sink), _stream()))
     return sink
 
 

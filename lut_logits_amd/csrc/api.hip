@@ -651,6 +651,16 @@ rq_status rq_lut_logits_static(const rq_matrix* W, const void* lut, int32_t lut_
                        (size_t)RQ_STATIC_SCRATCH_BYTES, stream);
 }
 
+size_t rq_lds_gather_sink_words(void) { return rq::lds_gather_sink_words(); }
+
+rq_status rq_lds_gather(int32_t width, int32_t reps, uint32_t* sink, hipStream_t stream) {
+  if (width != 2 && width != 4 && width != 8 && width != 16) return fail(RQ_ERR_SHAPE, "lds_gather: width %d", width);
+  if (reps < 0) return fail(RQ_ERR_SHAPE, "lds_gather: reps %d < 0", reps);
+  if (!sink) return fail(RQ_ERR_NULL, "lds_gather: sink is NULL");
+  if (!aligned(sink, 4)) return fail(RQ_ERR_ALIGN, "lds_gather: sink misaligned");
+  return launched(rq::launch_lds_gather(width, reps, sink, stream), "rq_lds_gather");
+}
+
 int32_t rq_stream_read_configs(void) { return rq::stream_read_configs(); }
 
 size_t rq_stream_read_sink_words(int32_t config) {

@@ -198,6 +198,10 @@ hipError_t launch_mm_logits(const rq_matrix* W, const MmPlan& p, const float* h,
 int stream_read_configs();
 size_t stream_read_sink_words(int config);
 hipError_t launch_stream_read(const void* src, size_t bytes, int config, uint32_t* sink, hipStream_t stream);
+// Measurement aid: random gathers of width-byte entries from 128 KB of LDS
+// (lds_gather_sink_words() words of sink).
+size_t lds_gather_sink_words();
+hipError_t launch_lds_gather(int width, int reps, uint32_t* sink, hipStream_t stream);
 
 hipError_t launch_decode_rows(const rq_matrix* W, const int32_t* ids, int n, int out_bf16, void* out,
                               int32_t* bad_ids, hipStream_t stream);
