@@ -402,13 +402,31 @@ def extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, dev, ms_step_b1):
     del v2, dv2, wsv2, y2
     torch.cuda.empty_cache()
 
-    # stress head: K=4096, L=4, B=64, bf16 table, softcap 30, top-50 (one call pair: build + logits)
+    # stress head: K=4096, L=4, B=64, softcap 30, top-50. rq_logits (one call: the matrix cores, one pair per
+    # staged slot, fp32-level accuracy), and the two-call bf16-table form (build + logits) beside it
     cs = synth.CONFIGS["stress"]
     smat, sh, _ = synth.make_head(cs)
     SW = la.to_device(smat)
     shd = torch.from_numpy(sh).to(dev)
-    slut = la.build_lut(SW, shd, lut_dtype="bf16")
     slg = torch.empty((cs.B, cs.V), dtype=torch.float32, device=dev)
+    sam = torch.empty(cs.B, dtype=torch.int32, device=dev)
+    sws1 = la.workspace(la.logits_workspace(SW, cs.B, cs.topk), dev)
+
+    def stress1(i=0):
+        la.logits(SW, shd, softcap=cs.softcap, topk=cs.topk, out=slg, argmax_out=sam, ws=sws1)
+
+    ts1 = timed(stress1, 5, torch)
+    mm1 = la.logits_method(SW, cs.B) == la.RQ_METHOD_MATRIX_CORES
+    # one 16x16x32 MFMA per 16 rows x 16 vectors x pair (h's three bf16 parts in its k-slots)
+    n_mfma_s = (cs.V // 16) * ((cs.B + 15) // 16) * (cs.L * cs.M)
+    tflops_s = n_mfma_s * 16 * 16 * 32 * 2 / (ts1 * 1e-3) / 1e12
+    res["stress"] = {"ms_per_call": ts1, "vocab_rows_per_s": cs.V / (ts1 * 1e-3),
+                     "method": "matrix_cores" if mm1 else "table",
+                     "mfma_tflops": tflops_s if mm1 else None,
+                     "mfma_frac_of_bf16_peak": tflops_s / 2500.0 if mm1 else None,
+                     "code_stream_gbs": formats.code_bytes(cs.V, cs.L, cs.M) / (ts1 * 1e-3) / 1e9}
+    del sws1
+    slut = la.build_lut(SW, shd, lut_dtype="bf16")
     sws = la.workspace(la.lut_logits_workspace(SW, cs.B, cs.topk, "bf16"), dev)
 
     def stress(i=0):
@@ -418,11 +436,10 @@ def extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, dev, ms_step_b1):
     ts = timed(stress, 3, torch)
     # LDS work of the bf16 table in batch tiles of 4: one 8-byte read per (row, pair, tile)
     lds_s = cs.V * cs.L * cs.M * ((cs.B + 3) // 4) * 8
-    res["stress"] = {"ms_per_call": ts, "vocab_rows_per_s": cs.V / (ts * 1e-3), "lds_bytes": lds_s,
-                     "lds_frac": lds_s / (ts * 1e-3) / (roof["w8"]["tbs"] * 1e12),
-                     "code_stream_gbs": formats.code_bytes(cs.V, cs.L, cs.M) / (ts * 1e-3) / 1e9,
-                     "method": "table (bf16), several batch tiles staged from a batch-tiled copy"}
-    del SW, slut, slg, sws
+    res["stress_table"] = {"ms_per_call": ts, "vocab_rows_per_s": cs.V / (ts * 1e-3), "lds_bytes": lds_s,
+                           "lds_frac": lds_s / (ts * 1e-3) / (roof["w8"]["tbs"] * 1e12),
+                           "method": "bf16 table: build + lookup+sum in batch tiles from a batch-tiled copy"}
+    del SW, slut, slg, sws, sam
     torch.cuda.empty_cache()
 
     # per-token composite: the token's embedding row, 26 distinct MLP layers chained (rq_lut_mlp) and the

@@ -52,6 +52,12 @@ constexpr int kMmThreads = 512;   // one workgroup per CU (LDS); 512: 2 waves pe
 constexpr int kMmWaves = kMmThreads / 64;
 constexpr int kParts = 3;           // bf16 parts of each hidden value
 constexpr int kMaxCwPerThread = 4 * kMmMaxK / kMmThreads;   // codewords of a half-block per thread
+// One pair per ring slot (K above kMmMaxK, 16-bit blocked codes): a slot holds
+// the K codewords of one (level, subspace) pair (64 KB at K = 4096) and the
+// MFMA's four k-slots carry that pair's codeword against h's three bf16 parts
+// and a zero: one MFMA per 16 rows x 16 vectors x pair, the three-part split
+// folded into the contraction.
+constexpr int kMmMaxKOnePair = 4 * kMmMaxK;
 
 struct MmArgs {
   const uint16_t* cb;     // bf16 codebooks [NP][K][d]
@@ -94,24 +100,30 @@ __global__ void split_h_kernel(const float* __restrict__ h, int B, int D, int M,
   }
 }
 
-template <int DS, int NT>
+template <int DS, int NT, bool ONEPAIR = false>
 struct Staged {
-  static constexpr int kH = (kParts * 4 * 16 * NT + kMmThreads - 1) / kMmThreads;   // h vectors per thread
+  // h vectors per thread: three parts x four slots, or (one pair) four slots
+  static constexpr int kH = ((ONEPAIR ? 4 : kParts * 4) * 16 * NT + kMmThreads - 1) / kMmThreads;
   uint32_t cw[kMaxCwPerThread][DS / 2];
   u32x4 hv[kH];
 };
 
 // NSUB sub-blocks per code block: 2 for 16-bit codes (pairs 2kg, 2kg+1 in
 // dword kg), 3 for RQ_CODES_PACKED10 (pairs 3kg .. 3kg+2, 10 bits each).
-template <int DS, int NT, int T, int NSUB>
+// ONEPAIR (16-bit codes only): a code block's 8 pairs are 8 sub-blocks of one
+// pair each (see kMmMaxKOnePair).
+template <int DS, int NT, int T, int NSUB, bool ONEPAIR = false>
 __global__ __launch_bounds__(kMmThreads) void mm_logits_kernel(MmArgs a) {
+  static_assert(!ONEPAIR || NSUB == 2, "one pair per slot: 16-bit codes");
   constexpr int PPB = 4 * NSUB;                 // pairs per code block
+  constexpr int SB = ONEPAIR ? PPB : NSUB;      // sub-blocks (ring slots) per code block
+  constexpr int SP = ONEPAIR ? 1 : 4;           // pairs per slot
   constexpr int CBITS = NSUB == 2 ? 16 : 10;    // bits per code
   constexpr uint32_t CMASK = (1u << CBITS) - 1u;
-  extern __shared__ __align__(16) u32x4 ring[];   // [2][4*K + kParts*4*16*NT]
+  extern __shared__ __align__(16) u32x4 ring[];   // [2][SP*K + h entries]
   const int K = a.K;
-  const int cw_entries = 4 * K;
-  const int h_entries = kParts * 4 * 16 * NT;
+  const int cw_entries = SP * K;
+  const int h_entries = (ONEPAIR ? 4 : kParts * 4) * 16 * NT;
   const int slot_entries = cw_entries + h_entries;
 
   // workgroup -> (batch tile, group, slab). Workgroups are dealt to the 8 XCDs
@@ -183,46 +195,50 @@ __global__ __launch_bounds__(kMmThreads) void mm_logits_kernel(MmArgs a) {
   // guarded, so some entries are written twice with the same value and no
   // branch (whose join would make the compiler wait for every load in flight)
   // is needed.
-  auto stage_load = [&](Staged<DS, NT>& st, int q, int hs) {
+  // Pair held by slot position kk (0 .. SP-1) of sub-block hs of block q.
+  auto slot_pair = [&](int q, int kk, int hs) { return ONEPAIR ? PPB * q + hs : PPB * q + NSUB * kk + hs; };
+  auto stage_load = [&](Staged<DS, NT, ONEPAIR>& st, int q, int hs) {
 #pragma unroll
     for (int u = 0; u < kMaxCwPerThread; ++u) {
       const int c = (tid + u * kMmThreads) % cw_entries;
       const int kk = c / K;
       const int k = c - kk * K;
-      const int p = min(PPB * q + NSUB * kk + hs, a.NP - 1);
+      const int p = min(slot_pair(q, kk, hs), a.NP - 1);
       const uint32_t* src = reinterpret_cast<const uint32_t*>(a.cb + ((size_t)p * K + k) * DS);
 #pragma unroll
       for (int w = 0; w < DS / 2; ++w) st.cw[u][w] = src[w];
     }
 #pragma unroll
-    for (int u = 0; u < Staged<DS, NT>::kH; ++u) {
+    for (int u = 0; u < Staged<DS, NT, ONEPAIR>::kH; ++u) {
       const int e = (tid + u * kMmThreads) % h_entries;
-      const int pr = e / (4 * n_bt);
-      const int rem = e - pr * 4 * n_bt;
-      const int kk = rem / n_bt;
-      const int n = rem - kk * n_bt;
-      const int p = min(PPB * q + NSUB * kk + hs, a.NP - 1);
+      // ONEPAIR: entry (slot kg, vector n) is part kg of the pair's slice of h (kg < 3), the
+      // fourth slot is zero; else entry (part, slot kk, vector n)
+      const int pr = ONEPAIR ? min(e / n_bt, kParts - 1) : e / (4 * n_bt);
+      const int rem = ONEPAIR ? e % n_bt : e - pr * 4 * n_bt;
+      const int kk = ONEPAIR ? 0 : rem / n_bt;
+      const int n = ONEPAIR ? rem : rem - kk * n_bt;
+      const int p = min(slot_pair(q, kk, hs), a.NP - 1);
       const int m = p % a.M;
       st.hv[u] = a.hp[((size_t)pr * a.M + m) * a.Bp + (size_t)bt * n_bt + n];
     }
   };
-  auto stage_store = [&](const Staged<DS, NT>& st, int slot, int q, int hs) {
+  auto stage_store = [&](const Staged<DS, NT, ONEPAIR>& st, int slot, int q, int hs) {
     u32x4* base = ring + slot * slot_entries;
 #pragma unroll
     for (int u = 0; u < kMaxCwPerThread; ++u) {
       const int c = (tid + u * kMmThreads) % cw_entries;
-      const bool live = PPB * q + NSUB * (c / K) + hs < a.NP;
+      const bool live = slot_pair(q, c / K, hs) < a.NP;
       u32x4 v = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int w = 0; w < DS / 2; ++w) v[w] = live ? st.cw[u][w] : 0u;
       base[c] = v;
     }
 #pragma unroll
-    for (int u = 0; u < Staged<DS, NT>::kH; ++u) {
+    for (int u = 0; u < Staged<DS, NT, ONEPAIR>::kH; ++u) {
       const int e = (tid + u * kMmThreads) % h_entries;
       const int pr = e / (4 * n_bt);
-      const int kk = (e - pr * 4 * n_bt) / n_bt;
-      const bool live = PPB * q + NSUB * kk + hs < a.NP;
+      const int kk = ONEPAIR ? 0 : (e - pr * 4 * n_bt) / n_bt;
+      const bool live = slot_pair(q, kk, hs) < a.NP && (!ONEPAIR || e < kParts * n_bt);
       const u32x4 z = {0u, 0u, 0u, 0u};
       base[cw_entries + e] = live ? st.hv[u] : z;
     }
@@ -236,6 +252,25 @@ __global__ __launch_bounds__(kMmThreads) void mm_logits_kernel(MmArgs a) {
 
   auto compute = [&](int slot, const uint32_t (&codes)[T], int hs) {
     const u32x4* base = ring + slot * slot_entries;
+    if constexpr (ONEPAIR) {
+      // B: slot kg of vector 16t + i16 is part kg of h (zero for kg = 3); A: every
+      // k-slot holds the row's codeword of this pair, read by all four lanes of a
+      // row (one address). The pair's code is in dword hs/2 of the row's block,
+      // which the arranged codes give to the lanes of row-of-lanes hs/2.
+      bf16x8 hb1[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) hb1[t] = __builtin_bit_cast(bf16x8, base[cw_entries + kg * n_bt + 16 * t + i16]);
+      const int src_lane = i16 + 16 * (hs >> 1);
+      const int shift = 16 * (hs & 1);
+#pragma unroll
+      for (int j = 0; j < T; ++j) {
+        const uint32_t dw = (uint32_t)__shfl((int)codes[j], src_lane, 64);
+        const bf16x8 av1 = __builtin_bit_cast(bf16x8, base[(dw >> shift) & 0xffffu]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av1, hb1[t], acc[j][t], 0, 0, 0);
+      }
+      return;
+    }
     bf16x8 hb[kParts][NT];
 #pragma unroll
     for (int pr = 0; pr < kParts; ++pr)
@@ -275,7 +310,7 @@ __global__ __launch_bounds__(kMmThreads) void mm_logits_kernel(MmArgs a) {
 
   if (q0 < q1) {
     uint32_t ca[T], cbk[T];
-    Staged<DS, NT> st;
+    Staged<DS, NT, ONEPAIR> st;
     load_codes(ca, q0);
     stage_load(st, q0, 0);
     int slot = 0;
@@ -285,10 +320,10 @@ __global__ __launch_bounds__(kMmThreads) void mm_logits_kernel(MmArgs a) {
     auto do_block = [&](int q, uint32_t (&cur)[T], uint32_t (&nxt)[T]) {
       arrange_codes(cur);
 #pragma unroll
-      for (int hs = 0; hs < NSUB; ++hs) {
+      for (int hs = 0; hs < SB; ++hs) {
         stage_store(st, slot, q, hs);
         __syncthreads();
-        if (hs + 1 < NSUB) stage_load(st, q, hs + 1);
+        if (hs + 1 < SB) stage_load(st, q, hs + 1);
         else stage_load(st, min(q + 1, q1 - 1), 0);
         if (hs == 0) {
           __builtin_amdgcn_sched_barrier(0);   // keep the staging loads ahead of the code loads (vmcnt is in order)
@@ -366,50 +401,56 @@ __global__ __launch_bounds__(kMmThreads) void mm_logits_kernel(MmArgs a) {
 // code registers (2*T) and the staged half-block share a wave's 256 VGPRs.
 // (Three sub-blocks per code block keep more values live: fewer tiles.) A
 // multiple of 4 takes the wide code loads; 4 at NT = 4 uses 254 VGPRs.
-constexpr int tiles_for(int NT, int NSUB = 2) {
-  return kMmThreads == 512 ? (NSUB == 2 ? (NT == 1 ? 16 : NT == 2 ? 8 : 4) : (NT == 1 ? 12 : NT == 2 ? 6 : 3))
-                           : (NT == 1 ? 8 : NT == 2 ? 4 : 2);
+// One pair per slot keeps a third of the h registers, so four column tiles take
+// 8 row tiles (1,024 rows per staged slot and workgroup); codewords of 6 values
+// take 6 and of 8 values 4 (their staging needs more registers; 8 spilled).
+constexpr int tiles_for(int NT, int NSUB = 2, bool ONEPAIR = false, int DS = 2) {
+  return ONEPAIR ? (NT == 1 ? 16 : (NT == 4 && DS >= 6 ? (DS == 8 ? 4 : 6) : 8))
+                 : (NSUB == 2 ? (NT == 1 ? 16 : NT == 2 ? 8 : 4) : (NT == 1 ? 12 : NT == 2 ? 6 : 3));
 }
 
-template <int DS, int NT, int NSUB>
+template <int DS, int NT, int NSUB, bool ONEPAIR = false>
 hipError_t launch_typed(const MmArgs& a, int wgs, size_t lds, hipStream_t stream) {
-  auto kern = mm_logits_kernel<DS, NT, tiles_for(NT, NSUB), NSUB>;
+  auto kern = mm_logits_kernel<DS, NT, tiles_for(NT, NSUB, ONEPAIR, DS), NSUB, ONEPAIR>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(kMmThreads), lds, stream, a);
   return hipGetLastError();
 }
 
-template <int DS, int NSUB>
+template <int DS, int NSUB, bool ONEPAIR = false>
 hipError_t launch_ds(const MmArgs& a, const MmPlan& p, hipStream_t stream) {
   const int wgs = p.G * p.S * p.NBT;
-  if (p.NT == 1) return launch_typed<DS, 1, NSUB>(a, wgs, p.lds, stream);
-  if (p.NT == 2) return launch_typed<DS, 2, NSUB>(a, wgs, p.lds, stream);
-  return launch_typed<DS, 4, NSUB>(a, wgs, p.lds, stream);
+  if (p.NT == 1) return launch_typed<DS, 1, NSUB, ONEPAIR>(a, wgs, p.lds, stream);
+  if (p.NT == 2) return launch_typed<DS, 2, NSUB, ONEPAIR>(a, wgs, p.lds, stream);
+  return launch_typed<DS, 4, NSUB, ONEPAIR>(a, wgs, p.lds, stream);
 }
 
-template <int NSUB>
+template <int NSUB, bool ONEPAIR = false>
 hipError_t launch_nsub(const MmArgs& a, const MmPlan& p, int d, hipStream_t stream) {
   switch (d) {
-    case 2: return launch_ds<2, NSUB>(a, p, stream);
-    case 4: return launch_ds<4, NSUB>(a, p, stream);
-    case 6: return launch_ds<6, NSUB>(a, p, stream);
-    default: return launch_ds<8, NSUB>(a, p, stream);
+    case 2: return launch_ds<2, NSUB, ONEPAIR>(a, p, stream);
+    case 4: return launch_ds<4, NSUB, ONEPAIR>(a, p, stream);
+    case 6: return launch_ds<6, NSUB, ONEPAIR>(a, p, stream);
+    default: return launch_ds<8, NSUB, ONEPAIR>(a, p, stream);
   }
 }
 
 }  // namespace
 
+// One pair per ring slot for K beyond what four pairs per slot can stage.
+static bool mm_one_pair(const rq_matrix* W) { return W->K > kMmMaxK; }
+
 bool mm_supported(const rq_matrix* W) {
-  return W->cb_dtype == RQ_BF16 && (W->codes_layout == RQ_CODES_BLOCKED || W->codes_layout == RQ_CODES_PACKED10) &&
-         W->d <= 8 && (W->d % 2) == 0 &&
-         W->K <= kMmMaxK && ((uintptr_t)W->codebooks % 4) == 0;
+  if (W->cb_dtype != RQ_BF16 || W->d > 8 || (W->d % 2) != 0 || ((uintptr_t)W->codebooks % 4) != 0) return false;
+  if (W->K <= kMmMaxK) return W->codes_layout == RQ_CODES_BLOCKED || W->codes_layout == RQ_CODES_PACKED10;
+  return W->K <= kMmMaxKOnePair && W->codes_layout == RQ_CODES_BLOCKED;
 }
 
 MmPlan plan_mm(const rq_matrix* W, int B) {
   MmPlan p{};
   p.NT = B <= 16 ? 1 : (B <= 32 ? 2 : 4);
-  p.T = tiles_for(p.NT, W->codes_layout == RQ_CODES_PACKED10 ? 3 : 2);
+  p.T = tiles_for(p.NT, W->codes_layout == RQ_CODES_PACKED10 ? 3 : 2, mm_one_pair(W), W->d);
   p.NBT = (B + 16 * p.NT - 1) / (16 * p.NT);
   p.Bp = p.NBT * 16 * p.NT;
   const int64_t slab = (int64_t)kMmWaves * p.T * 16;
@@ -427,13 +468,16 @@ MmPlan plan_mm(const rq_matrix* W, int B) {
     const int gg = (p.NQ + qpg - 1) / qpg;
     const int64_t wgs = (int64_t)gg * p.S * p.NBT;
     const double rounds = (double)((wgs + kCUs - 1) / kCUs);
-    const double per_block = 3.9 * (double)(p.T * p.NT) / 16.0 * (double)pairs_per_block(W) / 8.0;
+    // one pair per slot: four times the slots per block, each a third of the MFMAs
+    const double per_block = 3.9 * (double)(p.T * p.NT) / 16.0 * (double)pairs_per_block(W) / 8.0 *
+                             (mm_one_pair(W) ? 4.0 / 3.0 : 1.0);
     const double cost = rounds * qpg * per_block + (gg > 1 ? 5.0 + (double)(gg + 1) * B * W->rows * 4.0 / 2.2e6 : 0.0);
     if (cost < best * 0.999) { best = cost; G = gg; }
   }
   p.qpg = (p.NQ + G - 1) / G;
   p.G = (p.NQ + p.qpg - 1) / p.qpg;
-  p.lds = (size_t)2 * (4 * (size_t)W->K + (size_t)kParts * 4 * 16 * p.NT) * 16;
+  p.lds = mm_one_pair(W) ? (size_t)2 * ((size_t)W->K + (size_t)4 * 16 * p.NT) * 16
+                         : (size_t)2 * (4 * (size_t)W->K + (size_t)kParts * 4 * 16 * p.NT) * 16;
   return p;
 }
 
@@ -467,7 +511,9 @@ hipError_t launch_mm_logits(const rq_matrix* W, const MmPlan& p, const float* h,
   hipEvent_t before, after;
   take_stage_events(&before, &after);
   if (before && (e = hipEventRecord(before, stream)) != hipSuccess) return e;
-  e = W->codes_layout == RQ_CODES_PACKED10 ? launch_nsub<3>(a, p, W->d, stream) : launch_nsub<2>(a, p, W->d, stream);
+  e = mm_one_pair(W)                            ? launch_nsub<2, true>(a, p, W->d, stream)
+      : W->codes_layout == RQ_CODES_PACKED10 ? launch_nsub<3>(a, p, W->d, stream)
+                                             : launch_nsub<2>(a, p, W->d, stream);
   if (e != hipSuccess) return e;
   if (after) e = hipEventRecord(after, stream);
   return e;

@@ -138,8 +138,9 @@ def test_other_entry_points_reject():
 
 
 def test_logits_method_and_checks():
-    """rq_logits routes B >= RQ_MM_MIN_B with bf16 codebooks, even d <= 8, K <= 1024 and blocked codes to the
-    matrix cores, everything else to the table path; its host checks run before any launch."""
+    """rq_logits routes B >= RQ_MM_MIN_B with bf16 codebooks and even d <= 8 to the matrix cores when the codes
+    are blocked (K <= 4096; above 1024 one pair per staged slot) or 10-bit (K <= 1024), everything else to the
+    table path; its host checks run before any launch."""
     lib = B.lib()
     W = gemma_desc()
     m = lambda w, b: lib.rq_logits_method(ctypes.byref(w), b)
@@ -148,7 +149,9 @@ def test_logits_method_and_checks():
     assert m(W, 8) == B.RQ_METHOD_MATRIX_CORES
     assert m(W, 128) == B.RQ_METHOD_MATRIX_CORES
     assert m(gemma_desc(cb_dtype=B.RQ_F32), 16) == B.RQ_METHOD_TABLE           # fp32 codebooks
-    assert m(gemma_desc(K=4096, L=4), 64) == B.RQ_METHOD_TABLE                 # K above the staged maximum
+    assert m(gemma_desc(K=4096, L=4), 64) == B.RQ_METHOD_MATRIX_CORES          # one pair per staged slot
+    assert m(gemma_desc(K=4097, L=4), 64) == B.RQ_METHOD_TABLE                 # K above the staged maximum
+    assert m(gemma_desc(K=2048, codes_layout=B.RQ_CODES_ROWS), 64) == B.RQ_METHOD_TABLE
     assert m(gemma_desc(codes_layout=B.RQ_CODES_ROWS), 16) == B.RQ_METHOD_TABLE
     assert m(gemma_desc(M=256, d=9), 16) == B.RQ_METHOD_TABLE                  # d > 8
     assert m(gemma_desc(M=768, d=3), 16) == B.RQ_METHOD_TABLE                  # odd d

@@ -80,6 +80,22 @@ def test_stress_head_full():
     check_topk(g, host(ti), host(tv), host(am), ref, tolv, cfg.topk)
 
 
+def test_stress_head_one_call_full():
+    """The stress head through rq_logits (matrix cores, one pair per staged slot at K=4096): every logit within
+    1e-5 of max|logit| of the oracle (fp32-level, stricter than the bf16-table bound) and the top-50 rules."""
+    cfg = synth.CONFIGS["stress"]
+    mat, h, _ = synth.make_head(cfg)
+    W = to_dev(mat)
+    assert la.logits_method(W, cfg.B) == la.RQ_METHOD_MATRIX_CORES
+    lg, am, ti, tv = la.logits(W, dev(h), softcap=cfg.softcap, topk=cfg.topk)
+    g = host(lg)
+    _, ref = oracle_head(mat, h, cfg.softcap)
+    worst = check_logits(g, ref)
+    tol = 1e-5 * np.abs(ref).max(axis=1, keepdims=True) * np.ones_like(ref)
+    check_topk(g, host(ti), host(tv), host(am), ref, tol, cfg.topk)
+    print(f"stress one call: worst |gpu-oracle|/max|oracle| = {worst:.2e}")
+
+
 def test_mlp_26_layers_full():
     """All 26 Gemma-2-2B MLP layers (independent codes and codebooks, the same x): g, u and y of every layer,
     and rq_lut_mlp's y against the three calls."""

@@ -44,6 +44,46 @@ def test_logits_matrix_cores_exact(shape, layout):
     assert np.array_equal(host(am), np.argmax(got, axis=1).astype(np.int32))
 
 
+MM_ONE_PAIR_EXACT = [
+    # rows, D, M, K, L, B: K above 1024, one (level, subspace) pair per staged slot
+    (3000, 96, 16, 2048, 2, 16),    # d=6, one column tile
+    (2500, 96, 16, 4096, 4, 64),    # the stress head's K and L, four column tiles
+    (1000, 96, 48, 1500, 2, 33),    # d=2, K not a power of two, 33 of 64 columns
+    (700, 64, 8, 3000, 1, 100),     # d=8, one code block, two batch tiles
+    (4097, 102, 17, 1025, 3, 8),    # odd M (last block partly empty), K just above 1024, ragged rows
+]
+
+
+@pytest.mark.parametrize("shape", MM_ONE_PAIR_EXACT, ids=lambda s: "x".join(map(str, s)))
+def test_logits_matrix_cores_one_pair_exact(shape):
+    """K above 1024 (blocked codes): one pair per staged slot, the three bf16 parts of h in the MFMA's k-slots.
+    Small-integer inputs make every product and sum exact, so z matches the oracle bit for bit."""
+    rows, D, M, K, L, B = shape
+    mat, h = synth.gen_exact(rows + 3 * K, rows, D, M, K, L, B, cb_dtype="bf16")
+    W = to_dev(mat)
+    assert la.logits_method(W, B) == la.RQ_METHOD_MATRIX_CORES
+    lg, am, _, _ = la.logits(W, dev(h), softcap=0.0)
+    z, _ = O().logits(mat.codes, mat.codebooks, True, h, 0.0)
+    got = host(lg)
+    assert np.array_equal(got.astype(np.float64), z)
+    assert np.array_equal(host(am), np.argmax(got, axis=1).astype(np.int32))
+
+
+def test_logits_one_pair_float_parity():
+    """Gaussian inputs at K=4096, L=4 (the stress head's codebooks, 4000 rows, B=64): within 1e-5 of max|logit|
+    of the oracle, softcap and top-10 included."""
+    cfg = synth.CONFIGS["stress"]
+    mat, h, _ = synth.make_head(cfg, V=4000)
+    W = to_dev(mat)
+    assert la.logits_method(W, cfg.B) == la.RQ_METHOD_MATRIX_CORES
+    lg, am, ti, tv = la.logits(W, dev(h), softcap=cfg.softcap, topk=10)
+    _, ref = oracle_head(mat, h, cfg.softcap)
+    g = host(lg)
+    check_logits(g, ref)
+    tol = 1e-5 * np.abs(ref).max(axis=1, keepdims=True) * np.ones_like(ref)
+    check_topk(g, host(ti), host(tv), host(am), ref, tol, 10)
+
+
 def test_logits_split_reaches_fp32():
     """One subspace of d=6, L=1: z is a 6-term dot product. Splitting h into three bf16 parts keeps it to
     fp32 rounding (|err| <= 2^-20 |z|-scale); two parts would leave ~2^-16 and fail this bound."""
