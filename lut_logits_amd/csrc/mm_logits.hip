@@ -52,12 +52,6 @@ constexpr int kMmThreads = 512;   // one workgroup per CU (LDS); 512: 2 waves pe
 constexpr int kMmWaves = kMmThreads / 64;
 constexpr int kParts = 3;           // bf16 parts of each hidden value
 constexpr int kMaxCwPerThread = 4 * kMmMaxK / kMmThreads;   // codewords of a half-block per thread
-// One pair per ring slot (K above kMmMaxK, 16-bit blocked codes): a slot holds
-// the K codewords of one (level, subspace) pair (64 KB at K = 4096) and the
-// MFMA's four k-slots carry that pair's codeword against h's three bf16 parts
-// and a zero: one MFMA per 16 rows x 16 vectors x pair, the three-part split
-// folded into the contraction.
-constexpr int kMmMaxKOnePair = 4 * kMmMaxK;
 
 struct MmArgs {
   const uint16_t* cb;     // bf16 codebooks [NP][K][d]
@@ -100,30 +94,82 @@ __global__ void split_h_kernel(const float* __restrict__ h, int B, int D, int M,
   }
 }
 
-template <int DS, int NT, bool ONEPAIR = false>
+template <int DS, int NT>
 struct Staged {
-  // h vectors per thread: three parts x four slots, or (one pair) four slots
-  static constexpr int kH = ((ONEPAIR ? 4 : kParts * 4) * 16 * NT + kMmThreads - 1) / kMmThreads;
+  static constexpr int kH = (kParts * 4 * 16 * NT + kMmThreads - 1) / kMmThreads;   // h vectors per thread
   uint32_t cw[kMaxCwPerThread][DS / 2];
   u32x4 hv[kH];
 };
 
+// Partial sums or finished logits of one workgroup: acc[j][t][e] is z for batch
+// bt*16NT + 16t + i16 and row tile0 + 16j + 4kg + e (lane = 16kg + i16).
+template <int NT, int T>
+__device__ __forceinline__ void mm_epilogue(const MmArgs& a, const floatx4 (&acc)[T][NT], int bt, int g, int s,
+                                            int64_t tile0, int tid) {
+  const int lane = tid & 63;
+  const int i16 = lane & 15;
+  const int kg = lane >> 4;
+  const int n_bt = 16 * NT;
+  if (a.G > 1) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int b = bt * n_bt + 16 * t + i16;
+      if (b >= a.B) continue;
+      float* dst = a.partial + ((size_t)g * a.B + b) * a.rows;
+#pragma unroll
+      for (int j = 0; j < T; ++j) {
+        const int64_t r = tile0 + 16 * j + 4 * kg;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (r + e < a.rows) dst[r + e] = acc[j][t][e];
+      }
+    }
+    return;
+  }
+  // G == 1: the sums are final -- softcap, store, best selection key of this
+  // slab for each hidden vector (the selection kernel reduces the S keys).
+  __shared__ unsigned long long s_keys[16 * NT];
+  if (tid < 16 * NT) s_keys[tid] = 0ull;
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int b = bt * n_bt + 16 * t + i16;
+    unsigned long long kbest = 0ull;
+    if (b < a.B) {
+#pragma unroll
+      for (int j = 0; j < T; ++j) {
+        const int64_t r = tile0 + 16 * j + 4 * kg;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (r + e >= a.rows) continue;
+          const float z = acc[j][t][e];
+          const float v = a.softcap > 0.0f ? a.softcap * tanhf(z / a.softcap) : z;
+          if (a.out) a.out[(size_t)b * a.rows + r + e] = v;
+          const unsigned long long k = select_key(v, (uint32_t)(r + e));
+          kbest = k > kbest ? k : kbest;
+        }
+      }
+    }
+    if (kbest) atomicMax(&s_keys[16 * t + i16], kbest);   // LDS atomics, this workgroup only
+  }
+  __syncthreads();
+  if (a.block_keys && tid < 16 * NT) {
+    const int b = bt * n_bt + tid;
+    if (b < a.B) a.block_keys[(size_t)b * a.S + s] = s_keys[tid];
+  }
+}
+
 // NSUB sub-blocks per code block: 2 for 16-bit codes (pairs 2kg, 2kg+1 in
 // dword kg), 3 for RQ_CODES_PACKED10 (pairs 3kg .. 3kg+2, 10 bits each).
-// ONEPAIR (16-bit codes only): a code block's 8 pairs are 8 sub-blocks of one
-// pair each (see kMmMaxKOnePair).
-template <int DS, int NT, int T, int NSUB, bool ONEPAIR = false>
+template <int DS, int NT, int T, int NSUB>
 __global__ __launch_bounds__(kMmThreads) void mm_logits_kernel(MmArgs a) {
-  static_assert(!ONEPAIR || NSUB == 2, "one pair per slot: 16-bit codes");
   constexpr int PPB = 4 * NSUB;                 // pairs per code block
-  constexpr int SB = ONEPAIR ? PPB : NSUB;      // sub-blocks (ring slots) per code block
-  constexpr int SP = ONEPAIR ? 1 : 4;           // pairs per slot
   constexpr int CBITS = NSUB == 2 ? 16 : 10;    // bits per code
   constexpr uint32_t CMASK = (1u << CBITS) - 1u;
-  extern __shared__ __align__(16) u32x4 ring[];   // [2][SP*K + h entries]
+  extern __shared__ __align__(16) u32x4 ring[];   // [2][4*K + kParts*4*16*NT]
   const int K = a.K;
-  const int cw_entries = SP * K;
-  const int h_entries = (ONEPAIR ? 4 : kParts * 4) * 16 * NT;
+  const int cw_entries = 4 * K;
+  const int h_entries = kParts * 4 * 16 * NT;
   const int slot_entries = cw_entries + h_entries;
 
   // workgroup -> (batch tile, group, slab). Workgroups are dealt to the 8 XCDs
@@ -195,50 +241,46 @@ __global__ __launch_bounds__(kMmThreads) void mm_logits_kernel(MmArgs a) {
   // guarded, so some entries are written twice with the same value and no
   // branch (whose join would make the compiler wait for every load in flight)
   // is needed.
-  // Pair held by slot position kk (0 .. SP-1) of sub-block hs of block q.
-  auto slot_pair = [&](int q, int kk, int hs) { return ONEPAIR ? PPB * q + hs : PPB * q + NSUB * kk + hs; };
-  auto stage_load = [&](Staged<DS, NT, ONEPAIR>& st, int q, int hs) {
+  auto stage_load = [&](Staged<DS, NT>& st, int q, int hs) {
 #pragma unroll
     for (int u = 0; u < kMaxCwPerThread; ++u) {
       const int c = (tid + u * kMmThreads) % cw_entries;
       const int kk = c / K;
       const int k = c - kk * K;
-      const int p = min(slot_pair(q, kk, hs), a.NP - 1);
+      const int p = min(PPB * q + NSUB * kk + hs, a.NP - 1);
       const uint32_t* src = reinterpret_cast<const uint32_t*>(a.cb + ((size_t)p * K + k) * DS);
 #pragma unroll
       for (int w = 0; w < DS / 2; ++w) st.cw[u][w] = src[w];
     }
 #pragma unroll
-    for (int u = 0; u < Staged<DS, NT, ONEPAIR>::kH; ++u) {
+    for (int u = 0; u < Staged<DS, NT>::kH; ++u) {
       const int e = (tid + u * kMmThreads) % h_entries;
-      // ONEPAIR: entry (slot kg, vector n) is part kg of the pair's slice of h (kg < 3), the
-      // fourth slot is zero; else entry (part, slot kk, vector n)
-      const int pr = ONEPAIR ? min(e / n_bt, kParts - 1) : e / (4 * n_bt);
-      const int rem = ONEPAIR ? e % n_bt : e - pr * 4 * n_bt;
-      const int kk = ONEPAIR ? 0 : rem / n_bt;
-      const int n = ONEPAIR ? rem : rem - kk * n_bt;
-      const int p = min(slot_pair(q, kk, hs), a.NP - 1);
+      const int pr = e / (4 * n_bt);
+      const int rem = e - pr * 4 * n_bt;
+      const int kk = rem / n_bt;
+      const int n = rem - kk * n_bt;
+      const int p = min(PPB * q + NSUB * kk + hs, a.NP - 1);
       const int m = p % a.M;
       st.hv[u] = a.hp[((size_t)pr * a.M + m) * a.Bp + (size_t)bt * n_bt + n];
     }
   };
-  auto stage_store = [&](const Staged<DS, NT, ONEPAIR>& st, int slot, int q, int hs) {
+  auto stage_store = [&](const Staged<DS, NT>& st, int slot, int q, int hs) {
     u32x4* base = ring + slot * slot_entries;
 #pragma unroll
     for (int u = 0; u < kMaxCwPerThread; ++u) {
       const int c = (tid + u * kMmThreads) % cw_entries;
-      const bool live = slot_pair(q, c / K, hs) < a.NP;
+      const bool live = PPB * q + NSUB * (c / K) + hs < a.NP;
       u32x4 v = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int w = 0; w < DS / 2; ++w) v[w] = live ? st.cw[u][w] : 0u;
       base[c] = v;
     }
 #pragma unroll
-    for (int u = 0; u < Staged<DS, NT, ONEPAIR>::kH; ++u) {
+    for (int u = 0; u < Staged<DS, NT>::kH; ++u) {
       const int e = (tid + u * kMmThreads) % h_entries;
       const int pr = e / (4 * n_bt);
-      const int kk = ONEPAIR ? 0 : (e - pr * 4 * n_bt) / n_bt;
-      const bool live = slot_pair(q, kk, hs) < a.NP && (!ONEPAIR || e < kParts * n_bt);
+      const int kk = (e - pr * 4 * n_bt) / n_bt;
+      const bool live = PPB * q + NSUB * kk + hs < a.NP;
       const u32x4 z = {0u, 0u, 0u, 0u};
       base[cw_entries + e] = live ? st.hv[u] : z;
     }
@@ -252,25 +294,6 @@ __global__ __launch_bounds__(kMmThreads) void mm_logits_kernel(MmArgs a) {
 
   auto compute = [&](int slot, const uint32_t (&codes)[T], int hs) {
     const u32x4* base = ring + slot * slot_entries;
-    if constexpr (ONEPAIR) {
-      // B: slot kg of vector 16t + i16 is part kg of h (zero for kg = 3); A: every
-      // k-slot holds the row's codeword of this pair, read by all four lanes of a
-      // row (one address). The pair's code is in dword hs/2 of the row's block,
-      // which the arranged codes give to the lanes of row-of-lanes hs/2.
-      bf16x8 hb1[NT];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) hb1[t] = __builtin_bit_cast(bf16x8, base[cw_entries + kg * n_bt + 16 * t + i16]);
-      const int src_lane = i16 + 16 * (hs >> 1);
-      const int shift = 16 * (hs & 1);
-#pragma unroll
-      for (int j = 0; j < T; ++j) {
-        const uint32_t dw = (uint32_t)__shfl((int)codes[j], src_lane, 64);
-        const bf16x8 av1 = __builtin_bit_cast(bf16x8, base[(dw >> shift) & 0xffffu]);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av1, hb1[t], acc[j][t], 0, 0, 0);
-      }
-      return;
-    }
     bf16x8 hb[kParts][NT];
 #pragma unroll
     for (int pr = 0; pr < kParts; ++pr)
@@ -310,7 +333,7 @@ __global__ __launch_bounds__(kMmThreads) void mm_logits_kernel(MmArgs a) {
 
   if (q0 < q1) {
     uint32_t ca[T], cbk[T];
-    Staged<DS, NT, ONEPAIR> st;
+    Staged<DS, NT> st;
     load_codes(ca, q0);
     stage_load(st, q0, 0);
     int slot = 0;
@@ -320,10 +343,10 @@ __global__ __launch_bounds__(kMmThreads) void mm_logits_kernel(MmArgs a) {
     auto do_block = [&](int q, uint32_t (&cur)[T], uint32_t (&nxt)[T]) {
       arrange_codes(cur);
 #pragma unroll
-      for (int hs = 0; hs < SB; ++hs) {
+      for (int hs = 0; hs < NSUB; ++hs) {
         stage_store(st, slot, q, hs);
         __syncthreads();
-        if (hs + 1 < SB) stage_load(st, q, hs + 1);
+        if (hs + 1 < NSUB) stage_load(st, q, hs + 1);
         else stage_load(st, min(q + 1, q1 - 1), 0);
         if (hs == 0) {
           __builtin_amdgcn_sched_barrier(0);   // keep the staging loads ahead of the code loads (vmcnt is in order)
@@ -347,110 +370,451 @@ __global__ __launch_bounds__(kMmThreads) void mm_logits_kernel(MmArgs a) {
     }
   }
 
-  // acc[j][t][e] = z[batch bt*16NT + 16t + i16][row tile0 + 16j + 4kg + e]
-  if (a.G > 1) {
+  mm_epilogue<NT, T>(a, acc, bt, g, s, tile0, tid);
+}
+
+// ---- K above kMmMaxK (16-bit blocked codes): one pair per ring slot.
+//
+// A slot holds the K codewords of one (level, subspace) pair exactly as they
+// lie in the codebook (K*d bf16, 48 KB at K = 4096, d = 6) and the pair's slice
+// of h's three bf16 parts. The MFMA's four k-slots carry the row's codeword
+// against parts 0, 1, 2 and a zero: one 16x16x32 MFMA per 16 rows x 16
+// vectors x pair, the three-part split folded into the contraction.
+//
+// Staging goes straight from global memory into LDS (global_load_lds, 16
+// bytes per lane, lane-contiguous), so no registers hold the next slot and a
+// wave takes 8 row tiles at four column tiles. Per pair: wait for this slot's
+// copy, barrier, read the h fragments and the T codeword fragments, start the
+// next pair's copy into the other slot, then the MFMAs. The wait is an explicit
+// count, so the code loads issued after a copy stay in flight past it.
+constexpr int kMmMaxKOnePair = 4 * kMmMaxK;
+constexpr int kHSlot = 64;   // h entries per part in a slot (16-byte units; >= 16 NT)
+
+// Codeword k of a slot's segment: DS bf16 values at byte 2 DS k, zero-extended to 8.
+template <int DS>
+__device__ __forceinline__ bf16x8 read_codeword(const unsigned char* seg, uint32_t k) {
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if constexpr (DS == 8) {
+    v = *reinterpret_cast<const u32x4*>(seg + k * 16u);
+  } else if constexpr (DS == 4) {
+    const uint2 w = *reinterpret_cast<const uint2*>(seg + k * 8u);
+    v[0] = w.x;
+    v[1] = w.y;
+  } else if constexpr (DS == 2) {
+    v[0] = *reinterpret_cast<const uint32_t*>(seg + k * 4u);
+  } else {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(seg + k * 12u);
+    v[0] = w[0];
+    v[1] = w[1];
+    v[2] = w[2];
+  }
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// s_waitcnt with vmcnt(n) (n < 16) and the other counters left alone.
+#define RQ_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
+
+template <int DS, int NT, int T>
+__global__ __launch_bounds__(kMmThreads) void mm_pair_kernel(MmArgs a) {
+  constexpr int PPB = 8;   // pairs per 16-bit code block
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int K = a.K;
+  const int n_bt = 16 * NT;
+  const int seg_words = K * DS / 8;   // 16-byte words of one pair's codewords (the host keeps K*DS % 8 == 0)
+  // rounded up to whole copy rounds: every lane of every round lands inside the slot
+  const int cw_words = (seg_words + kMmThreads - 1) / kMmThreads * kMmThreads;
+  const int slot_bytes = (cw_words + 4 * kHSlot) * 16;
+
+  const int per_bt = a.G * a.S;
+  const int bt = blockIdx.x / per_bt;
+  const int li = blockIdx.x - bt * per_bt;
+  const int g = li % a.G;
+  const int s = li / a.G;
+  const int q0 = g * a.qpg;
+  const int q1 = min(a.NQ, q0 + a.qpg);
+  const int p_end = min(a.NP, PPB * q1);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int i16 = lane & 15;
+  const int kg = lane >> 4;
+  const int64_t tile0 = (int64_t)s * (kMmWaves * T * 16) + (int64_t)wave * (T * 16);
+
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc((void*)a.codes, (short)0, (int)0xffffffffu,
+                                                                        0x00020000);
+  const uint32_t blk_bytes = (uint32_t)a.rows * 16u;
+  // code loads as in mm_logits_kernel: whole 16-byte rows for T a multiple of 4,
+  // transposed across the wave's rows of lanes so that lane (i16, kg) holds
+  // dword kg of every tile's row i16
+  constexpr bool kWide = T % 4 == 0;
+  constexpr int NV = kWide ? T / 4 : T;
+  uint32_t voff[NV];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int b = bt * n_bt + 16 * t + i16;
-      if (b >= a.B) continue;
-      float* dst = a.partial + ((size_t)g * a.B + b) * a.rows;
+  for (int v = 0; v < NV; ++v) {
+    const int64_t r = min(tile0 + 16 * (kWide ? 4 * v + kg : v) + i16, a.rows - 1);
+    voff[v] = (uint32_t)r * 16u + (kWide ? 0u : (uint32_t)kg * 4u);
+  }
+  auto load_codes = [&](uint32_t (&dst)[T], int q) {
 #pragma unroll
-      for (int j = 0; j < T; ++j) {
-        const int64_t r = tile0 + 16 * j + 4 * kg;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (r + e < a.rows) dst[r + e] = acc[j][t][e];
+    for (int v = 0; v < NV; ++v) {
+      if constexpr (kWide) {
+        const u32x4 w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(crs, voff[v], (uint32_t)q * blk_bytes, 0));
+        dst[4 * v + 0] = w[0]; dst[4 * v + 1] = w[1]; dst[4 * v + 2] = w[2]; dst[4 * v + 3] = w[3];
+      } else {
+        dst[v] = __builtin_amdgcn_raw_buffer_load_b32(crs, voff[v], (uint32_t)q * blk_bytes, 0);
       }
     }
-    return;
+  };
+  auto arrange_codes = [&](uint32_t (&c)[T]) {
+    if constexpr (kWide) {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const auto x02 = __builtin_amdgcn_permlane32_swap(c[4 * v + 0], c[4 * v + 2], false, false);
+        const auto x13 = __builtin_amdgcn_permlane32_swap(c[4 * v + 1], c[4 * v + 3], false, false);
+        const auto y01 = __builtin_amdgcn_permlane16_swap(x02[0], x13[0], false, false);
+        const auto y23 = __builtin_amdgcn_permlane16_swap(x02[1], x13[1], false, false);
+        c[4 * v + 0] = y01[0]; c[4 * v + 1] = y01[1]; c[4 * v + 2] = y23[0]; c[4 * v + 3] = y23[1];
+      }
+    }
+  };
+
+  // The fourth h part of both slots is zero (written once, never copied over).
+  if (tid < 2 * kHSlot) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(lds + (tid / kHSlot) * slot_bytes + (cw_words + 3 * kHSlot + tid % kHSlot) * 16) = z;
   }
-  // G == 1: the sums are final -- softcap, store, best selection key of this
-  // slab for each hidden vector (the selection kernel reduces the S keys).
-  __shared__ unsigned long long s_keys[16 * NT];
-  if (tid < 16 * NT) s_keys[tid] = 0ull;
   __syncthreads();
+  // Copy pair p into slot r: its codewords (lane-contiguous 16-byte words;
+  // lanes past the segment re-read its last word into the slot's slack) and,
+  // by waves 0-2, parts 0-2 of h for this batch tile (lanes past the tile's
+  // vectors re-read its last one into unused entries).
+  auto copy_pair = [&](int r, int p) {
+    unsigned char* sb = lds + r * slot_bytes;
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.cb) + (size_t)p * seg_words;
+    for (int w0 = 0; w0 < cw_words; w0 += kMmThreads)
+      __builtin_amdgcn_global_load_lds((const void*)(src + min(w0 + tid, seg_words - 1)),
+                                       (lds_ptr_t)(sb + (size_t)(w0 + wave * 64) * 16), 16, 0, 0);
+    if (wave < kParts) {
+      const u32x4* hsrc = a.hp + ((size_t)wave * a.M + p % a.M) * a.Bp + (size_t)bt * n_bt;
+      __builtin_amdgcn_global_load_lds((const void*)(hsrc + min(lane, n_bt - 1)),
+                                       (lds_ptr_t)(sb + (size_t)(cw_words + wave * kHSlot) * 16), 16, 0, 0);
+    }
+  };
+
+  floatx4 acc[T][NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int b = bt * n_bt + 16 * t + i16;
-    unsigned long long kbest = 0ull;
-    if (b < a.B) {
+  for (int j = 0; j < T; ++j)
 #pragma unroll
-      for (int j = 0; j < T; ++j) {
-        const int64_t r = tile0 + 16 * j + 4 * kg;
+    for (int t = 0; t < NT; ++t) acc[j][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  if (PPB * q0 < p_end) {
+    uint32_t ca[T], cbk[T];
+    load_codes(ca, q0);
+    copy_pair(0, PPB * q0);
+    // Block q: its 8 pairs, pair p in slot p & 1; the first pair also starts
+    // the next block's code loads, after its copy of the next pair.
+    auto do_block = [&](int q, uint32_t (&cur)[T], uint32_t (&nxt)[T]) {
+      arrange_codes(cur);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (r + e >= a.rows) continue;
-          const float z = acc[j][t][e];
-          const float v = a.softcap > 0.0f ? a.softcap * tanhf(z / a.softcap) : z;
-          if (a.out) a.out[(size_t)b * a.rows + r + e] = v;
-          const unsigned long long k = select_key(v, (uint32_t)(r + e));
-          kbest = k > kbest ? k : kbest;
+      for (int hs = 0; hs < PPB; ++hs) {
+        const int p = PPB * q + hs;
+        if (p >= p_end) break;   // uniform
+        // this pair's copy is done: only the code loads issued after it (by the
+        // block's first pair) may still be in flight
+        if (hs == 1) RQ_WAIT_VMCNT(NV);
+        else RQ_WAIT_VMCNT(0);
+        __builtin_amdgcn_s_barrier();
+        const unsigned char* sb = lds + (hs & 1) * slot_bytes;
+        bf16x8 hb[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          hb[t] = *reinterpret_cast<const bf16x8*>(sb + (size_t)(cw_words + kg * kHSlot + 16 * t + i16) * 16);
+        const int src_lane = i16 + 16 * (hs >> 1);
+        bf16x8 av[T];
+#pragma unroll
+        for (int j = 0; j < T; ++j) {
+          const uint32_t dw = (uint32_t)__shfl((int)cur[j], src_lane, 64);
+          av[j] = read_codeword<DS>(sb, (dw >> (16 * (hs & 1))) & 0xffffu);
         }
+        __builtin_amdgcn_sched_barrier(0);   // this slot's reads before the copy into the other
+        if (p + 1 < p_end) copy_pair((hs + 1) & 1, p + 1);
+        __builtin_amdgcn_sched_barrier(0);   // the copy before the code loads (the waits count in order)
+        if (hs == 0) load_codes(nxt, min(q + 1, q1 - 1));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < T; ++j)
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[j], hb[t], acc[j][t], 0, 0, 0);
+      }
+    };
+    for (int q = q0; q < q1; q += 2) {
+      do_block(q, ca, cbk);
+      if (q + 1 < q1) do_block(q + 1, cbk, ca);
+    }
+  }
+  mm_epilogue<NT, T>(a, acc, bt, g, s, tile0, tid);
+}
+
+// Row tiles per wave of the one-pair kernel: the accumulators (4*T*NT) beside
+// the codeword fragments (4*T), the codes (2*T) and the h fragments (4*NT).
+constexpr int pair_tiles_for(int NT) { return NT == 1 ? 16 : 8; }
+
+// ---- The same with three slots (pairs whose codewords fit 48 KB): the copy of
+// pair p + 2 starts while pair p is read, so each copy has two pairs' work to
+// land. The slots sit at fixed offsets, every copy issues the same number of
+// loads (kPair3Rounds rounds of codewords, past the segment clamped into the
+// slot's slack, then one h part per wave), and codeword reads are masked to
+// the slot: so the waits are counted exactly and the compiler can tell the
+// slot being read from the two being filled.
+constexpr int kPair3CwWords = 3072;                     // 48 KB of codewords per slot
+constexpr int kPair3Rounds = kPair3CwWords / kMmThreads;   // copy rounds (6)
+constexpr int kPair3SlotBytes = (kPair3CwWords + 4 * kHSlot) * 16;
+constexpr int kPair3Ops = kPair3Rounds + 1;             // loads per copy, per thread
+
+template <int DS, int NT, int T>
+__global__ __launch_bounds__(kMmThreads) void mm_pair3_kernel(MmArgs a) {
+  constexpr int PPB = 8;   // pairs per 16-bit code block
+  constexpr uint32_t kCwMax = (uint32_t)(kPair3CwWords * 16 / (2 * DS)) - 1u;   // last codeword a slot holds
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int K = a.K;
+  const int n_bt = 16 * NT;
+  const int seg_words = K * DS / 8;   // <= kPair3CwWords (host check)
+
+  const int per_bt = a.G * a.S;
+  const int bt = blockIdx.x / per_bt;
+  const int li = blockIdx.x - bt * per_bt;
+  const int g = li % a.G;
+  const int s = li / a.G;
+  const int q0 = g * a.qpg;
+  const int q1 = min(a.NQ, q0 + a.qpg);
+  const int p_begin = PPB * q0;
+  const int p_end = min(a.NP, PPB * q1);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int i16 = lane & 15;
+  const int kg = lane >> 4;
+  const int64_t tile0 = (int64_t)s * (kMmWaves * T * 16) + (int64_t)wave * (T * 16);
+
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc((void*)a.codes, (short)0, (int)0xffffffffu,
+                                                                        0x00020000);
+  const uint32_t blk_bytes = (uint32_t)a.rows * 16u;
+  constexpr bool kWide = T % 4 == 0;
+  constexpr int NV = kWide ? T / 4 : T;
+  uint32_t voff[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int64_t r = min(tile0 + 16 * (kWide ? 4 * v + kg : v) + i16, a.rows - 1);
+    voff[v] = (uint32_t)r * 16u + (kWide ? 0u : (uint32_t)kg * 4u);
+  }
+  auto load_codes = [&](uint32_t (&dst)[T], int q) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      if constexpr (kWide) {
+        const u32x4 w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(crs, voff[v], (uint32_t)q * blk_bytes, 0));
+        dst[4 * v + 0] = w[0]; dst[4 * v + 1] = w[1]; dst[4 * v + 2] = w[2]; dst[4 * v + 3] = w[3];
+      } else {
+        dst[v] = __builtin_amdgcn_raw_buffer_load_b32(crs, voff[v], (uint32_t)q * blk_bytes, 0);
       }
     }
-    if (kbest) atomicMax(&s_keys[16 * t + i16], kbest);   // LDS atomics, this workgroup only
+  };
+  auto arrange_codes = [&](uint32_t (&c)[T]) {
+    if constexpr (kWide) {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const auto x02 = __builtin_amdgcn_permlane32_swap(c[4 * v + 0], c[4 * v + 2], false, false);
+        const auto x13 = __builtin_amdgcn_permlane32_swap(c[4 * v + 1], c[4 * v + 3], false, false);
+        const auto y01 = __builtin_amdgcn_permlane16_swap(x02[0], x13[0], false, false);
+        const auto y23 = __builtin_amdgcn_permlane16_swap(x02[1], x13[1], false, false);
+        c[4 * v + 0] = y01[0]; c[4 * v + 1] = y01[1]; c[4 * v + 2] = y23[0]; c[4 * v + 3] = y23[1];
+      }
+    }
+  };
+
+  if (tid < 3 * kHSlot) {   // the fourth h part of every slot is zero
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(lds + (tid / kHSlot) * kPair3SlotBytes + (kPair3CwWords + 3 * kHSlot + tid % kHSlot) * 16) = z;
   }
   __syncthreads();
-  if (a.block_keys && tid < 16 * NT) {
-    const int b = bt * n_bt + tid;
-    if (b < a.B) a.block_keys[(size_t)b * a.S + s] = s_keys[tid];
+  // Copy pair p into slot R: kPair3Rounds rounds of lane-contiguous 16-byte
+  // codeword words, then part (wave mod 3) of h (three waves copy each part, the
+  // same bytes to the same place).
+  auto copy_pair = [&](int R, int p) {
+    unsigned char* sb = lds + R * kPair3SlotBytes;
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.cb) + (size_t)p * seg_words;
+#pragma unroll
+    for (int rd = 0; rd < kPair3Rounds; ++rd)
+      __builtin_amdgcn_global_load_lds((const void*)(src + min(rd * kMmThreads + tid, seg_words - 1)),
+                                       (lds_ptr_t)(sb + (size_t)(rd * kMmThreads + wave * 64) * 16), 16, 0, 0);
+    const int part = wave % kParts;
+    const u32x4* hsrc = a.hp + ((size_t)part * a.M + p % a.M) * a.Bp + (size_t)bt * n_bt;
+    __builtin_amdgcn_global_load_lds((const void*)(hsrc + min(lane, n_bt - 1)),
+                                     (lds_ptr_t)(sb + (size_t)(kPair3CwWords + part * kHSlot) * 16), 16, 0, 0);
+  };
+
+  floatx4 acc[T][NT];
+#pragma unroll
+  for (int j = 0; j < T; ++j)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[j][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int nsteps = p_end - p_begin;
+  if (nsteps > 0) {
+    uint32_t cur[T], nxt[T];
+    load_codes(nxt, q0);
+    copy_pair(0, p_begin);
+    if (nsteps > 1) copy_pair(1, p_begin + 1);
+    // Step i: pair p = p_begin + i in slot i mod 3 (R, static in the unrolled
+    // loop). Issue order within a step: reads of slot R, [the next block's code
+    // loads at a block's first pair], the copy of pair p + 2 into slot R + 2.
+    // So at step i the loads issued after pair p's copy are step i-1's: its
+    // code loads (if step i-1 began a block) and pair p + 1's copy.
+    auto step = [&](auto Rc, int i) {
+      constexpr int R = decltype(Rc)::value;
+      const int p = p_begin + i;
+      const int hs = p & (PPB - 1);
+      if (hs == 0) {   // (uniform) this block's codes, loaded during the previous block
+#pragma unroll
+        for (int j = 0; j < T; ++j) cur[j] = nxt[j];
+        arrange_codes(cur);
+      }
+      const bool next_copied = i + 1 < nsteps;      // pair p + 1's copy was issued at step i-1
+      const bool prev_began_block = i > 0 && hs == 1;   // step i-1 issued code loads before that copy
+      if (next_copied) {
+        if (prev_began_block) RQ_WAIT_VMCNT(kPair3Ops + NV);
+        else RQ_WAIT_VMCNT(kPair3Ops);
+      } else {
+        if (prev_began_block) RQ_WAIT_VMCNT(NV);
+        else RQ_WAIT_VMCNT(0);
+      }
+      __builtin_amdgcn_s_barrier();
+      const unsigned char* sb = lds + R * kPair3SlotBytes;
+      bf16x8 hb[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        hb[t] = *reinterpret_cast<const bf16x8*>(sb + (size_t)(kPair3CwWords + kg * kHSlot + 16 * t + i16) * 16);
+      const int src_lane = i16 + 16 * (hs >> 1);
+      bf16x8 av[T];
+#pragma unroll
+      for (int j = 0; j < T; ++j) {
+        const uint32_t dw = (uint32_t)__shfl((int)cur[j], src_lane, 64);
+        av[j] = read_codeword<DS>(sb, min((dw >> (16 * (hs & 1))) & 0xffffu, kCwMax));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (hs == 0) load_codes(nxt, min((p >> 3) + 1, q1 - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 2 < nsteps) copy_pair((R + 2) % 3, p + 2);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < T; ++j)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[j], hb[t], acc[j][t], 0, 0, 0);
+    };
+    for (int i = 0; i < nsteps; i += 3) {
+      step(std::integral_constant<int, 0>{}, i);
+      if (i + 1 < nsteps) step(std::integral_constant<int, 1>{}, i + 1);
+      if (i + 2 < nsteps) step(std::integral_constant<int, 2>{}, i + 2);
+    }
   }
+  mm_epilogue<NT, T>(a, acc, bt, g, s, tile0, tid);
 }
 
 // Row tiles per wave for NT column tiles: the accumulators (4*T*NT VGPRs), the
 // code registers (2*T) and the staged half-block share a wave's 256 VGPRs.
 // (Three sub-blocks per code block keep more values live: fewer tiles.) A
 // multiple of 4 takes the wide code loads; 4 at NT = 4 uses 254 VGPRs.
-// One pair per slot keeps a third of the h registers, so four column tiles take
-// 8 row tiles (1,024 rows per staged slot and workgroup); codewords of 6 values
-// take 6 and of 8 values 4 (their staging needs more registers; 8 spilled).
-constexpr int tiles_for(int NT, int NSUB = 2, bool ONEPAIR = false, int DS = 2) {
-  return ONEPAIR ? (NT == 1 ? 16 : (NT == 4 && DS >= 6 ? (DS == 8 ? 4 : 6) : 8))
-                 : (NSUB == 2 ? (NT == 1 ? 16 : NT == 2 ? 8 : 4) : (NT == 1 ? 12 : NT == 2 ? 6 : 3));
+constexpr int tiles_for(int NT, int NSUB = 2) {
+  return kMmThreads == 512 ? (NSUB == 2 ? (NT == 1 ? 16 : NT == 2 ? 8 : 4) : (NT == 1 ? 12 : NT == 2 ? 6 : 3))
+                           : (NT == 1 ? 8 : NT == 2 ? 4 : 2);
 }
 
-template <int DS, int NT, int NSUB, bool ONEPAIR = false>
+template <int DS, int NT, int NSUB>
 hipError_t launch_typed(const MmArgs& a, int wgs, size_t lds, hipStream_t stream) {
-  auto kern = mm_logits_kernel<DS, NT, tiles_for(NT, NSUB, ONEPAIR, DS), NSUB, ONEPAIR>;
+  auto kern = mm_logits_kernel<DS, NT, tiles_for(NT, NSUB), NSUB>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(kMmThreads), lds, stream, a);
   return hipGetLastError();
 }
 
-template <int DS, int NSUB, bool ONEPAIR = false>
+template <int DS, int NSUB>
 hipError_t launch_ds(const MmArgs& a, const MmPlan& p, hipStream_t stream) {
   const int wgs = p.G * p.S * p.NBT;
-  if (p.NT == 1) return launch_typed<DS, 1, NSUB, ONEPAIR>(a, wgs, p.lds, stream);
-  if (p.NT == 2) return launch_typed<DS, 2, NSUB, ONEPAIR>(a, wgs, p.lds, stream);
-  return launch_typed<DS, 4, NSUB, ONEPAIR>(a, wgs, p.lds, stream);
+  if (p.NT == 1) return launch_typed<DS, 1, NSUB>(a, wgs, p.lds, stream);
+  if (p.NT == 2) return launch_typed<DS, 2, NSUB>(a, wgs, p.lds, stream);
+  return launch_typed<DS, 4, NSUB>(a, wgs, p.lds, stream);
 }
 
-template <int NSUB, bool ONEPAIR = false>
+template <int NSUB>
 hipError_t launch_nsub(const MmArgs& a, const MmPlan& p, int d, hipStream_t stream) {
   switch (d) {
-    case 2: return launch_ds<2, NSUB, ONEPAIR>(a, p, stream);
-    case 4: return launch_ds<4, NSUB, ONEPAIR>(a, p, stream);
-    case 6: return launch_ds<6, NSUB, ONEPAIR>(a, p, stream);
-    default: return launch_ds<8, NSUB, ONEPAIR>(a, p, stream);
+    case 2: return launch_ds<2, NSUB>(a, p, stream);
+    case 4: return launch_ds<4, NSUB>(a, p, stream);
+    case 6: return launch_ds<6, NSUB>(a, p, stream);
+    default: return launch_ds<8, NSUB>(a, p, stream);
+  }
+}
+
+template <int DS, int NT>
+hipError_t launch_pair_typed(const MmArgs& a, int wgs, size_t lds, hipStream_t stream) {
+  auto kern = (int64_t)a.K * DS / 8 <= kPair3CwWords ? mm_pair3_kernel<DS, NT, pair_tiles_for(NT)>
+                                                      : mm_pair_kernel<DS, NT, pair_tiles_for(NT)>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(kMmThreads), lds, stream, a);
+  return hipGetLastError();
+}
+
+template <int DS>
+hipError_t launch_pair_ds(const MmArgs& a, const MmPlan& p, hipStream_t stream) {
+  const int wgs = p.G * p.S * p.NBT;
+  if (p.NT == 1) return launch_pair_typed<DS, 1>(a, wgs, p.lds, stream);
+  if (p.NT == 2) return launch_pair_typed<DS, 2>(a, wgs, p.lds, stream);
+  return launch_pair_typed<DS, 4>(a, wgs, p.lds, stream);
+}
+
+hipError_t launch_pair(const MmArgs& a, const MmPlan& p, int d, hipStream_t stream) {
+  switch (d) {
+    case 2: return launch_pair_ds<2>(a, p, stream);
+    case 4: return launch_pair_ds<4>(a, p, stream);
+    case 6: return launch_pair_ds<6>(a, p, stream);
+    default: return launch_pair_ds<8>(a, p, stream);
   }
 }
 
 }  // namespace
 
-// One pair per ring slot for K beyond what four pairs per slot can stage.
+// One pair per ring slot (mm_pair_kernel) for K beyond what four pairs per slot can stage.
 static bool mm_one_pair(const rq_matrix* W) { return W->K > kMmMaxK; }
 
 bool mm_supported(const rq_matrix* W) {
   if (W->cb_dtype != RQ_BF16 || W->d > 8 || (W->d % 2) != 0 || ((uintptr_t)W->codebooks % 4) != 0) return false;
   if (W->K <= kMmMaxK) return W->codes_layout == RQ_CODES_BLOCKED || W->codes_layout == RQ_CODES_PACKED10;
-  return W->K <= kMmMaxKOnePair && W->codes_layout == RQ_CODES_BLOCKED;
+  // one pair per slot: 16-bit blocked codes, each pair's codewords a whole number of 16-byte words
+  return W->K <= kMmMaxKOnePair && W->codes_layout == RQ_CODES_BLOCKED && ((int64_t)W->K * W->d) % 8 == 0 &&
+         ((uintptr_t)W->codebooks % 16) == 0;
+}
+
+// Three slots when a pair's codewords fit one (mm_pair3_kernel), else two.
+static bool pair3_fits(const rq_matrix* W) { return (int64_t)W->K * W->d / 8 <= kPair3CwWords; }
+
+// Bytes of one ring slot of mm_pair_kernel.
+static size_t pair_slot_bytes(const rq_matrix* W) {
+  const size_t seg_words = (size_t)W->K * W->d / 8;
+  const size_t cw_words = (seg_words + kMmThreads - 1) / kMmThreads * kMmThreads;
+  return (cw_words + 4 * kHSlot) * 16;
 }
 
 MmPlan plan_mm(const rq_matrix* W, int B) {
   MmPlan p{};
   p.NT = B <= 16 ? 1 : (B <= 32 ? 2 : 4);
-  p.T = tiles_for(p.NT, W->codes_layout == RQ_CODES_PACKED10 ? 3 : 2, mm_one_pair(W), W->d);
+  p.T = mm_one_pair(W) ? pair_tiles_for(p.NT) : tiles_for(p.NT, W->codes_layout == RQ_CODES_PACKED10 ? 3 : 2);
   p.NBT = (B + 16 * p.NT - 1) / (16 * p.NT);
   p.Bp = p.NBT * 16 * p.NT;
   const int64_t slab = (int64_t)kMmWaves * p.T * 16;
@@ -476,8 +840,9 @@ MmPlan plan_mm(const rq_matrix* W, int B) {
   }
   p.qpg = (p.NQ + G - 1) / G;
   p.G = (p.NQ + p.qpg - 1) / p.qpg;
-  p.lds = mm_one_pair(W) ? (size_t)2 * ((size_t)W->K + (size_t)4 * 16 * p.NT) * 16
-                         : (size_t)2 * (4 * (size_t)W->K + (size_t)kParts * 4 * 16 * p.NT) * 16;
+  p.lds = !mm_one_pair(W)  ? (size_t)2 * (4 * (size_t)W->K + (size_t)kParts * 4 * 16 * p.NT) * 16
+          : pair3_fits(W) ? (size_t)3 * kPair3SlotBytes
+                          : 2 * pair_slot_bytes(W);
   return p;
 }
 
@@ -511,7 +876,7 @@ hipError_t launch_mm_logits(const rq_matrix* W, const MmPlan& p, const float* h,
   hipEvent_t before, after;
   take_stage_events(&before, &after);
   if (before && (e = hipEventRecord(before, stream)) != hipSuccess) return e;
-  e = mm_one_pair(W)                            ? launch_nsub<2, true>(a, p, W->d, stream)
+  e = mm_one_pair(W)                            ? launch_pair(a, p, W->d, stream)
       : W->codes_layout == RQ_CODES_PACKED10 ? launch_nsub<3>(a, p, W->d, stream)
                                              : launch_nsub<2>(a, p, W->d, stream);
   if (e != hipSuccess) return e;

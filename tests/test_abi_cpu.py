@@ -152,6 +152,7 @@ def test_logits_method_and_checks():
     assert m(gemma_desc(K=4096, L=4), 64) == B.RQ_METHOD_MATRIX_CORES          # one pair per staged slot
     assert m(gemma_desc(K=4097, L=4), 64) == B.RQ_METHOD_TABLE                 # K above the staged maximum
     assert m(gemma_desc(K=2048, codes_layout=B.RQ_CODES_ROWS), 64) == B.RQ_METHOD_TABLE
+    assert m(gemma_desc(K=1025), 64) == B.RQ_METHOD_TABLE                      # a pair's codewords not whole 16 B
     assert m(gemma_desc(codes_layout=B.RQ_CODES_ROWS), 16) == B.RQ_METHOD_TABLE
     assert m(gemma_desc(M=256, d=9), 16) == B.RQ_METHOD_TABLE                  # d > 8
     assert m(gemma_desc(M=768, d=3), 16) == B.RQ_METHOD_TABLE                  # odd d

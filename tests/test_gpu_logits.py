@@ -50,14 +50,15 @@ MM_ONE_PAIR_EXACT = [
     (2500, 96, 16, 4096, 4, 64),    # the stress head's K and L, four column tiles
     (1000, 96, 48, 1500, 2, 33),    # d=2, K not a power of two, 33 of 64 columns
     (700, 64, 8, 3000, 1, 100),     # d=8, one code block, two batch tiles
-    (4097, 102, 17, 1025, 3, 8),    # odd M (last block partly empty), K just above 1024, ragged rows
+    (4097, 102, 17, 1028, 3, 8),    # odd M (last block partly empty), K just above 1024, ragged rows
 ]
 
 
 @pytest.mark.parametrize("shape", MM_ONE_PAIR_EXACT, ids=lambda s: "x".join(map(str, s)))
 def test_logits_matrix_cores_one_pair_exact(shape):
-    """K above 1024 (blocked codes): one pair per staged slot, the three bf16 parts of h in the MFMA's k-slots.
-    Small-integer inputs make every product and sum exact, so z matches the oracle bit for bit."""
+    """K above 1024 (blocked codes): one pair per staged slot, copied straight into LDS, the three bf16 parts of
+    h in the MFMA's k-slots. Small-integer inputs make every product and sum exact, so z matches the oracle bit
+    for bit."""
     rows, D, M, K, L, B = shape
     mat, h = synth.gen_exact(rows + 3 * K, rows, D, M, K, L, B, cb_dtype="bf16")
     W = to_dev(mat)
