@@ -41,7 +41,8 @@
  *     aligned, workspaces 256-byte aligned (torch allocations satisfy this).
  *   - Workspaces hold per-call scratch only (no state carries over between
  *     calls, no initial contents are required). Calls that overlap in time
- *     must not share a workspace.
+ *     must not share a workspace. A workspace may be NULL when its query
+ *     returns 0.
  *   - Concurrency. Calls on different streams may run concurrently as long as
  *     they do not share output or workspace buffers.
  */
@@ -346,8 +347,9 @@ rq_status rq_dense_logits(const uint16_t* E, int64_t rows, int32_t D, const floa
                           hipStream_t stream);
 
 
-/* Static text for a status code. */
-const char* rq_status_string(rq_status s);
+/* Static text for a status code. Takes any int (an rq_status value converts
+ * to it); a value that is no rq_status gives "unknown status". */
+const char* rq_status_string(int32_t s);
 /* Description of the last failure on the calling thread ("" if none). */
 const char* rq_last_error(void);
 /* Library version, "major.minor.patch". */

@@ -3,6 +3,8 @@
 Argument marshalling only: torch tensors provide device memory and the
 current HIP stream; every step of the computation runs in the library's
 kernels. The library is loaded on first use and a missing build raises.
+RQ_LUT_LIB names another build of the same sources to load instead (the
+host-only sanitizer build of the CPU test run uses it).
 """
 import ctypes
 import os
@@ -11,7 +13,7 @@ import numpy as np
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "librq_lut.so")
+LIB_PATH = os.environ.get("RQ_LUT_LIB") or os.path.join(HERE, "librq_lut.so")
 
 RQ_OK, RQ_ERR_NULL, RQ_ERR_SHAPE, RQ_ERR_DTYPE, RQ_ERR_ALIGN, RQ_ERR_WORKSPACE, RQ_ERR_HIP = 0, -1, -2, -3, -4, -5, -6
 RQ_F32, RQ_BF16 = 0, 1

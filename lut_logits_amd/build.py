@@ -17,11 +17,16 @@ HIPCC_FLAGS = [
 ]
 
 
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+# roctx: one named range per C-ABI call (shown by rocprofv3 --marker-trace)
+LINK_LIBS = ["-L" + os.path.join(ROCM, "lib"), "-lrocprofiler-sdk-roctx", "-Wl,-rpath," + os.path.join(ROCM, "lib")]
+
+
 def sources():
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
 
 
-def build(out=LIB, extra=()):
+def build(out=LIB, extra=(), link_extra=()):
     """Compile every HIP source into `out` (always recompiles); returns `out`.
 
     Each source is compiled to an object in its own hipcc process (in parallel),
@@ -37,7 +42,8 @@ def build(out=LIB, extra=()):
         failed = [src for src, pr in procs if pr.wait() != 0]
         if failed:
             raise subprocess.CalledProcessError(1, "hipcc -c " + " ".join(failed))
-        subprocess.run(["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], check=True)
+        subprocess.run(["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", *extra, *objs, "-o", tmp, *LINK_LIBS,
+                        *link_extra], check=True)
     os.replace(tmp, out)
     return out
 

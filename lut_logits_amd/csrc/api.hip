@@ -10,6 +10,8 @@
 #include <algorithm>
 #include <mutex>
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 #include "rq_internal.h"
 
 // The scratch of rq_lut_logits_static: one copy per GPU the library runs on,
@@ -35,6 +37,16 @@ rq_status launched(hipError_t e, const char* what) {
   if (e == hipSuccess) return RQ_OK;
   return fail(RQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
+
+// A roctx range named for the entry point, open for the call (argument checks
+// and launches; the kernels themselves run later, on the caller's stream).
+// With no profiler attached a push or pop costs a few nanoseconds.
+struct CallRange {
+  explicit CallRange(const char* name) { roctxRangePushA(name); }
+  ~CallRange() { roctxRangePop(); }
+  CallRange(const CallRange&) = delete;
+  CallRange& operator=(const CallRange&) = delete;
+};
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -145,7 +157,7 @@ rq_status rq_set_stage_events(hipEvent_t before, hipEvent_t after) {
 
 const char* rq_last_error(void) { return g_last_error; }
 
-const char* rq_status_string(rq_status s) {
+const char* rq_status_string(int32_t s) {
   switch (s) {
     case RQ_OK: return "ok";
     case RQ_ERR_NULL: return "null pointer";
@@ -164,6 +176,7 @@ size_t rq_blocked_codes_bytes(int64_t rows, int32_t L, int32_t M) {
 }
 
 rq_status rq_pack_codes(const uint16_t* src, int64_t rows, int32_t L, int32_t M, uint16_t* dst, hipStream_t stream) {
+  CallRange range(__func__);
   if (rows < 0 || rows >= ((int64_t)1 << 29) || L < 1 || L > RQ_MAX_L || M < 1 || (int64_t)L * M > (1 << 24))
     return fail(RQ_ERR_SHAPE, "bad pack shape rows=%lld L=%d M=%d", (long long)rows, L, M);
   if (rows == 0) return RQ_OK;
@@ -179,6 +192,7 @@ size_t rq_packed10_codes_bytes(int64_t rows, int32_t L, int32_t M) {
 
 rq_status rq_pack_codes10(const uint16_t* src, int64_t rows, int32_t L, int32_t M, uint16_t* dst,
                           hipStream_t stream) {
+  CallRange range(__func__);
   if (rows < 0 || rows >= ((int64_t)1 << 29) || L < 1 || L > RQ_MAX_L || M < 1 || (int64_t)L * M > (1 << 24))
     return fail(RQ_ERR_SHAPE, "bad pack shape rows=%lld L=%d M=%d", (long long)rows, L, M);
   if (rows == 0) return RQ_OK;
@@ -194,6 +208,7 @@ size_t rq_packed8_codes_bytes(int64_t rows, int32_t L, int32_t M) {
 
 rq_status rq_pack_codes8(const uint16_t* src, int64_t rows, int32_t L, int32_t M, uint16_t* dst,
                          hipStream_t stream) {
+  CallRange range(__func__);
   if (rows < 0 || rows >= ((int64_t)1 << 29) || L < 1 || L > RQ_MAX_L || M < 1 || (int64_t)L * M > (1 << 24))
     return fail(RQ_ERR_SHAPE, "bad pack shape rows=%lld L=%d M=%d", (long long)rows, L, M);
   if (rows == 0) return RQ_OK;
@@ -209,6 +224,7 @@ size_t rq_lut_bytes(const rq_matrix* W, int32_t B, int32_t lut_dtype) {
 
 rq_status rq_build_lut(const rq_matrix* W, const float* x, const float* x2, int32_t prologue, int32_t B,
                        int32_t lut_dtype, void* lut, hipStream_t stream) {
+  CallRange range(__func__);
   rq_status s = check_matrix(W, false);
   if (s != RQ_OK) return s;
   if (B < 0 || B > 65535) return fail(RQ_ERR_SHAPE, "B=%d outside [0, 65535]", B);
@@ -231,6 +247,7 @@ size_t rq_lut_logits_workspace(const rq_matrix* W, int32_t B, int32_t topk, int3
 rq_status rq_lut_logits(const rq_matrix* W, const void* lut, int32_t lut_dtype, int32_t B, float softcap,
                         float* logits, int32_t* argmax, int32_t topk, int32_t* topk_ids, float* topk_vals, void* ws,
                         size_t ws_bytes, hipStream_t stream) {
+  CallRange range(__func__);
   rq_status s = check_lut_call(W, B, lut_dtype);
   if (s != RQ_OK) return s;
   if (topk < 0 || topk > 1024 || (W->rows > 0 && topk > W->rows))
@@ -245,7 +262,7 @@ rq_status rq_lut_logits(const rq_matrix* W, const void* lut, int32_t lut_dtype, 
   const rq::GatherPlan plan = rq::plan_gather(W, B, lut_dtype == RQ_BF16);
   if (plan.BT == 0) return fail(RQ_ERR_SHAPE, "no table tiling fits on chip for K=%d", W->K);
   const LogitsWs w = logits_ws(W, plan, B, topk, logits != nullptr, lut_dtype == RQ_BF16);
-  if (!ws || ws_bytes < w.total) return fail(RQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, w.total);
+  if (ws_bytes < w.total || (!ws && w.total > 0)) return fail(RQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, w.total);
   if (!aligned(ws, 256)) return fail(RQ_ERR_ALIGN, "workspace must be 256-byte aligned");
   char* base = static_cast<char*>(ws);
   const bool select = argmax || topk > 0;
@@ -324,6 +341,7 @@ size_t rq_logits_workspace(const rq_matrix* W, int32_t B, int32_t topk) {
 rq_status rq_logits(const rq_matrix* W, const float* h, int32_t B, float softcap, float* logits, int32_t* argmax,
                     int32_t topk, int32_t* topk_ids, float* topk_vals, void* ws, size_t ws_bytes,
                     hipStream_t stream) {
+  CallRange range(__func__);
   rq_status s = check_lut_call(W, B, RQ_F32);
   if (s != RQ_OK) return s;
   if (topk < 0 || topk > 1024 || (W->rows > 0 && topk > W->rows))
@@ -336,7 +354,7 @@ rq_status rq_logits(const rq_matrix* W, const float* h, int32_t B, float softcap
     return fail(RQ_ERR_ALIGN, "argument misaligned");
   const HeadWs w = head_ws(W, B, topk, logits != nullptr);
   if (!w.mm && w.gp.BT == 0) return fail(RQ_ERR_SHAPE, "no table tiling fits on chip for K=%d", W->K);
-  if (!ws || ws_bytes < w.total) return fail(RQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, w.total);
+  if (ws_bytes < w.total || (!ws && w.total > 0)) return fail(RQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, w.total);
   if (!aligned(ws, 256)) return fail(RQ_ERR_ALIGN, "workspace must be 256-byte aligned");
   char* base = static_cast<char*>(ws);
   const bool select = argmax || topk > 0;
@@ -378,6 +396,7 @@ rq_status rq_logits(const rq_matrix* W, const float* h, int32_t B, float softcap
 
 rq_status rq_decode_rows(const rq_matrix* W, const int32_t* ids, int32_t n, int32_t out_dtype, void* out,
                          int32_t* bad_ids, hipStream_t stream) {
+  CallRange range(__func__);
   rq_status s = check_matrix(W, true);
   if (s != RQ_OK) return s;
   if (n < 0) return fail(RQ_ERR_SHAPE, "n=%d < 0", n);
@@ -423,6 +442,7 @@ size_t rq_lut_matvec_workspace(const rq_matrix* W, int32_t B) {
 
 rq_status rq_lut_matvec(const rq_matrix* W, const float* x, const float* x2, int32_t prologue, int32_t B, float* y,
                         void* ws, size_t ws_bytes, hipStream_t stream) {
+  CallRange range(__func__);
   rq_status s = check_lut_call(W, B, RQ_F32);
   if (s != RQ_OK) return s;
   if (prologue != RQ_PRO_NONE && prologue != RQ_PRO_GELU_TANH_MUL) return fail(RQ_ERR_DTYPE, "unknown prologue %d", prologue);
@@ -431,7 +451,7 @@ rq_status rq_lut_matvec(const rq_matrix* W, const float* x, const float* x2, int
   if (!aligned(x, 4) || (x2 && !aligned(x2, 4)) || !aligned(y, 4)) return fail(RQ_ERR_ALIGN, "lut_matvec: misaligned buffer");
   const MatvecWs m = matvec_ws(W, B);
   if (m.plan.BT == 0) return fail(RQ_ERR_SHAPE, "no table tiling fits on chip for K=%d", W->K);
-  if (!ws || ws_bytes < m.total) return fail(RQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, m.total);
+  if (ws_bytes < m.total || (!ws && m.total > 0)) return fail(RQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, m.total);
   if (!aligned(ws, 256)) return fail(RQ_ERR_ALIGN, "workspace must be 256-byte aligned");
   char* base = static_cast<char*>(ws);
   rq::GatherOut o;
@@ -517,6 +537,7 @@ size_t rq_lut_mlp_workspace(const rq_matrix* gate, const rq_matrix* up, const rq
 
 rq_status rq_lut_mlp(const rq_matrix* gate, const rq_matrix* up, const rq_matrix* down, const float* x, int32_t B,
                      float* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  CallRange range(__func__);
   rq_status s = check_mlp(gate, up, down, B);
   if (s != RQ_OK) return s;
   if (B == 0 || down->rows == 0) return RQ_OK;
@@ -524,7 +545,7 @@ rq_status rq_lut_mlp(const rq_matrix* gate, const rq_matrix* up, const rq_matrix
   if (!aligned(x, 4) || !aligned(y, 4)) return fail(RQ_ERR_ALIGN, "lut_mlp: misaligned buffer");
   const MlpWs w = mlp_ws(gate, up, down, B);
   if (w.total == 0) return fail(RQ_ERR_SHAPE, "no table tiling fits on chip for K=%d", gate->K);
-  if (!ws || ws_bytes < w.total) return fail(RQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, w.total);
+  if (ws_bytes < w.total || (!ws && w.total > 0)) return fail(RQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, w.total);
   if (!aligned(ws, 256)) return fail(RQ_ERR_ALIGN, "workspace must be 256-byte aligned");
   char* base = static_cast<char*>(ws);
   if (w.fused) {
@@ -567,6 +588,7 @@ size_t rq_dense_logits_workspace(int64_t rows, int32_t B) {
 
 rq_status rq_dense_logits(const uint16_t* E, int64_t rows, int32_t D, const float* h, int32_t B, float softcap,
                           float* logits, int32_t* argmax, void* ws, size_t ws_bytes, hipStream_t stream) {
+  CallRange range(__func__);
   if (rows < 0 || rows >= ((int64_t)1 << 31)) return fail(RQ_ERR_SHAPE, "rows out of range");
   if (D < 8 || D % 8 != 0 || D > 4096) return fail(RQ_ERR_SHAPE, "dense head needs D %% 8 == 0 and 8 <= D <= 4096");
   if (B < 0 || B > 128) return fail(RQ_ERR_SHAPE, "dense head supports 0 <= B <= 128");
@@ -633,6 +655,7 @@ extern "C" {
 rq_status rq_lut_logits_static(const rq_matrix* W, const void* lut, int32_t lut_dtype, int32_t B, float softcap,
                                float* logits, int32_t* argmax, int32_t topk, int32_t* topk_ids, float* topk_vals,
                                hipStream_t stream) {
+  CallRange range(__func__);
   rq_status s = check_lut_call(W, B, lut_dtype);
   if (s != RQ_OK) return s;
   if (topk < 0 || topk > 1024 || (W->rows > 0 && topk > W->rows))
@@ -654,6 +677,7 @@ rq_status rq_lut_logits_static(const rq_matrix* W, const void* lut, int32_t lut_
 size_t rq_lds_gather_sink_words(void) { return rq::lds_gather_sink_words(); }
 
 rq_status rq_lds_gather(int32_t width, int32_t reps, uint32_t* sink, hipStream_t stream) {
+  CallRange range(__func__);
   if (width != 2 && width != 4 && width != 8 && width != 16) return fail(RQ_ERR_SHAPE, "lds_gather: width %d", width);
   if (reps < 0) return fail(RQ_ERR_SHAPE, "lds_gather: reps %d < 0", reps);
   if (!sink) return fail(RQ_ERR_NULL, "lds_gather: sink is NULL");
@@ -669,6 +693,7 @@ size_t rq_stream_read_sink_words(int32_t config) {
 }
 
 rq_status rq_stream_read(const void* src, size_t bytes, int32_t config, uint32_t* sink, hipStream_t stream) {
+  CallRange range(__func__);
   if (config < 0 || config >= rq::stream_read_configs())
     return fail(RQ_ERR_SHAPE, "stream_read: config %d outside [0, %d)", config, rq::stream_read_configs());
   if (bytes == 0) return RQ_OK;

@@ -184,8 +184,9 @@ _default = None
 
 
 def default():
-    """The oracle built from oracle/rq_oracle.c."""
+    """The oracle built from oracle/rq_oracle.c (RQ_ORACLE_LIB names another build of it, such as the
+    sanitizer build of the CPU test run)."""
     global _default
     if _default is None:
-        _default = Oracle()
+        _default = Oracle(os.environ.get("RQ_ORACLE_LIB") or LIB)
     return _default

@@ -15,9 +15,10 @@ CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off"
           "-fno-fast-math", "-D_GNU_SOURCE", "-Wall", "-Wextra"]
 
 
-def build(src=SRC, out=LIB, extra=()):
-    """Compile `src` to the shared library `out`; returns `out`."""
-    cmd = ["gcc", *CFLAGS, *extra, src, "-o", out, "-lm"]
+def build(src=SRC, out=LIB, extra=(), cc="gcc", openmp=True):
+    """Compile `src` to the shared library `out` with `cc`; returns `out`."""
+    flags = [f for f in CFLAGS if openmp or f != "-fopenmp"]
+    cmd = [cc, *flags, *extra, src, "-o", out, "-lm"]
     subprocess.run(cmd, check=True)
     return out
 

@@ -125,6 +125,12 @@ def test_other_entry_points_reject():
     assert lib.rq_decode_rows(ctypes.byref(W), None, 0, 0, None, None, None) == B.RQ_OK
     assert lib.rq_lut_matvec(ctypes.byref(W), 0x1000, None, 0, 1, 0x2000, None, 0, None) == B.RQ_ERR_WORKSPACE
     assert lib.rq_lut_matvec(ctypes.byref(W), 0x1000, None, 1, 1, 0x2000, None, 0, None) == B.RQ_ERR_NULL
+    # a matrix whose workspace query returns 0 takes a NULL workspace: the checks pass (without a GPU the
+    # launch itself then fails)
+    Ws = gemma_desc(rows=160, D=96, M=48, d=2, K=64, cb_dtype=B.RQ_F32)
+    assert lib.rq_lut_matvec_workspace(ctypes.byref(Ws), 1) == 0
+    assert lib.rq_lut_matvec(ctypes.byref(Ws), 0x1000, None, 0, 1, 0x2000, None, 0, None) not in (
+        B.RQ_OK, B.RQ_ERR_WORKSPACE, B.RQ_ERR_NULL, B.RQ_ERR_ALIGN)
     assert lib.rq_pack_codes(None, 10, 2, 3, 0x1000, None) == B.RQ_ERR_NULL
     assert lib.rq_pack_codes(0x1000, 10, 0, 3, 0x1000, None) == B.RQ_ERR_SHAPE
     assert lib.rq_pack_codes(0x1000, 10, 2, 3, 0x1008, None) == B.RQ_ERR_ALIGN
@@ -230,3 +236,18 @@ def test_stream_read_checks():
     assert lib.rq_stream_read(0x1008, 4096, 0, 0x2000, None) == B.RQ_ERR_ALIGN
     assert lib.rq_stream_read(0x1000, 4100, 0, 0x2000, None) == B.RQ_ERR_ALIGN
     assert lib.rq_stream_read(None, 0, 0, None, None) == B.RQ_OK
+
+
+def test_roctx_ranges_linked():
+    """Each C-ABI call opens a roctx range (shown by rocprofv3 --marker-trace): the library imports the roctx
+    push/pop pair and every compute entry point calls them."""
+    import subprocess
+    syms = subprocess.run(["nm", "-D", "--undefined-only", B.LIB_PATH], capture_output=True, text=True,
+                          check=True).stdout
+    assert "roctxRangePushA" in syms and "roctxRangePop" in syms
+    src = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "lut_logits_amd", "csrc",
+                            "api.hip")).read()
+    for name in ("rq_build_lut", "rq_lut_logits", "rq_logits", "rq_decode_rows", "rq_lut_matvec", "rq_lut_mlp",
+                 "rq_dense_logits", "rq_lut_logits_static", "rq_pack_codes"):
+        head = src.split(f"\nrq_status {name}(", 1)[1].split("{", 1)[1]
+        assert head.lstrip().startswith("CallRange range(__func__);"), name
