@@ -302,7 +302,7 @@ struct HeadWs {
 
 static HeadWs head_ws(const rq_matrix* W, int32_t B, int32_t topk, bool logits_out) {
   HeadWs w{};
-  w.mm = B >= RQ_MM_MIN_B && rq::mm_supported(W);
+  w.mm = rq::mm_usable(W, B);
   size_t partial_bytes;
   w.front = 0;
   if (w.mm) {
@@ -327,7 +327,7 @@ static HeadWs head_ws(const rq_matrix* W, int32_t B, int32_t topk, bool logits_o
 int32_t rq_logits_method(const rq_matrix* W, int32_t B) {
   const rq_status s = check_lut_call(W, B, RQ_F32);
   if (s != RQ_OK) return s;
-  return B >= RQ_MM_MIN_B && rq::mm_supported(W) ? RQ_METHOD_MATRIX_CORES : RQ_METHOD_TABLE;
+  return rq::mm_usable(W, B) ? RQ_METHOD_MATRIX_CORES : RQ_METHOD_TABLE;
 }
 
 size_t rq_logits_workspace(const rq_matrix* W, int32_t B, int32_t topk) {

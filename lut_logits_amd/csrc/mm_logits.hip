@@ -63,6 +63,7 @@ struct MmArgs {
   uint64_t* block_keys;   // G == 1: [B][S] best selection key per slab, or null
   int64_t rows;
   int K, M, NP, NQ, B, Bp, G, qpg, S;
+  uint32_t cb_bytes, hp_bytes;   // byte ranges of cb and hp (the one-pair kernels' buffer loads; < 2^32)
 };
 
 // hp[part][m][n] = part `part` of h[n][m*d .. m*d+d), padded to 8 with zeros.
@@ -595,7 +596,7 @@ __global__ __launch_bounds__(kMmThreads) void mm_pair3_kernel(MmArgs a) {
   const int p_end = min(a.NP, PPB * q1);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: the copies' LDS bases and offsets are scalars
   const int lane = tid & 63;
   const int i16 = lane & 15;
   const int kg = lane >> 4;
@@ -644,17 +645,27 @@ __global__ __launch_bounds__(kMmThreads) void mm_pair3_kernel(MmArgs a) {
   // Copy pair p into slot R: kPair3Rounds rounds of lane-contiguous 16-byte
   // codeword words, then part (wave mod 3) of h (three waves copy each part, the
   // same bytes to the same place).
+  // Buffer loads into LDS: the lane's byte offset is the same in every round
+  // and copy (one register), the pair's and the round's offset a scalar. Words
+  // past the pair's segment carry the next pair's codewords (or zeros past the
+  // codebook: the buffer's range check) into the slot's slack, never read.
+  const __amdgpu_buffer_rsrc_t cbrs = __builtin_amdgcn_make_buffer_rsrc((void*)a.cb, (short)0, (int)a.cb_bytes,
+                                                                         0x00020000);
+  const __amdgpu_buffer_rsrc_t hprs = __builtin_amdgcn_make_buffer_rsrc((void*)a.hp, (short)0, (int)a.hp_bytes,
+                                                                         0x00020000);
+  const uint32_t cw_voff = (uint32_t)tid * 16u;
+  const uint32_t h_voff = (uint32_t)min(lane, n_bt - 1) * 16u;
   auto copy_pair = [&](int R, int p) {
     unsigned char* sb = lds + R * kPair3SlotBytes;
-    const u32x4* src = reinterpret_cast<const u32x4*>(a.cb) + (size_t)p * seg_words;
+    const uint32_t base = (uint32_t)p * (uint32_t)(seg_words * 16);
 #pragma unroll
     for (int rd = 0; rd < kPair3Rounds; ++rd)
-      __builtin_amdgcn_global_load_lds((const void*)(src + min(rd * kMmThreads + tid, seg_words - 1)),
-                                       (lds_ptr_t)(sb + (size_t)(rd * kMmThreads + wave * 64) * 16), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(cbrs, (lds_ptr_t)(sb + (size_t)(rd * kMmThreads + wave * 64) * 16), 16,
+                                               cw_voff, base + (uint32_t)(rd * kMmThreads * 16), 0, 0);
     const int part = wave % kParts;
-    const u32x4* hsrc = a.hp + ((size_t)part * a.M + p % a.M) * a.Bp + (size_t)bt * n_bt;
-    __builtin_amdgcn_global_load_lds((const void*)(hsrc + min(lane, n_bt - 1)),
-                                     (lds_ptr_t)(sb + (size_t)(kPair3CwWords + part * kHSlot) * 16), 16, 0, 0);
+    const uint32_t hbase = (uint32_t)((((size_t)part * a.M + p % a.M) * a.Bp + (size_t)bt * n_bt) * 16);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(hprs, (lds_ptr_t)(sb + (size_t)(kPair3CwWords + part * kHSlot) * 16), 16,
+                                             h_voff, hbase, 0, 0);
   };
 
   floatx4 acc[T][NT];
@@ -663,64 +674,132 @@ __global__ __launch_bounds__(kMmThreads) void mm_pair3_kernel(MmArgs a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[j][t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const int nsteps = p_end - p_begin;
-  if (nsteps > 0) {
-    uint32_t cur[T], nxt[T];
-    load_codes(nxt, q0);
-    copy_pair(0, p_begin);
-    if (nsteps > 1) copy_pair(1, p_begin + 1);
-    // Step i: pair p = p_begin + i in slot i mod 3 (R, static in the unrolled
-    // loop). Issue order within a step: reads of slot R, [the next block's code
-    // loads at a block's first pair], the copy of pair p + 2 into slot R + 2.
-    // So at step i the loads issued after pair p's copy are step i-1's: its
-    // code loads (if step i-1 began a block) and pair p + 1's copy.
-    auto step = [&](auto Rc, int i) {
-      constexpr int R = decltype(Rc)::value;
-      const int p = p_begin + i;
-      const int hs = p & (PPB - 1);
-      if (hs == 0) {   // (uniform) this block's codes, loaded during the previous block
+  // Reads of pair p from its slot: the h fragments of the NT column tiles and
+  // the codewords of row tiles [j0, j1) (the row's code broadcast from the lane
+  // row that holds the dword of pair p).
+  auto read_h = [&](bf16x8 (&hb)[NT], int p) {
+    const unsigned char* sb = lds + ((p - p_begin) % 3) * kPair3SlotBytes;
 #pragma unroll
-        for (int j = 0; j < T; ++j) cur[j] = nxt[j];
-        arrange_codes(cur);
-      }
-      const bool next_copied = i + 1 < nsteps;      // pair p + 1's copy was issued at step i-1
-      const bool prev_began_block = i > 0 && hs == 1;   // step i-1 issued code loads before that copy
-      if (next_copied) {
-        if (prev_began_block) RQ_WAIT_VMCNT(kPair3Ops + NV);
-        else RQ_WAIT_VMCNT(kPair3Ops);
-      } else {
-        if (prev_began_block) RQ_WAIT_VMCNT(NV);
-        else RQ_WAIT_VMCNT(0);
-      }
-      __builtin_amdgcn_s_barrier();
-      const unsigned char* sb = lds + R * kPair3SlotBytes;
-      bf16x8 hb[NT];
+    for (int t = 0; t < NT; ++t)
+      hb[t] = *reinterpret_cast<const bf16x8*>(sb + (size_t)(kPair3CwWords + kg * kHSlot + 16 * t + i16) * 16);
+  };
+  auto read_a = [&](bf16x8 (&av)[T], const uint32_t (&codes)[T], int p, int j0, int j1) {
+    const unsigned char* sb = lds + ((p - p_begin) % 3) * kPair3SlotBytes;
+    const int hs = p & (PPB - 1);
+    const int src_lane = i16 + 16 * (hs >> 1);
+#pragma unroll
+    for (int j = j0; j < j1; ++j) {
+      const uint32_t dw = (uint32_t)__shfl((int)codes[j], src_lane, 64);
+      av[j] = read_codeword<DS>(sb, min((dw >> (16 * (hs & 1))) & 0xffffu, kCwMax));
+    }
+  };
+  auto mfma = [&](const bf16x8 (&av)[T], const bf16x8 (&hb)[NT], int j0, int j1) {
+#pragma unroll
+    for (int j = j0; j < j1; ++j)
 #pragma unroll
       for (int t = 0; t < NT; ++t)
-        hb[t] = *reinterpret_cast<const bf16x8*>(sb + (size_t)(kPair3CwWords + kg * kHSlot + 16 * t + i16) * 16);
-      const int src_lane = i16 + 16 * (hs >> 1);
-      bf16x8 av[T];
-#pragma unroll
-      for (int j = 0; j < T; ++j) {
-        const uint32_t dw = (uint32_t)__shfl((int)cur[j], src_lane, 64);
-        av[j] = read_codeword<DS>(sb, min((dw >> (16 * (hs & 1))) & 0xffffu, kCwMax));
+        acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[j], hb[t], acc[j][t], 0, 0, 0);
+  };
+
+  const int nsteps = p_end - p_begin;
+  if (nsteps > 0) {
+    // Software pipeline: the codewords and h of pair p + 1 are read from LDS
+    // while the matrix cores work on pair p, so a wave's LDS reads and MFMAs
+    // overlap instead of taking turns between barriers.
+    //   prologue: copies of pairs 0, 1, 2 into slots 0, 1, 2; reads of pair 0.
+    //   step for pair p (slot p mod 3):
+    //     MFMAs of the first half of the row tiles (pair p);
+    //     wait until pair p + 1's copy has landed and this wave's reads of
+    //       pair p are done; barrier (every wave's are: slot p is free);
+    //     copy of pair p + 3 into slot p mod 3 (issued even past the group's
+    //       last pair, clamped, so that every step issues the same loads);
+    //       at a code block's last pair, the loads of the codes two blocks on;
+    //     reads of pair p + 1's h and of the first half's codewords;
+    //     MFMAs of the second half (pair p), then reads of the second half's
+    //       codewords (pair p + 1).
+    // Each copy has two steps to land. The waits count vector-memory loads in
+    // issue order: after pair p + 1's copy come pair p + 2's and, when p is a
+    // block's first or second pair, one set of code loads.
+    // Two code buffers alternate by block (codes_a: even blocks of the group,
+    // codes_b: odd), so 16 steps make one unrolled round and no code register
+    // is ever moved (a move would make the compiler wait for the loads in
+    // flight). Rounds whose 16 steps all have a next pair run unguarded; the
+    // last round checks each step.
+    constexpr int TH = T / 2;
+    uint32_t codes_a[T], codes_b[T];
+    bf16x8 av[T];
+    bf16x8 hb0[NT], hb1[NT];
+    load_codes(codes_a, q0);
+    copy_pair(0, p_begin);
+    copy_pair(1, min(p_begin + 1, a.NP - 1));
+    copy_pair(2, min(p_begin + 2, a.NP - 1));
+    RQ_WAIT_VMCNT(2 * kPair3Ops);
+    __builtin_amdgcn_s_barrier();
+    arrange_codes(codes_a);
+    __builtin_amdgcn_sched_barrier(0);
+    load_codes(codes_b, min(q0 + 1, q1 - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    read_h(hb0, p_begin);
+    read_a(av, codes_a, p_begin, 0, T);
+
+    auto step = [&](auto kc, auto guarded, int i) {
+      constexpr int k = decltype(kc)::value;   // position in the round of two code blocks
+      constexpr bool checks = decltype(guarded)::value;
+      constexpr bool odd = k & 1;
+      constexpr bool block_end = (k & 7) == 7;
+      constexpr bool read_b = k >= 7 && k < 15;   // pair p + 1 lies in an odd block
+      bf16x8(&hc)[NT] = odd ? hb1 : hb0;
+      bf16x8(&hn)[NT] = odd ? hb0 : hb1;
+      uint32_t(&rd)[T] = read_b ? codes_b : codes_a;
+      uint32_t(&ld)[T] = k == 7 ? codes_a : codes_b;   // (used at a block's last pair only)
+      if (checks && i >= nsteps) return;
+      const int p = p_begin + i;
+      mfma(av, hc, 0, TH);
+      __builtin_amdgcn_sched_barrier(0);
+      const bool more = !checks || i + 1 < nsteps;
+      if (more) {
+        // vmcnt(n) with lgkmcnt(0): this wave's reads of slot p are complete
+        if constexpr ((k & 7) <= 1) __builtin_amdgcn_s_waitcnt(0x0070 | (kPair3Ops + NV));
+        else __builtin_amdgcn_s_waitcnt(0x0070 | kPair3Ops);
+        __builtin_amdgcn_s_barrier();
+        copy_pair(i % 3, min(p + 3, a.NP - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (block_end) {
+          arrange_codes(rd);
+          __builtin_amdgcn_sched_barrier(0);
+          load_codes(ld, min(((p + 1) >> 3) + 1, q1 - 1));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        read_h(hn, p + 1);
+        read_a(av, rd, p + 1, 0, TH);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (hs == 0) load_codes(nxt, min((p >> 3) + 1, q1 - 1));
+      mfma(av, hc, TH, T);
       __builtin_amdgcn_sched_barrier(0);
-      if (i + 2 < nsteps) copy_pair((R + 2) % 3, p + 2);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < T; ++j)
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-          acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[j], hb[t], acc[j][t], 0, 0, 0);
+      if (more) read_a(av, rd, p + 1, TH, T);
     };
-    for (int i = 0; i < nsteps; i += 3) {
-      step(std::integral_constant<int, 0>{}, i);
-      if (i + 1 < nsteps) step(std::integral_constant<int, 1>{}, i + 1);
-      if (i + 2 < nsteps) step(std::integral_constant<int, 2>{}, i + 2);
-    }
+    auto round = [&](auto guarded, int i0) {
+      step(std::integral_constant<int, 0>{}, guarded, i0 + 0);
+      step(std::integral_constant<int, 1>{}, guarded, i0 + 1);
+      step(std::integral_constant<int, 2>{}, guarded, i0 + 2);
+      step(std::integral_constant<int, 3>{}, guarded, i0 + 3);
+      step(std::integral_constant<int, 4>{}, guarded, i0 + 4);
+      step(std::integral_constant<int, 5>{}, guarded, i0 + 5);
+      step(std::integral_constant<int, 6>{}, guarded, i0 + 6);
+      step(std::integral_constant<int, 7>{}, guarded, i0 + 7);
+      step(std::integral_constant<int, 8>{}, guarded, i0 + 8);
+      step(std::integral_constant<int, 9>{}, guarded, i0 + 9);
+      step(std::integral_constant<int, 10>{}, guarded, i0 + 10);
+      step(std::integral_constant<int, 11>{}, guarded, i0 + 11);
+      step(std::integral_constant<int, 12>{}, guarded, i0 + 12);
+      step(std::integral_constant<int, 13>{}, guarded, i0 + 13);
+      step(std::integral_constant<int, 14>{}, guarded, i0 + 14);
+      step(std::integral_constant<int, 15>{}, guarded, i0 + 15);
+    };
+    int i0 = 0;
+    for (; i0 + 16 < nsteps; i0 += 16) round(std::false_type{}, i0);
+    round(std::true_type{}, i0);
+    RQ_WAIT_VMCNT(0);   // no copy into LDS may be in flight when the workgroup ends
   }
   mm_epilogue<NT, T>(a, acc, bt, g, s, tile0, tid);
 }
@@ -801,6 +880,16 @@ bool mm_supported(const rq_matrix* W) {
          ((uintptr_t)W->codebooks % 16) == 0;
 }
 
+// Bytes of the bf16 codebooks [NP][K][d].
+static size_t cb_bytes(const rq_matrix* W) { return (size_t)W->L * W->M * W->K * W->d * sizeof(uint16_t); }
+
+bool mm_usable(const rq_matrix* W, int B) {
+  if (B < RQ_MM_MIN_B || !mm_supported(W)) return false;
+  if (!mm_one_pair(W)) return true;
+  // the one-pair kernels address the codebooks and the split h with 32-bit buffer offsets
+  return cb_bytes(W) < ((size_t)1 << 32) && mm_hp_bytes(W, plan_mm(W, B)) < ((size_t)1 << 32);
+}
+
 // Three slots when a pair's codewords fit one (mm_pair3_kernel), else two.
 static bool pair3_fits(const rq_matrix* W) { return (int64_t)W->K * W->d / 8 <= kPair3CwWords; }
 
@@ -873,6 +962,8 @@ hipError_t launch_mm_logits(const rq_matrix* W, const MmPlan& p, const float* h,
   a.G = p.G;
   a.qpg = p.qpg;
   a.S = p.S;
+  a.cb_bytes = (uint32_t)std::min<size_t>(cb_bytes(W), 0xffffffffu);
+  a.hp_bytes = (uint32_t)std::min<size_t>(mm_hp_bytes(W, p), 0xffffffffu);
   hipEvent_t before, after;
   take_stage_events(&before, &after);
   if (before && (e = hipEventRecord(before, stream)) != hipSuccess) return e;

@@ -185,6 +185,9 @@ struct MmPlan {
   size_t lds;  // dynamic LDS bytes per workgroup
 };
 bool mm_supported(const rq_matrix* W);
+// The matrix-core method runs this matrix at batch B (B >= RQ_MM_MIN_B and mm_supported, plus the size
+// limits of its kernels).
+bool mm_usable(const rq_matrix* W, int B);
 MmPlan plan_mm(const rq_matrix* W, int B);
 size_t mm_hp_bytes(const rq_matrix* W, const MmPlan& p);
 // G > 1: partial sums [G][B][rows] (then launch_finish). G == 1: the logits
