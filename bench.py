@@ -34,6 +34,11 @@ METRIC = "LUT-logits vocab-rows/s at B=1/16 + achieved HBM GB/s vs peak (256000x
 HBM_PEAK_GBS = 8000.0
 
 
+def note(msg):
+    """A progress line on stderr (stdout carries only the result line)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -171,6 +176,7 @@ def main():
         torch.cuda.synchronize()
         out["copy_calibration_bytes"] = src.numel()
 
+    note(f"headline step done: {ms_step * 1e3:.1f} us")
     if not args.no_extras:
         out.update(extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, idt, dev, ms_step))
     del Ws, lut, ws
@@ -178,6 +184,7 @@ def main():
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(mat, h, cfg)
+        note("cpu baseline done")
     print(json.dumps(out))
 
 
@@ -260,6 +267,7 @@ def extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, idt, dev, ms_step_
     V = cfg.V
     roof = lds_roof(la, torch)
     res["lds_roof"] = roof
+    note("lds_roof done")
     # the same B=1 step (row decode on a second stream, table build, lookup+sum, softcap, argmax) on the
     # 10-bit code stream: 1024 bytes per row instead of 1536
     P10 = [la.to_device(mat, layout="packed10"), la.to_device(mat, layout="packed10")]
@@ -290,6 +298,7 @@ def extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, idt, dev, ms_step_
     res["b1_packed10"] = {"ms_per_step": t10, "vocab_rows_per_s": V / (t10 * 1e-3),
                           "gather_kernel_ms": tg10, "code_bytes": cb10,
                           "gather_gbs": (cb10 + formats.lut_bytes(1, cfg.L, cfg.M, cfg.K)) / (tg10 * 1e-3) / 1e9}
+    note("b1_packed10 done")
     del P10, lut10, lg10, ws10, rows10
 
     # batched heads, B=16 and B=128 (same matrix): rq_logits, which puts B >= 8 on the matrix cores
@@ -319,6 +328,7 @@ def extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, idt, dev, ms_step_
                         "code_stream_gbs": formats.code_bytes(V, cfg.L, cfg.M) / (tB * 1e-3) / 1e9,
                         "mfma_tflops": mfma_tflops if mm else None,
                         "mfma_frac_of_bf16_peak": mfma_tflops / 2500.0 if mm else None}
+        note(f"b{B} done")
         del lgB, amB, wsB
     # the two-call table form at B=16, for comparison
     h16 = hb[:16].contiguous()
@@ -336,6 +346,7 @@ def extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, idt, dev, ms_step_
     lds16 = V * cfg.L * cfg.M * 64
     res["b16_table"] = {"ms_per_call": t16, "vocab_rows_per_s": V / (t16 * 1e-3), "lds_bytes": lds16,
                         "lds_frac": lds16 / (t16 * 1e-3) / (roof["w16"]["tbs"] * 1e12)}
+    note("b16_table done")
     del lut16, lg16, ws16, hb
 
     # dense bf16 head on the same GPU: E = bf16(decode(all rows)), built by rq_decode_rows
@@ -354,6 +365,7 @@ def extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, idt, dev, ms_step_
         lut_ms = res[f"b{B}"]["ms_per_call"] if B > 1 else ms_step_b1
         dense[f"b{B}"]["lut_over_dense_time"] = lut_ms / tdB
     res["dense_bf16"] = dense
+    note("dense_bf16 done")
     del E, E2, Es, lgd, wsd, h128
 
     # one Gemma-2-2B MLP layer: the fused block (rq_lut_mlp), and the three rq_lut_matvec calls
@@ -385,6 +397,7 @@ def extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, idt, dev, ms_step_
                         "ms_three_matvec_calls": tm3, "code_bytes": code_b, "codebook_bytes": cb_b,
                         "gbs_codes_plus_codebooks": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
                         "ms_26_layers_est": 26 * tm}
+    note("mlp_layer done")
     del dl, wsm, wsf, g, u, y
     torch.cuda.empty_cache()
 
@@ -398,6 +411,7 @@ def extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, idt, dev, ms_step_
     gbs_p = (code_p + cb_b) / (tp * 1e-3) / 1e9
     res["mlp_layer_packed10"] = {"ms": tp, "code_bytes": code_p, "codebook_bytes": cb_b,
                                  "gbs_codes_plus_codebooks": gbs_p, "hbm_frac": gbs_p / HBM_PEAK_GBS}
+    note("mlp_layer_packed10 done")
     del dp, wsp, yp
     torch.cuda.empty_cache()
 
@@ -420,6 +434,7 @@ def extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, idt, dev, ms_step_
         "bits_per_param": formats.mlp_average_bpp(synth.MLP_HIDDEN, synth.MLP_INTER, synth.MLP_V2_D_SUB,
                                                   synth.MLP_V2_K_GATE_UP, synth.MLP_V2_K_DOWN, synth.MLP_L),
         "what": "d=8; gate/up K=1024 (10-bit codes), down K=256 (8-bit codes); fp32 codebooks; rq_lut_mlp"}
+    note("mlp_v2_layer done")
     del v2, dv2, wsv2, y2
     torch.cuda.empty_cache()
 
@@ -446,6 +461,7 @@ def extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, idt, dev, ms_step_
                      "mfma_tflops": tflops_s if mm1 else None,
                      "mfma_frac_of_bf16_peak": tflops_s / 2500.0 if mm1 else None,
                      "code_stream_gbs": formats.code_bytes(cs.V, cs.L, cs.M) / (ts1 * 1e-3) / 1e9}
+    note("stress done")
     del sws1
     slut = la.build_lut(SW, shd, lut_dtype="bf16")
     sws = la.workspace(la.lut_logits_workspace(SW, cs.B, cs.topk, "bf16"), dev)
@@ -460,6 +476,7 @@ def extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, idt, dev, ms_step_
     res["stress_table"] = {"ms_per_call": ts, "vocab_rows_per_s": cs.V / (ts * 1e-3), "lds_bytes": lds_s,
                            "lds_frac": lds_s / (ts * 1e-3) / (roof["w8"]["tbs"] * 1e12),
                            "method": "bf16 table: build + lookup+sum in batch tiles from a batch-tiled copy"}
+    note("stress_table done")
     del SW, slut, slg, sws, sam
     torch.cuda.empty_cache()
 
@@ -490,6 +507,7 @@ def extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, idt, dev, ms_step_
         "resident_bytes": sum(m.resident_bytes() for lay in layers for m in lay) + Ws[0].resident_bytes(),
         "distinct_tokens": int(torch.unique(loop.ids[:ntok + 1]).numel()),
         "what": "embedding row (x sqrt(D)) -> 26 RQ MLP blocks chained -> RQ head softcap+argmax; no attention"}
+    note("per_token_composite done")
     del loop, layers
     torch.cuda.empty_cache()
     return res
