@@ -414,8 +414,10 @@ __device__ __forceinline__ bf16x8 read_codeword(const unsigned char* seg, uint32
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// s_waitcnt with vmcnt(n) (n < 16) and the other counters left alone.
-#define RQ_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
+// s_waitcnt with vmcnt(n) (n < 64: bits 3:0 and 15:14 of the immediate) and the other counters left alone.
+#define RQ_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 0xF) | (((n) >> 4) << 14))
+// The same with lgkmcnt(0): this wave's LDS reads (and other LDS operations) are complete too.
+#define RQ_WAIT_VMCNT_LDS(n) __builtin_amdgcn_s_waitcnt(0x0070 | ((n) & 0xF) | (((n) >> 4) << 14))
 
 template <int DS, int NT, int T>
 __global__ __launch_bounds__(kMmThreads) void mm_pair_kernel(MmArgs a) {
@@ -758,9 +760,9 @@ __global__ __launch_bounds__(kMmThreads) void mm_pair3_kernel(MmArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       const bool more = !checks || i + 1 < nsteps;
       if (more) {
-        // vmcnt(n) with lgkmcnt(0): this wave's reads of slot p are complete
-        if constexpr ((k & 7) <= 1) __builtin_amdgcn_s_waitcnt(0x0070 | (kPair3Ops + NV));
-        else __builtin_amdgcn_s_waitcnt(0x0070 | kPair3Ops);
+        // with lgkmcnt(0): this wave's reads of slot p are complete
+        if constexpr ((k & 7) <= 1) RQ_WAIT_VMCNT_LDS(kPair3Ops + NV);
+        else RQ_WAIT_VMCNT_LDS(kPair3Ops);
         __builtin_amdgcn_s_barrier();
         copy_pair(i % 3, min(p + 3, a.NP - 1));
         __builtin_amdgcn_sched_barrier(0);
