@@ -806,6 +806,194 @@ __global__ __launch_bounds__(kMmThreads) void mm_pair3_kernel(MmArgs a) {
   mm_epilogue<NT, T>(a, acc, bt, g, s, tile0, tid);
 }
 
+// ---- All of 65..128 hidden vectors in one workgroup (eight column tiles),
+// 16-bit blocked codes, a half-block's codewords within 48 KB (K <= 1024 at
+// d = 6). With two batch tiles of 64 every slab of rows staged the codebook
+// twice; here one staging serves all 128 vectors. The half-block goes straight
+// into a two-slot LDS ring with buffer loads: the codewords as they lie in the
+// codebook (d bf16 each; their LDS reads are few beside 24 MFMAs per read, so
+// the 12-byte reads' bank conflicts do not matter) and the three h parts of
+// the four pairs for the 128 vectors. Per step the copy of the next
+// half-block is issued first and has the whole step (96 MFMAs per wave) to
+// land; the h fragments are read from LDS one column tile and part at a time,
+// the next one while the matrix cores work on the current one.
+constexpr int kWideNT = 8;
+constexpr int kWideTiles = 4;                                      // row tiles per wave (accumulators: 128 VGPRs)
+constexpr int kWideCwWords = 3072;                                 // 48 KB of codewords per slot
+constexpr int kWideHWords = kParts * 4 * 16 * kWideNT;             // 1536
+constexpr int kWideSlotBytes = (kWideCwWords + kWideHWords) * 16;  // 72 KB
+constexpr int kWideCwRounds = kWideCwWords / kMmThreads;           // 6
+constexpr int kWideHRounds = kWideHWords / kMmThreads;             // 3
+constexpr int kWideOps = kWideCwRounds + kWideHRounds;             // loads per copy, per thread
+static_assert(kWideHWords % kMmThreads == 0 && 4 * 16 * kWideNT == kMmThreads, "h: one part per copy round");
+
+template <int DS>
+__global__ __launch_bounds__(kMmThreads) void mm_wide_kernel(MmArgs a) {
+  constexpr int T = kWideTiles;
+  constexpr int NT = kWideNT;
+  constexpr int PPB = 8;
+  constexpr int NV = T / 4;   // wide code loads per block
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int K = a.K;
+  const int seg_words = K * DS / 8;   // host: 4 * seg_words <= kWideCwWords
+  const uint32_t seg_bytes = (uint32_t)seg_words * 16u;
+  const uint32_t kmax = (uint32_t)K - 1u;
+
+  const int g = blockIdx.x % a.G;     // one batch tile
+  const int s = blockIdx.x / a.G;
+  const int q0 = g * a.qpg;
+  const int q1 = min(a.NQ, q0 + a.qpg);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int i16 = lane & 15;
+  const int kg = lane >> 4;
+  const int64_t tile0 = (int64_t)s * (kMmWaves * T * 16) + (int64_t)wave * (T * 16);
+
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc((void*)a.codes, (short)0, (int)0xffffffffu,
+                                                                        0x00020000);
+  const uint32_t blk_bytes = (uint32_t)a.rows * 16u;
+  uint32_t voff[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int64_t r = min(tile0 + 16 * (4 * v + kg) + i16, a.rows - 1);
+    voff[v] = (uint32_t)r * 16u;
+  }
+  auto load_codes = [&](uint32_t (&dst)[T], int q) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const u32x4 w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(crs, voff[v], (uint32_t)q * blk_bytes, 0));
+      dst[4 * v + 0] = w[0]; dst[4 * v + 1] = w[1]; dst[4 * v + 2] = w[2]; dst[4 * v + 3] = w[3];
+    }
+  };
+  auto arrange_codes = [&](uint32_t (&c)[T]) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const auto x02 = __builtin_amdgcn_permlane32_swap(c[4 * v + 0], c[4 * v + 2], false, false);
+      const auto x13 = __builtin_amdgcn_permlane32_swap(c[4 * v + 1], c[4 * v + 3], false, false);
+      const auto y01 = __builtin_amdgcn_permlane16_swap(x02[0], x13[0], false, false);
+      const auto y23 = __builtin_amdgcn_permlane16_swap(x02[1], x13[1], false, false);
+      c[4 * v + 0] = y01[0]; c[4 * v + 1] = y01[1]; c[4 * v + 2] = y23[0]; c[4 * v + 3] = y23[1];
+    }
+  };
+
+  // Copy of half-block (q, hs) into slot R. Codewords: slot word w = rd * 512 +
+  // tid is word (w mod seg_words) of pair 8q + 2 (w div seg_words) + hs, the
+  // lane's offset past pair 8q + hs fixed per round. h: round rd copies part rd,
+  // slot word rd * 512 + tid = (part * 4 + kk) * 128 + n for kk = tid / 128,
+  // n = tid mod 128 (vectors past B are zero in the split h).
+  const __amdgpu_buffer_rsrc_t cbrs = __builtin_amdgcn_make_buffer_rsrc((void*)a.cb, (short)0, (int)a.cb_bytes,
+                                                                         0x00020000);
+  const __amdgpu_buffer_rsrc_t hprs = __builtin_amdgcn_make_buffer_rsrc((void*)a.hp, (short)0, (int)a.hp_bytes,
+                                                                         0x00020000);
+  uint32_t cw_voff[kWideCwRounds];
+#pragma unroll
+  for (int rd = 0; rd < kWideCwRounds; ++rd) {
+    const int w = min(rd * kMmThreads + tid, 4 * seg_words - 1);   // past four segments: a copy of the last word
+    const int kk = w / seg_words;
+    cw_voff[rd] = (uint32_t)(2 * kk) * seg_bytes + (uint32_t)(w - kk * seg_words) * 16u;
+  }
+  const int h_kk = tid / (16 * NT);
+  const int h_n = tid % (16 * NT);
+  auto copy_half = [&](int R, int q, int hs) {
+    unsigned char* sb = lds + R * kWideSlotBytes;
+    const uint32_t base = (uint32_t)(PPB * q + hs) * seg_bytes;
+#pragma unroll
+    for (int rd = 0; rd < kWideCwRounds; ++rd)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(cbrs, (lds_ptr_t)(sb + (size_t)(rd * kMmThreads + wave * 64) * 16), 16,
+                                               cw_voff[rd], base, 0, 0);
+    const int m = (PPB * q + 2 * h_kk + hs) % a.M;
+    const uint32_t hv = (uint32_t)((size_t)m * a.Bp + h_n) * 16u;
+#pragma unroll
+    for (int rd = 0; rd < kWideHRounds; ++rd)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          hprs, (lds_ptr_t)(sb + (size_t)(kWideCwWords + rd * kMmThreads + wave * 64) * 16), 16, hv,
+          (uint32_t)((size_t)rd * a.M * a.Bp * 16), 0, 0);
+  };
+
+  floatx4 acc[T][NT];
+#pragma unroll
+  for (int j = 0; j < T; ++j)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[j][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // One half-block from slot R: the row tiles' codewords, then for each column
+  // tile and part one h fragment (the next one read while these four MFMAs run).
+  auto compute = [&](int R, const uint32_t (&codes)[T], int hs) {
+    const unsigned char* sb = lds + R * kWideSlotBytes;
+    const unsigned char* seg = sb + (size_t)kg * seg_bytes;
+    bf16x8 av[T];
+#pragma unroll
+    for (int j = 0; j < T; ++j) av[j] = read_codeword<DS>(seg, min((codes[j] >> (16 * hs)) & 0xffffu, kmax));
+    const unsigned char* hbase = sb + (size_t)kWideCwWords * 16;
+    auto read_hb = [&](int t, int pr) {
+      return *reinterpret_cast<const bf16x8*>(hbase + (size_t)((pr * 4 + kg) * (16 * NT) + 16 * t + i16) * 16);
+    };
+    bf16x8 hb[2];
+    hb[0] = read_hb(0, 0);
+#pragma unroll
+    for (int i = 0; i < NT * kParts; ++i) {
+      const int t = i / kParts;
+      const int pr = i % kParts;
+      if (i + 1 < NT * kParts) hb[(i + 1) & 1] = read_hb((i + 1) / kParts, (i + 1) % kParts);
+#pragma unroll
+      for (int j = 0; j < T; ++j) acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[j], hb[i & 1], acc[j][t], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);   // one fragment read ahead, no more (registers)
+    }
+  };
+
+  const int nsteps = 2 * (q1 - q0);   // half-blocks: step st is block q0 + st / 2, sub-block st mod 2
+  if (nsteps > 0) {
+    // Step st (slot st mod 2): wait until its copy has landed (issued at the
+    // start of step st - 1; after it only the code loads of a block's first
+    // half); barrier (every wave is done with slot st + 1's previous
+    // contents); copy of step st + 1 into the other slot (clamped past the
+    // group's end so every step issues the same loads); at a block's first
+    // half, the codes of the next block; the half-block's MFMAs. Code buffers
+    // alternate by block (codes_a: even blocks of the group), so a round of
+    // four steps is unrolled and no loaded register is moved.
+    uint32_t codes_a[T], codes_b[T];
+    const int qlast = q1 - 1;
+    load_codes(codes_a, q0);
+    copy_half(0, q0, 0);
+    auto step = [&](auto kc, auto guarded, int st) {
+      constexpr int k = decltype(kc)::value;   // position in a round of two blocks
+      constexpr bool checks = decltype(guarded)::value;
+      constexpr int hs = k & 1;
+      uint32_t(&cur)[T] = k < 2 ? codes_a : codes_b;
+      uint32_t(&nxt)[T] = k < 2 ? codes_b : codes_a;
+      if (checks && st >= nsteps) return;
+      // (with lgkmcnt(0): this wave's reads of the slot the next copy overwrites are complete)
+      if constexpr (hs == 1) RQ_WAIT_VMCNT_LDS(NV);   // this step's copy; the next block's codes may still fly
+      else RQ_WAIT_VMCNT_LDS(0);                      // this step's copy and this block's codes
+      __builtin_amdgcn_s_barrier();
+      const int st1 = st + 1;
+      copy_half(st1 & 1, min(q0 + (st1 >> 1), qlast), st1 & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (hs == 0) {
+        arrange_codes(cur);
+        __builtin_amdgcn_sched_barrier(0);
+        load_codes(nxt, min(q0 + (st >> 1) + 1, qlast));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      compute(st & 1, cur, hs);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto round = [&](auto guarded, int s0) {
+      step(std::integral_constant<int, 0>{}, guarded, s0 + 0);
+      step(std::integral_constant<int, 1>{}, guarded, s0 + 1);
+      step(std::integral_constant<int, 2>{}, guarded, s0 + 2);
+      step(std::integral_constant<int, 3>{}, guarded, s0 + 3);
+    };
+    int s0 = 0;
+    for (; s0 + 4 <= nsteps; s0 += 4) round(std::false_type{}, s0);
+    round(std::true_type{}, s0);
+    RQ_WAIT_VMCNT(0);   // no copy into LDS may be in flight when the workgroup ends
+  }
+  mm_epilogue<NT, T>(a, acc, 0, g, s, tile0, tid);
+}
+
 // Row tiles per wave for NT column tiles: the accumulators (4*T*NT VGPRs), the
 // code registers (2*T) and the staged half-block share a wave's 256 VGPRs.
 // (Three sub-blocks per code block keep more values live: fewer tiles.) A
@@ -860,6 +1048,24 @@ hipError_t launch_pair_ds(const MmArgs& a, const MmPlan& p, hipStream_t stream) 
   return launch_pair_typed<DS, 4>(a, wgs, p.lds, stream);
 }
 
+template <int DS>
+hipError_t launch_wide_ds(const MmArgs& a, const MmPlan& p, hipStream_t stream) {
+  auto kern = mm_wide_kernel<DS>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(p.G * p.S)), dim3(kMmThreads), p.lds, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_wide(const MmArgs& a, const MmPlan& p, int d, hipStream_t stream) {
+  switch (d) {
+    case 2: return launch_wide_ds<2>(a, p, stream);
+    case 4: return launch_wide_ds<4>(a, p, stream);
+    case 6: return launch_wide_ds<6>(a, p, stream);
+    default: return launch_wide_ds<8>(a, p, stream);
+  }
+}
+
 hipError_t launch_pair(const MmArgs& a, const MmPlan& p, int d, hipStream_t stream) {
   switch (d) {
     case 2: return launch_pair_ds<2>(a, p, stream);
@@ -892,6 +1098,14 @@ bool mm_usable(const rq_matrix* W, int B) {
   return cb_bytes(W) < ((size_t)1 << 32) && mm_hp_bytes(W, plan_mm(W, B)) < ((size_t)1 << 32);
 }
 
+// 65..128 vectors on 16-bit blocked codes whose half-block of codewords fits 48 KB: mm_wide_kernel.
+static bool mm_wide(const rq_matrix* W, int B) {
+  return B > 4 * 16 && B <= 16 * kWideNT && !mm_one_pair(W) && W->codes_layout == RQ_CODES_BLOCKED &&
+         ((int64_t)W->K * W->d) % 8 == 0 && (int64_t)W->K * W->d / 2 <= kWideCwWords &&
+         ((uintptr_t)W->codebooks % 16) == 0 && cb_bytes(W) < ((size_t)1 << 32) &&
+         (size_t)kParts * W->M * 16 * kWideNT * 16 < ((size_t)1 << 32);
+}
+
 // Three slots when a pair's codewords fit one (mm_pair3_kernel), else two.
 static bool pair3_fits(const rq_matrix* W) { return (int64_t)W->K * W->d / 8 <= kPair3CwWords; }
 
@@ -904,8 +1118,11 @@ static size_t pair_slot_bytes(const rq_matrix* W) {
 
 MmPlan plan_mm(const rq_matrix* W, int B) {
   MmPlan p{};
-  p.NT = B <= 16 ? 1 : (B <= 32 ? 2 : 4);
-  p.T = mm_one_pair(W) ? pair_tiles_for(p.NT) : tiles_for(p.NT, W->codes_layout == RQ_CODES_PACKED10 ? 3 : 2);
+  const bool wide = mm_wide(W, B);
+  p.NT = wide ? kWideNT : (B <= 16 ? 1 : (B <= 32 ? 2 : 4));
+  p.T = wide             ? kWideTiles
+        : mm_one_pair(W) ? pair_tiles_for(p.NT)
+                         : tiles_for(p.NT, W->codes_layout == RQ_CODES_PACKED10 ? 3 : 2);
   p.NBT = (B + 16 * p.NT - 1) / (16 * p.NT);
   p.Bp = p.NBT * 16 * p.NT;
   const int64_t slab = (int64_t)kMmWaves * p.T * 16;
@@ -931,9 +1148,10 @@ MmPlan plan_mm(const rq_matrix* W, int B) {
   }
   p.qpg = (p.NQ + G - 1) / G;
   p.G = (p.NQ + p.qpg - 1) / p.qpg;
-  p.lds = !mm_one_pair(W)  ? (size_t)2 * (4 * (size_t)W->K + (size_t)kParts * 4 * 16 * p.NT) * 16
-          : pair3_fits(W) ? (size_t)3 * kPair3SlotBytes
-                          : 2 * pair_slot_bytes(W);
+  p.lds = wide              ? (size_t)2 * kWideSlotBytes
+          : !mm_one_pair(W) ? (size_t)2 * (4 * (size_t)W->K + (size_t)kParts * 4 * 16 * p.NT) * 16
+          : pair3_fits(W)   ? (size_t)3 * kPair3SlotBytes
+                            : 2 * pair_slot_bytes(W);
   return p;
 }
 
@@ -969,7 +1187,8 @@ hipError_t launch_mm_logits(const rq_matrix* W, const MmPlan& p, const float* h,
   hipEvent_t before, after;
   take_stage_events(&before, &after);
   if (before && (e = hipEventRecord(before, stream)) != hipSuccess) return e;
-  e = mm_one_pair(W)                            ? launch_pair(a, p, W->d, stream)
+  e = p.NT == kWideNT                           ? launch_wide(a, p, W->d, stream)
+      : mm_one_pair(W)                          ? launch_pair(a, p, W->d, stream)
       : W->codes_layout == RQ_CODES_PACKED10 ? launch_nsub<3>(a, p, W->d, stream)
                                              : launch_nsub<2>(a, p, W->d, stream);
   if (e != hipSuccess) return e;

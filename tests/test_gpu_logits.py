@@ -23,8 +23,14 @@ MM_EXACT = [
     (3000, 102, 17, 1000, 2, 33),   # odd M: the last code block is partly empty; K not a power of two; 33 of 64 columns
     (1500, 96, 48, 64, 2, 20),      # d=2
     (1200, 96, 24, 128, 3, 64),     # d=4, L=3, four column tiles
-    (700, 64, 8, 256, 1, 100),      # d=8, one code block, two batch tiles (64 + 36)
+    (700, 64, 8, 256, 1, 100),      # d=8, one code block; blocked: all 100 in one workgroup, packed10: 64 + 36
     (1, 6, 1, 1, 1, 16),            # one row, one codeword, one pair
+    # 65..128 vectors on blocked codes: eight column tiles in one workgroup, half-blocks loaded into LDS
+    (4097, 96, 16, 1024, 2, 128),   # d=6 at the largest K, ragged rows
+    (3000, 102, 17, 1000, 2, 65),   # odd M (the last block partly empty), K not a power of two, 65 of 128
+    (1500, 96, 48, 64, 2, 128),     # d=2
+    (1200, 96, 24, 128, 3, 96),     # d=4, L=3
+    (3, 6, 1, 2, 1, 128),           # three rows, one pair
 ]
 
 
