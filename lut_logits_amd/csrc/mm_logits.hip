@@ -64,13 +64,26 @@ struct MmArgs {
   int64_t rows;
   int K, M, NP, NQ, B, Bp, G, qpg, S;
   uint32_t cb_bytes, hp_bytes;   // byte ranges of cb and hp (the one-pair kernels' buffer loads; < 2^32)
+  const u32x4* cbp;       // mm_pad_kernel: the codebooks with each codeword padded to 16 bytes [NP][K], or null
+  uint32_t cbp_bytes;
 };
 
 // hp[part][m][n] = part `part` of h[n][m*d .. m*d+d), padded to 8 with zeros.
+// Threads past M*Bp, when cbp is set, copy the codebook with each codeword
+// padded to 16 bytes: cbp[i] = codeword i (d bf16, then zeros), i < n_cw.
 __global__ void split_h_kernel(const float* __restrict__ h, int B, int D, int M, int d, int Bp,
-                               u32x4* __restrict__ hp) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= M * Bp) return;
+                               u32x4* __restrict__ hp, const uint16_t* __restrict__ cb, int64_t n_cw,
+                               u32x4* __restrict__ cbp) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (int64_t)M * Bp) {
+    const int64_t i = t - (int64_t)M * Bp;
+    if (!cbp || i >= n_cw) return;
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(cb + i * d);   // d even: whole 4-byte words
+    u32x4 v = {0u, 0u, 0u, 0u};
+    for (int w = 0; w < d / 2; ++w) v[w] = src[w];
+    cbp[i] = v;
+    return;
+  }
   const int m = t / Bp;
   const int n = t - m * Bp;
   uint32_t w[kParts][4];
@@ -860,18 +873,19 @@ __global__ __launch_bounds__(kMmThreads) void mm_wide_kernel(MmArgs a) {
     const int64_t r = min(tile0 + 16 * (4 * v + kg) + i16, a.rows - 1);
     voff[v] = (uint32_t)r * 16u;
   }
-  auto load_codes = [&](uint32_t (&dst)[T], int q) {
+  // Codes stay in the registers they are loaded into (u32x4 per wide load):
+  // the arranged copy each block uses is a fresh value, so no loaded register
+  // is ever moved (a move right after a load made the compiler wait for it).
+  auto load_codes = [&](u32x4 (&dst)[NV], int q) {
 #pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      const u32x4 w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(crs, voff[v], (uint32_t)q * blk_bytes, 0));
-      dst[4 * v + 0] = w[0]; dst[4 * v + 1] = w[1]; dst[4 * v + 2] = w[2]; dst[4 * v + 3] = w[3];
-    }
+    for (int v = 0; v < NV; ++v)
+      dst[v] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(crs, voff[v], (uint32_t)q * blk_bytes, 0));
   };
-  auto arrange_codes = [&](uint32_t (&c)[T]) {
+  auto arranged = [&](const u32x4 (&raw)[NV], uint32_t (&c)[T]) {
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-      const auto x02 = __builtin_amdgcn_permlane32_swap(c[4 * v + 0], c[4 * v + 2], false, false);
-      const auto x13 = __builtin_amdgcn_permlane32_swap(c[4 * v + 1], c[4 * v + 3], false, false);
+      const auto x02 = __builtin_amdgcn_permlane32_swap(raw[v][0], raw[v][2], false, false);
+      const auto x13 = __builtin_amdgcn_permlane32_swap(raw[v][1], raw[v][3], false, false);
       const auto y01 = __builtin_amdgcn_permlane16_swap(x02[0], x13[0], false, false);
       const auto y23 = __builtin_amdgcn_permlane16_swap(x02[1], x13[1], false, false);
       c[4 * v + 0] = y01[0]; c[4 * v + 1] = y01[1]; c[4 * v + 2] = y23[0]; c[4 * v + 3] = y23[1];
@@ -953,16 +967,16 @@ __global__ __launch_bounds__(kMmThreads) void mm_wide_kernel(MmArgs a) {
     // half, the codes of the next block; the half-block's MFMAs. Code buffers
     // alternate by block (codes_a: even blocks of the group), so a round of
     // four steps is unrolled and no loaded register is moved.
-    uint32_t codes_a[T], codes_b[T];
+    u32x4 raw_a[NV], raw_b[NV];   // loaded codes of the group's even / odd blocks
     const int qlast = q1 - 1;
-    load_codes(codes_a, q0);
+    load_codes(raw_a, q0);
     copy_half(0, q0, 0);
-    auto step = [&](auto kc, auto guarded, int st) {
+    auto step = [&](auto kc, auto guarded, int st, uint32_t (&cur)[T]) {
       constexpr int k = decltype(kc)::value;   // position in a round of two blocks
       constexpr bool checks = decltype(guarded)::value;
       constexpr int hs = k & 1;
-      uint32_t(&cur)[T] = k < 2 ? codes_a : codes_b;
-      uint32_t(&nxt)[T] = k < 2 ? codes_b : codes_a;
+      u32x4(&raw)[NV] = k < 2 ? raw_a : raw_b;
+      u32x4(&nxt)[NV] = k < 2 ? raw_b : raw_a;
       if (checks && st >= nsteps) return;
       // (with lgkmcnt(0): this wave's reads of the slot the next copy overwrites are complete)
       if constexpr (hs == 1) RQ_WAIT_VMCNT_LDS(NV);   // this step's copy; the next block's codes may still fly
@@ -972,7 +986,7 @@ __global__ __launch_bounds__(kMmThreads) void mm_wide_kernel(MmArgs a) {
       copy_half(st1 & 1, min(q0 + (st1 >> 1), qlast), st1 & 1);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (hs == 0) {
-        arrange_codes(cur);
+        arranged(raw, cur);
         __builtin_amdgcn_sched_barrier(0);
         load_codes(nxt, min(q0 + (st >> 1) + 1, qlast));
       }
@@ -981,10 +995,11 @@ __global__ __launch_bounds__(kMmThreads) void mm_wide_kernel(MmArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     };
     auto round = [&](auto guarded, int s0) {
-      step(std::integral_constant<int, 0>{}, guarded, s0 + 0);
-      step(std::integral_constant<int, 1>{}, guarded, s0 + 1);
-      step(std::integral_constant<int, 2>{}, guarded, s0 + 2);
-      step(std::integral_constant<int, 3>{}, guarded, s0 + 3);
+      uint32_t cur_a[T], cur_b[T];   // arranged codes of this round's two blocks
+      step(std::integral_constant<int, 0>{}, guarded, s0 + 0, cur_a);
+      step(std::integral_constant<int, 1>{}, guarded, s0 + 1, cur_a);
+      step(std::integral_constant<int, 2>{}, guarded, s0 + 2, cur_b);
+      step(std::integral_constant<int, 3>{}, guarded, s0 + 3, cur_b);
     };
     int s0 = 0;
     for (; s0 + 4 <= nsteps; s0 += 4) round(std::false_type{}, s0);
@@ -992,6 +1007,186 @@ __global__ __launch_bounds__(kMmThreads) void mm_wide_kernel(MmArgs a) {
     RQ_WAIT_VMCNT(0);   // no copy into LDS may be in flight when the workgroup ends
   }
   mm_epilogue<NT, T>(a, acc, 0, g, s, tile0, tid);
+}
+
+// ---- Up to 16 vectors (one column tile), 16-bit blocked codes, K <= 1024:
+// mm_logits_kernel's half-blocks, loaded straight into LDS from a copy of the
+// codebooks with every codeword padded to 16 bytes (written by the split
+// kernel into the workspace each call). The padding keeps the conflict-light
+// 16-byte codeword reads of the register-staged kernel; the straight loads
+// drop its register copies and LDS stores. Two slots of 64 KB + 3 KB: per step
+// wait for this half-block's copy (issued at the start of the previous step),
+// barrier, issue the next one into the other slot, then the MFMAs with the
+// codewords of the next four row tiles read while the current four compute.
+constexpr int kPadTiles = 16;
+constexpr int kPadCwWords = 4 * kMmMaxK;                            // 64 KB of codewords per slot
+constexpr int kPadHWords = kParts * 4 * 16;                         // h parts of one column tile
+constexpr int kPadSlotBytes = (kPadCwWords + kPadHWords) * 16;
+constexpr int kPadCwRounds = kPadCwWords / kMmThreads;              // 8
+constexpr int kPadOps = kPadCwRounds + 1;                           // loads per copy, per thread
+static_assert(kPadHWords % 64 == 0 && kPadHWords <= kMmThreads, "one h load per lane");
+
+__global__ __launch_bounds__(kMmThreads) void mm_pad_kernel(MmArgs a) {
+  constexpr int T = kPadTiles;
+  constexpr int PPB = 8;
+  constexpr int NV = T / 4;
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int K = a.K;
+  const uint32_t kmax = (uint32_t)K - 1u;
+  const uint32_t seg_bytes = (uint32_t)K * 16u;
+
+  const int g = blockIdx.x % a.G;     // one batch tile
+  const int s = blockIdx.x / a.G;
+  const int q0 = g * a.qpg;
+  const int q1 = min(a.NQ, q0 + a.qpg);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int i16 = lane & 15;
+  const int kg = lane >> 4;
+  const int64_t tile0 = (int64_t)s * (kMmWaves * T * 16) + (int64_t)wave * (T * 16);
+
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc((void*)a.codes, (short)0, (int)0xffffffffu,
+                                                                        0x00020000);
+  const uint32_t blk_bytes = (uint32_t)a.rows * 16u;
+  uint32_t voff[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int64_t r = min(tile0 + 16 * (4 * v + kg) + i16, a.rows - 1);
+    voff[v] = (uint32_t)r * 16u;
+  }
+  // Codes stay in the registers they are loaded into (u32x4 per wide load):
+  // the arranged copy each block uses is a fresh value, so no loaded register
+  // is ever moved (a move right after a load made the compiler wait for it).
+  auto load_codes = [&](u32x4 (&dst)[NV], int q) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+      dst[v] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(crs, voff[v], (uint32_t)q * blk_bytes, 0));
+  };
+  auto arranged = [&](const u32x4 (&raw)[NV], uint32_t (&c)[T]) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const auto x02 = __builtin_amdgcn_permlane32_swap(raw[v][0], raw[v][2], false, false);
+      const auto x13 = __builtin_amdgcn_permlane32_swap(raw[v][1], raw[v][3], false, false);
+      const auto y01 = __builtin_amdgcn_permlane16_swap(x02[0], x13[0], false, false);
+      const auto y23 = __builtin_amdgcn_permlane16_swap(x02[1], x13[1], false, false);
+      c[4 * v + 0] = y01[0]; c[4 * v + 1] = y01[1]; c[4 * v + 2] = y23[0]; c[4 * v + 3] = y23[1];
+    }
+  };
+
+  // Copy of half-block (q, hs) into slot R. Codewords: slot word w = rd * 512 +
+  // tid is codeword (w mod K) of pair 8q + 2 (w div K) + hs (a dead pair past
+  // L*M reads zeros: the buffer's range check). h: slot word e = (part * 4 + kk)
+  // * 16 + n; every wave loads one 64-word run (waves past the third repeat
+  // the first runs: the same bytes to the same place).
+  const __amdgpu_buffer_rsrc_t cbrs = __builtin_amdgcn_make_buffer_rsrc((void*)a.cbp, (short)0, (int)a.cbp_bytes,
+                                                                         0x00020000);
+  const __amdgpu_buffer_rsrc_t hprs = __builtin_amdgcn_make_buffer_rsrc((void*)a.hp, (short)0, (int)a.hp_bytes,
+                                                                         0x00020000);
+  uint32_t cw_voff[kPadCwRounds];
+#pragma unroll
+  for (int rd = 0; rd < kPadCwRounds; ++rd) {
+    const int w = min(rd * kMmThreads + tid, 4 * K - 1);   // past four segments (K < 1024): a copy of the last word
+    const int kk = w / K;
+    cw_voff[rd] = (uint32_t)(2 * kk) * seg_bytes + (uint32_t)(w - kk * K) * 16u;
+  }
+  const int h_run = wave % (kPadHWords / 64);
+  const int h_e = h_run * 64 + lane;
+  const int h_part = h_e / 64;
+  const int h_kk = (h_e / 16) % 4;
+  const int h_n = h_e % 16;
+  auto copy_half = [&](int R, int q, int hs) {
+    unsigned char* sb = lds + R * kPadSlotBytes;
+    const uint32_t base = (uint32_t)(PPB * q + hs) * seg_bytes;
+#pragma unroll
+    for (int rd = 0; rd < kPadCwRounds; ++rd)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(cbrs, (lds_ptr_t)(sb + (size_t)(rd * kMmThreads + wave * 64) * 16), 16,
+                                               cw_voff[rd], base, 0, 0);
+    const int m = (PPB * q + 2 * h_kk + hs) % a.M;
+    const uint32_t hoff = (uint32_t)(((size_t)h_part * a.M + m) * a.Bp + h_n) * 16u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(hprs, (lds_ptr_t)(sb + (size_t)(kPadCwWords + h_run * 64) * 16), 16,
+                                             hoff, 0, 0, 0);
+  };
+
+  floatx4 acc[T];
+#pragma unroll
+  for (int j = 0; j < T; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int R, const uint32_t (&codes)[T], int hs) {
+    const unsigned char* sb = lds + R * kPadSlotBytes;
+    bf16x8 hb[kParts];
+#pragma unroll
+    for (int pr = 0; pr < kParts; ++pr)
+      hb[pr] = *reinterpret_cast<const bf16x8*>(sb + (size_t)(kPadCwWords + (pr * 4 + kg) * 16 + i16) * 16);
+    const unsigned char* cwb = sb + (size_t)kg * seg_bytes;
+    auto cw = [&](int j) {
+      return *reinterpret_cast<const bf16x8*>(cwb + min((codes[j] >> (16 * hs)) & 0xffffu, kmax) * 16u);
+    };
+    constexpr int kI = 4;   // row tiles whose codewords are read while the previous four compute
+    constexpr int kGroups = T / kI;
+    bf16x8 av[2][kI];
+#pragma unroll
+    for (int u = 0; u < kI; ++u) av[0][u] = cw(u);
+#pragma unroll
+    for (int gi = 0; gi < kGroups; ++gi) {
+      const int cur = gi & 1;
+      if (gi + 1 < kGroups) {
+#pragma unroll
+        for (int u = 0; u < kI; ++u) av[cur ^ 1][u] = cw((gi + 1) * kI + u);
+      }
+#pragma unroll
+      for (int pr = 0; pr < kParts; ++pr)
+#pragma unroll
+        for (int u = 0; u < kI; ++u)
+          acc[gi * kI + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[cur][u], hb[pr], acc[gi * kI + u], 0, 0, 0);
+    }
+  };
+
+  const int nsteps = 2 * (q1 - q0);
+  if (nsteps > 0) {
+    // The same step structure as mm_wide_kernel: after this step's copy come
+    // only the code loads of a block's first half (issued after the copy of
+    // the step that began the block).
+    u32x4 raw_a[NV], raw_b[NV];   // loaded codes of the group's even / odd blocks
+    const int qlast = q1 - 1;
+    load_codes(raw_a, q0);
+    copy_half(0, q0, 0);
+    auto step = [&](auto kc, auto guarded, int st, uint32_t (&cur)[T]) {
+      constexpr int k = decltype(kc)::value;
+      constexpr bool checks = decltype(guarded)::value;
+      constexpr int hs = k & 1;
+      u32x4(&raw)[NV] = k < 2 ? raw_a : raw_b;
+      u32x4(&nxt)[NV] = k < 2 ? raw_b : raw_a;
+      if (checks && st >= nsteps) return;
+      if constexpr (hs == 1) RQ_WAIT_VMCNT_LDS(NV);
+      else RQ_WAIT_VMCNT_LDS(0);
+      __builtin_amdgcn_s_barrier();
+      const int st1 = st + 1;
+      copy_half(st1 & 1, min(q0 + (st1 >> 1), qlast), st1 & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (hs == 0) {
+        arranged(raw, cur);
+        __builtin_amdgcn_sched_barrier(0);
+        load_codes(nxt, min(q0 + (st >> 1) + 1, qlast));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      compute(st & 1, cur, hs);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto round = [&](auto guarded, int s0) {
+      uint32_t cur_a[T], cur_b[T];   // arranged codes of this round's two blocks
+      step(std::integral_constant<int, 0>{}, guarded, s0 + 0, cur_a);
+      step(std::integral_constant<int, 1>{}, guarded, s0 + 1, cur_a);
+      step(std::integral_constant<int, 2>{}, guarded, s0 + 2, cur_b);
+      step(std::integral_constant<int, 3>{}, guarded, s0 + 3, cur_b);
+    };
+    int s0 = 0;
+    for (; s0 + 4 <= nsteps; s0 += 4) round(std::false_type{}, s0);
+    round(std::true_type{}, s0);
+    RQ_WAIT_VMCNT(0);
+  }
+  mm_epilogue<1, T>(a, reinterpret_cast<const floatx4(&)[T][1]>(acc), 0, g, s, tile0, tid);
 }
 
 // Row tiles per wave for NT column tiles: the accumulators (4*T*NT VGPRs), the
@@ -1048,6 +1243,13 @@ hipError_t launch_pair_ds(const MmArgs& a, const MmPlan& p, hipStream_t stream) 
   return launch_pair_typed<DS, 4>(a, wgs, p.lds, stream);
 }
 
+hipError_t launch_pad(const MmArgs& a, const MmPlan& p, hipStream_t stream) {
+  hipError_t e = hipFuncSetAttribute((const void*)mm_pad_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(mm_pad_kernel, dim3((unsigned)(p.G * p.S)), dim3(kMmThreads), p.lds, stream, a);
+  return hipGetLastError();
+}
+
 template <int DS>
 hipError_t launch_wide_ds(const MmArgs& a, const MmPlan& p, hipStream_t stream) {
   auto kern = mm_wide_kernel<DS>;
@@ -1098,6 +1300,12 @@ bool mm_usable(const rq_matrix* W, int B) {
   return cb_bytes(W) < ((size_t)1 << 32) && mm_hp_bytes(W, plan_mm(W, B)) < ((size_t)1 << 32);
 }
 
+// Up to 16 vectors on 16-bit blocked codes, K <= 1024: mm_pad_kernel.
+static bool mm_pad(const rq_matrix* W, int B) {
+  return B <= 16 && !mm_one_pair(W) && W->codes_layout == RQ_CODES_BLOCKED &&
+         (size_t)W->L * W->M * W->K * 16 < ((size_t)1 << 32);
+}
+
 // 65..128 vectors on 16-bit blocked codes whose half-block of codewords fits 48 KB: mm_wide_kernel.
 static bool mm_wide(const rq_matrix* W, int B) {
   return B > 4 * 16 && B <= 16 * kWideNT && !mm_one_pair(W) && W->codes_layout == RQ_CODES_BLOCKED &&
@@ -1119,8 +1327,10 @@ static size_t pair_slot_bytes(const rq_matrix* W) {
 MmPlan plan_mm(const rq_matrix* W, int B) {
   MmPlan p{};
   const bool wide = mm_wide(W, B);
+  p.pad = mm_pad(W, B) ? 1 : 0;
   p.NT = wide ? kWideNT : (B <= 16 ? 1 : (B <= 32 ? 2 : 4));
   p.T = wide             ? kWideTiles
+        : p.pad          ? kPadTiles
         : mm_one_pair(W) ? pair_tiles_for(p.NT)
                          : tiles_for(p.NT, W->codes_layout == RQ_CODES_PACKED10 ? 3 : 2);
   p.NBT = (B + 16 * p.NT - 1) / (16 * p.NT);
@@ -1149,19 +1359,28 @@ MmPlan plan_mm(const rq_matrix* W, int B) {
   p.qpg = (p.NQ + G - 1) / G;
   p.G = (p.NQ + p.qpg - 1) / p.qpg;
   p.lds = wide              ? (size_t)2 * kWideSlotBytes
+          : p.pad           ? (size_t)2 * kPadSlotBytes
           : !mm_one_pair(W) ? (size_t)2 * (4 * (size_t)W->K + (size_t)kParts * 4 * 16 * p.NT) * 16
           : pair3_fits(W)   ? (size_t)3 * kPair3SlotBytes
                             : 2 * pair_slot_bytes(W);
   return p;
 }
 
-size_t mm_hp_bytes(const rq_matrix* W, const MmPlan& p) { return (size_t)kParts * W->M * p.Bp * 16; }
+static size_t split_bytes(const rq_matrix* W, const MmPlan& p) { return (size_t)kParts * W->M * p.Bp * 16; }
+
+// The front of the workspace: the split h, then (mm_pad_kernel) the padded codebooks [NP][K] at 256 bytes.
+size_t mm_hp_bytes(const rq_matrix* W, const MmPlan& p) {
+  const size_t hp = split_bytes(W, p);
+  return p.pad ? (hp + 255) / 256 * 256 + (size_t)W->L * W->M * W->K * 16 : hp;
+}
 
 hipError_t launch_mm_logits(const rq_matrix* W, const MmPlan& p, const float* h, int B, void* hp, float* partial,
                             float* out, float softcap, uint64_t* block_keys, hipStream_t stream) {
-  const int n = W->M * p.Bp;
-  hipLaunchKernelGGL(split_h_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, h, B, W->D, W->M, W->d,
-                     p.Bp, static_cast<u32x4*>(hp));
+  const int64_t n = (int64_t)W->M * p.Bp;
+  const int64_t n_cw = p.pad ? (int64_t)W->L * W->M * W->K : 0;
+  u32x4* cbp = p.pad ? reinterpret_cast<u32x4*>(static_cast<char*>(hp) + (split_bytes(W, p) + 255) / 256 * 256) : nullptr;
+  hipLaunchKernelGGL(split_h_kernel, dim3((unsigned)((n + n_cw + 255) / 256)), dim3(256), 0, stream, h, B, W->D, W->M,
+                     W->d, p.Bp, static_cast<u32x4*>(hp), static_cast<const uint16_t*>(W->codebooks), n_cw, cbp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   MmArgs a;
@@ -1183,11 +1402,14 @@ hipError_t launch_mm_logits(const rq_matrix* W, const MmPlan& p, const float* h,
   a.qpg = p.qpg;
   a.S = p.S;
   a.cb_bytes = (uint32_t)std::min<size_t>(cb_bytes(W), 0xffffffffu);
-  a.hp_bytes = (uint32_t)std::min<size_t>(mm_hp_bytes(W, p), 0xffffffffu);
+  a.hp_bytes = (uint32_t)std::min<size_t>(split_bytes(W, p), 0xffffffffu);
+  a.cbp = cbp;
+  a.cbp_bytes = (uint32_t)std::min<size_t>((size_t)n_cw * 16, 0xffffffffu);
   hipEvent_t before, after;
   take_stage_events(&before, &after);
   if (before && (e = hipEventRecord(before, stream)) != hipSuccess) return e;
-  e = p.NT == kWideNT                           ? launch_wide(a, p, W->d, stream)
+  e = p.pad                                     ? launch_pad(a, p, stream)
+      : p.NT == kWideNT                         ? launch_wide(a, p, W->d, stream)
       : mm_one_pair(W)                          ? launch_pair(a, p, W->d, stream)
       : W->codes_layout == RQ_CODES_PACKED10 ? launch_nsub<3>(a, p, W->d, stream)
                                              : launch_nsub<2>(a, p, W->d, stream);

@@ -183,6 +183,7 @@ struct MmPlan {
   int G;       // groups of code blocks (partial sums per output)
   int qpg;     // code blocks per group
   size_t lds;  // dynamic LDS bytes per workgroup
+  int pad;     // 1: the codebooks are copied, codewords padded to 16 bytes, into the workspace after the split h
 };
 bool mm_supported(const rq_matrix* W);
 // The matrix-core method runs this matrix at batch B (B >= RQ_MM_MIN_B and mm_supported, plus the size
