@@ -628,27 +628,24 @@ __global__ __launch_bounds__(kMmThreads) void mm_pair3_kernel(MmArgs a) {
     const int64_t r = min(tile0 + 16 * (kWide ? 4 * v + kg : v) + i16, a.rows - 1);
     voff[v] = (uint32_t)r * 16u + (kWide ? 0u : (uint32_t)kg * 4u);
   }
-  auto load_codes = [&](uint32_t (&dst)[T], int q) {
+  // Codes stay in the registers they are loaded into (u32x4 per wide load);
+  // each block's arranged copy is a fresh value, so no loaded register is ever
+  // moved (a move right after a load made the compiler wait for it, and for
+  // the copy into LDS issued before it).
+  static_assert(kWide, "the one-pair kernels take row tiles in multiples of 4");
+  auto load_codes = [&](u32x4 (&dst)[NV], int q) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+      dst[v] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(crs, voff[v], (uint32_t)q * blk_bytes, 0));
+  };
+  auto arranged = [&](const u32x4 (&raw)[NV], uint32_t (&c)[T]) {
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-      if constexpr (kWide) {
-        const u32x4 w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(crs, voff[v], (uint32_t)q * blk_bytes, 0));
-        dst[4 * v + 0] = w[0]; dst[4 * v + 1] = w[1]; dst[4 * v + 2] = w[2]; dst[4 * v + 3] = w[3];
-      } else {
-        dst[v] = __builtin_amdgcn_raw_buffer_load_b32(crs, voff[v], (uint32_t)q * blk_bytes, 0);
-      }
-    }
-  };
-  auto arrange_codes = [&](uint32_t (&c)[T]) {
-    if constexpr (kWide) {
-#pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        const auto x02 = __builtin_amdgcn_permlane32_swap(c[4 * v + 0], c[4 * v + 2], false, false);
-        const auto x13 = __builtin_amdgcn_permlane32_swap(c[4 * v + 1], c[4 * v + 3], false, false);
-        const auto y01 = __builtin_amdgcn_permlane16_swap(x02[0], x13[0], false, false);
-        const auto y23 = __builtin_amdgcn_permlane16_swap(x02[1], x13[1], false, false);
-        c[4 * v + 0] = y01[0]; c[4 * v + 1] = y01[1]; c[4 * v + 2] = y23[0]; c[4 * v + 3] = y23[1];
-      }
+      const auto x02 = __builtin_amdgcn_permlane32_swap(raw[v][0], raw[v][2], false, false);
+      const auto x13 = __builtin_amdgcn_permlane32_swap(raw[v][1], raw[v][3], false, false);
+      const auto y01 = __builtin_amdgcn_permlane16_swap(x02[0], x13[0], false, false);
+      const auto y23 = __builtin_amdgcn_permlane16_swap(x02[1], x13[1], false, false);
+      c[4 * v + 0] = y01[0]; c[4 * v + 1] = y01[1]; c[4 * v + 2] = y23[0]; c[4 * v + 3] = y23[1];
     }
   };
 
@@ -741,18 +738,19 @@ __global__ __launch_bounds__(kMmThreads) void mm_pair3_kernel(MmArgs a) {
     // flight). Rounds whose 16 steps all have a next pair run unguarded; the
     // last round checks each step.
     constexpr int TH = T / 2;
-    uint32_t codes_a[T], codes_b[T];
+    u32x4 raw_a[NV], raw_b[NV];        // loaded codes of the group's even / odd blocks
+    uint32_t codes_a[T], codes_b[T];   // their arranged copies
     bf16x8 av[T];
     bf16x8 hb0[NT], hb1[NT];
-    load_codes(codes_a, q0);
+    load_codes(raw_a, q0);
     copy_pair(0, p_begin);
     copy_pair(1, min(p_begin + 1, a.NP - 1));
     copy_pair(2, min(p_begin + 2, a.NP - 1));
     RQ_WAIT_VMCNT(2 * kPair3Ops);
     __builtin_amdgcn_s_barrier();
-    arrange_codes(codes_a);
+    arranged(raw_a, codes_a);
     __builtin_amdgcn_sched_barrier(0);
-    load_codes(codes_b, min(q0 + 1, q1 - 1));
+    load_codes(raw_b, min(q0 + 1, q1 - 1));
     __builtin_amdgcn_sched_barrier(0);
     read_h(hb0, p_begin);
     read_a(av, codes_a, p_begin, 0, T);
@@ -766,7 +764,8 @@ __global__ __launch_bounds__(kMmThreads) void mm_pair3_kernel(MmArgs a) {
       bf16x8(&hc)[NT] = odd ? hb1 : hb0;
       bf16x8(&hn)[NT] = odd ? hb0 : hb1;
       uint32_t(&rd)[T] = read_b ? codes_b : codes_a;
-      uint32_t(&ld)[T] = k == 7 ? codes_a : codes_b;   // (used at a block's last pair only)
+      u32x4(&raw_rd)[NV] = read_b ? raw_b : raw_a;
+      u32x4(&ld)[NV] = k == 7 ? raw_a : raw_b;   // (used at a block's last pair only)
       if (checks && i >= nsteps) return;
       const int p = p_begin + i;
       mfma(av, hc, 0, TH);
@@ -780,7 +779,7 @@ __global__ __launch_bounds__(kMmThreads) void mm_pair3_kernel(MmArgs a) {
         copy_pair(i % 3, min(p + 3, a.NP - 1));
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (block_end) {
-          arrange_codes(rd);
+          arranged(raw_rd, rd);
           __builtin_amdgcn_sched_barrier(0);
           load_codes(ld, min(((p + 1) >> 3) + 1, q1 - 1));
         }
@@ -940,9 +939,10 @@ __global__ __launch_bounds__(kMmThreads) void mm_wide_kernel(MmArgs a) {
     bf16x8 av[T];
 #pragma unroll
     for (int j = 0; j < T; ++j) av[j] = read_codeword<DS>(seg, min((codes[j] >> (16 * hs)) & 0xffffu, kmax));
-    const unsigned char* hbase = sb + (size_t)kWideCwWords * 16;
+    // the lane's h fragment address in this slot, once; part and column tile are constant offsets
+    const unsigned char* hl = sb + (size_t)(kWideCwWords + kg * (16 * NT) + i16) * 16;
     auto read_hb = [&](int t, int pr) {
-      return *reinterpret_cast<const bf16x8*>(hbase + (size_t)((pr * 4 + kg) * (16 * NT) + 16 * t + i16) * 16);
+      return *reinterpret_cast<const bf16x8*>(hl + (size_t)(pr * 4 * (16 * NT) + 16 * t) * 16);
     };
     bf16x8 hb[2];
     hb[0] = read_hb(0, 0);
