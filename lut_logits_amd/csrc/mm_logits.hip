@@ -932,25 +932,31 @@ __global__ __launch_bounds__(kMmThreads) void mm_wide_kernel(MmArgs a) {
     for (int t = 0; t < NT; ++t) acc[j][t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   // One half-block from slot R: the row tiles' codewords, then for each column
-  // tile and part one h fragment (the next one read while these four MFMAs run).
-  auto compute = [&](int R, const uint32_t (&codes)[T], int hs) {
-    const unsigned char* sb = lds + R * kWideSlotBytes;
-    const unsigned char* seg = sb + (size_t)kg * seg_bytes;
-    bf16x8 av[T];
+  // tile and part one h fragment (the next one read while these four MFMAs
+  // run). The codewords and the first fragment are read first (begin_reads),
+  // before the step issues its copy and code loads, so their LDS latency runs
+  // under those issues.
+  bf16x8 av[T];
+  bf16x8 hb[2];
+  auto hl_of = [&](int R) {   // the lane's h fragment address in slot R; part and column tile are constant offsets
+    return lds + R * kWideSlotBytes + (size_t)(kWideCwWords + kg * (16 * NT) + i16) * 16;
+  };
+  auto read_hb = [&](const unsigned char* hl, int t, int pr) {
+    return *reinterpret_cast<const bf16x8*>(hl + (size_t)(pr * 4 * (16 * NT) + 16 * t) * 16);
+  };
+  auto begin_reads = [&](int R, const uint32_t (&codes)[T], int hs) {
+    const unsigned char* seg = lds + R * kWideSlotBytes + (size_t)kg * seg_bytes;
 #pragma unroll
     for (int j = 0; j < T; ++j) av[j] = read_codeword<DS>(seg, min((codes[j] >> (16 * hs)) & 0xffffu, kmax));
-    // the lane's h fragment address in this slot, once; part and column tile are constant offsets
-    const unsigned char* hl = sb + (size_t)(kWideCwWords + kg * (16 * NT) + i16) * 16;
-    auto read_hb = [&](int t, int pr) {
-      return *reinterpret_cast<const bf16x8*>(hl + (size_t)(pr * 4 * (16 * NT) + 16 * t) * 16);
-    };
-    bf16x8 hb[2];
-    hb[0] = read_hb(0, 0);
+    hb[0] = read_hb(hl_of(R), 0, 0);
+  };
+  auto compute = [&](int R) {
+    const unsigned char* hl = hl_of(R);
 #pragma unroll
     for (int i = 0; i < NT * kParts; ++i) {
       const int t = i / kParts;
       const int pr = i % kParts;
-      if (i + 1 < NT * kParts) hb[(i + 1) & 1] = read_hb((i + 1) / kParts, (i + 1) % kParts);
+      if (i + 1 < NT * kParts) hb[(i + 1) & 1] = read_hb(hl, (i + 1) / kParts, (i + 1) % kParts);
 #pragma unroll
       for (int j = 0; j < T; ++j) acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[j], hb[i & 1], acc[j][t], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);   // one fragment read ahead, no more (registers)
@@ -982,16 +988,15 @@ __global__ __launch_bounds__(kMmThreads) void mm_wide_kernel(MmArgs a) {
       if constexpr (hs == 1) RQ_WAIT_VMCNT_LDS(NV);   // this step's copy; the next block's codes may still fly
       else RQ_WAIT_VMCNT_LDS(0);                      // this step's copy and this block's codes
       __builtin_amdgcn_s_barrier();
+      if constexpr (hs == 0) arranged(raw, cur);
+      begin_reads(st & 1, cur, hs);
+      __builtin_amdgcn_sched_barrier(0);
       const int st1 = st + 1;
       copy_half(st1 & 1, min(q0 + (st1 >> 1), qlast), st1 & 1);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (hs == 0) {
-        arranged(raw, cur);
-        __builtin_amdgcn_sched_barrier(0);
-        load_codes(nxt, min(q0 + (st >> 1) + 1, qlast));
-      }
+      if constexpr (hs == 0) load_codes(nxt, min(q0 + (st >> 1) + 1, qlast));
       __builtin_amdgcn_sched_barrier(0);
-      compute(st & 1, cur, hs);
+      compute(st & 1);
       __builtin_amdgcn_sched_barrier(0);
     };
     auto round = [&](auto guarded, int s0) {
@@ -1018,16 +1023,15 @@ __global__ __launch_bounds__(kMmThreads) void mm_wide_kernel(MmArgs a) {
 // wait for this half-block's copy (issued at the start of the previous step),
 // barrier, issue the next one into the other slot, then the MFMAs with the
 // codewords of the next four row tiles read while the current four compute.
-// Sixteen waves of eight row tiles (four waves per SIMD, 110 VGPRs) cover the
-// same 2,048 rows per workgroup as eight waves of sixteen would, with more
-// waves to hide the LDS latency (4% faster at B=16, same-session A/B).
-constexpr int kPadThreads = 1024;                                 // 16 waves: 4 per SIMD
+// Eight waves of sixteen row tiles (2,048 rows per workgroup); sixteen waves of
+// eight measured 3% slower.
+constexpr int kPadThreads = 512;
 constexpr int kPadWaves = kPadThreads / 64;
-constexpr int kPadTiles = 2048 / 16 / kPadWaves;                    // row tiles per wave (8)
+constexpr int kPadTiles = 2048 / 16 / kPadWaves;                    // row tiles per wave (16)
 constexpr int kPadCwWords = 4 * kMmMaxK;                            // 64 KB of codewords per slot
 constexpr int kPadHWords = kParts * 4 * 16;                         // h parts of one column tile
 constexpr int kPadSlotBytes = (kPadCwWords + kPadHWords) * 16;
-constexpr int kPadCwRounds = kPadCwWords / kPadThreads;             // 4
+constexpr int kPadCwRounds = kPadCwWords / kPadThreads;             // 8
 constexpr int kPadOps = kPadCwRounds + 1;                           // loads per copy, per thread
 static_assert(kPadHWords % 64 == 0 && kPadHWords <= kPadThreads, "one h load per lane");
 
@@ -1118,27 +1122,33 @@ __global__ __launch_bounds__(kPadThreads) void mm_pad_kernel(MmArgs a) {
 #pragma unroll
   for (int j = 0; j < T; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int R, const uint32_t (&codes)[T], int hs) {
+  // The h fragments and the first four row tiles' codewords are read first
+  // (begin_reads), before the step issues its copy and code loads, so their LDS
+  // latency runs under those issues; then the codewords of the next four row
+  // tiles are read while the current four compute.
+  constexpr int kI = 4;
+  constexpr int kGroups = T / kI;
+  bf16x8 hb[kParts];
+  bf16x8 av[2][kI];
+  auto cw = [&](int R, const uint32_t (&codes)[T], int hs, int j) {
+    const unsigned char* cwb = lds + R * kPadSlotBytes + (size_t)kg * seg_bytes;
+    return *reinterpret_cast<const bf16x8*>(cwb + min((codes[j] >> (16 * hs)) & 0xffffu, kmax) * 16u);
+  };
+  auto begin_reads = [&](int R, const uint32_t (&codes)[T], int hs) {
     const unsigned char* sb = lds + R * kPadSlotBytes;
-    bf16x8 hb[kParts];
 #pragma unroll
     for (int pr = 0; pr < kParts; ++pr)
       hb[pr] = *reinterpret_cast<const bf16x8*>(sb + (size_t)(kPadCwWords + (pr * 4 + kg) * 16 + i16) * 16);
-    const unsigned char* cwb = sb + (size_t)kg * seg_bytes;
-    auto cw = [&](int j) {
-      return *reinterpret_cast<const bf16x8*>(cwb + min((codes[j] >> (16 * hs)) & 0xffffu, kmax) * 16u);
-    };
-    constexpr int kI = 4;   // row tiles whose codewords are read while the previous four compute
-    constexpr int kGroups = T / kI;
-    bf16x8 av[2][kI];
 #pragma unroll
-    for (int u = 0; u < kI; ++u) av[0][u] = cw(u);
+    for (int u = 0; u < kI; ++u) av[0][u] = cw(R, codes, hs, u);
+  };
+  auto compute = [&](int R, const uint32_t (&codes)[T], int hs) {
 #pragma unroll
     for (int gi = 0; gi < kGroups; ++gi) {
       const int cur = gi & 1;
       if (gi + 1 < kGroups) {
 #pragma unroll
-        for (int u = 0; u < kI; ++u) av[cur ^ 1][u] = cw((gi + 1) * kI + u);
+        for (int u = 0; u < kI; ++u) av[cur ^ 1][u] = cw(R, codes, hs, (gi + 1) * kI + u);
       }
 #pragma unroll
       for (int pr = 0; pr < kParts; ++pr)
@@ -1167,14 +1177,13 @@ __global__ __launch_bounds__(kPadThreads) void mm_pad_kernel(MmArgs a) {
       if constexpr (hs == 1) RQ_WAIT_VMCNT_LDS(NV);
       else RQ_WAIT_VMCNT_LDS(0);
       __builtin_amdgcn_s_barrier();
+      if constexpr (hs == 0) arranged(raw, cur);
+      begin_reads(st & 1, cur, hs);
+      __builtin_amdgcn_sched_barrier(0);
       const int st1 = st + 1;
       copy_half(st1 & 1, min(q0 + (st1 >> 1), qlast), st1 & 1);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (hs == 0) {
-        arranged(raw, cur);
-        __builtin_amdgcn_sched_barrier(0);
-        load_codes(nxt, min(q0 + (st >> 1) + 1, qlast));
-      }
+      if constexpr (hs == 0) load_codes(nxt, min(q0 + (st >> 1) + 1, qlast));
       __builtin_amdgcn_sched_barrier(0);
       compute(st & 1, cur, hs);
       __builtin_amdgcn_sched_barrier(0);
@@ -1340,7 +1349,7 @@ MmPlan plan_mm(const rq_matrix* W, int B) {
                          : tiles_for(p.NT, W->codes_layout == RQ_CODES_PACKED10 ? 3 : 2);
   p.NBT = (B + 16 * p.NT - 1) / (16 * p.NT);
   p.Bp = p.NBT * 16 * p.NT;
-  const int64_t slab = (int64_t)kMmWaves * p.T * 16;
+  const int64_t slab = (int64_t)(p.pad ? kPadWaves : kMmWaves) * p.T * 16;   // rows per workgroup
   p.S = (int)((W->rows + slab - 1) / slab);
   p.NQ = (W->L * W->M + pairs_per_block(W) - 1) / pairs_per_block(W);
   // Group count: workgroups run in rounds of one per CU; a round costs the
