@@ -349,24 +349,33 @@ def extras(args, la, synth, formats, torch, cfg, mat, Ws, ht, idt, dev, ms_step_
     note("b16_table done")
     del lut16, lg16, ws16, hb
 
-    # dense bf16 head on the same GPU: E = bf16(decode(all rows)), built by rq_decode_rows
+    # dense bf16 head on the same GPU: E = bf16(decode(all rows)), built by rq_decode_rows. Two
+    # comparators: this library's dense kernel (tiled E, with the softcap and argmax), and the
+    # vendor GEMM behind torch's linear (hipBLASLt, row-major E, logits only, no epilogue); the
+    # LUT is set against the faster of the two.
     E = la.decode_rows(Ws[0], torch.arange(V, dtype=torch.int32, device=dev), "bf16")
-    E2 = E.clone()
-    Es = [E, E2]
+    Es = [la.pack_dense(E), la.pack_dense(E)]   # the tiled layout the dense kernel reads (same bytes: no padding)
+    Eb = [E.view(torch.bfloat16), E.view(torch.bfloat16).clone()]
+    del E
     lgd = torch.empty((128, V), dtype=torch.float32, device=dev)
     wsd = la.workspace(la.dense_logits_workspace(V, 128), dev)
     h128 = torch.from_numpy(synth.gen_hidden(np.random.default_rng(c16.seed), 128, cfg.D)).to(dev)
     dense = {"resident_bytes": formats.dense_bytes(V, cfg.D)}
     for B, hB, n in ((1, ht, 50), (16, h16, 20), (128, h128, 10)):
         tdB = timed(lambda i=0: la.dense_logits(Es[i & 1], hB, 30.0, ws=wsd, out=lgd[:B]), n, torch)
+        hbf = hB.to(torch.bfloat16)
+        tlib = timed(lambda i=0: torch.nn.functional.linear(hbf, Eb[i & 1]), n, torch)
         gbs = formats.dense_bytes(V, cfg.D) / (tdB * 1e-3) / 1e9
         dense[f"b{B}"] = {"ms": tdB, "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
-                          "mfma_tflops": 2.0 * B * V * cfg.D / (tdB * 1e-3) / 1e12}
+                          "mfma_tflops": 2.0 * B * V * cfg.D / (tdB * 1e-3) / 1e12,
+                          "library_gemm_ms": tlib,
+                          "library_gemm_hbm_frac": formats.dense_bytes(V, cfg.D) / (tlib * 1e-3) / 1e9 / HBM_PEAK_GBS}
         lut_ms = res[f"b{B}"]["ms_per_call"] if B > 1 else ms_step_b1
         dense[f"b{B}"]["lut_over_dense_time"] = lut_ms / tdB
+        dense[f"b{B}"]["lut_over_best_dense_time"] = lut_ms / min(tdB, tlib)
     res["dense_bf16"] = dense
     note("dense_bf16 done")
-    del E, E2, Es, lgd, wsd, h128
+    del Es, Eb, lgd, wsd, h128
 
     # one Gemma-2-2B MLP layer: the fused block (rq_lut_mlp), and the three rq_lut_matvec calls
     # (gate, up, down with the gelu_tanh*up prologue) it replaces

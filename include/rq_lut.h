@@ -330,19 +330,33 @@ rq_status rq_lut_mlp(const rq_matrix* gate, const rq_matrix* up, const rq_matrix
 
 /*
  * Comparison baseline: the standard dense path with the head stored as a
- * dense bf16 matrix E[rows][D] (row-major), as deployed before LUT serving
+ * dense bf16 matrix E[rows][D], as deployed before LUT serving
  * (runtime-compression page, variant table "Uncompressed" row):
  *     logits[b][r] = softcap(sum_i E[r][i] * bf16(h[b][i])) in fp32, plus argmax
  * (a GEMV at B=1, a GEMM on the matrix cores for larger batches).
+ *
+ * The matrix is held tiled: Et = [ceil(rows/16)][ceil(D/32)][16][32] bf16,
+ * zero past rows and D, so each 16-row x 32-column tile is one contiguous
+ * 1 KB block (one wave-wide load of the matrix-core operand).
+ * rq_dense_tiled_bytes gives its size (0 when rows <= 0 or D is out of range);
+ * rq_pack_dense writes it, stream-ordered, from row-major E:
  *   E       device bf16 bit patterns [rows][D], 16-byte aligned, D % 8 == 0,
- *           8 <= D <= 4096
+ *           8 <= D <= 4096; rows < 2^31
+ *   Et      device, 16-byte aligned, rq_dense_tiled_bytes(rows, D) bytes,
+ *           not overlapping E
+ * rq_dense_logits:
+ *   Et      the tiled matrix of rows x D written by rq_pack_dense
  *   h       device fp32 [B][D], 0 <= B <= 128
  *   logits  device fp32 [B][rows] (required); argmax device int32 [B] or NULL
  *   ws      device workspace of at least rq_dense_logits_workspace() bytes
  *           (the bf16 copy of h and the per-block selection keys)
+ * Shapes out of range return RQ_ERR_SHAPE, NULL buffers RQ_ERR_NULL,
+ * misaligned ones RQ_ERR_ALIGN, a short workspace RQ_ERR_WORKSPACE.
  */
+size_t rq_dense_tiled_bytes(int64_t rows, int32_t D);
+rq_status rq_pack_dense(const uint16_t* E, int64_t rows, int32_t D, uint16_t* Et, hipStream_t stream);
 size_t rq_dense_logits_workspace(int64_t rows, int32_t B);
-rq_status rq_dense_logits(const uint16_t* E, int64_t rows, int32_t D, const float* h, int32_t B,
+rq_status rq_dense_logits(const uint16_t* Et, int64_t rows, int32_t D, const float* h, int32_t B,
                           float softcap, float* logits, int32_t* argmax, void* ws, size_t ws_bytes,
                           hipStream_t stream);
 

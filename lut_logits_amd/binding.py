@@ -27,7 +27,7 @@ RQ_METHOD_TABLE, RQ_METHOD_MATRIX_CORES = 0, 1
 EXPORTS = ("rq_blocked_codes_bytes", "rq_pack_codes", "rq_packed10_codes_bytes", "rq_pack_codes10",
            "rq_packed8_codes_bytes", "rq_pack_codes8", "rq_lut_bytes", "rq_build_lut", "rq_lut_logits_workspace",
            "rq_lut_logits", "rq_lut_logits_static", "rq_logits_method", "rq_logits_workspace", "rq_logits", "rq_decode_rows", "rq_lut_matvec_workspace", "rq_lut_matvec",
-           "rq_lut_mlp_workspace", "rq_lut_mlp", "rq_dense_logits_workspace", "rq_dense_logits", "rq_stream_read_configs",
+           "rq_lut_mlp_workspace", "rq_lut_mlp", "rq_dense_tiled_bytes", "rq_pack_dense", "rq_dense_logits_workspace", "rq_dense_logits", "rq_stream_read_configs",
            "rq_stream_read_sink_words", "rq_stream_read", "rq_lds_gather_sink_words", "rq_lds_gather",
            "rq_set_stage_events", "rq_lut_logits_plan", "rq_status_string",
            "rq_last_error", "rq_version")
@@ -77,6 +77,8 @@ def lib():
             "rq_lut_matvec": (_i32, [_MP, _vp, _vp, _i32, _i32, _vp, _vp, _sz, _vp]),
             "rq_lut_mlp_workspace": (_sz, [_MP, _MP, _MP, _i32]),
             "rq_lut_mlp": (_i32, [_MP, _MP, _MP, _vp, _i32, _vp, _vp, _sz, _vp]),
+            "rq_dense_tiled_bytes": (_sz, [_i64, _i32]),
+            "rq_pack_dense": (_i32, [_vp, _i64, _i32, _vp, _vp]),
             "rq_dense_logits_workspace": (_sz, [_i64, _i32]),
             "rq_dense_logits": (_i32, [_vp, _i64, _i32, _vp, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
             "rq_stream_read_configs": (_i32, []),
@@ -406,24 +408,55 @@ def lds_gather(width, reps, sink=None):
     return sink
 
 
-def dense_logits_workspace(rows, B):
-    return lib().rq_dense_logits_workspace(rows, B)
+class DenseHead:
+    """A dense bf16 matrix E[rows][D] in the tiled layout rq_dense_logits reads
+    ([ceil(rows/16)][ceil(D/32)][16][32] bf16, zero padded), made by pack_dense."""
+
+    def __init__(self, tiles, rows, D):
+        self.tiles, self.rows, self.D = tiles, rows, D
+
+    @property
+    def nbytes(self):
+        return self.tiles.numel() * self.tiles.element_size()
 
 
-def dense_logits(E, h, softcap=30.0, argmax=True, ws=None, out=None):
-    """rq_dense_logits: the dense bf16 comparison head; E is [rows][D] bf16 bits (int16 tensor)."""
+def dense_tiled_bytes(rows, D):
+    return lib().rq_dense_tiled_bytes(rows, D)
+
+
+def pack_dense(E):
+    """rq_pack_dense: the tiled copy of E ([rows][D] bf16 bits, int16 tensor on the GPU)."""
     if E.dim() != 2:
         raise ValueError("E: expected [rows][D] bf16 bits")
     rows, D = E.shape
     _arg(E, "E", torch.int16, shape=(rows, D))
+    nb = dense_tiled_bytes(rows, D)
+    if nb == 0:
+        raise RQError(RQ_ERR_SHAPE, f"dense matrix {rows} x {D} out of range")
+    Et = torch.empty(nb // 2, dtype=torch.int16, device=E.device)
+    _gpu(E=E, Et=Et)
+    check(lib().rq_pack_dense(_ptr(E), rows, D, _ptr(Et), _stream()))
+    return DenseHead(Et, rows, D)
+
+
+def dense_logits_workspace(rows, B):
+    return lib().rq_dense_logits_workspace(rows, B)
+
+
+def dense_logits(head, h, softcap=30.0, argmax=True, ws=None, out=None):
+    """rq_dense_logits: the dense bf16 comparison head (a DenseHead from pack_dense)."""
+    if not isinstance(head, DenseHead):
+        raise TypeError("dense_logits takes the DenseHead that pack_dense returns")
+    rows, D = head.rows, head.D
+    _arg(head.tiles, "head.tiles", torch.int16, numel=dense_tiled_bytes(rows, D) // 2)
     B = h.shape[0] if h.dim() == 2 else -1
     _arg(h, "h", torch.float32, shape=(B, D))
     lg = out if out is not None else torch.empty((B, rows), dtype=torch.float32, device=h.device)
     _arg(lg, "out", torch.float32, numel=B * rows)
     am = torch.empty(B, dtype=torch.int32, device=h.device) if argmax else None
     ws = _ws(ws, dense_logits_workspace(rows, B), h.device)
-    _gpu(E=E, h=h, out=lg, ws=ws)
-    check(lib().rq_dense_logits(_ptr(E), rows, D, _ptr(h), B, softcap, _ptr(lg), _ptr(am), _ptr(ws),
+    _gpu(Et=head.tiles, h=h, out=lg, ws=ws)
+    check(lib().rq_dense_logits(_ptr(head.tiles), rows, D, _ptr(h), B, softcap, _ptr(lg), _ptr(am), _ptr(ws),
                                 ws.numel() if ws is not None else 0, _stream()))
     return lg, am
 

@@ -586,6 +586,21 @@ size_t rq_dense_logits_workspace(int64_t rows, int32_t B) {
   return round_up(rq::dense_hb_bytes(4096, B), 256) + round_up((size_t)B * rq::dense_blocks(rows) * sizeof(uint64_t), 256);
 }
 
+size_t rq_dense_tiled_bytes(int64_t rows, int32_t D) {
+  if (rows <= 0 || rows >= ((int64_t)1 << 31) || D < 8 || D % 8 != 0 || D > 4096) return 0;
+  return rq::dense_tiled_bytes(rows, D);
+}
+
+rq_status rq_pack_dense(const uint16_t* E, int64_t rows, int32_t D, uint16_t* Et, hipStream_t stream) {
+  CallRange range(__func__);
+  if (rows < 0 || rows >= ((int64_t)1 << 31)) return fail(RQ_ERR_SHAPE, "rows out of range");
+  if (D < 8 || D % 8 != 0 || D > 4096) return fail(RQ_ERR_SHAPE, "dense head needs D %% 8 == 0 and 8 <= D <= 4096");
+  if (rows == 0) return RQ_OK;
+  if (!E || !Et) return fail(RQ_ERR_NULL, "pack_dense: NULL buffer");
+  if (!aligned(E, 16) || !aligned(Et, 16)) return fail(RQ_ERR_ALIGN, "pack_dense: buffers must be 16-byte aligned");
+  return launched(rq::launch_pack_dense(E, rows, D, Et, stream), "rq_pack_dense");
+}
+
 rq_status rq_dense_logits(const uint16_t* E, int64_t rows, int32_t D, const float* h, int32_t B, float softcap,
                           float* logits, int32_t* argmax, void* ws, size_t ws_bytes, hipStream_t stream) {
   CallRange range(__func__);

@@ -836,7 +836,6 @@ constexpr int kWideHWords = kParts * 4 * 16 * kWideNT;             // 1536
 constexpr int kWideSlotBytes = (kWideCwWords + kWideHWords) * 16;  // 72 KB
 constexpr int kWideCwRounds = kWideCwWords / kMmThreads;           // 6
 constexpr int kWideHRounds = kWideHWords / kMmThreads;             // 3
-constexpr int kWideOps = kWideCwRounds + kWideHRounds;             // loads per copy, per thread
 static_assert(kWideHWords % kMmThreads == 0 && 4 * 16 * kWideNT == kMmThreads, "h: one part per copy round");
 
 template <int DS>
@@ -955,7 +954,6 @@ __global__ __launch_bounds__(kMmThreads) void mm_wide_kernel(MmArgs a) {
 #pragma unroll
     for (int i = 0; i < NT * kParts; ++i) {
       const int t = i / kParts;
-      const int pr = i % kParts;
       if (i + 1 < NT * kParts) hb[(i + 1) & 1] = read_hb(hl, (i + 1) / kParts, (i + 1) % kParts);
 #pragma unroll
       for (int j = 0; j < T; ++j) acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[j], hb[i & 1], acc[j][t], 0, 0, 0);
@@ -1032,7 +1030,6 @@ constexpr int kPadCwWords = 4 * kMmMaxK;                            // 64 KB of 
 constexpr int kPadHWords = kParts * 4 * 16;                         // h parts of one column tile
 constexpr int kPadSlotBytes = (kPadCwWords + kPadHWords) * 16;
 constexpr int kPadCwRounds = kPadCwWords / kPadThreads;             // 8
-constexpr int kPadOps = kPadCwRounds + 1;                           // loads per copy, per thread
 static_assert(kPadHWords % 64 == 0 && kPadHWords <= kPadThreads, "one h load per lane");
 
 __global__ __launch_bounds__(kPadThreads) void mm_pad_kernel(MmArgs a) {

@@ -215,7 +215,10 @@ hipError_t launch_pack_codes8(const uint16_t* src, int64_t rows, int NP, uint16_
 // Dense comparator: hb is a bf16 copy of h padded to whole 16-vector tiles
 // (dense_hb_bytes), written first by the same call.
 size_t dense_hb_bytes(int D, int B);
-hipError_t launch_dense_logits(const uint16_t* E, int64_t rows, int D, const float* h, int B, float softcap,
+// Et is E[rows][D] tiled as [ceil(rows/16)][ceil(D/32)][16][32] bf16 (dense_tiled_bytes, written by launch_pack_dense).
+size_t dense_tiled_bytes(int64_t rows, int D);
+hipError_t launch_pack_dense(const uint16_t* E, int64_t rows, int D, uint16_t* Et, hipStream_t stream);
+hipError_t launch_dense_logits(const uint16_t* Et, int64_t rows, int D, const float* h, int B, float softcap,
                                float* logits, uint64_t* block_keys, uint16_t* hb, hipStream_t stream);
 
 constexpr int kEpiRowsPerBlock = 1024;   // rows per epilogue workgroup

@@ -109,6 +109,12 @@ def test_workspace_queries():
     assert lib.rq_lut_matvec_workspace(ctypes.byref(Wm), 2) >= 2 * 1152 * 1024 * 4 * 2
     assert lib.rq_dense_logits_workspace(256000, 1) > 0
     assert lib.rq_dense_logits_workspace(256000, 129) == 0
+    # tiled dense matrix: 16-row x 32-column tiles of 1 KB, rows and D padded up
+    assert lib.rq_dense_tiled_bytes(256000, 2304) == 256000 * 2304 * 2
+    assert lib.rq_dense_tiled_bytes(17, 40) == 2 * 2 * 1024
+    assert lib.rq_dense_tiled_bytes(0, 2304) == 0
+    assert lib.rq_dense_tiled_bytes(16, 2300) == 0
+    assert lib.rq_dense_tiled_bytes(16, 4104) == 0
 
 
 def test_other_entry_points_reject():
@@ -138,6 +144,11 @@ def test_other_entry_points_reject():
     assert lib.rq_pack_codes10(0x1000, 10, 0, 3, 0x1000, None) == B.RQ_ERR_SHAPE
     assert lib.rq_pack_codes10(0x1000, 10, 2, 3, 0x1008, None) == B.RQ_ERR_ALIGN
     assert lib.rq_pack_codes10(None, 0, 2, 3, None, None) == B.RQ_OK
+    assert lib.rq_pack_dense(None, 100, 2304, 0x1000, None) == B.RQ_ERR_NULL
+    assert lib.rq_pack_dense(0x1000, 100, 2300, 0x2000, None) == B.RQ_ERR_SHAPE
+    assert lib.rq_pack_dense(0x1000, -1, 2304, 0x2000, None) == B.RQ_ERR_SHAPE
+    assert lib.rq_pack_dense(0x1008, 100, 2304, 0x2000, None) == B.RQ_ERR_ALIGN
+    assert lib.rq_pack_dense(None, 0, 2304, None, None) == B.RQ_OK
     assert lib.rq_dense_logits(0x1000, 100, 2300, 0x2000, 1, 30.0, 0x3000, None, None, 0, None) == B.RQ_ERR_SHAPE
     assert lib.rq_dense_logits(0x1000, 100, 2304, 0x2000, 129, 30.0, 0x3000, None, None, 0, None) == B.RQ_ERR_SHAPE
     assert lib.rq_dense_logits(0x1000, 100, 2304, 0x2000, 1, 30.0, 0x3000, 0x4000, None, 0, None) == B.RQ_ERR_WORKSPACE

@@ -106,7 +106,7 @@ def test_matvec_and_mlp_workspace_guard():
 def test_dense_workspace_guard(B):
     mat, rng = _mat(360 + B, 3000, 96, 16, 256, 2, "bf16")
     W = to_dev(mat)
-    E = la.decode_rows(W, torch.arange(3000, dtype=torch.int32, device="cuda"), "bf16")
+    E = la.pack_dense(la.decode_rows(W, torch.arange(3000, dtype=torch.int32, device="cuda"), "bf16"))
     h = dev(synth.gen_hidden(rng, B, 96))
     need = la.dense_logits_workspace(3000, B)
     buf, ws = guarded(need)

@@ -423,17 +423,35 @@ def test_mlp_layer_gemma_shapes():
 
 # ------------------------------------------------------------------ dense comparison head
 
-@pytest.mark.parametrize("B,D", [(1, 96), (3, 96), (16, 96), (17, 96), (40, 200), (128, 96), (128, 600)])
-def test_dense_comparator(B, D):
+@pytest.mark.parametrize("rows,D", [(1, 8), (16, 32), (33, 40), (300, 2304), (1001, 104)])
+def test_pack_dense_layout(rows, D):
+    """rq_pack_dense: Et[tile][kstep][i][j] = E[16 tile + i][32 kstep + j], zero past rows and D, byte-exact
+    against the layout written out in numpy (row and column counts that are and are not whole tiles)."""
+    rng = np.random.default_rng(rows * 7 + D)
+    E = rng.integers(-32768, 32768, size=(rows, D), dtype=np.int64).astype(np.int16)
+    head = la.pack_dense(dev(E))
+    nt, ks = (rows + 15) // 16, (D + 31) // 32
+    P = np.zeros((nt * 16, ks * 32), np.int16)
+    P[:rows, :D] = E
+    want = P.reshape(nt, 16, ks, 32).transpose(0, 2, 1, 3).reshape(-1)
+    assert head.nbytes == la.dense_tiled_bytes(rows, D) == want.size * 2
+    assert np.array_equal(host(head.tiles), want)
+
+
+@pytest.mark.parametrize("B,D,rows", [(1, 96, 5000), (3, 96, 5000), (16, 96, 5000), (17, 96, 5000), (40, 200, 5000),
+                                      (128, 96, 5000), (128, 600, 5000), (5, 200, 4993), (70, 104, 1001),
+                                      (2, 2304, 300)])
+def test_dense_comparator(B, D, rows):
     """The dense bf16 head (GEMV at B=1, matrix-core GEMM up to B=128, with h staged in chunks of columns for
-    B > 16) against an fp64 numpy product of the same bf16 values, over 5000 rows (a ragged last block of
-    256): every logit, the softcap, and the argmax as the first maximum of the GPU's own logits."""
+    B > 16) against an fp64 numpy product of the same bf16 values: every logit, the softcap, and the argmax as
+    the first maximum of the GPU's own logits. Ragged cases: a last block of 256 rows cut short (5000), a last
+    tile of 16 rows cut short (4993, 1001), D not a multiple of 32 (200, 104: zero-padded k-steps)."""
     M = D // 6 if D % 6 == 0 else D // 8
-    mat, rng = _rand(110 + B, 5000, D, M, 256, 2, "bf16")
+    mat, rng = _rand(110 + B + rows, rows, D, M, 256, 2, "bf16")
     h = synth.gen_hidden(rng, B, D)
     W = to_dev(mat)
-    E = la.decode_rows(W, torch.arange(5000, dtype=torch.int32, device="cuda"), "bf16")
-    lg, am = la.dense_logits(E, dev(h), softcap=30.0)
+    E = la.decode_rows(W, torch.arange(rows, dtype=torch.int32, device="cuda"), "bf16")
+    lg, am = la.dense_logits(la.pack_dense(E), dev(h), softcap=30.0)
     Ef = synth.bf16_bits_to_f32(host(E).view(np.uint16)).astype(np.float64)
     hb = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(h)).astype(np.float64)
     ref = 30.0 * np.tanh((hb @ Ef.T) / 30.0)
