@@ -276,12 +276,15 @@ __device__ __forceinline__ void regs_to_lds(const ChunkRegs<RS>& r, u32x4* dst, 
 // sums of every set stay in registers), so a slab of RSET times the rows
 // stages each chunk once: with several batch tiles the table restaging, not
 // the code stream, bounds the pass.
-template <typename LutT, int BT, int NSTEP, bool REG, int FD = 0, int CB = 16, int RSET = 1>
+// PIPE (fused build with FD = 2, one code block per chunk, K <= 1024): see the
+// pipelined loop below.
+template <typename LutT, int BT, int NSTEP, bool REG, int FD = 0, int CB = 16, int RSET = 1, bool PIPE = false>
 __global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(1, 4)))
 void gather_kernel(GatherArgs a) {
   constexpr int PPB = CB == 10 ? 12 : (CB == 8 ? 16 : 8);   // pairs per code block
   static_assert(FD == 0 || (BT == 1 && REG && sizeof(LutT) == 4 && (4 % FD == 0 || FD == 8)),
                 "fused build: fp32, B=1, FD in {1, 2, 4, 8}");
+  static_assert(!PIPE || (FD == 2 && RSET == 1 && CB != 8), "pipelined fused build: d = 2, 16- or 10-bit codes");
   constexpr int QL = (BT >= 16) ? 4 : 1;   // lanes per row
   constexpr int BQ = BT / QL;              // batch entries per lane
   constexpr int RPS = kGatherThreads / QL; // rows per step
@@ -345,8 +348,13 @@ void gather_kernel(GatherArgs a) {
 
   // batch-tiled table: this tile's [NP][K][BT] slice is contiguous
   const LutT* lut = static_cast<const LutT*>(second ? a.lut2 : a.lut) + (a.tiled ? (size_t)bt * a.NP * a.K * BT : 0);
-  const int pa = g * a.cpg * a.P;                       // this group's pairs [pa, pb)
-  const int pb = min(a.NP, (g * a.cpg + a.cpg) * a.P);
+  // This group's chunks [c_begin, c_end): cpg each, the last group the rest;
+  // PIPE splits them evenly instead (cpg or cpg - 1 each), so that any number
+  // of groups can be had. Its pairs are [pa, pb).
+  const int c_begin = PIPE ? (int)((int64_t)g * a.chunks / a.G) : g * a.cpg;
+  const int c_end = PIPE ? (int)((int64_t)(g + 1) * a.chunks / a.G) : min(a.chunks, c_begin + a.cpg);
+  const int pa = c_begin * a.P;
+  const int pb = min(a.NP, c_end * a.P);
 
   // 16 bytes = the codes of PPB consecutive pairs of one row. Two register
   // buffers alternate: while one block is looked up, the next one loads into
@@ -402,8 +410,6 @@ void gather_kernel(GatherArgs a) {
       }
     }
   };
-  const int c_begin = g * a.cpg;
-  const int c_end = min(a.chunks, c_begin + a.cpg);
   uint4 wa[NSTEP], wb[NSTEP];
   constexpr int RS = reg_stage(BT, FD);
   ChunkRegs<RS> nxt;
@@ -412,14 +418,43 @@ void gather_kernel(GatherArgs a) {
   const int words_per_pair = FD ? a.K * FD / 4 : a.K * BT * (int)sizeof(LutT) / 16;
   // REG: chunk c's words go to registers with a fixed count of unconditional
   // loads (clamped to the last word of the chunk).
-  if (REG) {
+  // PIPE: chunk i (of this group's nc) has its codebook words in cbA or cbB and
+  // its code block in wA or wB (by the parity of i). Chunk i+2's words and
+  // block are issued right after chunk i's build and lookups have used those
+  // registers, so at any time the loads of the next two chunks are in flight,
+  // and every wait is for loads issued before the ones still flying (waits
+  // count loads in issue order): the codebook staging and the code stream
+  // overlap. (One register buffer, as below, makes each chunk's lookups wait
+  // for the next chunk's codebook, issued just before its codes.)
+  constexpr int RSP = PIPE ? PPB / 2 : 1;   // words of a chunk of PPB pairs at K <= 1024, d = 2
+  ChunkRegs<RSP> cbA, cbB;
+  uint4 wA[NSTEP], wB[NSTEP];
+  const int nc = c_end - c_begin;
+  // chunk i's first pair is a code block's first: P == PPB, or one chunk of P < PPB pairs
+  auto blk_of = [&](int i) { return (c_begin + min(i, nc - 1)) * a.P / PPB; };
+  auto pipe_words = [&](ChunkRegs<RSP>& cb, int i) {
+    const int c = c_begin + min(i, nc - 1);   // past the group's end: its last chunk again
+    const int n4 = min(a.P, a.NP - c * a.P) * words_per_pair;
+    chunk_to_regs<RSP>(cb, lut4 + (size_t)c * a.P * words_per_pair, tid, n4 - 1);
+  };
+  if constexpr (PIPE) {
+    // in this order, not interleaved: the loop's waits count on it
+    pipe_words(cbA, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_block(wA, blk_of(0));
+    __builtin_amdgcn_sched_barrier(0);
+    pipe_words(cbB, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_block(wB, blk_of(1));
+    __builtin_amdgcn_sched_barrier(0);
+  } else if (REG) {
     const int n4 = min(a.P, a.NP - c_begin * a.P) * words_per_pair;
     chunk_to_regs<RS, FD == 8>(nxt, lut4 + (size_t)c_begin * a.P * words_per_pair, tid, n4 - 1);
   }
   // FD: the activation slices of this group's pairs [pa, pb) go to LDS after
   // the chunk, once (pair p uses elements (p % M)*FD .. +FD of the vector).
   // Their loads follow the first chunk's, so the two latencies overlap.
-  float* act_s = reinterpret_cast<float*>(smem + (size_t)a.P * a.K * sizeof(float));
+  float* act_s = reinterpret_cast<float*>(smem + (size_t)(PIPE ? 2 : 1) * a.P * a.K * sizeof(float));   // PIPE: two tables
   if (FD && a.pro_partial) {
     // g and u of each element: pro_tpr parts per element and matrix, part t
     // adding groups t, t+pro_tpr, ... in order, then the parts in order -- the
@@ -486,7 +521,31 @@ void gather_kernel(GatherArgs a) {
   };
   // The loads are unconditional (past the end they repeat the last block, a
   // cache hit), so the same count is always in flight.
-  if (RSET == 1 && BT == 1 && a.P % PPB == 0) {
+  if constexpr (PIPE) {
+    // Chunks in pairs, so each register buffer keeps its role, and two tables
+    // in LDS, so one barrier per chunk suffices: chunk i's table is built into
+    // table i % 2, which every wave stopped reading before the barrier of chunk
+    // i - 1. A step past the group's end rebuilds its last chunk (the same
+    // table) and looks nothing up.
+    LutT* const tabs[2] = {tab, tab + (size_t)a.P * a.K};
+    auto run = [&](ChunkRegs<RSP>& cb, uint4 (&w)[NSTEP], int i, int t) {
+      const int ic = min(i, nc - 1);
+      const int p0 = (c_begin + ic) * a.P;
+      const int pc = min(a.P, a.NP - p0);
+      regs_to_lds_fused<FD, RSP>(cb, reinterpret_cast<float*>(tabs[t]), act_s, tid, pc * words_per_pair - 1, p0 - pa,
+                                 a.K);
+      __syncthreads();
+      pipe_words(cb, i + 2);
+      tab = tabs[t];   // the table lookup_block reads
+      lookup_block(w, i < nc ? blk_of(i) : (c_end * a.P + PPB - 1) / PPB, pa, pb, p0);
+      load_block(w, blk_of(i + 2));
+    };
+    __syncthreads();   // the activation slices are in LDS
+    for (int i = 0; i < nc; i += 2) {
+      run(cbA, wA, i, 0);
+      run(cbB, wB, i + 1, 1);
+    }
+  } else if (RSET == 1 && BT == 1 && a.P % PPB == 0) {
     // Chunks hold whole code blocks: one flat loop over the group's blocks, so
     // the next block's codes are already in flight across a chunk switch.
     // (Batch tiles keep the per-chunk loop: both loops in one kernel spill.)
@@ -569,17 +628,22 @@ void gather_kernel(GatherArgs a) {
   if (tid < BT && b0 + tid < a.B) a.block_keys[(size_t)(b0 + tid) * a.S + s] = s_keys[tid];
 }
 
-template <typename LutT, int BT, int NSTEP, int FD = 0, int CB = 16, int RSET = 1>
+template <typename LutT, int BT, int NSTEP, int FD = 0, int CB = 16, int RSET = 1, bool PIPE = false>
 hipError_t launch_gather_typed(const GatherArgs& a, const GatherPlan& plan, hipStream_t stream) {
   if (plan.steps < 1 || plan.steps > NSTEP) return hipErrorInvalidValue;   // a lane holds NSTEP rows at most
   if (plan.rset != RSET) return hipErrorInvalidValue;                       // slabs are sized for this many row sets
+  if (PIPE) {
+    // one code block per chunk, and a chunk's codebook words fit the two register buffers
+    constexpr int PPB = CB == 10 ? 12 : 8;
+    if (!(plan.P == PPB || (plan.chunks == 1 && plan.P < PPB)) || a.K > 1024) return hipErrorInvalidValue;
+  }
   const size_t chunk_bytes = (size_t)plan.P * a.K * BT * sizeof(LutT);
   const bool reg = (a.B == BT || a.tiled) && chunk_bytes % 16 == 0 &&
                    chunk_bytes <= (size_t)reg_stage(BT, FD) * 16 * kGatherThreads &&
                    ((size_t)a.K * BT * sizeof(LutT)) % 16 == 0;
   void (*kern)(GatherArgs);
   if constexpr (FD != 0)
-    kern = gather_kernel<LutT, BT, NSTEP, true, FD, CB>;
+    kern = gather_kernel<LutT, BT, NSTEP, true, FD, CB, 1, PIPE>;
   else
     kern = reg ? gather_kernel<LutT, BT, NSTEP, true, 0, CB, RSET> : gather_kernel<LutT, BT, NSTEP, false, 0, CB, RSET>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget);
@@ -951,8 +1015,10 @@ namespace {
 // ~150 GB/s per CU (staging is not overlapped with the stream); random 4-byte
 // LDS lookups run at ~9 per clock per CU (quad-contiguous 64-byte lookups at
 // ~120 B/clock); G > 1 adds the partial-sum traffic and a finish launch.
+// pipe: the pipelined fused build, whose staging shares the CU's bandwidth
+// with the code stream instead of stalling it (one round trip at the start).
 double plan_cost_us(int64_t rows, int NP, int K, int B, int es, int BT, int P, int steps, int G, int cpg,
-                    int stage_es, int lane_steps, int mats) {
+                    int stage_es, int lane_steps, int mats, bool pipe = false) {
   const int QL = BT >= 16 ? 4 : 1;
   const int rps = kGatherThreads / QL;
   const int64_t S = (rows + (int64_t)steps * rps - 1) / ((int64_t)steps * rps);
@@ -964,13 +1030,23 @@ double plan_cost_us(int64_t rows, int NP, int K, int B, int es, int BT, int P, i
   const double pairs = (double)cpg * P;
   const double chunk_bytes = (double)P * K * BT * stage_es;
   const double t_stage = cpg * (2.0 + chunk_bytes / 150e3);
-  const double per_cu_bw = std::min(150e3, 6.4e6 / (double)active);          // bytes per us
+  // bytes per us; one CU of the pipelined kernel (codes and codebook streamed at once)
+  // sustains about the chip's share per CU: fewer workgroups cannot draw the whole bandwidth
+  const double per_cu_bw = pipe ? 6.4e6 / kCUs : std::min(150e3, 6.4e6 / (double)active);
   const double t_codes = slab_rows * pairs * 2.0 / per_cu_bw;
   const double lookups_per_us = BT == 1 ? 9.0 * 2400.0 : (120.0 * 2400.0) / (BT * es);
   // every lane looks up all lane_steps rows of its kernel, also those past
   // the slab or the last row
   const double t_look = (double)lane_steps * rps * pairs / lookups_per_us;
-  const double t_wg = t_stage + std::max(t_codes, t_look);
+  // The pipelined kernel splits the chunks evenly over the G groups: a workgroup streams the
+  // codes and codebook of NP / G pairs on average.
+  const double pairs_avg = (double)NP / G;
+  // (a tenth of the lookups is charged on top: the barrier per chunk exposes some of them,
+  // and of two plans that stream alike the one with fewer idle lane steps wins)
+  const double t_look_avg = t_look * pairs_avg / pairs;
+  const double t_wg = pipe ? 2.0 + std::max((slab_rows * pairs_avg * 2.0 + pairs_avg * K * stage_es) / per_cu_bw,
+                                            t_look_avg) + 0.1 * t_look_avg
+                           : t_stage + std::max(t_codes, t_look);
   const double t_stream = (double)rows * NP * 2.0 * NBT * mats / 6.4e6;
   const double t_partial = G > 1 ? 5.0 + (double)G * B * rows * 8.0 * mats / 6.4e6 : 0.0;
   return std::max(t_stream, (double)rounds * t_wg) + t_partial;
@@ -1016,7 +1092,15 @@ GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16, int fus
   // block loop the code stream runs through chunk switches, and smaller
   // switches stall the workgroup for less time.
   if (BT == 1 && !fused_d) pmax = std::min(pmax, 24);
-  if (pmax < NP && pmax > 1) pmax &= ~1;
+  // Fused build at d = 2 with 16- or 10-bit codes and K <= 1024, on a matrix
+  // taller than one slab: the pipelined kernel, whose chunks are one code block
+  // each (the codebook words of two chunks then fit its registers). Measured on
+  // the Gemma-2 MLP: 26.4 us against 30.3 for gate and up (9,216 rows, one
+  // launch), but 29.1 against 27.2 for down (2,304 rows, one slab, codebook
+  // bytes twice its code bytes), which keeps the one-buffer kernel.
+  const bool pipe = fused_d == 2 && (ppb == 8 || ppb == 12) && K <= 1024 && rows > 4 * (int64_t)kGatherThreads;
+  if (pipe) pmax = std::min(NP, ppb);
+  if (pmax < NP && pmax > 1 && !pipe) pmax &= ~1;
   double best_cost = 1e300;
   int tried = 0;
   for (int P = pmax; P >= 1 && P >= pmax / 2 && tried < 8; --P) {
@@ -1024,6 +1108,7 @@ GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16, int fus
     // a chunk smaller than a code block loads every block once per chunk it
     // touches: only when nothing larger fits
     if (P < ppb && P < NP && pmax >= ppb) continue;
+    if (pipe && P != pmax) continue;
     ++tried;
     const int chunks = (NP + P - 1) / P;
     for (int steps = nstep; steps >= 1; --steps) {
@@ -1033,17 +1118,19 @@ GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16, int fus
       const int64_t gmax = std::max<int64_t>(1, std::min<int64_t>(chunks, 4 * kCUs / (S * NBT * mats) + 1));
       for (int64_t G0 = 1; G0 <= gmax; ++G0) {
         const int cpg = (int)((chunks + G0 - 1) / G0);
-        const int G = (chunks + cpg - 1) / cpg;
+        const int G = pipe ? (int)G0 : (chunks + cpg - 1) / cpg;   // the pipelined kernel splits chunks evenly
         if (G != G0) continue;
-        if ((size_t)P * K * 4 + fused_act_bytes(P, cpg, NP, fused_d) > (size_t)kLdsBudget && fused_d) continue;
+        if ((size_t)(pipe ? 2 : 1) * P * K * 4 + fused_act_bytes(P, cpg, NP, fused_d) > (size_t)kLdsBudget && fused_d)
+          continue;
         // prefer aligned chunks (staging outside the block loop) on near-ties
         const int lane_steps = (fused_d == 2 || fused_d == 8) ? steps : nstep;   // the kernel instances (dispatch_gather)
-        const double cost = plan_cost_us(rows, NP, K, B, es, BT, P, steps, G, cpg, stage_es, lane_steps, mats) *
+        const double cost = plan_cost_us(rows, NP, K, B, es, BT, P, steps, G, cpg, stage_es, lane_steps, mats, pipe) *
                             ((P % ppb == 0 || chunks == 1) ? 1.0 : 1.03);
         if (cost < best_cost * 0.999) {
           best_cost = cost;
           best.BT = BT; best.P = P; best.chunks = chunks; best.cpg = cpg; best.G = G;
           best.steps = steps; best.rps = rps; best.S = (int)S; best.NBT = NBT;
+          best.pipe = pipe ? 1 : 0;
         }
       }
     }
@@ -1077,7 +1164,7 @@ GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16, int fus
       best.G = (best.chunks + best.cpg - 1) / best.cpg;
     }
   }
-  best.lds = (size_t)best.P * K * BT * es + fused_act_bytes(best.P, best.cpg, NP, fused_d);
+  best.lds = (size_t)(best.pipe ? 2 : 1) * best.P * K * BT * es + fused_act_bytes(best.P, best.cpg, NP, fused_d);
   return best;
 }
 
@@ -1128,6 +1215,16 @@ hipError_t dispatch_gather(const GatherArgs& a, const GatherPlan& plan, int d, i
                            hipStream_t stream) {
   if (fused) {
     if (d == 1) return launch_gather_typed<float, 1, 4, 1, CB>(a, plan, stream);
+    if (d == 2 && plan.pipe) {
+      if constexpr (CB != 8) {
+        switch (plan.steps) {
+          case 2: return launch_gather_typed<float, 1, 2, 2, CB, 1, true>(a, plan, stream);
+          case 3: return launch_gather_typed<float, 1, 3, 2, CB, 1, true>(a, plan, stream);
+          default: return launch_gather_typed<float, 1, 4, 2, CB, 1, true>(a, plan, stream);
+        }
+      }
+      return hipErrorInvalidValue;
+    }
     if (d == 2) {
       switch (plan.steps) {
         case 2: return launch_gather_typed<float, 1, 2, 2, CB>(a, plan, stream);

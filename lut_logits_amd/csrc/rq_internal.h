@@ -101,6 +101,7 @@ struct GatherPlan {
   int rset = 1;  // row sets per workgroup (2: bf16 tables in several batch tiles of 4, fp32 tables of 16 vectors)
   int NBT;       // batch tiles
   size_t lds;    // dynamic LDS bytes per workgroup
+  int pipe = 0;  // fused build, d = 2: one code block per chunk, two chunks in flight (the pipelined kernel)
   int64_t wgs() const { return (int64_t)G * S * NBT; }
 };
 // fused != 0: the table is built while staging (fused_build_supported).

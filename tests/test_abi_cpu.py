@@ -133,7 +133,7 @@ def test_other_entry_points_reject():
     assert lib.rq_lut_matvec(ctypes.byref(W), 0x1000, None, 1, 1, 0x2000, None, 0, None) == B.RQ_ERR_NULL
     # a matrix whose workspace query returns 0 takes a NULL workspace: the checks pass (without a GPU the
     # launch itself then fails)
-    Ws = gemma_desc(rows=160, D=96, M=48, d=2, K=64, cb_dtype=B.RQ_F32)
+    Ws = gemma_desc(rows=160, D=8, M=4, d=2, K=64, cb_dtype=B.RQ_F32)   # 8 pairs: one chunk, one group
     assert lib.rq_lut_matvec_workspace(ctypes.byref(Ws), 1) == 0
     assert lib.rq_lut_matvec(ctypes.byref(Ws), 0x1000, None, 0, 1, 0x2000, None, 0, None) not in (
         B.RQ_OK, B.RQ_ERR_WORKSPACE, B.RQ_ERR_NULL, B.RQ_ERR_ALIGN)
