@@ -276,15 +276,16 @@ __device__ __forceinline__ void regs_to_lds(const ChunkRegs<RS>& r, u32x4* dst, 
 // sums of every set stay in registers), so a slab of RSET times the rows
 // stages each chunk once: with several batch tiles the table restaging, not
 // the code stream, bounds the pass.
-// PIPE (fused build with FD = 2, one code block per chunk, K <= 1024): see the
-// pipelined loop below.
+// PIPE (one code block per chunk, K <= 1024; the fused build with FD = 2, or
+// an fp32 table for one vector): see the pipelined loop below.
 template <typename LutT, int BT, int NSTEP, bool REG, int FD = 0, int CB = 16, int RSET = 1, bool PIPE = false>
 __global__ __launch_bounds__(kGatherThreads) __attribute__((amdgpu_waves_per_eu(1, 4)))
 void gather_kernel(GatherArgs a) {
   constexpr int PPB = CB == 10 ? 12 : (CB == 8 ? 16 : 8);   // pairs per code block
   static_assert(FD == 0 || (BT == 1 && REG && sizeof(LutT) == 4 && (4 % FD == 0 || FD == 8)),
                 "fused build: fp32, B=1, FD in {1, 2, 4, 8}");
-  static_assert(!PIPE || (FD == 2 && RSET == 1 && CB != 8), "pipelined fused build: d = 2, 16- or 10-bit codes");
+  static_assert(!PIPE || ((FD == 2 || (FD == 0 && BT == 1 && sizeof(LutT) == 4)) && RSET == 1 && CB != 8),
+                "pipelined kernel: fused build at d = 2 or an fp32 table for one vector; 16- or 10-bit codes");
   constexpr int QL = (BT >= 16) ? 4 : 1;   // lanes per row
   constexpr int BQ = BT / QL;              // batch entries per lane
   constexpr int RPS = kGatherThreads / QL; // rows per step
@@ -426,7 +427,8 @@ void gather_kernel(GatherArgs a) {
   // count loads in issue order): the codebook staging and the code stream
   // overlap. (One register buffer, as below, makes each chunk's lookups wait
   // for the next chunk's codebook, issued just before its codes.)
-  constexpr int RSP = PIPE ? PPB / 2 : 1;   // words of a chunk of PPB pairs at K <= 1024, d = 2
+  // words of a chunk of PPB pairs at K <= 1024: 8 bytes of codebook per entry at d = 2, 4 of table
+  constexpr int RSP = PIPE ? (FD ? PPB * FD / 4 : PPB / 4) : 1;
   ChunkRegs<RSP> cbA, cbB;
   uint4 wA[NSTEP], wB[NSTEP];
   const int nc = c_end - c_begin;
@@ -532,8 +534,11 @@ void gather_kernel(GatherArgs a) {
       const int ic = min(i, nc - 1);
       const int p0 = (c_begin + ic) * a.P;
       const int pc = min(a.P, a.NP - p0);
-      regs_to_lds_fused<FD, RSP>(cb, reinterpret_cast<float*>(tabs[t]), act_s, tid, pc * words_per_pair - 1, p0 - pa,
-                                 a.K);
+      if constexpr (FD != 0)
+        regs_to_lds_fused<FD, RSP>(cb, reinterpret_cast<float*>(tabs[t]), act_s, tid, pc * words_per_pair - 1,
+                                   p0 - pa, a.K);
+      else
+        regs_to_lds(cb, reinterpret_cast<u32x4*>(tabs[t]), tid, pc * words_per_pair - 1);
       __syncthreads();
       pipe_words(cb, i + 2);
       tab = tabs[t];   // the table lookup_block reads
@@ -642,7 +647,7 @@ hipError_t launch_gather_typed(const GatherArgs& a, const GatherPlan& plan, hipS
                    chunk_bytes <= (size_t)reg_stage(BT, FD) * 16 * kGatherThreads &&
                    ((size_t)a.K * BT * sizeof(LutT)) % 16 == 0;
   void (*kern)(GatherArgs);
-  if constexpr (FD != 0)
+  if constexpr (FD != 0 || PIPE)
     kern = gather_kernel<LutT, BT, NSTEP, true, FD, CB, 1, PIPE>;
   else
     kern = reg ? gather_kernel<LutT, BT, NSTEP, true, 0, CB, RSET> : gather_kernel<LutT, BT, NSTEP, false, 0, CB, RSET>;
@@ -1098,7 +1103,8 @@ GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16, int fus
   // the Gemma-2 MLP: 26.4 us against 30.3 for gate and up (9,216 rows, one
   // launch), but 29.1 against 27.2 for down (2,304 rows, one slab, codebook
   // bytes twice its code bytes), which keeps the one-buffer kernel.
-  const bool pipe = fused_d == 2 && (ppb == 8 || ppb == 12) && K <= 1024 && rows > 4 * (int64_t)kGatherThreads;
+  const bool pipe = (fused_d == 2 || (fused_d == 0 && BT == 1 && !lut_bf16)) && (ppb == 8 || ppb == 12) &&
+                    K <= 1024 && rows > 4 * (int64_t)kGatherThreads;
   if (pipe) pmax = std::min(NP, ppb);
   if (pmax < NP && pmax > 1 && !pipe) pmax &= ~1;
   double best_cost = 1e300;
@@ -1243,6 +1249,10 @@ hipError_t dispatch_gather(const GatherArgs& a, const GatherPlan& plan, int d, i
       return plan.rset == 2 ? launch_gather_typed<uint16_t, 4, 4, 0, CB, 2>(a, plan, stream)
                             : launch_gather_typed<uint16_t, 4, 4, 0, CB>(a, plan, stream);
     return launch_gather_typed<uint16_t, 16, 4, 0, CB>(a, plan, stream);
+  }
+  if (plan.BT == 1 && plan.pipe) {
+    if constexpr (CB != 8) return launch_gather_typed<float, 1, 4, 0, CB, 1, true>(a, plan, stream);
+    return hipErrorInvalidValue;
   }
   if (plan.BT == 1) return launch_gather_typed<float, 1, 4, 0, CB>(a, plan, stream);
   if (plan.BT == 4) return launch_gather_typed<float, 4, 4, 0, CB>(a, plan, stream);
