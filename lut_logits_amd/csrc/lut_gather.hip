@@ -1097,14 +1097,17 @@ GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16, int fus
   // block loop the code stream runs through chunk switches, and smaller
   // switches stall the workgroup for less time.
   if (BT == 1 && !fused_d) pmax = std::min(pmax, 24);
-  // Fused build at d = 2 with 16- or 10-bit codes and K <= 1024, on a matrix
-  // taller than one slab: the pipelined kernel, whose chunks are one code block
-  // each (the codebook words of two chunks then fit its registers). Measured on
-  // the Gemma-2 MLP: 26.4 us against 30.3 for gate and up (9,216 rows, one
-  // launch), but 29.1 against 27.2 for down (2,304 rows, one slab, codebook
-  // bytes twice its code bytes), which keeps the one-buffer kernel.
+  // The pipelined kernel, whose chunks are one code block each (the words of
+  // two chunks then fit its registers): fused build at d = 2 or an fp32 table
+  // for one vector, 16- or 10-bit codes, K <= 1024, a matrix taller than one
+  // slab and at least 64 blocks of pairs (so that a group holds several
+  // chunks). Measured: the Gemma-2 MLP's gate and up 26.4 us against 30.3
+  // (9,216 rows, 288 blocks, one launch); its down 29.1 against 27.2 (2,304
+  // rows, one slab) and the second attempt's gate and up from their tables
+  // 12.8 against 10.8 (48 blocks: one or two chunks per group) keep the
+  // one-buffer kernel.
   const bool pipe = (fused_d == 2 || (fused_d == 0 && BT == 1 && !lut_bf16)) && (ppb == 8 || ppb == 12) &&
-                    K <= 1024 && rows > 4 * (int64_t)kGatherThreads;
+                    K <= 1024 && rows > 4 * (int64_t)kGatherThreads && (NP + ppb - 1) / ppb >= 64;
   if (pipe) pmax = std::min(NP, ppb);
   if (pmax < NP && pmax > 1 && !pipe) pmax &= ~1;
   double best_cost = 1e300;

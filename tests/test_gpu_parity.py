@@ -388,20 +388,22 @@ def test_lut_matvec_fused_build_exact(d, layout):
 
 
 @pytest.mark.parametrize("rows,D,K,layout", [
-    (5000, 100, 256, "blocked"),    # 100 pairs: a partly empty last code block of 8
-    (5000, 100, 256, "packed10"),   # ... and of 12
+    (5000, 1004, 256, "blocked"),   # 1004 pairs: a partly empty last code block of 8
+    (5000, 1004, 256, "packed10"),  # ... and of 12
     (4097, 2304, 1024, "packed10"), # one row past four slabs of 1024
     (9216, 2304, 1024, "blocked"),  # the MLP gate's shape
-    (6000, 12, 64, "blocked"),      # 24 pairs: three chunks, groups of one
+    (6000, 520, 64, "blocked"),     # 520 pairs (65 blocks), K = 64
+    (6000, 100, 256, "blocked"),    # 13 blocks of pairs: the one-buffer kernel
     (3001, 100, 256, "blocked"),    # one slab: the one-buffer kernel
     (1, 2304, 1024, "blocked"),     # one row
     (37, 4608, 1024, "packed10"),   # the MLP down's width, few rows
     (700, 600, 2048, "blocked"),    # K > 1024
 ])
 def test_lut_matvec_fused_d2_exact(rows, D, K, layout):
-    """The fused build at d = 2. Matrices taller than one slab (4096 rows) with 16- or 10-bit codes and
-    K <= 1024 take the pipelined kernel (one code block per chunk, two chunks in flight, chunks split evenly
-    over the groups); the others the one-buffer kernel. Exact inputs, bit-exact against the oracle."""
+    """The fused build at d = 2. Matrices taller than one slab (4096 rows) with 16- or 10-bit codes, K <= 1024
+    and at least 64 blocks of pairs take the pipelined kernel (one code block per chunk, two chunks in flight,
+    chunks split evenly over the groups); the others the one-buffer kernel. Exact inputs, bit-exact against
+    the oracle."""
     mat, x = synth.gen_exact(rows + D + K, rows, D, D // 2, K, 2, 1)
     W = to_dev(mat, layout)
     y = la.lut_matvec(W, dev(x))
