@@ -361,6 +361,21 @@ rq_status rq_dense_logits(const uint16_t* Et, int64_t rows, int32_t D, const flo
                           hipStream_t stream);
 
 
+/*
+ * Glue of a per-token decode loop around each MLP block (not part of the
+ * pages' method: Gemma-2's residual stream, read in its plainest form), in one
+ * launch on the residual stream h, with the unit-scale RMSNorm
+ *     rms(v) = v / sqrt(mean(v^2) + eps):
+ *     if y != NULL:  h += rms(y)   (a block's output, normalised, added back)
+ *     x = rms(h)                   (the next block's input, or the head's vector)
+ *   y   device fp32 [D] or NULL; h device fp32 [D], updated in place;
+ *   x   device fp32 [D], written; x must not overlap h or y;
+ *   1 <= D <= 1048576, eps > 0. All 4-byte aligned. One workgroup, stream-ordered.
+ * Bad sizes return RQ_ERR_SHAPE, NULL h or x RQ_ERR_NULL, misaligned buffers
+ * RQ_ERR_ALIGN.
+ */
+rq_status rq_residual_norm(const float* y, float* h, float* x, int32_t D, float eps, hipStream_t stream);
+
 /* Static text for a status code. Takes any int (an rq_status value converts
  * to it); a value that is no rq_status gives "unknown status". */
 const char* rq_status_string(int32_t s);

@@ -27,7 +27,7 @@ RQ_METHOD_TABLE, RQ_METHOD_MATRIX_CORES = 0, 1
 EXPORTS = ("rq_blocked_codes_bytes", "rq_pack_codes", "rq_packed10_codes_bytes", "rq_pack_codes10",
            "rq_packed8_codes_bytes", "rq_pack_codes8", "rq_lut_bytes", "rq_build_lut", "rq_lut_logits_workspace",
            "rq_lut_logits", "rq_lut_logits_static", "rq_logits_method", "rq_logits_workspace", "rq_logits", "rq_decode_rows", "rq_lut_matvec_workspace", "rq_lut_matvec",
-           "rq_lut_mlp_workspace", "rq_lut_mlp", "rq_dense_tiled_bytes", "rq_pack_dense", "rq_dense_logits_workspace", "rq_dense_logits", "rq_stream_read_configs",
+           "rq_lut_mlp_workspace", "rq_lut_mlp", "rq_residual_norm", "rq_dense_tiled_bytes", "rq_pack_dense", "rq_dense_logits_workspace", "rq_dense_logits", "rq_stream_read_configs",
            "rq_stream_read_sink_words", "rq_stream_read", "rq_lds_gather_sink_words", "rq_lds_gather",
            "rq_set_stage_events", "rq_lut_logits_plan", "rq_status_string",
            "rq_last_error", "rq_version")
@@ -77,6 +77,7 @@ def lib():
             "rq_lut_matvec": (_i32, [_MP, _vp, _vp, _i32, _i32, _vp, _vp, _sz, _vp]),
             "rq_lut_mlp_workspace": (_sz, [_MP, _MP, _MP, _i32]),
             "rq_lut_mlp": (_i32, [_MP, _MP, _MP, _vp, _i32, _vp, _vp, _sz, _vp]),
+            "rq_residual_norm": (_i32, [_vp, _vp, _vp, _i32, _f32, _vp]),
             "rq_dense_tiled_bytes": (_sz, [_i64, _i32]),
             "rq_pack_dense": (_i32, [_vp, _i64, _i32, _vp, _vp]),
             "rq_dense_logits_workspace": (_sz, [_i64, _i32]),
@@ -406,6 +407,19 @@ def lds_gather(width, reps, sink=None):
     _gpu(sink=sink)
     check(lib().rq_lds_gather(width, reps, _ptr(sink), _stream()))
     return sink
+
+
+def residual_norm(h, x, y=None, eps=1e-6):
+    """rq_residual_norm: h += rms(y) (when y is given), then x = rms(h); fp32 vectors of one length
+    ([D] or [1][D]) on the GPU, x not overlapping h or y. Returns x."""
+    D = h.numel()
+    _arg(h, "h", torch.float32, numel=D)
+    _arg(x, "x", torch.float32, numel=D)
+    if y is not None:
+        _arg(y, "y", torch.float32, numel=D)
+    _gpu(h=h, x=x, y=y)
+    check(lib().rq_residual_norm(_ptr(y), _ptr(h), _ptr(x), D, eps, _stream()))
+    return x
 
 
 class DenseHead:

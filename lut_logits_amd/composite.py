@@ -5,10 +5,10 @@ the last hidden vector (rq_build_lut + rq_lut_logits: softcap and argmax, no log
 argmax id stays on the device and is the next token's row id, so a run of tokens is enqueued with no
 host synchronisation.
 
-Around each block sits Gemma-2's own glue, in plain torch arithmetic outside the method: an RMSNorm
-before the block and one after it, the block's output added to the residual stream, and a final
-RMSNorm before the head. The norms carry unit scales (Gemma-2 stores each RMSNorm scale as 1 + w, and
-w starts at zero). Without them the chain diverges on these synthetic weights: a block maps an input of
+Around each block sits Gemma-2's own glue, outside the method: an RMSNorm before the block and one
+after it, the block's output added to the residual stream, and a final RMSNorm before the head. One
+rq_residual_norm launch per block does it (h += rms(y), then the next input rms(h)). The norms carry
+unit scales (Gemma-2 stores each RMSNorm scale as 1 + w, and w starts at zero). Without them the chain diverges on these synthetic weights: a block maps an input of
 scale s to about 1.3 s^2, so an unnormalised chain of 26 blocks overflows fp32 within ten. Attention is
 not part of the loop (it needs the model's weights)."""
 import math
@@ -18,12 +18,6 @@ import torch
 from . import binding as B
 
 RMS_EPS = 1e-6
-
-
-def rms_norm(x, out):
-    """out = x / sqrt(mean(x^2) + eps), unit scale."""
-    out.copy_(torch.nn.functional.rms_norm(x, (x.shape[-1],), eps=RMS_EPS))
-    return out
 
 
 class DecodeLoop:
@@ -42,7 +36,6 @@ class DecodeLoop:
 
         self.row = buf()
         self.h = buf()       # residual stream
-        self.tmp = buf()
         self.last = buf()    # final-norm output: the head's hidden vector
         n = len(self.layers) if keep_layers else 1
         self.ins = [buf() for _ in range(n)]
@@ -57,13 +50,16 @@ class DecodeLoop:
         ids[t + 1]. Returns the head's hidden vector."""
         B.decode_rows(self.head, self.ids[t:t + 1], "f32", out=self.row)
         torch.mul(self.row, self.scale, out=self.h)
+        n = len(self.layers)
+
+        def block_input(i):   # block i's input buffer; past the last block, the head's vector
+            return self.ins[i % len(self.ins)] if i < n else self.last
+
+        B.residual_norm(self.h, block_input(0), eps=RMS_EPS)
         for i, (gate, up, down) in enumerate(self.layers):
-            x = self.ins[i % len(self.ins)]
             y = self.outs[i % len(self.outs)]
-            rms_norm(self.h, x)
-            B.lut_mlp(gate, up, down, x, ws=self.ws_mlp, out=y)
-            self.h.add_(rms_norm(y, self.tmp))
-        rms_norm(self.h, self.last)
+            B.lut_mlp(gate, up, down, block_input(i), ws=self.ws_mlp, out=y)
+            B.residual_norm(self.h, block_input(i + 1), y, eps=RMS_EPS)
         B.build_lut(self.head, self.last, out=self.lut)
         B.lut_logits(self.head, self.lut, 1, softcap=self.softcap, logits=False, ws=self.ws_head,
                      argmax_out=self.ids[t + 1:t + 2])

@@ -586,6 +586,17 @@ size_t rq_dense_logits_workspace(int64_t rows, int32_t B) {
   return round_up(rq::dense_hb_bytes(4096, B), 256) + round_up((size_t)B * rq::dense_blocks(rows) * sizeof(uint64_t), 256);
 }
 
+rq_status rq_residual_norm(const float* y, float* h, float* x, int32_t D, float eps, hipStream_t stream) {
+  CallRange range(__func__);
+  if (D < 1 || D > (1 << 20) || !(eps > 0.0f)) return fail(RQ_ERR_SHAPE, "residual_norm needs 1 <= D <= 2^20 and eps > 0");
+  if (!h || !x) return fail(RQ_ERR_NULL, "residual_norm: NULL buffer");
+  if (!aligned(h, 4) || !aligned(x, 4) || (y && !aligned(y, 4))) return fail(RQ_ERR_ALIGN, "residual_norm: misaligned buffer");
+  const uintptr_t xb = (uintptr_t)x, xe = xb + (size_t)D * 4;
+  auto overlaps = [&](const void* p) { return p && (uintptr_t)p < xe && xb < (uintptr_t)p + (size_t)D * 4; };
+  if (overlaps(h) || overlaps(y)) return fail(RQ_ERR_SHAPE, "residual_norm: x overlaps h or y");
+  return launched(rq::launch_residual_norm(y, h, x, D, eps, stream), "rq_residual_norm");
+}
+
 size_t rq_dense_tiled_bytes(int64_t rows, int32_t D) {
   if (rows <= 0 || rows >= ((int64_t)1 << 31) || D < 8 || D % 8 != 0 || D > 4096) return 0;
   return rq::dense_tiled_bytes(rows, D);

@@ -213,6 +213,8 @@ hipError_t launch_decode_rows(const rq_matrix* W, const int32_t* ids, int n, int
 hipError_t launch_pack_codes(const uint16_t* src, int64_t rows, int NP, uint16_t* dst, hipStream_t stream);
 hipError_t launch_pack_codes10(const uint16_t* src, int64_t rows, int NP, uint16_t* dst, hipStream_t stream);
 hipError_t launch_pack_codes8(const uint16_t* src, int64_t rows, int NP, uint16_t* dst, hipStream_t stream);
+// The decode loop's glue around an MLP block: h += rms(y) (y may be null), x = rms(h).
+hipError_t launch_residual_norm(const float* y, float* h, float* x, int D, float eps, hipStream_t stream);
 // Dense comparator: hb is a bf16 copy of h padded to whole 16-vector tiles
 // (dense_hb_bytes), written first by the same call.
 size_t dense_hb_bytes(int D, int B);

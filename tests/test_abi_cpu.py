@@ -144,6 +144,15 @@ def test_other_entry_points_reject():
     assert lib.rq_pack_codes10(0x1000, 10, 0, 3, 0x1000, None) == B.RQ_ERR_SHAPE
     assert lib.rq_pack_codes10(0x1000, 10, 2, 3, 0x1008, None) == B.RQ_ERR_ALIGN
     assert lib.rq_pack_codes10(None, 0, 2, 3, None, None) == B.RQ_OK
+    assert lib.rq_residual_norm(None, None, 0x2000, 16, 1e-6, None) == B.RQ_ERR_NULL
+    assert lib.rq_residual_norm(None, 0x1000, None, 16, 1e-6, None) == B.RQ_ERR_NULL
+    assert lib.rq_residual_norm(None, 0x1000, 0x2000, 0, 1e-6, None) == B.RQ_ERR_SHAPE
+    assert lib.rq_residual_norm(None, 0x1000, 0x2000, (1 << 20) + 1, 1e-6, None) == B.RQ_ERR_SHAPE
+    assert lib.rq_residual_norm(None, 0x1000, 0x2000, 16, 0.0, None) == B.RQ_ERR_SHAPE
+    assert lib.rq_residual_norm(None, 0x1002, 0x2000, 16, 1e-6, None) == B.RQ_ERR_ALIGN
+    assert lib.rq_residual_norm(0x3001, 0x1000, 0x2000, 16, 1e-6, None) == B.RQ_ERR_ALIGN
+    assert lib.rq_residual_norm(None, 0x1000, 0x1020, 16, 1e-6, None) == B.RQ_ERR_SHAPE   # x overlaps h
+    assert lib.rq_residual_norm(0x2030, 0x1000, 0x2000, 16, 1e-6, None) == B.RQ_ERR_SHAPE   # x overlaps y
     assert lib.rq_pack_dense(None, 100, 2304, 0x1000, None) == B.RQ_ERR_NULL
     assert lib.rq_pack_dense(0x1000, 100, 2300, 0x2000, None) == B.RQ_ERR_SHAPE
     assert lib.rq_pack_dense(0x1000, -1, 2304, 0x2000, None) == B.RQ_ERR_SHAPE

@@ -84,6 +84,10 @@ def test_workspace_and_dense_checks():
     lut = torch.zeros(B.lut_bytes(W, 1, "f32") // 4)
     _raises(lambda: la.lut_logits(W, lut, 1, ws=torch.zeros(4096, dtype=torch.float32)), "dtype")
     _raises(lambda: la.pack_dense(torch.zeros((64, 16), dtype=torch.float32)), "dtype")
+    _raises(lambda: la.residual_norm(torch.zeros(16), torch.zeros(8)), "elements")
+    _raises(lambda: la.residual_norm(torch.zeros(16, dtype=torch.float64), torch.zeros(16)), "dtype")
+    _raises(lambda: la.residual_norm(torch.zeros(16), torch.zeros(16), torch.zeros(15)), "elements")
+    _raises(lambda: la.residual_norm(torch.zeros(16), torch.zeros(16)), "GPU")
     _raises(lambda: la.dense_logits(torch.zeros((64, 16), dtype=torch.int16), torch.zeros((1, 16))), "DenseHead")
     head = la.DenseHead(torch.zeros(la.dense_tiled_bytes(64, 16) // 2, dtype=torch.int16), 64, 16)
     assert head.nbytes == 4 * 1 * 1024

@@ -26,7 +26,7 @@ def _rms(v):
 
 def check_loop_step(o, head, layers, loop, tok, softcap):
     """One step of the loop, teacher-forced: every block's GPU output against the oracle's block on the
-    GPU's input to it, the norms and residual stream (torch glue) against numpy to fp32 rounding, and the
+    GPU's input to it, the norms and residual stream (rq_residual_norm) against numpy to fp32 rounding, and the
     next token within 2t of the oracle head's maximum on the GPU's final hidden vector. Returns it."""
     row, _ = o.decode_rows(head.codes, head.codebooks, head.cb_is_bf16, np.array([tok], np.int32), False)
     h = row.astype(np.float64) * np.sqrt(head.D)
@@ -72,3 +72,34 @@ def test_decode_loop_teacher_forced():
     # a second run from the same token repeats the sequence (deterministic)
     ids2 = loop.run(7, 8).clone()
     assert torch.equal(ids2.cpu(), torch.tensor(tokens, dtype=torch.int32))
+
+
+@pytest.mark.parametrize("D", [1, 7, 1023, 1025, 2304, 9216, 70001])
+def test_residual_norm_against_numpy(D):
+    """rq_residual_norm: h += rms(y), x = rms(h), against the fp64 definition (rms(v) = v / sqrt(mean(v^2)
+    + eps)): fp32 rounding only, over lengths below, at and past one element per thread and several per
+    thread; without y it only normalises; h and x are distinct buffers and nothing else is written."""
+    rng = np.random.default_rng(D)
+    h0 = (rng.standard_normal(D) * 3.0).astype(np.float32)
+    y0 = (rng.standard_normal(D) * 0.5 + 0.1).astype(np.float32)
+    h = torch.from_numpy(h0.copy()).cuda()
+    y = torch.from_numpy(y0.copy()).cuda()
+    x = torch.full((D + 64,), 7.0, device="cuda")
+    la.residual_norm(h, x[:D], y, eps=1e-6)
+    hr = h0.astype(np.float64) + _rms(y0)
+    assert np.allclose(host(h), hr, rtol=0, atol=1e-6 * np.abs(hr).max() + 1e-7)
+    xr = _rms(hr)
+    assert np.allclose(host(x[:D]), xr, rtol=0, atol=2e-6 * np.abs(xr).max())
+    assert torch.equal(x[D:], torch.full((64,), 7.0, device="cuda"))
+    assert torch.equal(y.cpu(), torch.from_numpy(y0))
+    # without y: h untouched, x = rms(h)
+    h2 = torch.from_numpy(h0.copy()).cuda()
+    x2 = torch.empty(D, device="cuda")
+    la.residual_norm(h2, x2)
+    assert torch.equal(h2.cpu(), torch.from_numpy(h0))
+    assert np.allclose(host(x2), _rms(h0), rtol=0, atol=2e-6 * np.abs(_rms(h0)).max())
+    # the same call twice gives the same bits
+    h3 = torch.from_numpy(h0.copy()).cuda()
+    x3 = torch.empty(D, device="cuda")
+    la.residual_norm(h3, x3, y)
+    assert torch.equal(h3, h) and torch.equal(x3, x[:D])
