@@ -640,7 +640,9 @@ hipError_t launch_gather_typed(const GatherArgs& a, const GatherPlan& plan, hipS
   if (PIPE) {
     // one code block per chunk, and a chunk's codebook words fit the two register buffers
     constexpr int PPB = CB == 10 ? 12 : 8;
-    if (!(plan.P == PPB || (plan.chunks == 1 && plan.P < PPB)) || a.K > 1024) return hipErrorInvalidValue;
+    if (!(plan.P == PPB || (plan.chunks == 1 && plan.P < PPB)) || a.K > 1024 ||
+        ((size_t)a.K * (FD ? FD : BT) * sizeof(LutT)) % 16 != 0)
+      return hipErrorInvalidValue;
   }
   const size_t chunk_bytes = (size_t)plan.P * a.K * BT * sizeof(LutT);
   const bool reg = (a.B == BT || a.tiled) && chunk_bytes % 16 == 0 &&
@@ -1106,8 +1108,11 @@ GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16, int fus
   // rows, one slab) and the second attempt's gate and up from their tables
   // 12.8 against 10.8 (48 blocks: one or two chunks per group) keep the
   // one-buffer kernel.
+  // (A pair's table or codebook must be whole 16-byte words: K % 4 == 0 for
+  // the table, K*d % 4 == 0 for the fused build.)
   const bool pipe = (fused_d == 2 || (fused_d == 0 && BT == 1 && !lut_bf16)) && (ppb == 8 || ppb == 12) &&
-                    K <= 1024 && rows > 4 * (int64_t)kGatherThreads && (NP + ppb - 1) / ppb >= 64;
+                    K <= 1024 && (K * (fused_d ? fused_d : 1)) % 4 == 0 && rows > 4 * (int64_t)kGatherThreads &&
+                    (NP + ppb - 1) / ppb >= 64;
   if (pipe) pmax = std::min(NP, ppb);
   if (pmax < NP && pmax > 1 && !pipe) pmax &= ~1;
   double best_cost = 1e300;

@@ -176,6 +176,9 @@ EXACT_SHAPES = [
     (1500, 96, 16, 128, 3, 17),     # batch 16 + ragged 1
     (700, 96, 96, 64, 2, 5),        # d = 1
     (333, 64, 1, 512, 2, 3),        # M = 1, d = D
+    (4500, 2304, 384, 1000, 2, 1),  # the Gemma head's pairs: the pipelined kernel (16- and 10-bit codes)
+    (5000, 1536, 256, 64, 2, 1),    # 512 pairs, K = 64: the pipelined kernel on 16-bit codes
+    (4500, 2304, 384, 1001, 2, 1),  # K % 4 != 0: a pair's table is no whole number of 16-byte words
 ]
 
 
