@@ -344,6 +344,11 @@ void gather_kernel(GatherArgs a) {
   // 64-bit per-lane addresses. (The host keeps the code array below 4 GiB.)
   const __amdgpu_buffer_rsrc_t code_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)cv.codes, (short)0, (int)0xffffffffu, 0x00020000);
+  // A resource with no records: loads through it are out of range, return
+  // zeros and touch no memory. The loads that run ahead past a group's last
+  // block use it, so they keep the fixed count per block (and the exact wait
+  // counts) without fetching that block again.
+  const __amdgpu_buffer_rsrc_t none_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)cv.codes, (short)0, 0, 0x00020000);
   const uint32_t blk_bytes = (uint32_t)(cv.s_blk * 2);
   const int steps = a.steps;
 
@@ -360,11 +365,13 @@ void gather_kernel(GatherArgs a) {
   // 16 bytes = the codes of PPB consecutive pairs of one row. Two register
   // buffers alternate: while one block is looked up, the next one loads into
   // the other buffer (no register copy, so no wait on the load in flight).
-  auto load_block = [&](uint4 (&dst)[NSTEP], int q, int rs = 0) {
+  // live == false (uniform): a block past the group's end, whose codes are never looked up.
+  auto load_block = [&](uint4 (&dst)[NSTEP], int q, int rs = 0, bool live = true) {
     const uint32_t boff = (uint32_t)q * blk_bytes;
+    const __amdgpu_buffer_rsrc_t rsrc = live ? code_rsrc : none_rsrc;
 #pragma unroll
     for (int st = 0; st < NSTEP; ++st) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(code_rsrc, (int)roff[rs][st], (int)boff, kCodeCachePolicy);
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)roff[rs][st], (int)boff, kCodeCachePolicy);
       dst[st] = make_uint4(v[0], v[1], v[2], v[3]);
     }
   };
@@ -521,8 +528,8 @@ void gather_kernel(GatherArgs a) {
     }
     __syncthreads();
   };
-  // The loads are unconditional (past the end they repeat the last block, a
-  // cache hit), so the same count is always in flight.
+  // The loads are unconditional (past the group's end they go through the
+  // no-record resource and fetch nothing), so the same count is always in flight.
   if constexpr (PIPE) {
     // Chunks in pairs, so each register buffer keeps its role, and two tables
     // in LDS, so one barrier per chunk suffices: chunk i's table is built into
@@ -543,7 +550,7 @@ void gather_kernel(GatherArgs a) {
       pipe_words(cb, i + 2);
       tab = tabs[t];   // the table lookup_block reads
       lookup_block(w, i < nc ? blk_of(i) : (c_end * a.P + PPB - 1) / PPB, pa, pb, p0);
-      load_block(w, blk_of(i + 2));
+      load_block(w, blk_of(i + 2), 0, i + 2 < nc);
     };
     __syncthreads();   // the activation slices are in LDS
     for (int i = 0; i < nc; i += 2) {
@@ -559,10 +566,10 @@ void gather_kernel(GatherArgs a) {
     load_block(wa, qa);
     for (int q = qa; q < qb; q += 2) {
       if ((q - qa) % bpc == 0) switch_chunk(c_begin + (q - qa) / bpc);
-      load_block(wb, min(q + 1, qb - 1));
+      load_block(wb, min(q + 1, qb - 1), 0, q + 1 < qb);
       lookup_block(wa, q, pa, pb, (c_begin + (q - qa) / bpc) * a.P);
       if (q + 1 < qb && (q + 1 - qa) % bpc == 0) switch_chunk(c_begin + (q + 1 - qa) / bpc);
-      load_block(wa, min(q + 2, qb - 1));
+      load_block(wa, min(q + 2, qb - 1), 0, q + 2 < qb);
       lookup_block(wb, q + 1, pa, pb, (c_begin + (q + 1 - qa) / bpc) * a.P);
     }
   } else {
@@ -577,9 +584,9 @@ void gather_kernel(GatherArgs a) {
       for (int rs = 0; rs < RSET; ++rs) {
         if (rs > 0) load_block(wa, q0, rs);
         for (int q = q0; q < q1; q += 2) {
-          load_block(wb, min(q + 1, q1 - 1), rs);
+          load_block(wb, min(q + 1, q1 - 1), rs, q + 1 < q1);
           lookup_block(wa, q, lo, hi, p0, rs);
-          load_block(wa, min(q + 2, q1 - 1), rs);
+          load_block(wa, min(q + 2, q1 - 1), rs, q + 2 < q1);
           lookup_block(wb, q + 1, lo, hi, p0, rs);
         }
       }
