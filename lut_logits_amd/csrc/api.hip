@@ -555,8 +555,9 @@ rq_status rq_lut_mlp(const rq_matrix* gate, const rq_matrix* up, const rq_matrix
     if (w.pair_tables) {
       float* tg = reinterpret_cast<float*>(base + w.tables);
       float* tu = reinterpret_cast<float*>(base + w.tables + round_up(lut_elems(gate, B) * sizeof(float), 256));
-      e = rq::launch_build_lut(gate, x, nullptr, RQ_PRO_NONE, B, 0, tg, stream);
-      if (e == hipSuccess) e = rq::launch_build_lut(up, x, nullptr, RQ_PRO_NONE, B, 0, tu, stream);
+      e = B == 1 ? rq::launch_build_lut_pair(gate, up, x, tg, tu, stream)
+                 : rq::launch_build_lut(gate, x, nullptr, RQ_PRO_NONE, B, 0, tg, stream);
+      if (e == hipSuccess && B != 1) e = rq::launch_build_lut(up, x, nullptr, RQ_PRO_NONE, B, 0, tu, stream);
       if (e != hipSuccess) return launched(e, "rq_lut_mlp: gate and up tables");
       e = rq::launch_gather_pair(gate, up, w.pgu, nullptr, tg, tu, pg, pu, stream);
     } else {

@@ -189,11 +189,18 @@ constexpr int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
 // 16-byte loads (CW chosen so CW codewords fill whole 16-byte words) and writes
 // their CW table entries. The activation slice is the same for every thread of
 // the pair and comes from cache.
+//
+// gridDim.y == 2: a second matrix of the same shape (cb2, its table lut2) on
+// the same activation, in the same launch (the MLP's gate and up).
 template <typename CbT, typename OutT, int DS>
-__global__ __launch_bounds__(kBuildThreads) void build_lut_b1_kernel(const CbT* __restrict__ cb,
+__global__ __launch_bounds__(kBuildThreads) void build_lut_b1_kernel(const CbT* __restrict__ cb1,
                                                                      const float* __restrict__ x,
                                                                      const float* __restrict__ x2, int gelu, int M,
-                                                                     int K, int64_t total, OutT* __restrict__ lut) {
+                                                                     int K, int64_t total, OutT* __restrict__ lut1,
+                                                                     const CbT* __restrict__ cb2,
+                                                                     OutT* __restrict__ lut2) {
+  const CbT* const cb = blockIdx.y ? cb2 : cb1;   // uniform
+  OutT* const lut = blockIdx.y ? lut2 : lut1;
   constexpr int ES = (int)sizeof(CbT);
   constexpr int CW = 16 / gcd_int(16, DS * ES);
   constexpr int NV = CW * DS * ES / 16;
@@ -221,16 +228,20 @@ __global__ __launch_bounds__(kBuildThreads) void build_lut_b1_kernel(const CbT* 
   }
 }
 
+// W2 (or null): a second matrix of W's shape whose table goes to lut2, in the same launch.
 template <typename CbT, typename OutT, int DS>
 bool try_b1(const rq_matrix* W, const float* x, const float* x2, int gelu, OutT* lut, hipStream_t stream,
-            hipError_t* err) {
+            hipError_t* err, const rq_matrix* W2 = nullptr, OutT* lut2 = nullptr) {
   constexpr int ES = (int)sizeof(CbT);
   constexpr int CW = 16 / gcd_int(16, DS * ES);
   if (W->d != DS || W->K % CW != 0 || ((uintptr_t)W->codebooks & 15)) return false;
+  if (W2 && ((uintptr_t)W2->codebooks & 15)) return false;
   const int64_t total = (int64_t)W->L * W->M * (W->K / CW);
-  hipLaunchKernelGGL((build_lut_b1_kernel<CbT, OutT, DS>), dim3((unsigned)((total + kBuildThreads - 1) / kBuildThreads)),
-                     dim3(kBuildThreads), 0, stream, static_cast<const CbT*>(W->codebooks), x, x2, gelu, W->M, W->K,
-                     total, lut);
+  const CbT* cb = static_cast<const CbT*>(W->codebooks);
+  hipLaunchKernelGGL((build_lut_b1_kernel<CbT, OutT, DS>),
+                     dim3((unsigned)((total + kBuildThreads - 1) / kBuildThreads), W2 ? 2u : 1u), dim3(kBuildThreads),
+                     0, stream, cb, x, x2, gelu, W->M, W->K, total, lut,
+                     W2 ? static_cast<const CbT*>(W2->codebooks) : cb, W2 ? lut2 : lut);
   *err = hipGetLastError();
   return true;
 }
@@ -265,7 +276,28 @@ hipError_t launch_typed(const rq_matrix* W, const float* x, const float* x2, int
   return hipGetLastError();
 }
 
+template <typename CbT>
+bool try_b1_pair(const rq_matrix* W, const rq_matrix* W2, const float* x, float* lut, float* lut2, hipStream_t stream,
+                 hipError_t* err) {
+  return try_b1<CbT, float, 6>(W, x, nullptr, 0, lut, stream, err, W2, lut2) ||
+         try_b1<CbT, float, 2>(W, x, nullptr, 0, lut, stream, err, W2, lut2) ||
+         try_b1<CbT, float, 8>(W, x, nullptr, 0, lut, stream, err, W2, lut2);
+}
+
 }  // namespace
+
+hipError_t launch_build_lut_pair(const rq_matrix* W, const rq_matrix* W2, const float* x, float* lut, float* lut2,
+                                 hipStream_t stream) {
+  const bool same = W->cb_dtype == W2->cb_dtype && W->L == W2->L && W->M == W2->M && W->K == W2->K &&
+                    W->d == W2->d && W->D == W2->D;
+  hipError_t e = hipSuccess;
+  if (same && (W->cb_dtype == RQ_BF16 ? try_b1_pair<uint16_t>(W, W2, x, lut, lut2, stream, &e)
+                                      : try_b1_pair<float>(W, W2, x, lut, lut2, stream, &e)))
+    return e;
+  e = launch_build_lut(W, x, nullptr, RQ_PRO_NONE, 1, 0, lut, stream);
+  if (e == hipSuccess) e = launch_build_lut(W2, x, nullptr, RQ_PRO_NONE, 1, 0, lut2, stream);
+  return e;
+}
 
 hipError_t launch_build_lut(const rq_matrix* W, const float* x, const float* x2, int prologue, int B,
                             int lut_bf16, void* lut, hipStream_t stream) {

@@ -114,6 +114,10 @@ bool fused_build_supported(const rq_matrix* W, int B);
 // Launchers: return hipSuccess or the launch error. All enqueue on `stream`.
 hipError_t launch_build_lut(const rq_matrix* W, const float* x, const float* x2, int prologue, int B,
                             int lut_bf16, void* lut, hipStream_t stream);
+// Fp32 tables of two matrices of one shape on the same vector (B = 1), in one launch where the
+// single-vector kernel takes them (else two launches): the MLP's gate and up.
+hipError_t launch_build_lut_pair(const rq_matrix* W, const rq_matrix* W2, const float* x, float* lut, float* lut2,
+                                 hipStream_t stream);
 // Outputs and workspace of one lookup+sum pass.
 struct GatherOut {
   float* partial;        // [G][B][rows] partial sums (G > 1)

@@ -25,6 +25,12 @@ MM_EXACT = [
     (1200, 96, 24, 128, 3, 64),     # d=4, L=3, four column tiles
     (700, 64, 8, 256, 1, 100),      # d=8, one code block; blocked: all 100 in one workgroup, packed10: 64 + 36
     (1, 6, 1, 1, 1, 16),            # one row, one codeword, one pair
+    # up to 16 vectors on blocked codes: half-blocks of the padded codebook copy loaded into LDS
+    (3000, 102, 17, 1000, 2, 16),   # odd M, K not a power of two
+    (1500, 96, 48, 64, 2, 12),      # d=2
+    (1200, 96, 24, 128, 3, 16),     # d=4, L=3
+    (700, 64, 8, 256, 1, 9),        # d=8, one code block
+    (2100, 96, 16, 1023, 2, 16),    # K*d not whole 16-byte words
     # 65..128 vectors on blocked codes: eight column tiles in one workgroup, half-blocks loaded into LDS
     (4097, 96, 16, 1024, 2, 128),   # d=6 at the largest K, ragged rows
     (3000, 102, 17, 1000, 2, 65),   # odd M (the last block partly empty), K not a power of two, 65 of 128
