@@ -56,6 +56,7 @@ struct GatherArgs {
   int64_t rows;
   int NP, K, B;
   int P, chunks, cpg, G, steps, S, NBT;
+  int64_t slab_rows;          // rows of a slab (the last one may be shorter)
   float* partial;             // [G][B][rows] (G > 1)
   float* out;                 // [B][rows] or null (G == 1)
   float* out2;                // second matrix of a two-matrix launch: its out
@@ -316,7 +317,9 @@ void gather_kernel(GatherArgs a) {
   const int rq = tid % QL;
   const int rl = tid / QL;
   const int b0 = bt * BT;
-  const int64_t row0 = (int64_t)s * RSET * a.steps * RPS + rl;
+  const int64_t slab_lo = (int64_t)s * a.slab_rows;
+  const int64_t slab_hi = min(slab_lo + a.slab_rows, a.rows);   // this slab's rows: [slab_lo, slab_hi)
+  const int64_t row0 = slab_lo + rl;
 
   float acc[RSET][NSTEP][BQ];
 #pragma unroll
@@ -336,7 +339,7 @@ void gather_kernel(GatherArgs a) {
   for (int rs = 0; rs < RSET; ++rs)
 #pragma unroll
     for (int st = 0; st < NSTEP; ++st) {
-      const int64_t r = min(row0 + (int64_t)(rs * a.steps + (st < a.steps ? st : 0)) * RPS, a.rows - 1);
+      const int64_t r = min(row0 + (int64_t)(rs * a.steps + (st < a.steps ? st : 0)) * RPS, slab_hi - 1);
       roff[rs][st] = (uint32_t)(r * cv.s_row * 2);
     }
   // The code stream is read with buffer loads: a scalar resource, the row
@@ -599,7 +602,7 @@ void gather_kernel(GatherArgs a) {
 #pragma unroll
       for (int st = 0; st < NSTEP; ++st) {
         const int64_t r = row0 + (int64_t)(rs * steps + st) * RPS;
-        if (st >= steps || r >= a.rows) continue;
+        if (st >= steps || r >= slab_hi) continue;
 #pragma unroll
         for (int i = 0; i < BQ; ++i) {
           const int b = b0 + rq * BQ + i;
@@ -618,7 +621,7 @@ void gather_kernel(GatherArgs a) {
 #pragma unroll
   for (int st = 0; st < NSTEP; ++st) {
     const int64_t r = row0 + (int64_t)(rs * steps + st) * RPS;
-    if (st >= steps || r >= a.rows) continue;
+    if (st >= steps || r >= slab_hi) continue;
 #pragma unroll
     for (int i = 0; i < BQ; ++i) {
       const int b = b0 + rq * BQ + i;
@@ -1185,6 +1188,18 @@ GatherPlan search_plan(int64_t rows, int NP, int K, int B, int lut_bf16, int fus
       best.G = (best.chunks + best.cpg - 1) / best.cpg;
     }
   }
+  // One vector on the pipelined kernel with fewer workgroups than CUs (the
+  // Gemma head: 63 slabs of 4,096 rows x 4 groups = 252): shorter slabs, in
+  // whole 8-row units (128-byte lines of codes), so that every CU has one
+  // workgroup and each does less (64 slabs of 4,000 rows).
+  if (best.pipe && !fused_d && BT == 1 && mats == 1 && best.NBT == 1 && best.G * (int64_t)best.S < kCUs) {
+    const int64_t S2 = kCUs / best.G;
+    const int64_t slab = ((rows + S2 - 1) / S2 + 7) / 8 * 8;
+    if (slab >= 8 && slab < (int64_t)best.steps * best.rps && (rows + slab - 1) / slab * best.G <= kCUs) {
+      best.slab = slab;
+      best.S = (int)((rows + slab - 1) / slab);
+    }
+  }
   best.lds = (size_t)(best.pipe ? 2 : 1) * best.P * K * BT * es + fused_act_bytes(best.P, best.cpg, NP, fused_d);
   return best;
 }
@@ -1408,6 +1423,7 @@ GatherArgs gather_args(const rq_matrix* W, const GatherPlan& plan, const void* l
   a.B = B;
   a.P = plan.P; a.chunks = plan.chunks; a.cpg = plan.cpg; a.G = plan.G;
   a.steps = plan.steps; a.S = plan.S; a.NBT = plan.NBT;
+  a.slab_rows = plan.slab_rows();
   a.partial = o.partial;
   a.out = o.out;
   a.softcap = o.softcap;

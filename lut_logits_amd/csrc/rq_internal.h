@@ -97,11 +97,13 @@ struct GatherPlan {
   int G;         // groups: partial sums per output, reduced in a fixed order
   int steps;     // row steps per row set
   int rps;       // rows per step
-  int S;         // row slabs of rset * steps * rps rows
+  int S;         // row slabs of slab_rows() rows
   int rset = 1;  // row sets per workgroup (2: bf16 tables in several batch tiles of 4, fp32 tables of 16 vectors)
   int NBT;       // batch tiles
   size_t lds;    // dynamic LDS bytes per workgroup
   int pipe = 0;  // fused build, d = 2: one code block per chunk, two chunks in flight (the pipelined kernel)
+  int64_t slab = 0;  // rows per slab when shorter than rset * steps * rps (0: that many)
+  int64_t slab_rows() const { return slab ? slab : (int64_t)rset * steps * rps; }
   int64_t wgs() const { return (int64_t)G * S * NBT; }
 };
 // fused != 0: the table is built while staging (fused_build_supported).
