@@ -271,3 +271,24 @@ def test_roctx_ranges_linked():
                  "rq_dense_logits", "rq_lut_logits_static", "rq_pack_codes"):
         head = src.split(f"\nrq_status {name}(", 1)[1].split("{", 1)[1]
         assert head.lstrip().startswith("CallRange range(__func__);"), name
+
+
+def _plan(W, Bn=1, lut_dtype=B.RQ_F32):
+    buf = (ctypes.c_int32 * 10)()
+    assert B.lib().rq_lut_logits_plan(ctypes.byref(W), Bn, lut_dtype, buf) == B.RQ_OK
+    return dict(zip(B.PLAN_FIELDS, list(buf)))
+
+
+@pytest.mark.parametrize("layout", [B.RQ_CODES_BLOCKED, B.RQ_CODES_PACKED10])
+def test_head_plan_fills_every_cu(layout):
+    """The single-vector plan at the Gemma head (host-side planner, no GPU): 4 groups of pairs and slabs
+    shorter than 4 x 1,024 rows, so that exactly one workgroup per CU (256) covers the 256,000 rows."""
+    p = _plan(gemma_desc(codes_layout=layout))
+    assert p["BT"] == 1 and p["G"] == 4 and p["steps"] == 4 and p["rps"] == 1024, p
+    assert p["S"] == 64 and p["G"] * p["S"] == 256, p
+
+
+def test_tall_matrix_plan_keeps_full_slabs():
+    """A matrix tall enough that its slabs give a workgroup per CU or more keeps slabs of steps x rows per step."""
+    p = _plan(gemma_desc(rows=2_000_000))
+    assert p["S"] == -(-2_000_000 // (p["steps"] * p["rps"])), p
