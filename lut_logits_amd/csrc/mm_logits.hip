@@ -1119,10 +1119,11 @@ __global__ __launch_bounds__(kPadThreads) void mm_pad_kernel(MmArgs a) {
 #pragma unroll
   for (int j = 0; j < T; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // The h fragments and the first four row tiles' codewords are read first
-  // (begin_reads), before the step issues its copy and code loads, so their LDS
-  // latency runs under those issues; then the codewords of the next four row
-  // tiles are read while the current four compute.
+  // Right after the barrier the step issues the next half-block's copy (so it
+  // has the whole step to land), then reads the h fragments and the first four
+  // row tiles' codewords (begin_reads), then the code loads; the codewords of
+  // the next four row tiles are read while the current four compute. (Reads
+  // first and the copy after them measured 4-5% slower per B=16 call.)
   constexpr int kI = 4;
   constexpr int kGroups = T / kI;
   bf16x8 hb[kParts];
@@ -1174,11 +1175,11 @@ __global__ __launch_bounds__(kPadThreads) void mm_pad_kernel(MmArgs a) {
       if constexpr (hs == 1) RQ_WAIT_VMCNT_LDS(NV);
       else RQ_WAIT_VMCNT_LDS(0);
       __builtin_amdgcn_s_barrier();
-      if constexpr (hs == 0) arranged(raw, cur);
-      begin_reads(st & 1, cur, hs);
-      __builtin_amdgcn_sched_barrier(0);
       const int st1 = st + 1;
       copy_half(st1 & 1, min(q0 + (st1 >> 1), qlast), st1 & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (hs == 0) arranged(raw, cur);
+      begin_reads(st & 1, cur, hs);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (hs == 0) load_codes(nxt, min(q0 + (st >> 1) + 1, qlast));
       __builtin_amdgcn_sched_barrier(0);
