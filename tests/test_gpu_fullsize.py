@@ -63,6 +63,27 @@ def test_gemma_head_one_call_full(name, layout):
     print(f"{name} {layout} one call: worst |gpu-oracle|/max|oracle| = {worst:.2e}")
 
 
+def test_gemma_head_b16_one_workspace_calls():
+    """rq_logits at B=16 on the full head, three calls on one workspace with other hidden vectors in between:
+    nothing a call leaves in the workspace (split vectors, padded codebooks, partial sums, keys) reaches the
+    next one (the second call's logits against the oracle; the third, on the first call's vectors,
+    bit-identical to the first)."""
+    cfg = synth.CONFIGS["gemma_b16"]
+    mat, h1, _ = synth.make_head(cfg)
+    h2 = synth.gen_hidden(np.random.default_rng(77), cfg.B, mat.D)
+    W = to_dev(mat)
+    ws = torch.zeros(la.logits_workspace(W, cfg.B, 0), dtype=torch.uint8, device="cuda")
+    lg1, am1, _, _ = la.logits(W, dev(h1), softcap=cfg.softcap, ws=ws)
+    first = host(lg1).copy()
+    lg2, am2, _, _ = la.logits(W, dev(h2), softcap=cfg.softcap, ws=ws)
+    _, ref2 = oracle_head(mat, h2, cfg.softcap)
+    check_logits(host(lg2), ref2)
+    check_argmax(host(am2), host(lg2), ref2)
+    lg3, am3, _, _ = la.logits(W, dev(h1), softcap=cfg.softcap, ws=ws)
+    assert np.array_equal(host(lg3), first)
+    assert np.array_equal(host(am3), host(am1))
+
+
 def test_stress_head_full():
     """Stress head: K=4096, L=4, B=64, bf16 table, softcap 30 and per-vector top-50."""
     cfg = synth.CONFIGS["stress"]
